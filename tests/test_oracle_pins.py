@@ -1,0 +1,431 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these tests re-types an oracle formula and compares it with itself:
+each checks a printed value, a closed form, an invariant, a brute-force
+evaluation with exact rational arithmetic, or an independent library
+conversion.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+from workloads import C1, make_layer
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+# ------------------------------------------------------------------ rounding
+def test_round_binary_matches_ieee_casts():
+    rng = np.random.default_rng(1)
+    y = np.concatenate([
+        rng.standard_normal(200000) * np.exp2(rng.integers(-30, 30, 200000)),
+        rng.standard_normal(20000) * 1e-6,      # fp16 subnormals
+        np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, 1e-8, 6e-8, 3e-8]),
+    ])
+    assert np.array_equal(O.to_fp32(y), y.astype(np.float32).astype(np.float64))
+    assert np.array_equal(O.to_fp16(y), y.astype(np.float16).astype(np.float64))
+
+
+def test_round_bf16_matches_torch_and_hand_cases():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(2)
+    f = (rng.standard_normal(100000) * np.exp2(rng.integers(-60, 60, 100000))).astype(np.float32)
+    ref = torch.from_numpy(f).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.to_bf16(f.astype(np.float64)), ref)
+    one = 1.0
+    # 1 + 2^-8 is the midpoint of 1 and 1 + 2^-7: ties to even (1.0)
+    assert O.to_bf16(one + 2.0 ** -8) == 1.0
+    assert O.to_bf16(one + 3 * 2.0 ** -8) == one + 2 * 2.0 ** -7
+    # a hair above the midpoint rounds up even though the fp32 value would tie
+    assert O.to_bf16(one + 2.0 ** -8 + 2.0 ** -40) == one + 2.0 ** -7
+
+
+# ------------------------------------------------------------ eq. (1), INT4
+def _int4_one_group(vals):
+    v = np.zeros(64)
+    v[: len(vals)] = vals
+    q, s = O.quantize_int4_groups(v[None, :])
+    return q[0, : len(vals)], s[0, 0]
+
+
+def test_int4_hand_worked_unit_scale():
+    # max |x| = 7 gives s = 7/7 = 1 exactly, so codes are round-half-even of x
+    q, s = _int4_one_group([7.0, 2.5, -2.5, 3.5, 0.5, -0.5, 1.5, -7.0, 6.49, -3.51])
+    assert s == 1.0
+    assert q.tolist() == [7, 2, -2, 4, 0, 0, 2, -7, 6, -4]
+    # -0.5 rounds to zero and is encoded +0
+    assert O.int4_nibble(q).tolist()[5] == 0
+
+
+def test_int4_hand_worked_fp16_scale():
+    # max |x| = 1.4: 1.4/7 = 0.2 -> fp16 0.199951171875 (= 3276 * 2^-14)
+    q, s = _int4_one_group([1.4, 0.7, -0.1, 0.05])
+    assert s == 0.199951171875
+    # 0.7 / s = 3.50085... -> 4 ; 1.4 / s = 7.0017 -> 7 ; 0.1/s = 0.50012 -> 1
+    assert q.tolist() == [7, 4, -1, 0]
+
+
+def test_int4_zero_group_and_exact_ties():
+    q, s = _int4_one_group([0.0, -0.0])
+    assert s == 0.0 and q.tolist() == [0, 0]
+    # s = fp16(5/7) = 0.71435546875; put values exactly on (k + 1/2) s and one
+    # fp32 ulp either side of it
+    s_expect = O.to_fp16(5.0 / 7.0)
+    ties = [(k + 0.5) * s_expect for k in range(0, 6)]
+    up = [np.nextafter(np.float32(t), np.float32(10)) for t in ties]
+    dn = [np.nextafter(np.float32(t), np.float32(-10)) for t in ties]
+    vals = [5.0] + ties + [float(u) for u in up] + [float(d) for d in dn]
+    q, s = _int4_one_group(vals)
+    assert s == s_expect
+    k = np.arange(6)
+    assert q[1:7].tolist() == [int(x) for x in np.where(k % 2 == 0, k, k + 1)]
+    assert q[7:13].tolist() == (k + 1).tolist()
+    assert q[13:19].tolist() == k.tolist()
+
+
+def test_int4_matches_exact_rational_brute_force():
+    """Scalar re-derivation with Fractions: A, s, and round-half-even of x/s."""
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((3, 192)) * np.exp2(rng.integers(-8, 8, (3, 1)))).astype(np.float32)
+    x[0, :64] = np.round(x[0, :64] * 4) / 4            # many exact ties
+    q, s = O.quantize_int4_groups(x.astype(np.float64))
+    for i in range(3):
+        for g in range(3):
+            grp = [Fraction(float(v)) for v in x[i, 64 * g: 64 * g + 64]]
+            A = max(abs(v) for v in grp)
+            s_ref = Fraction(float(np.float16(float(A / 7))))   # fp16 of the exact quotient
+            # np.float16(float(A/7)): A/7 rounded to fp64 first; fp64 has
+            # enough precision for the fp16 rounding to be unaffected
+            assert s[i, g] == float(s_ref)
+            for j, v in enumerate(grp):
+                ref = 0 if s_ref == 0 else max(-7, min(7, round(v / s_ref)))
+                assert q[i, 64 * g + j] == ref
+
+
+def test_fp16_scale_double_rounding_is_innocuous():
+    """fp16(fp32(A/7)) == fp16(A/7) for fp32 A (the GPU divides in fp32)."""
+    rng = np.random.default_rng(4)
+    A = (rng.random(400000) * np.exp2(rng.integers(-30, 16, 400000))).astype(np.float32)
+    # plus A = 7 m (and fp32 neighbours) for fp16 midpoints m
+    h = (rng.random(50000) * 8 + 2.0 ** -10).astype(np.float16).astype(np.float64)
+    m = h + np.exp2(np.floor(np.log2(h)) - 11)
+    a0 = (7 * m).astype(np.float32)
+    near = [a0]
+    for _ in range(3):
+        near.append(np.nextafter(near[-1], np.float32(np.inf)))
+    lo = [a0]
+    for _ in range(3):
+        lo.append(np.nextafter(lo[-1], np.float32(0)))
+    A = np.concatenate([A] + near + lo)
+    via32 = (A / np.float32(7.0)).astype(np.float16).astype(np.float64)
+    assert np.array_equal(via32, O.to_fp16(A.astype(np.float64) / 7.0))
+
+
+# ------------------------------------------------------------- FP4 E2M1/E8M0
+def test_e8m0_boundaries():
+    A = np.array([6.0, 6.0 * (1 + 2.0 ** -23), 3.0, 3.0000001, 1.5, 0.0,
+                  6.0 * 2.0 ** 100, 1e-45, 2.0 ** -130])
+    e = O.e8m0_exponent(A)
+    assert e.tolist() == [0, 1, -1, 0, -2, -127, 100, -127, -127]
+    rng = np.random.default_rng(5)
+    a = rng.random(100000) * np.exp2(rng.integers(-100, 100, 100000))
+    e = O.e8m0_exponent(a).astype(np.float64)
+    assert np.all(a <= 6 * np.exp2(e)) and np.all(a > 6 * np.exp2(e - 1))
+
+
+def test_e2m1_midpoints_and_grid():
+    y = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    assert O.e2m1_value(O.e2m1_code(y)).tolist() == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]
+    eps = 1e-9
+    assert O.e2m1_value(O.e2m1_code(y + eps)).tolist() == [0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert O.e2m1_value(O.e2m1_code(y - eps)).tolist() == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0]
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
+    assert O.e2m1_code(grid).tolist() == list(range(8))
+    assert O.e2m1_code(-grid).tolist() == [0] + [8 + i for i in range(1, 8)]
+    assert O.e2m1_code(np.array([-0.2, -0.0])).tolist() == [0, 0]   # +0 encoding
+
+
+def test_fp4_group_quant_brute_force():
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal((2, 64)) * 3).astype(np.float32).astype(np.float64)
+    codes, e = O.quantize_fp4_groups(x)
+    grid = [Fraction(v) for v in (0, .5, 1, 1.5, 2, 3, 4, 6)]
+    for i in range(2):
+        for g in range(2):
+            vals = [Fraction(float(v)) for v in x[i, 32 * g: 32 * g + 32]]
+            A = max(abs(v) for v in vals)
+            ee = -200
+            while A > 6 * Fraction(2) ** ee:
+                ee += 1
+            assert e[i, g] == ee
+            for j, v in enumerate(vals):
+                y = abs(v) / Fraction(2) ** ee
+                d = [abs(y - gv) for gv in grid]
+                best = min(d)
+                cands = [k for k in range(8) if d[k] == best]
+                k = cands[0] if len(cands) == 1 else [c for c in cands if c % 2 == 0][0]
+                sgn = 8 if (v < 0 and k > 0) else 0
+                assert codes[i, 32 * g + j] == (k | sgn)
+
+
+def test_nibble_packing_layout():
+    nib = np.array([[1, 2, 3, 4, 15, 8]], dtype=np.uint8)
+    assert O.pack_nibbles(nib).tolist() == [[0x21, 0x43, 0x8F]]
+    assert np.array_equal(O.unpack_nibbles(O.pack_nibbles(nib)), nib)
+    assert O.nibble_to_int4(O.int4_nibble(np.arange(-7, 8))).tolist() == list(range(-7, 8))
+
+
+# ------------------------------------------------------- smoothing and split
+def _c1_small():
+    X, W, _ = make_layer(C1)
+    return X, W
+
+
+def test_smoothing_equivalence():
+    X, Wb = _c1_small()
+    Xf = O.bf16_bits_to_f64(X)
+    W = O.bf16_bits_to_f64(Wb)
+    a = O.act_absmax(X)
+    assert np.array_equal(a, np.abs(Xf).max(axis=0))
+    # exact lambda: X diag(lam)^-1 diag(lam) W = X W to fp64 rounding
+    lam = a.astype(np.float64) ** 0.5 / np.abs(W).max(axis=1) ** 0.5
+    Y = Xf @ W
+    assert O.rel_fro((Xf / lam) @ (lam[:, None] * W), Y) < 1e-12
+    # stored (lam32, inv32) pair with fp32 x_hat
+    lam32, inv32 = O.smoothing_factors(a, W, 0.5)
+    assert np.all(np.abs(lam32 * inv32 - 1) < 2 ** -23)
+    xh = O.smooth_act(X, inv32)
+    assert O.rel_fro(xh @ (lam32[:, None] * W), Y) < 1e-6
+    # smoothing flattens the activation outliers (channels 0-3 were x50):
+    # with alpha = 0.5 the outlier-to-typical ratio of channel maxima drops
+    # roughly to its square root
+    before = a[:4].max() / np.median(a)
+    ah = np.abs(xh).max(axis=0)
+    after = ah[:4].max() / np.median(ah)
+    assert before > 40 and after < before / 4
+
+
+def test_smoothing_degenerate_channels():
+    a = np.array([0.0, 4.0, 4.0], np.float32)
+    W = np.array([[1.0, -2.0], [0.0, 0.0], [0.5, 0.25]])
+    lam32, inv32 = O.smoothing_factors(a, W, 0.5)
+    assert lam32.tolist()[:2] == [1.0, 1.0]
+    assert lam32[2] == O.to_fp32(np.sqrt(4.0) / np.sqrt(0.5))
+    lam32, _ = O.smoothing_factors(a, W, 0.5, no_smoothing=True)
+    assert lam32.tolist() == [1.0, 1.0, 1.0]
+
+
+def test_eckart_young_on_known_spectrum():
+    rng = np.random.default_rng(7)
+    K, N, r = 96, 80, 8
+    U, _ = np.linalg.qr(rng.standard_normal((K, K)))
+    V, _ = np.linalg.qr(rng.standard_normal((N, N)))
+    sig = np.sort(rng.random(N) * 10)[::-1]
+    sig[:4] += 50
+    W = (U[:, :N] * sig) @ V.T
+    L1, L2 = O.lowrank_factors(W, r)
+    best = (U[:, :r] * sig[:r]) @ V[:, :r].T
+    assert O.rel_fro(L1 @ L2, best) < 1e-10
+    assert abs(np.linalg.norm(W - L1 @ L2) - np.sqrt(np.sum(sig[r:] ** 2))) < 1e-9 * sig[0]
+    # L2 rows are orthonormal, L1 columns carry the singular values
+    assert np.allclose(L2 @ L2.T, np.eye(r), atol=1e-12)
+    assert np.allclose(np.linalg.norm(L1, axis=0), sig[:r], rtol=1e-12)
+
+
+def test_exact_split_and_residual_order():
+    X, Wb = _c1_small()
+    prep = O.prepare(Wb, O.act_absmax(X), alpha=0.5, rank=16, fmt=O.INT4)
+    recon = prep["L1b"] @ prep["L2b"] + prep["R"]
+    assert np.max(np.abs(recon - prep["W_hat"])) < 1e-13 * np.abs(prep["W_hat"]).max()
+    # an exactly rank-r product of the stored factors leaves no residual
+    L1b, L2b = prep["L1b"], prep["L2b"]
+    P = L1b @ L2b
+    assert np.max(np.abs(O.residual(P, L1b, L2b))) <= 1e-14 * np.abs(P).max()
+    # the low-rank branch absorbs the outliers (walkthrough Fig. 4: the
+    # residual's range is much narrower than W_hat's) ...
+    assert np.abs(prep["R"]).max() < 0.5 * np.abs(prep["W_hat"]).max()
+    # ... and rounding the factors to bf16 costs only second order in ||R||
+    sig = np.linalg.svd(prep["W_hat"], compute_uv=False)
+    opt = np.sqrt(np.sum(sig[16:] ** 2))
+    assert opt <= np.linalg.norm(prep["R"]) <= opt * (1 + 1e-4)
+
+
+# ------------------------------------------------------------ linear layer
+def _brute_linear(prep, X_bits, act):
+    """Triple loop from the group-wise definition (eq. (2) per group + low-rank + bias)."""
+    fmt = prep["fmt"]
+    g = O.GROUP[fmt]
+    M, K = X_bits.shape
+    N = prep["N"]
+    Tb = O.down_proj(act["xhat"], prep["L1b"])[1]
+    Y = np.zeros((M, N))
+    for i in range(M):
+        for n in range(N):
+            acc = 0.0
+            for gi in range(K // g):
+                if fmt == O.INT4:
+                    sx, sw = act["scales"][i, gi], prep["w_scales"][gi, n]
+                    p = sum(int(act["codes"][i, k]) * int(prep["w_codes"][k, n])
+                            for k in range(gi * g, gi * g + g))
+                else:
+                    sx = 2.0 ** act["scales"][i, gi]
+                    sw = 2.0 ** prep["w_scales"][gi, n]
+                    p = sum(O.e2m1_value(act["codes"][i, k]) * O.e2m1_value(prep["w_codes"][k, n])
+                            for k in range(gi * g, gi * g + g))
+                acc += sx * sw * p
+            for t in range(prep["rank"]):
+                acc += Tb[i, t] * prep["L2b"][t, n]
+            if prep["bias"] is not None:
+                acc += prep["bias"][n]
+            Y[i, n] = acc
+    return Y
+
+
+@pytest.mark.parametrize("fmt", [O.INT4, O.FP4])
+def test_linear_matches_brute_force(fmt):
+    rng = np.random.default_rng(8)
+    M, K, N, r = 5, 128, 6, 4
+    X = O.bf16_bits_of(O.to_bf16(rng.standard_normal((M, K)) * 2).astype(np.float32))
+    W = O.bf16_bits_of(O.to_bf16(rng.standard_normal((K, N)) * 0.1).astype(np.float32))
+    b = O.bf16_bits_of(O.to_bf16(rng.standard_normal(N)).astype(np.float32))
+    prep = O.prepare(W, O.act_absmax(X), alpha=0.5, rank=r, fmt=fmt, bias_bits=b)
+    res = O.linear(prep, X, out="f32")
+    ref = _brute_linear(prep, X, res["act"])
+    assert np.max(np.abs(res["Y64"] - ref)) <= 1e-12 * np.abs(ref).max()
+
+
+def test_lossless_special_case():
+    """lambda = 1, r = 0, integer X and W in [-7, 7] with a 7 in every group:
+    every scale is 1 and the layer is exactly X W."""
+    rng = np.random.default_rng(9)
+    M, K, N = 16, 256, 24
+    X = rng.integers(-7, 8, (M, K)).astype(np.float64)
+    W = rng.integers(-7, 8, (K, N)).astype(np.float64)
+    X[:, ::64] = 7
+    W[::64, :] = -7
+    Xb = O.bf16_bits_of(X.astype(np.float32))
+    Wb = O.bf16_bits_of(W.astype(np.float32))
+    prep = O.prepare(Wb, O.act_absmax(Xb), alpha=0.5, rank=0, fmt=O.INT4, no_smoothing=True)
+    res = O.linear(prep, Xb, out="f32")
+    assert np.all(res["act"]["scales"] == 1.0) and np.all(prep["w_scales"] == 1.0)
+    assert np.array_equal(res["Y64"], X @ W)
+
+
+def test_eq6_residual_error_identity():
+    """With an exact low-rank branch, the layer error equals E(X_hat, R)."""
+    X, Wb = _c1_small()
+    prep = O.prepare(Wb, O.act_absmax(X), alpha=0.5, rank=16, fmt=O.INT4, no_smoothing=True)
+    res = O.linear(prep, X, out="f32")
+    xh = res["act"]["xhat"]                       # lambda = 1: x_hat is X exactly (bf16)
+    assert np.array_equal(O.to_bf16(xh), xh)
+    Y_exactT = res["main"] + res["T"] @ prep["L2b"]
+    lhs = np.linalg.norm(xh @ prep["W_hat"] - Y_exactT)
+    Qx = O.dequant_groups(res["act"]["codes"], res["act"]["scales"], O.INT4)
+    QR = O.dequant_groups(prep["w_codes"].T, prep["w_scales"].T, O.INT4).T
+    rhs = O.quant_error(xh, prep["R"], Qx, QR)
+    assert abs(lhs - rhs) <= 1e-9 * rhs
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_prop41_bound_random(seed):
+    rng = np.random.default_rng(100 + seed)
+    M, K, N = rng.integers(1, 40), 64 * rng.integers(1, 4), rng.integers(1, 40)
+    X = rng.standard_normal((M, K)) * np.exp(rng.standard_normal(K))[None, :]
+    W = rng.standard_normal((K, N))
+    QX = O.dequant_groups(*O.quantize_int4_groups(X), O.INT4)
+    QWt = O.dequant_groups(*O.quantize_int4_groups(W.T), O.INT4)
+    assert O.quant_error(X, W, QX, QWt.T) <= O.prop41_bound(X, W, QX, QWt.T) * (1 + 1e-12)
+    Xf = O.dequant_groups(*O.quantize_fp4_groups(X), O.FP4)
+    Wf = O.dequant_groups(*O.quantize_fp4_groups(W.T), O.FP4).T
+    assert O.quant_error(X, W, Xf, Wf) <= O.prop41_bound(X, W, Xf, Wf) * (1 + 1e-12)
+
+
+def test_eq8_gaussian_residual_bound_monte_carlo():
+    """eq. (8) with eq. (12)-(14)'s c: E||R - Q(R)|| <= c sqrt(n)/q_max E||R||."""
+    rng = np.random.default_rng(11)
+    n_side = 64
+    errs, norms = [], []
+    for _ in range(30):
+        R = rng.standard_normal((n_side, n_side)) * 0.3
+        errs.append(np.linalg.norm(R - O.fake_quant(R, 4)))
+        norms.append(np.linalg.norm(R))
+    size = n_side * n_side
+    c = O.gaussian_c(size)
+    assert np.mean(errs) <= c * np.sqrt(size) / 7 * np.mean(norms)
+    # eq. (12): E max|R| <= sigma sqrt(2 log size); eq. (13): E||R|| >= sigma sqrt(2 size / pi)
+    Rs = rng.standard_normal((200, size))
+    assert np.abs(Rs).max(axis=1).mean() <= np.sqrt(2 * np.log(size))
+    assert np.linalg.norm(Rs, axis=1).mean() >= np.sqrt(2 * size / np.pi)
+
+
+def test_unfused_rounding_model_differs_only_by_double_rounding():
+    X, Wb = _c1_small()
+    prep = O.prepare(Wb, O.act_absmax(X), alpha=0.5, rank=16, fmt=O.INT4)
+    fused = O.linear(prep, X, out="bf16")
+    unf = O.linear_unfused(prep, X, out="bf16")
+    assert O.rel_fro(unf["Y"], fused["Y64"]) < 1e-2
+    assert O.rel_fro(fused["Y"], fused["Y64"]) < 5e-3
+
+
+# ---------------------------------------------------- the handbook's tables
+def _handbook_inputs():
+    torch = pytest.importorskip("torch")
+    torch.manual_seed(0)
+    base = torch.randn(1024, 512).double().numpy()
+    W = (torch.randn(512, 512) * 0.02).double().numpy()
+    return base, W
+
+
+def _smooth_plain(x, W, alpha=0.5):
+    """The handbook's per-channel smoothing, through the oracle's factors."""
+    lam32, inv32 = O.smoothing_factors(np.abs(x).max(axis=0), W, alpha)
+    return x * inv32[None, :], W * lam32[:, None]
+
+
+def test_handbook_printed_tables():
+    gold = json.load(open(os.path.join(HERE, "golden", "handbook_toy_tables.json")))
+    base, W = _handbook_inputs()
+    tol = 6e-5   # printed to 4 decimals; the page computed in fp32
+    for factor, row in gold["outlier_table"]["rows"].items():
+        x = base.copy()
+        x[:, :4] *= float(factor)
+        got = [O.rel_fro(O.fake_quant(x, 8)[:, 4:], x[:, 4:]),
+               O.rel_fro(O.fake_quant(x, 8, axis=0)[:, 4:], x[:, 4:]),
+               O.rel_fro(O.fake_quant(x, 4)[:, 4:], x[:, 4:]),
+               O.rel_fro(O.fake_quant(x, 4, axis=0)[:, 4:], x[:, 4:])]
+        assert np.allclose(got, row, atol=tol), (factor, got, row)
+    x = base.copy()
+    x[:, :4] *= 50
+    y = x @ W
+    sq = gold["smoothquant_table"]
+    xs, Ws = _smooth_plain(x, W)
+    assert abs(O.rel_fro(O.fake_quant(x, 8) @ O.fake_quant(W, 8), y) - sq["w8a8_direct"]) < tol
+    assert abs(O.rel_fro(O.fake_quant(xs, 8) @ O.fake_quant(Ws, 8), y) - sq["w8a8_smooth"]) < tol
+    assert abs(O.rel_fro(O.fake_quant(x, 4) @ O.fake_quant(W, 4), y) - sq["w4a4_direct"]) < tol
+    assert abs(O.rel_fro(O.fake_quant(xs, 4) @ O.fake_quant(Ws, 4), y) - sq["w4a4_smooth"]) < tol
+    for r, want in gold["svdquant_table"]["rank"].items():
+        r = int(r)
+        L1, L2 = O.lowrank_factors(Ws, r)
+        R = O.residual(Ws, L1, L2)
+        yq = O.fake_quant(xs, 4) @ O.fake_quant(R, 4) + xs @ L1 @ L2
+        assert abs(O.rel_fro(yq, y) - want) < tol, (r, O.rel_fro(yq, y), want)
+    floor = O.rel_fro(O.fake_quant(base, 4) @ O.fake_quant(W, 4), base @ W)
+    assert abs(floor - gold["svdquant_table"]["no_outlier_w4a4_floor"]) < tol
+
+
+def test_error_ordering_on_tiny_config():
+    """Naive W4A4 > smoothing only > SVDQuant, and error falls with rank."""
+    X, Wb = _c1_small()
+    Xf, W = O.bf16_bits_to_f64(X), O.bf16_bits_to_f64(Wb)
+    y = Xf @ W
+    a = O.act_absmax(X)
+    naive = O.prepare(Wb, a, alpha=0.5, rank=0, fmt=O.INT4, no_smoothing=True)
+    errs = [O.rel_fro(O.linear(naive, X, "f32")["Y64"], y)]
+    for r in (0, 16, 32, 64):
+        p = O.prepare(Wb, a, alpha=0.5, rank=r, fmt=O.INT4)
+        errs.append(O.rel_fro(O.linear(p, X, "f32")["Y64"], y))
+    assert all(errs[i] > errs[i + 1] for i in range(len(errs) - 1)), errs

@@ -1,0 +1,216 @@
+/*
+ * svdq.h - C ABI of libsvdq: the SVDQuant W4A4 linear layer with its 16-bit
+ * low-rank branch fused into the 4-bit branch, for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The layer (SVDQuant paper walkthrough, devpress.csdn.net, eq. (5)):
+ *
+ *     Y = X W ~= (X diag(lambda)^-1) L1 L2  +  Q(X diag(lambda)^-1) Q(R)  + b
+ *
+ * with W (K x N) smoothed to W_hat = diag(lambda) W, split by a top-r SVD into
+ * L1 L2 (K x r, r x N, kept in bf16) and a residual R = W_hat - L1 L2 that is
+ * quantized to 4 bits.  Fused execution (the Nunchaku design, walkthrough
+ * Fig. 6): one kernel reads X once to produce the 4-bit activation codes and
+ * the down-projection X_hat L1; a second kernel runs the 4-bit GEMM and adds
+ * the up-projection (X_hat L1) L2 into the same accumulators.
+ *
+ * Conventions shared by every call
+ *  - Every entry point returns an svdq_status; 0 (SVDQ_OK) is success.  No
+ *    C++ exception, abort or exit crosses this boundary.
+ *  - Arguments are validated on the host before any GPU work; an invalid call
+ *    launches nothing and writes nothing.
+ *  - Pointers named d_* are device pointers (HIP device memory of the current
+ *    device); all other pointers are host pointers.  The caller owns every
+ *    buffer; the library keeps no pointer after a call returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Hot
+ *    path calls (svdq_act_absmax, svdq_quantize_act, svdq_linear,
+ *    svdq_linear_unfused) are asynchronous and stream-ordered: they enqueue
+ *    kernels and return.  They allocate nothing and may run concurrently on
+ *    different streams when their output buffers differ.
+ *  - Tensors are dense row-major with the leading dimension equal to the row
+ *    length, and 16-byte aligned.  bf16 is passed as raw 16-bit patterns.
+ *  - W is in the paper's orientation, K x N with Y = X W (walkthrough, eq.
+ *    (3): X in R^{b x m}, W in R^{m x n}); an nn.Linear weight is its
+ *    transpose.
+ *  - The device must be gfx950; any other device gives
+ *    SVDQ_ERR_UNSUPPORTED_DEVICE (unsupported GPU generations are refused
+ *    at load time, as the Diffusers/Nunchaku integration page describes for
+ *    its 4-bit operators).
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum svdq_status {
+  SVDQ_OK = 0,
+  SVDQ_ERR_INVALID_ARGUMENT = 1,   /* NULL pointer, bad enum, alpha out of [0,1] ... */
+  SVDQ_ERR_UNSUPPORTED_SHAPE = 2,  /* K, N, r or M outside the supported set */
+  SVDQ_ERR_UNSUPPORTED_DEVICE = 3, /* no device, or not gfx950 */
+  SVDQ_ERR_BUFFER_TOO_SMALL = 4,   /* prepared / workspace buffer smaller than required */
+  SVDQ_ERR_HIP = 5,                /* a HIP runtime call or a launch failed */
+  SVDQ_ERR_BAD_BLOB = 6,           /* prepared blob header does not match the descriptor */
+  SVDQ_ERR_MISALIGNED = 7          /* a pointer is not 16-byte aligned */
+} svdq_status;
+
+/* 4-bit formats (quantizer of eq. (1) of the walkthrough, applied per group
+ * along K).
+ *  SVDQ_INT4_G64_FP16: signed integer codes in [-7, 7] (q_max = 2^3 - 1),
+ *    one fp16 scale per 64 consecutive K elements (the quantization handbook's
+ *    "one scale per 64 elements"), s = fp16(max|v| / 7), codes
+ *    clamp(round_half_even(v / s)) of the exact quotient; s = 0 -> codes 0.
+ *    Codes are two's-complement nibbles.
+ *  SVDQ_FP4_E2M1_G32_E8M0: 4-bit float codes (sign, 2 exponent bits, 1
+ *    mantissa bit; q_max = 6 as the walkthrough states for 4-bit floats), one
+ *    power-of-two scale 2^e per 32 K elements stored as an E8M0 byte e + 127,
+ *    e the smallest integer with max|v| <= 6 * 2^e (clamped to [-127, 127];
+ *    an all-zero group has e = -127); codes round to nearest, ties to the
+ *    even code, and a value that rounds to zero is encoded +0.
+ * Two codes per byte; the even-K element is in the low nibble. */
+typedef enum svdq_format {
+  SVDQ_INT4_G64_FP16 = 0,
+  SVDQ_FP4_E2M1_G32_E8M0 = 1
+} svdq_format;
+
+typedef enum svdq_out_dtype {
+  SVDQ_OUT_BF16 = 0,  /* Y stored as bf16 (round to nearest even) */
+  SVDQ_OUT_F32 = 1    /* Y stored as fp32 */
+} svdq_out_dtype;
+
+enum {
+  SVDQ_F_NO_SMOOTHING = 1u,  /* lambda = 1 (smoothing already folded into the previous op) */
+  SVDQ_F_FACTORS_GIVEN = 2u, /* caller supplies L1, L2 instead of the SVD */
+  SVDQ_F_HAS_BIAS = 4u       /* the layer has a bias vector b (N) */
+};
+
+/* One layer.  Supported: K % 128 == 0, 128 <= K <= 65536; N % 64 == 0,
+ * 64 <= N <= 65536; rank % 16 == 0, 0 <= rank <= 128, rank <= min(K, N);
+ * 0 <= alpha <= 1.  rank = 0 is plain per-group W4A4. */
+typedef struct svdq_layer_desc {
+  int32_t K;        /* input features */
+  int32_t N;        /* output features */
+  int32_t rank;     /* r, width of the low-rank branch */
+  int32_t fmt;      /* svdq_format */
+  float alpha;      /* smoothing migration strength (0.5 in the pages) */
+  uint32_t flags;   /* SVDQ_F_* */
+} svdq_layer_desc;
+
+/* Text for a status code (static storage; never NULL). */
+const char* svdq_status_string(int status);
+
+/* Library version, as major * 10000 + minor * 100 + patch. */
+int svdq_version(void);
+
+/* Size in bytes of the prepared-weight blob for `desc`, or 0 if `desc` is
+ * NULL or invalid.  The blob is position-independent (a 256-byte header with
+ * byte offsets) and may be copied, saved and reloaded byte for byte. */
+size_t svdq_prepared_bytes(const svdq_layer_desc* desc);
+
+/* Device workspace that svdq_linear / svdq_linear_unfused need for M tokens:
+ * the packed activation codes (M x K/2 bytes), the activation scales and the
+ * bf16 down-projection (M x rank); 0 if arguments are invalid. */
+size_t svdq_workspace_bytes(const svdq_layer_desc* desc, int M, int unfused);
+
+/* Byte sizes of svdq_quantize_act's three outputs for M tokens (codes,
+ * scales, T).  Any output pointer may be NULL.  Returns SVDQ_OK or
+ * SVDQ_ERR_INVALID_ARGUMENT / SVDQ_ERR_UNSUPPORTED_SHAPE. */
+svdq_status svdq_act_sizes(const svdq_layer_desc* desc, int M, size_t* codes_bytes,
+                           size_t* scales_bytes, size_t* t_bytes);
+
+/* Calibration statistic for the smoothing factors (quantization handbook,
+ * SmoothQuant section: lambda_j uses max_i |X_ij| over calibration
+ * activations): d_absmax[j] = max_i |X[i, j]| over the M x K bf16 matrix
+ * d_X.  With accumulate != 0 the result is max'ed into the existing
+ * d_absmax (several calibration batches).  Asynchronous. */
+svdq_status svdq_act_absmax(const void* d_X, int M, int K, float* d_absmax, int accumulate,
+                            void* stream);
+
+/* Offline preparation of one layer (walkthrough eq. (5); handbook
+ * SmoothQuant and SVDQuant sections):
+ *   lambda_j = a_j^alpha / w_j^(1-alpha), a = d_act_absmax, w_j = max_n |W[j,n]|
+ *     (lambda = 1 where a_j or w_j is 0, or with SVDQ_F_NO_SMOOTHING);
+ *     stored as fp32 lambda and fp32 1/lambda;
+ *   W_hat = lambda * W (fp64); top-`rank` SVD W_hat ~ L1 L2 with
+ *     L1 = U_r Sigma_r, L2 = V_r^T (randomized subspace iteration on the GPU
+ *     with a Rayleigh-Ritz step), stored in bf16 - or, with
+ *     SVDQ_F_FACTORS_GIVEN, the caller's d_L1 (K x r bf16) and d_L2
+ *     (r x N bf16);
+ *   R = W_hat - L1b L2b (fp64, summed over t in increasing order);
+ *   R group-quantized along K for every output column, in `desc->fmt`, and
+ *   packed into the blob's GEMM-native layout; bias (bf16, N) stored as fp32.
+ * d_W: K x N bf16.  d_act_absmax: K fp32 (may be NULL only with
+ * SVDQ_F_NO_SMOOTHING).  d_bias: N bf16, required iff SVDQ_F_HAS_BIAS.
+ * d_prepared: device buffer of prepared_bytes >= svdq_prepared_bytes(desc).
+ * Synchronous: returns after the blob is complete.  Allocates temporary
+ * device memory (offline step). */
+svdq_status svdq_prepare_weights(const svdq_layer_desc* desc, const void* d_W,
+                                 const float* d_act_absmax, const void* d_bias,
+                                 const void* d_L1, const void* d_L2, void* d_prepared,
+                                 size_t prepared_bytes, void* stream);
+
+/* Reads the blob header back (synchronously) and checks it against `desc`:
+ * magic, version, format, K, N, rank and flags.  SVDQ_ERR_BAD_BLOB if they
+ * differ. */
+svdq_status svdq_check_blob(const svdq_layer_desc* desc, const void* d_prepared, void* stream);
+
+/* Fused activation pass (walkthrough Fig. 6, "down projection and
+ * quantization share one input"; handbook timestep section: dynamic scales):
+ *   x_hat = fp32(X * inv_lambda)                         (X: M x K bf16)
+ *   per token row and K group: scale and 4-bit codes of x_hat in desc->fmt
+ *     -> d_codes: M x K/2 bytes; d_scales: M x K/64 fp16 (INT4) or
+ *        M x K/32 E8M0 bytes (FP4)
+ *   T = bf16(x_hat) L1b accumulated in fp32, rounded once to bf16
+ *     -> d_T: M x rank bf16 (may be NULL when rank == 0).
+ * X is read from HBM once.  `desc` must be the descriptor the blob was
+ * prepared with.  Asynchronous. */
+svdq_status svdq_quantize_act(const svdq_layer_desc* desc, const void* d_prepared,
+                              const void* d_X, int M, void* d_codes, void* d_scales,
+                              void* d_T, void* stream);
+
+/* The fused layer: Y = Q(x_hat) Q(R) + Tb L2b + b, M x N in `out_dtype`.
+ * Two kernels: the activation pass above (into d_workspace), then the 4-bit
+ * GEMM whose K loop is followed by the rank-r bf16 K-slab Tb L2b in the same
+ * fp32 accumulators and a bias epilogue (walkthrough Fig. 6: the
+ * up-projection shares the 4-bit branch's output).  d_workspace must hold
+ * svdq_workspace_bytes(desc, M, 0) bytes.  Asynchronous. */
+svdq_status svdq_linear(const svdq_layer_desc* desc, const void* d_prepared, const void* d_X,
+                        int M, void* d_Y, int out_dtype, void* d_workspace, size_t ws_bytes,
+                        void* stream);
+
+/* The same layer computed the naive way, as separate kernels (walkthrough,
+ * Nunchaku section: a separately run low-rank branch re-reads the 16-bit
+ * activation and writes a 16-bit output again; Table 4's "SVDQuant" column):
+ *   quantize (codes + scales only) -> down-projection (re-reads X, writes T)
+ *   -> 4-bit GEMM + bias (writes Yp rounded to out_dtype)
+ *   -> up-projection (reads Yp and T, writes Y = round(Yp + Tb L2b)).
+ * Same arguments as svdq_linear; d_workspace holds
+ * svdq_workspace_bytes(desc, M, 1) bytes.  Asynchronous. */
+svdq_status svdq_linear_unfused(const svdq_layer_desc* desc, const void* d_prepared,
+                                const void* d_X, int M, void* d_Y, int out_dtype,
+                                void* d_workspace, size_t ws_bytes, void* stream);
+
+/* Byte offsets of the blob's sections (for inspection, serialization and
+ * tests).  All offsets are multiples of 256.
+ *   lambda      fp32[K]
+ *   inv_lambda  fp32[K]
+ *   l1t         bf16[rank][K]    (L1 transposed: row t holds column t of L1)
+ *   l2t         bf16[N][rank]    (L2 transposed: row n holds column n of L2)
+ *   wcodes      u8[N][K/2]       (column n's K residual codes, packed)
+ *   wscales     INT4: u16 fp16 bits [K/64][N]; FP4: u8 E8M0 [K/32][N]
+ *   bias        fp32[N]          (offset 0 when the layer has no bias) */
+typedef struct svdq_blob_layout {
+  uint64_t header, lambda, inv_lambda, l1t, l2t, wcodes, wscales, bias, total;
+} svdq_blob_layout;
+
+svdq_status svdq_blob_layout_of(const svdq_layer_desc* desc, svdq_blob_layout* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H */

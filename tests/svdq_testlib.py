@@ -1,0 +1,98 @@
+"""Test helpers: read libsvdq's buffers back into the canonical arrays the
+oracle produces.  The decoding follows the byte layouts documented in
+include/svdq.h; it is test code, shared by neither the oracle nor the
+library."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle as O
+
+
+def to_np(t) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def u16_tensor_to_np(t) -> np.ndarray:
+    """bf16 / fp16 / int16 tensor -> raw uint16 bits."""
+    import torch
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def np_bits_to_bf16_tensor(bits: np.ndarray, device):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def blob_sections(layer):
+    """Canonical numpy views of a prepared blob.
+
+    Returns dict(lam32, inv32, L1b (K x r), L2b (r x N), w_codes (K x N),
+    w_scales (K/g x N values: fp16 values for INT4, exponents for FP4),
+    bias (N or None), raw_wcodes, raw_wscales)."""
+    import ctypes
+    from w4a4_quantized_gemm_amd import svdq_blob_layout_of, INT4
+    d = layer.desc
+    L = svdq_blob_layout_of(d)
+    blob = to_np(layer.blob)
+    K, N, r = d.K, d.N, d.rank
+    g = 64 if d.fmt == INT4 else 32
+
+    def sec(off, nbytes):
+        return blob[off:off + nbytes]
+
+    lam32 = sec(L.lambda_, 4 * K).view(np.float32).astype(np.float64)
+    inv32 = sec(L.inv_lambda, 4 * K).view(np.float32).astype(np.float64)
+    l1t = sec(L.l1t, 2 * r * K).view(np.uint16).reshape(r, K)
+    l2t = sec(L.l2t, 2 * N * r).view(np.uint16).reshape(N, r)
+    L1b = O.bf16_bits_to_f64(l1t).T.copy()
+    L2b = O.bf16_bits_to_f64(l2t).T.copy()
+    raw_codes = sec(L.wcodes, N * K // 2).reshape(N, K // 2)
+    nib = O.unpack_nibbles(raw_codes)                       # N x K
+    if d.fmt == INT4:
+        codes = O.nibble_to_int4(nib).T.copy()
+        raw_scales = sec(L.wscales, 2 * (K // g) * N).view(np.uint16).reshape(K // g, N)
+        scales = O.fp16_bits_to_f64(raw_scales)
+    else:
+        codes = nib.T.copy()
+        raw_scales = sec(L.wscales, (K // g) * N).reshape(K // g, N)
+        scales = raw_scales.astype(np.int32) - 127
+    bias = None
+    if d.flags & 4:
+        bias = sec(L.bias, 4 * N).view(np.float32).astype(np.float64)
+    return dict(lam32=lam32, inv32=inv32, L1b=L1b, L2b=L2b, w_codes=codes, w_scales=scales,
+                bias=bias, raw_wcodes=raw_codes, raw_wscales=raw_scales, l1t=l1t, l2t=l2t)
+
+
+def oracle_prep_from_blob(sections, W_bits, fmt: str, bias_bits=None, cols=None) -> dict:
+    """The oracle's prepared layer built on the blob's stored lambda32, L1b,
+    L2b (the SVD factors are not unique, so parity is checked given them).
+    ``cols`` restricts the residual to a subset of output columns."""
+    W = O.bf16_bits_to_f64(W_bits)
+    lam32 = sections["lam32"]
+    inv32 = O.to_fp32(1.0 / lam32)
+    L2b = sections["L2b"]
+    if cols is not None:
+        W = W[:, cols]
+        L2b = L2b[:, cols]
+        if bias_bits is not None:
+            bias_bits = bias_bits[cols]
+    W_hat = lam32[:, None] * W
+    R = O.residual(W_hat, sections["L1b"], L2b)
+    w_codes, w_scales = O.quantize_weights(R, fmt)
+    bias = None if bias_bits is None else O.bf16_bits_to_f64(bias_bits)
+    return dict(fmt=fmt, K=W.shape[0], N=W.shape[1], rank=sections["L1b"].shape[1], lam32=lam32,
+                inv32=inv32, W_hat=W_hat, L1b=sections["L1b"], L2b=L2b, R=R, w_codes=w_codes,
+                w_scales=w_scales, bias=bias)
+
+
+def decode_act(codes_t, scales_t, fmt_id: int, M: int, K: int):
+    """Packed activation codes / scales from the GPU -> (codes M x K, scale values)."""
+    from w4a4_quantized_gemm_amd import INT4
+    raw = to_np(codes_t).reshape(M, K // 2)
+    nib = O.unpack_nibbles(raw)
+    if fmt_id == INT4:
+        sc = to_np(scales_t).view(np.uint16).reshape(M, K // 64)
+        return O.nibble_to_int4(nib), O.fp16_bits_to_f64(sc), raw, sc
+    sc = to_np(scales_t).reshape(M, K // 32)
+    return nib, sc.astype(np.int32) - 127, raw, sc

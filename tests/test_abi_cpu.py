@@ -1,0 +1,183 @@
+"""CPU tests of the C ABI boundary: the library loads, exports every symbol
+the header declares, validates arguments before touching a device, and its
+host-side helpers (blob layout, eigensolver) are right.  No compute call
+reaches a GPU here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svdq.h")
+
+import w4a4_quantized_gemm_amd as S  # noqa: E402
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(svdq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = S.load()
+    declared = _declared_functions()
+    assert set(declared) == set(S.EXPORTED), (declared, S.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for name in declared:
+        assert name in syms, name
+
+
+def test_status_strings_and_version():
+    lib = S.load()
+    for code, name in S.STATUS_NAMES.items():
+        assert lib.svdq_status_string(code).decode().startswith(name)
+    assert lib.svdq_status_string(999).decode() == "unknown svdq_status"
+    assert lib.svdq_version() >= 100
+
+
+def _desc(K=3072, N=9216, r=32, fmt=S.INT4, alpha=0.5, flags=0):
+    return S.make_desc(K, N, r, fmt, alpha, flags)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(K=100), dict(K=64), dict(K=3072 + 64), dict(N=32), dict(N=100), dict(r=8), dict(r=144),
+    dict(r=-16), dict(K=128, r=144),
+])
+def test_unsupported_shapes(kw):
+    d = _desc(**kw)
+    assert S.svdq_prepared_bytes(d) == 0
+    assert S.svdq_workspace_bytes(d, 16) == 0
+    lib = S.load()
+    st = lib.svdq_prepare_weights(ctypes.byref(d), 16, 16, None, None, None, 16, 1 << 30, None)
+    assert st == 2
+
+
+@pytest.mark.parametrize("kw", [dict(fmt=7), dict(alpha=-0.1), dict(alpha=1.5), dict(alpha=float("nan")),
+                                dict(flags=64)])
+def test_invalid_arguments(kw):
+    d = _desc(**kw)
+    lib = S.load()
+    assert S.svdq_prepared_bytes(d) == 0
+    assert lib.svdq_linear(ctypes.byref(d), 256, 256, 16, 256, 0, 256, 1 << 40, None) == 1
+
+
+def test_runtime_validation_before_device():
+    lib = S.load()
+    d = _desc()
+    ws = S.svdq_workspace_bytes(d, 4608)
+    good = 1 << 20   # any 16-byte aligned non-null value: never dereferenced when validation fails
+    # NULL pointers
+    assert lib.svdq_linear(ctypes.byref(d), None, good, 4608, good, 0, good, ws, None) == 1
+    assert lib.svdq_linear(ctypes.byref(d), good, good, 4608, None, 0, good, ws, None) == 1
+    assert lib.svdq_linear(None, good, good, 4608, good, 0, good, ws, None) == 1
+    # bad M, bad output dtype
+    assert lib.svdq_linear(ctypes.byref(d), good, good, 0, good, 0, good, ws, None) == 2
+    assert lib.svdq_linear(ctypes.byref(d), good, good, -5, good, 0, good, ws, None) == 2
+    assert lib.svdq_linear(ctypes.byref(d), good, good, 4608, good, 3, good, ws, None) == 1
+    # misaligned
+    assert lib.svdq_linear(ctypes.byref(d), good + 8, good, 4608, good, 0, good, ws, None) == 7
+    assert lib.svdq_linear_unfused(ctypes.byref(d), good, good, 4608, good + 2, 0, good, ws, None) == 7
+    # workspace too small
+    assert lib.svdq_linear(ctypes.byref(d), good, good, 4608, good, 0, good, ws - 1, None) == 4
+    # prepared buffer too small; missing act_absmax / bias / factors
+    pb = S.svdq_prepared_bytes(d)
+    assert lib.svdq_prepare_weights(ctypes.byref(d), good, good, None, None, None, good, pb - 1, None) == 4
+    assert lib.svdq_prepare_weights(ctypes.byref(d), good, None, None, None, None, good, pb, None) == 1
+    db = _desc(flags=S.F_HAS_BIAS)
+    assert lib.svdq_prepare_weights(ctypes.byref(db), good, good, None, None, None, good, pb, None) == 1
+    dg = _desc(flags=S.F_FACTORS_GIVEN)
+    assert lib.svdq_prepare_weights(ctypes.byref(dg), good, good, None, None, None, good, pb, None) == 1
+    # quantize_act: T required when rank > 0
+    assert lib.svdq_quantize_act(ctypes.byref(d), good, good, 16, good, good, None, None) == 1
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_has_gpu(), reason="checks the no-device path")
+def test_device_check_without_gpu():
+    lib = S.load()
+    d = _desc()
+    ws = S.svdq_workspace_bytes(d, 64)
+    good = 1 << 20
+    assert lib.svdq_linear(ctypes.byref(d), good, good, 64, good, 0, good, ws, None) == 3
+    assert lib.svdq_act_absmax(good, 64, 3072, good, 0, None) == 3
+
+
+def test_blob_layout_and_sizes():
+    for fmt, g, sb in ((S.INT4, 64, 2), (S.FP4, 32, 1)):
+        for flags in (0, S.F_HAS_BIAS):
+            d = _desc(K=3072, N=9216, r=32, fmt=fmt, flags=flags)
+            L = S.svdq_blob_layout_of(d)
+            offs = [L.header, L.lambda_, L.inv_lambda, L.l1t, L.l2t, L.wcodes, L.wscales]
+            sizes = [256, 4 * 3072, 4 * 3072, 2 * 32 * 3072, 2 * 9216 * 32, 9216 * 1536, (3072 // g) * 9216 * sb]
+            if flags:
+                offs.append(L.bias)
+                sizes.append(4 * 9216)
+            assert all(o % 256 == 0 for o in offs)
+            for (o, s), o_next in zip(zip(offs, sizes), offs[1:] + [L.total]):
+                assert o + s <= o_next
+            assert L.total == S.svdq_prepared_bytes(d)
+            assert (flags == 0) == (L.bias == 0)
+            c, s, t = S.svdq_act_sizes(d, 4608)
+            assert (c, s, t) == (4608 * 1536, 4608 * (3072 // g) * sb, 4608 * 32 * 2)
+            assert S.svdq_workspace_bytes(d, 4608) >= c + s + t
+    # compression: the 4-bit blob is ~0.27-0.28x the bf16 weight
+    d = _desc(K=3072, N=12288, r=32, fmt=S.FP4)
+    ratio = S.svdq_prepared_bytes(d) / (3072 * 12288 * 2)
+    assert 0.26 < ratio < 0.30
+
+
+JACOBI_MAIN = r"""
+#include <cstdio>
+#include <vector>
+namespace svdq { void jacobi_eigh(int, std::vector<double>&, std::vector<double>&, std::vector<double>&); }
+int main() {
+  int n; if (scanf("%d", &n) != 1) return 1;
+  std::vector<double> A(n * n), V, w;
+  for (auto& x : A) if (scanf("%lf", &x) != 1) return 1;
+  svdq::jacobi_eigh(n, A, V, w);
+  for (int i = 0; i < n; i++) printf("%.17g\n", w[i]);
+  for (int i = 0; i < n * n; i++) printf("%.17g\n", V[i]);
+  return 0;
+}
+"""
+
+
+def test_host_jacobi_eigensolver(tmp_path):
+    src = tmp_path / "main.cpp"
+    src.write_text(JACOBI_MAIN)
+    exe = tmp_path / "jac"
+    lin = os.path.join(ROOT, "w4a4_quantized_gemm_amd", "csrc", "svdq_linalg.cpp")
+    subprocess.run(["g++", "-O2", "-std=c++17", str(src), lin, "-o", str(exe)], check=True)
+    rng = np.random.default_rng(0)
+    for n, kind in ((1, "rand"), (7, "rand"), (48, "rand"), (96, "lowrank"), (64, "zero")):
+        if kind == "zero":
+            A = np.zeros((n, n))
+        elif kind == "lowrank":
+            B = rng.standard_normal((n, 5))
+            A = B @ B.T
+        else:
+            B = rng.standard_normal((n, n))
+            A = B + B.T
+        inp = f"{n}\n" + "\n".join(repr(float(x)) for x in A.ravel())
+        out = subprocess.run([str(exe)], input=inp, capture_output=True, text=True, check=True).stdout.split()
+        vals = np.array([float(x) for x in out])
+        w, V = vals[:n], vals[n:].reshape(n, n)
+        assert np.all(np.diff(w) <= 1e-12 * max(1.0, abs(w).max()))
+        ref = np.sort(np.linalg.eigvalsh(A))[::-1]
+        assert np.allclose(w, ref, atol=1e-10 * max(1.0, abs(ref).max()))
+        assert np.allclose(V.T @ V, np.eye(n), atol=1e-10)
+        assert np.allclose(A @ V, V * w, atol=1e-9 * max(1.0, abs(ref).max()))

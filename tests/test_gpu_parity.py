@@ -1,0 +1,307 @@
+"""GPU parity of libsvdq against the CPU oracle, through the C ABI.
+
+Bar (per the layer's definition):
+  * activation codes and scales: byte-equal to the oracle's;
+  * weight codes and scales: byte-equal to the oracle's quantization of the
+    residual taken against the blob's own lambda32, L1b, L2b (the SVD factors
+    are not unique, so the split itself is checked by Eckart-Young instead);
+  * lambda32: within one fp32 ulp of the oracle's (device pow vs host pow);
+  * Tb: within one bf16 ulp element-wise (fp32 vs fp64 accumulation order);
+  * Y: relative Frobenius error <= 1e-3 against the oracle's own quantized
+    computation (fp64 accumulation), rounded to the same output type; the
+    unfused path against the oracle's unfused rounding model.
+Sizes: small cases span several 128-wide tiles with ragged tails; the
+measured workloads run at full size and are checked on sampled rows and
+columns, in the launch configuration the benchmark times.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as WL
+from svdq_testlib import (blob_sections, decode_act, np_bits_to_bf16_tensor, oracle_prep_from_blob, to_np,
+                          u16_tensor_to_np)
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import w4a4_quantized_gemm_amd as S
+    S.load()          # fails loudly if the library is missing
+    return torch, "cuda:0"
+
+
+def _fmt_name(fmt_id):
+    import w4a4_quantized_gemm_amd as S
+    return O.INT4 if fmt_id == S.INT4 else O.FP4
+
+
+def _prepare(torch_dev, cfg, X_bits, W_bits, b_bits, **kw):
+    import w4a4_quantized_gemm_amd as S
+    torch, dev = torch_dev
+    X = np_bits_to_bf16_tensor(X_bits, dev)
+    W = np_bits_to_bf16_tensor(W_bits, dev)
+    a = torch.empty(cfg.K, dtype=torch.float32, device=dev)
+    S.svdq_act_absmax(X, a)
+    bias = None if b_bits is None else np_bits_to_bf16_tensor(b_bits, dev)
+    layer = S.SVDQLinear.prepare(W, a, cfg.rank, cfg.fmt, cfg.alpha, bias=bias, **kw)
+    torch.cuda.synchronize()
+    return layer, X, a
+
+
+def _check_weights(layer, W_bits, fmt, b_bits=None, cols=None):
+    sec = blob_sections(layer)
+    ref = oracle_prep_from_blob(sec, W_bits, fmt, b_bits, cols)
+    codes, scales = sec["w_codes"], sec["w_scales"]
+    if cols is not None:
+        codes, scales = codes[:, cols], scales[:, cols]
+    assert np.array_equal(codes, ref["w_codes"]), "weight codes differ"
+    assert np.array_equal(scales, ref["w_scales"]), "weight scales differ"
+    if b_bits is not None:
+        bref = O.bf16_bits_to_f64(b_bits if cols is None else b_bits[cols])
+        got = sec["bias"] if cols is None else sec["bias"][cols]
+        assert np.array_equal(got, bref)
+    # inv_lambda is fp32(1 / lambda32) exactly
+    assert np.array_equal(sec["inv32"], O.to_fp32(1.0 / sec["lam32"]))
+    return sec, ref
+
+
+def _check_lambda(sec, X_bits, W_bits, alpha, no_smoothing=False):
+    lam32, _ = O.smoothing_factors(O.act_absmax(X_bits), O.bf16_bits_to_f64(W_bits), alpha, no_smoothing)
+    got = sec["lam32"].astype(np.float32)
+    ref = lam32.astype(np.float32)
+    ulps = np.abs(got.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1, ulps.max()
+    return int((ulps > 0).sum())
+
+
+def _run_act(torch_dev, layer, X, M):
+    import w4a4_quantized_gemm_amd as S
+    torch, dev = torch_dev
+    cb, sb, tb = S.svdq_act_sizes(layer.desc, M)
+    codes = torch.empty(cb, dtype=torch.uint8, device=dev)
+    scales = torch.empty(sb, dtype=torch.uint8, device=dev)
+    T = torch.empty(max(tb // 2, 1), dtype=torch.bfloat16, device=dev)
+    S.svdq_quantize_act(layer.desc, layer.blob, X, codes, scales, T if layer.desc.rank else None)
+    torch.cuda.synchronize()
+    return codes, scales, T
+
+
+def _check_act(torch_dev, layer, X, X_bits, ref_prep, rows=None):
+    M, K = X_bits.shape
+    codes, scales, T = _run_act(torch_dev, layer, X, M)
+    q, s, raw, sraw = decode_act(codes, scales, layer.desc.fmt, M, K)
+    Xr = X_bits if rows is None else X_bits[rows]
+    ref = O.quantize_act(Xr, ref_prep["inv32"], ref_prep["fmt"])
+    sel = slice(None) if rows is None else rows
+    assert np.array_equal(raw[sel], ref["packed"]), "activation codes differ"
+    assert np.array_equal(sraw[sel], ref["scale_bytes"]), "activation scales differ"
+    if layer.desc.rank:
+        r = layer.desc.rank
+        Tg = O.bf16_bits_to_f64(u16_tensor_to_np(T[: M * r]).reshape(M, r))[sel]
+        _, Tref = O.down_proj(ref["xhat"], ref_prep["L1b"])
+        # within one bf16 ulp of the fp64-accumulated value
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(Tref), 1e-30))) - 7)
+        assert np.all(np.abs(Tg - Tref) <= ulp * 1.0001)
+        mism = float(np.mean(Tg != Tref))
+        assert mism < 0.01, mism
+    return codes, scales, T
+
+
+def _run_linear(torch_dev, layer, X, out, unfused):
+    import w4a4_quantized_gemm_amd as S
+    torch, _ = torch_dev
+    Y = layer(X, out_dtype=out, unfused=unfused)
+    torch.cuda.synchronize()
+    return Y.float().cpu().numpy().astype(np.float64)
+
+
+def _check_linear(torch_dev, layer, X, X_bits, ref_prep, rows=None, cols=None, modes=None):
+    import w4a4_quantized_gemm_amd as S
+    Xr = X_bits if rows is None else X_bits[rows]
+    errs = {}
+    for out, unfused in modes or [(S.OUT_BF16, False), (S.OUT_F32, False), (S.OUT_BF16, True), (S.OUT_F32, True)]:
+        oname = "bf16" if out == S.OUT_BF16 else "f32"
+        ref = (O.linear_unfused if unfused else O.linear)(ref_prep, Xr, oname)["Y"]
+        Y = _run_linear(torch_dev, layer, X, out, unfused)
+        if rows is not None:
+            Y = Y[rows]
+        if cols is not None:
+            Y = Y[:, cols]
+        e = O.rel_fro(Y, ref)
+        errs[(oname, unfused)] = e
+        assert e <= TOL, (oname, unfused, e)
+    return errs
+
+
+# ------------------------------------------------------------------ calibration
+def test_act_absmax_exact(torch_dev):
+    import w4a4_quantized_gemm_amd as S
+    torch, dev = torch_dev
+    _say("case: act_absmax c1")
+    X_bits = WL.make_x(WL.C1)
+    X = np_bits_to_bf16_tensor(X_bits, dev)
+    a = torch.empty(WL.C1.K, dtype=torch.float32, device=dev)
+    S.svdq_act_absmax(X, a)
+    assert np.array_equal(to_np(a), O.act_absmax(X_bits))
+    S.svdq_act_absmax(X[:100], a)
+    S.svdq_act_absmax(X[100:], a, accumulate=True)
+    assert np.array_equal(to_np(a), O.act_absmax(X_bits))
+
+
+# ------------------------------------------------------------------ tiny workload
+@pytest.mark.parametrize("fmt", [O.INT4, O.FP4])
+def test_tiny_config_end_to_end(torch_dev, fmt):
+    cfg = WL.C1.with_(fmt=fmt)
+    _say(f"case: tiny config {cfg.name} fmt={fmt}")
+    X_bits, W_bits, b_bits = WL.make_layer(cfg)
+    layer, X, _ = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
+    import w4a4_quantized_gemm_amd as S
+    S.svdq_check_blob(layer.desc, layer.blob)
+    sec, ref = _check_weights(layer, W_bits, fmt)
+    _check_lambda(sec, X_bits, W_bits, cfg.alpha)
+    # the GPU SVD reaches the Eckart-Young optimum (walkthrough: SVD gives the
+    # minimal ||W_hat - L1 L2||_F over rank-r approximations)
+    sig = np.linalg.svd(ref["W_hat"], compute_uv=False)
+    opt = np.sqrt(np.sum(sig[cfg.rank:] ** 2))
+    assert opt * (1 - 1e-12) <= np.linalg.norm(ref["R"]) <= opt * (1 + 1e-4)
+    _check_act(torch_dev, layer, X, X_bits, ref)
+    errs = _check_linear(torch_dev, layer, X, X_bits, ref)
+    _say(f"  rel errors {errs}")
+
+
+# ------------------------------------------------------------------ small shapes, edge cases
+SMALL = [
+    # M, K, N, rank, bias, fmt
+    (300, 384, 320, 16, True, O.INT4),
+    (300, 384, 320, 16, True, O.FP4),
+    (1, 128, 64, 0, False, O.INT4),
+    (17, 256, 192, 48, True, O.FP4),
+    (129, 512, 448, 128, False, O.INT4),
+    (64, 1024, 128, 32, True, O.INT4),
+    (257, 640, 576, 64, False, O.FP4),
+]
+
+
+@pytest.mark.parametrize("M,K,N,rank,bias,fmt", SMALL)
+def test_small_shapes(torch_dev, M, K, N, rank, bias, fmt):
+    _say(f"case: small M={M} K={K} N={N} r={rank} bias={bias} fmt={fmt}")
+    cfg = WL.C2.with_(name="small", M=M, K=K, N=N, rank=rank, fmt=fmt, w_std=1 / np.sqrt(K),
+                      n_outlier_channels=min(8, K // 16), bias_std=0.02 if bias else 0.0, seed=M + K + N)
+    X_bits, W_bits, b_bits = WL.make_layer(cfg)
+    layer, X, _ = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
+    sec, ref = _check_weights(layer, W_bits, fmt, b_bits)
+    _check_act(torch_dev, layer, X, X_bits, ref)
+    _check_linear(torch_dev, layer, X, X_bits, ref)
+
+
+def test_factors_given_and_no_smoothing(torch_dev):
+    """Caller-supplied factors are stored verbatim; with them the whole blob
+    equals the oracle's preparation."""
+    import w4a4_quantized_gemm_amd as S
+    torch, dev = torch_dev
+    _say("case: factors given + no smoothing")
+    cfg = WL.C1.with_(M=200, K=512, N=384, rank=32, seed=3)
+    X_bits, W_bits, _ = WL.make_layer(cfg)
+    a = O.act_absmax(X_bits)
+    ref = O.prepare(W_bits, a, alpha=0.5, rank=32, fmt=O.INT4)
+    L1 = np_bits_to_bf16_tensor(O.bf16_bits_of(ref["L1b"].astype(np.float32)), dev)
+    L2 = np_bits_to_bf16_tensor(O.bf16_bits_of(ref["L2b"].astype(np.float32)), dev)
+    X = np_bits_to_bf16_tensor(X_bits, dev)
+    W = np_bits_to_bf16_tensor(W_bits, dev)
+    ad = torch.from_numpy(a).to(dev)
+    layer = S.SVDQLinear.prepare(W, ad, 32, "int4", 0.5, L1=L1, L2=L2)
+    sec = blob_sections(layer)
+    assert np.array_equal(sec["L1b"], ref["L1b"]) and np.array_equal(sec["L2b"], ref["L2b"])
+    _check_lambda(sec, X_bits, W_bits, 0.5)
+    sec, ref2 = _check_weights(layer, W_bits, O.INT4)
+    _check_linear(torch_dev, layer, X, X_bits, ref2)
+    # no smoothing: lambda = 1 exactly
+    layer = S.SVDQLinear.prepare(W, None, 32, "fp4", 0.5, no_smoothing=True)
+    sec = blob_sections(layer)
+    assert np.all(sec["lam32"] == 1.0) and np.all(sec["inv32"] == 1.0)
+    sec, ref3 = _check_weights(layer, W_bits, O.FP4)
+    _check_act(torch_dev, layer, X, X_bits, ref3)
+    _check_linear(torch_dev, layer, X, X_bits, ref3)
+
+
+def test_quantizer_edge_values(torch_dev):
+    """Zero rows, exact ties of x/s, tiny values with subnormal fp16 scales,
+    E2M1 midpoints and large magnitudes, in both formats."""
+    import w4a4_quantized_gemm_amd as S
+    torch, dev = torch_dev
+    _say("case: quantizer edge values")
+    K, N, M = 256, 64, 48
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((M, K))
+    x[0] = 0.0                                            # all-zero row: s = 0, codes 0
+    x[1, :64] = np.arange(64) % 15 - 7.0                  # max 7 -> s = 1: integer codes
+    x[1, 64:128] = (np.arange(64) % 15 - 7.0) + 0.5       # ties at s = 7.5/7 -> fp16 rounding
+    x[2] = rng.standard_normal(K) * 1e-6                  # subnormal fp16 scales
+    x[3] = rng.standard_normal(K) * 2.0 ** -26            # scales that underflow to 0
+    x[4] = rng.standard_normal(K) * 3e3                   # large values
+    x[5, :32] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 4)   # E2M1 midpoints (A = 6: e = 0)
+    x[6] = -x[5]
+    X_bits = O.bf16_bits_of(O.to_bf16(x).astype(np.float32))
+    W_bits = O.bf16_bits_of(O.to_bf16(rng.standard_normal((K, N)) * 0.05).astype(np.float32))
+    X = np_bits_to_bf16_tensor(X_bits, dev)
+    W = np_bits_to_bf16_tensor(W_bits, dev)
+    for fmt in ("int4", "fp4"):
+        layer = S.SVDQLinear.prepare(W, None, 16, fmt, 0.5, no_smoothing=True)
+        sec, ref = _check_weights(layer, W_bits, fmt)
+        _check_act(torch_dev, layer, X, X_bits, ref)
+        _check_linear(torch_dev, layer, X, X_bits, ref, modes=[(S.OUT_F32, False), (S.OUT_F32, True)])
+
+
+def test_determinism_and_bad_blob(torch_dev):
+    import w4a4_quantized_gemm_amd as S
+    torch, dev = torch_dev
+    _say("case: determinism + bad blob")
+    cfg = WL.C1
+    X_bits, W_bits, b_bits = WL.make_layer(cfg)
+    layer, X, _ = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
+    y1 = layer(X, out_dtype=S.OUT_F32).clone()
+    y2 = layer(X, out_dtype=S.OUT_F32).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    blob2 = layer.blob.clone()
+    blob2[0] ^= 0xFF
+    with pytest.raises(S.SvdqError) as ei:
+        S.svdq_check_blob(layer.desc, blob2)
+    assert ei.value.status == 6
+    with pytest.raises(S.SvdqError) as ei:
+        ws = torch.empty(16, dtype=torch.uint8, device=dev)
+        S.svdq_linear(layer.desc, layer.blob, X, torch.empty_like(y1), ws, S.OUT_F32)
+    assert ei.value.status == 4
+
+
+# ------------------------------------------------------------------ measured workloads, full size
+FULL = [WL.C2, WL.C3, WL.C4_INT4, WL.C4_FP4]
+
+
+@pytest.mark.parametrize("cfg", FULL, ids=[c.name for c in FULL])
+def test_full_size_workloads(torch_dev, cfg):
+    _say(f"case: full size {cfg.name}")
+    X_bits, W_bits, b_bits = WL.make_layer(cfg)
+    layer, X, _ = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([rng.choice(cfg.M, 192, replace=False), [0, cfg.M - 1]]))
+    cols = np.unique(np.concatenate([rng.choice(cfg.N, 384, replace=False), [0, cfg.N - 1]]))
+    sec, ref = _check_weights(layer, W_bits, cfg.fmt, b_bits, cols=cols)
+    nlam = _check_lambda(sec, X_bits, W_bits, cfg.alpha)
+    _say(f"  lambda32 differing by one ulp: {nlam}")
+    _check_act(torch_dev, layer, X, X_bits, ref, rows=rows)
+    errs = _check_linear(torch_dev, layer, X, X_bits, ref, rows=rows, cols=cols)
+    _say(f"  rel errors {errs}")

@@ -1,0 +1,242 @@
+"""Python binding of libsvdq (the SVDQuant W4A4 linear layer for MI355X).
+
+Argument marshalling only: every function here forwards torch tensors'
+device pointers and the current HIP stream to the C ABI declared in
+``include/svdq.h`` and raises ``SvdqError`` on a non-zero status.  All
+arithmetic runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsvdq.so")
+
+INT4 = 0   # SVDQ_INT4_G64_FP16
+FP4 = 1    # SVDQ_FP4_E2M1_G32_E8M0
+OUT_BF16 = 0
+OUT_F32 = 1
+F_NO_SMOOTHING = 1
+F_FACTORS_GIVEN = 2
+F_HAS_BIAS = 4
+
+FORMAT_NAMES = {"int4": INT4, "fp4": FP4}
+GROUP = {INT4: 64, FP4: 32}
+
+STATUS_NAMES = {
+    0: "SVDQ_OK", 1: "SVDQ_ERR_INVALID_ARGUMENT", 2: "SVDQ_ERR_UNSUPPORTED_SHAPE",
+    3: "SVDQ_ERR_UNSUPPORTED_DEVICE", 4: "SVDQ_ERR_BUFFER_TOO_SMALL", 5: "SVDQ_ERR_HIP",
+    6: "SVDQ_ERR_BAD_BLOB", 7: "SVDQ_ERR_MISALIGNED",
+}
+
+# every symbol include/svdq.h declares
+EXPORTED = (
+    "svdq_status_string", "svdq_version", "svdq_prepared_bytes", "svdq_workspace_bytes",
+    "svdq_act_sizes", "svdq_act_absmax", "svdq_prepare_weights", "svdq_check_blob",
+    "svdq_quantize_act", "svdq_linear", "svdq_linear_unfused", "svdq_blob_layout_of",
+)
+
+
+class SvdqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib().svdq_status_string(status).decode() if _LIB is not None else STATUS_NAMES.get(status, "?")
+        super().__init__(f"{where}: {msg} (status {status})")
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_int32), ("N", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("fmt", ctypes.c_int32), ("alpha", ctypes.c_float), ("flags", ctypes.c_uint32)]
+
+    def __repr__(self):
+        return (f"LayerDesc(K={self.K}, N={self.N}, rank={self.rank}, fmt={self.fmt}, "
+                f"alpha={self.alpha}, flags={self.flags})")
+
+
+class BlobLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in
+                ("header", "lambda_", "inv_lambda", "l1t", "l2t", "wcodes", "wscales", "bias", "total")]
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def _lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m w4a4_quantized_gemm_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I, Z, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_int
+        D = ctypes.POINTER(LayerDesc)
+        sig = {
+            "svdq_status_string": ([I], ctypes.c_char_p),
+            "svdq_version": ([], I),
+            "svdq_prepared_bytes": ([D], Z),
+            "svdq_workspace_bytes": ([D, I, I], Z),
+            "svdq_act_sizes": ([D, I, ctypes.POINTER(Z), ctypes.POINTER(Z), ctypes.POINTER(Z)], S),
+            "svdq_act_absmax": ([P, I, I, P, I, P], S),
+            "svdq_prepare_weights": ([D, P, P, P, P, P, P, Z, P], S),
+            "svdq_check_blob": ([D, P, P], S),
+            "svdq_quantize_act": ([D, P, P, I, P, P, P, P], S),
+            "svdq_linear": ([D, P, P, I, P, I, P, Z, P], S),
+            "svdq_linear_unfused": ([D, P, P, I, P, I, P, Z, P], S),
+            "svdq_blob_layout_of": ([D, ctypes.POINTER(BlobLayout)], S),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _LIB = lib
+    return _LIB
+
+
+def load() -> ctypes.CDLL:
+    """Load libsvdq.so (raises ImportError if it has not been built)."""
+    return _lib()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise SvdqError(status, where)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def make_desc(K: int, N: int, rank: int, fmt, alpha: float = 0.5, flags: int = 0) -> LayerDesc:
+    if isinstance(fmt, str):
+        fmt = FORMAT_NAMES[fmt]
+    return LayerDesc(K, N, rank, fmt, alpha, flags)
+
+
+# ----------------------------------------------------------------- size queries
+def svdq_prepared_bytes(desc: LayerDesc) -> int:
+    return _lib().svdq_prepared_bytes(ctypes.byref(desc))
+
+
+def svdq_workspace_bytes(desc: LayerDesc, M: int, unfused: bool = False) -> int:
+    return _lib().svdq_workspace_bytes(ctypes.byref(desc), M, int(unfused))
+
+
+def svdq_act_sizes(desc: LayerDesc, M: int):
+    c, s, t = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(_lib().svdq_act_sizes(ctypes.byref(desc), M, ctypes.byref(c), ctypes.byref(s), ctypes.byref(t)),
+           "svdq_act_sizes")
+    return c.value, s.value, t.value
+
+
+def svdq_blob_layout_of(desc: LayerDesc) -> BlobLayout:
+    out = BlobLayout()
+    _check(_lib().svdq_blob_layout_of(ctypes.byref(desc), ctypes.byref(out)), "svdq_blob_layout_of")
+    return out
+
+
+# ----------------------------------------------------------------- GPU calls
+def svdq_act_absmax(X, out, accumulate: bool = False, stream=None):
+    """out[j] = max_i |X[i, j]| (X: M x K bf16 tensor, out: K float32 tensor)."""
+    M, K = X.shape
+    _check(_lib().svdq_act_absmax(_ptr(X), M, K, _ptr(out), int(accumulate), _stream(stream)),
+           "svdq_act_absmax")
+
+
+def svdq_prepare_weights(desc: LayerDesc, W, act_absmax, prepared, bias=None, L1=None, L2=None,
+                         stream=None):
+    """Offline preparation into the uint8 device tensor ``prepared`` (synchronous)."""
+    _check(_lib().svdq_prepare_weights(ctypes.byref(desc), _ptr(W), _ptr(act_absmax), _ptr(bias),
+                                       _ptr(L1), _ptr(L2), _ptr(prepared), prepared.numel(),
+                                       _stream(stream)), "svdq_prepare_weights")
+
+
+def svdq_check_blob(desc: LayerDesc, prepared, stream=None):
+    _check(_lib().svdq_check_blob(ctypes.byref(desc), _ptr(prepared), _stream(stream)), "svdq_check_blob")
+
+
+def svdq_quantize_act(desc: LayerDesc, prepared, X, codes, scales, T=None, stream=None):
+    M = X.shape[0]
+    _check(_lib().svdq_quantize_act(ctypes.byref(desc), _ptr(prepared), _ptr(X), M, _ptr(codes),
+                                    _ptr(scales), _ptr(T), _stream(stream)), "svdq_quantize_act")
+
+
+def svdq_linear(desc: LayerDesc, prepared, X, Y, workspace, out_dtype: int = OUT_BF16, stream=None):
+    M = X.shape[0]
+    _check(_lib().svdq_linear(ctypes.byref(desc), _ptr(prepared), _ptr(X), M, _ptr(Y), out_dtype,
+                              _ptr(workspace), workspace.numel(), _stream(stream)), "svdq_linear")
+
+
+def svdq_linear_unfused(desc: LayerDesc, prepared, X, Y, workspace, out_dtype: int = OUT_BF16, stream=None):
+    M = X.shape[0]
+    _check(_lib().svdq_linear_unfused(ctypes.byref(desc), _ptr(prepared), _ptr(X), M, _ptr(Y), out_dtype,
+                                      _ptr(workspace), workspace.numel(), _stream(stream)),
+           "svdq_linear_unfused")
+
+
+# ----------------------------------------------------------------- convenience
+class SVDQLinear:
+    """A prepared layer held on the GPU: the blob plus its descriptor.
+
+    ``SVDQLinear.prepare(W, act_absmax, rank, fmt, ...)`` runs the offline
+    preparation; ``layer(X)`` runs the fused forward pass.  Buffers are torch
+    tensors (device memory); the arithmetic is the library's.
+    """
+
+    def __init__(self, desc: LayerDesc, blob):
+        self.desc = desc
+        self.blob = blob
+        self._ws = None
+
+    @classmethod
+    def prepare(cls, W, act_absmax, rank: int, fmt="int4", alpha: float = 0.5, bias=None,
+                L1=None, L2=None, no_smoothing: bool = False, stream=None) -> "SVDQLinear":
+        import torch
+        K, N = W.shape
+        flags = (F_HAS_BIAS if bias is not None else 0) | (F_NO_SMOOTHING if no_smoothing else 0) | \
+                (F_FACTORS_GIVEN if L1 is not None else 0)
+        desc = make_desc(K, N, rank, fmt, alpha, flags)
+        nbytes = svdq_prepared_bytes(desc)
+        if nbytes == 0:
+            raise SvdqError(2, "svdq_prepared_bytes")
+        blob = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+        svdq_prepare_weights(desc, W, act_absmax, blob, bias=bias, L1=L1, L2=L2, stream=stream)
+        return cls(desc, blob)
+
+    def workspace(self, M: int, unfused: bool = False):
+        import torch
+        need = svdq_workspace_bytes(self.desc, M, unfused)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.blob.device)
+        return self._ws
+
+    def __call__(self, X, out_dtype: int = OUT_BF16, unfused: bool = False, Y=None, stream=None):
+        import torch
+        M = X.shape[0]
+        if Y is None:
+            Y = torch.empty((M, self.desc.N), dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32,
+                            device=X.device)
+        fn = svdq_linear_unfused if unfused else svdq_linear
+        fn(self.desc, self.blob, X, Y, self.workspace(M, unfused), out_dtype, stream)
+        return Y
+
+    def section(self, name: str):
+        """A uint8 view of one blob section (lambda_, inv_lambda, l1t, l2t, wcodes, wscales, bias)."""
+        L = svdq_blob_layout_of(self.desc)
+        names = ["header", "lambda_", "inv_lambda", "l1t", "l2t", "wcodes", "wscales", "bias", "total"]
+        offs = [getattr(L, n) for n in names]
+        i = names.index(name)
+        start = offs[i]
+        nxt = [o for o in offs[i + 1:] if o > start]
+        end = min(nxt) if nxt else L.total
+        return self.blob[start:end]

@@ -1,0 +1,205 @@
+// C ABI entry points of libsvdq: argument validation, device check, and
+// dispatch to the kernels.  Every argument is validated on the host before
+// any HIP call; nothing throws across the boundary.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
+#include "svdq_internal.h"
+#include "svdq_kernels.h"
+#include "svdq_prep.h"
+
+using namespace svdq;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+svdq_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return SVDQ_ERR_UNSUPPORTED_DEVICE;
+  }
+  if (dev < kMaxDevices) {
+    const int known = g_device_ok[dev].load(std::memory_order_relaxed);
+    if (known == 1) return SVDQ_OK;
+    if (known == 2) return SVDQ_ERR_UNSUPPORTED_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return SVDQ_ERR_UNSUPPORTED_DEVICE;
+  }
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_device_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? SVDQ_OK : SVDQ_ERR_UNSUPPORTED_DEVICE;
+}
+
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+svdq_status from_hip(hipError_t e) { return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP; }
+
+// Common validation of the runtime calls.
+svdq_status validate_runtime(const svdq_layer_desc* desc, const void* prepared, const void* X, int M) {
+  svdq_status st = validate_desc(desc);
+  if (st != SVDQ_OK) return st;
+  if ((st = validate_m(M)) != SVDQ_OK) return st;
+  if (!prepared || !X) return SVDQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(prepared) || !aligned16(X)) return SVDQ_ERR_MISALIGNED;
+  return SVDQ_OK;
+}
+
+struct BlobPtrs {
+  const float* inv_lam;
+  const uint16_t* l1t;
+  const uint16_t* l2t;
+  const uint8_t* wcodes;
+  const void* wscales;
+  const float* bias;
+};
+
+BlobPtrs blob_ptrs(const svdq_layer_desc& d, const void* prepared) {
+  const svdq_blob_layout L = layout_of(d);
+  const uint8_t* b = static_cast<const uint8_t*>(prepared);
+  BlobPtrs p;
+  p.inv_lam = reinterpret_cast<const float*>(b + L.inv_lambda);
+  p.l1t = reinterpret_cast<const uint16_t*>(b + L.l1t);
+  p.l2t = reinterpret_cast<const uint16_t*>(b + L.l2t);
+  p.wcodes = b + L.wcodes;
+  p.wscales = b + L.wscales;
+  p.bias = (d.flags & SVDQ_F_HAS_BIAS) ? reinterpret_cast<const float*>(b + L.bias) : nullptr;
+  return p;
+}
+
+svdq_status run_layer(const svdq_layer_desc* desc, const void* prepared, const void* X, int M, void* Y,
+                      int out_dtype, void* ws, size_t ws_bytes, void* stream, bool unfused) {
+  svdq_status st = validate_runtime(desc, prepared, X, M);
+  if (st != SVDQ_OK) return st;
+  if (!Y || !ws) return SVDQ_ERR_INVALID_ARGUMENT;
+  if (out_dtype != SVDQ_OUT_BF16 && out_dtype != SVDQ_OUT_F32) return SVDQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(Y) || !aligned16(ws)) return SVDQ_ERR_MISALIGNED;
+  const ActLayout A = act_layout(*desc, M);
+  if (ws_bytes < A.total) return SVDQ_ERR_BUFFER_TOO_SMALL;
+  if ((st = check_device()) != SVDQ_OK) return st;
+
+  const BlobPtrs bp = blob_ptrs(*desc, prepared);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  ActArgs a;
+  a.X = static_cast<const uint16_t*>(X);
+  a.M = M;
+  a.K = desc->K;
+  a.rank = desc->rank;
+  a.inv_lam = bp.inv_lam;
+  a.l1t = bp.l1t;
+  a.codes = w + A.codes;
+  a.scales = w + A.scales;
+  a.Tb = reinterpret_cast<uint16_t*>(w + A.tb);
+
+  GemmArgs g;
+  g.acodes = a.codes;
+  g.ascales = a.scales;
+  g.wcodes = bp.wcodes;
+  g.wscales = bp.wscales;
+  g.Tb = a.Tb;
+  g.l2t = bp.l2t;
+  g.bias = bp.bias;
+  g.Y = Y;
+  g.M = M;
+  g.K = desc->K;
+  g.N = desc->N;
+  g.rank = desc->rank;
+
+  const hipStream_t s = as_stream(stream);
+  if (!unfused) {
+    if ((st = from_hip(launch_act(desc->fmt, true, desc->rank > 0, a, s))) != SVDQ_OK) return st;
+    return from_hip(launch_gemm(desc->fmt, desc->rank > 0, out_dtype, g, s));
+  }
+  if ((st = from_hip(launch_act(desc->fmt, true, false, a, s))) != SVDQ_OK) return st;
+  if (desc->rank > 0 && (st = from_hip(launch_act(desc->fmt, false, true, a, s))) != SVDQ_OK) return st;
+  if ((st = from_hip(launch_gemm(desc->fmt, false, out_dtype, g, s))) != SVDQ_OK) return st;
+  return from_hip(launch_up(out_dtype, a.Tb, bp.l2t, Y, M, desc->N, desc->rank, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+svdq_status svdq_act_absmax(const void* d_X, int M, int K, float* d_absmax, int accumulate, void* stream) {
+  if (!d_X || !d_absmax) return SVDQ_ERR_INVALID_ARGUMENT;
+  if (validate_m(M) != SVDQ_OK || K < 1 || K > kMaxDim) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  svdq_status st = check_device();
+  if (st != SVDQ_OK) return st;
+  return from_hip(launch_absmax(static_cast<const uint16_t*>(d_X), M, K, d_absmax, accumulate != 0,
+                                as_stream(stream)));
+}
+
+svdq_status svdq_prepare_weights(const svdq_layer_desc* desc, const void* d_W, const float* d_act_absmax,
+                                 const void* d_bias, const void* d_L1, const void* d_L2, void* d_prepared,
+                                 size_t prepared_bytes, void* stream) {
+  svdq_status st = validate_desc(desc);
+  if (st != SVDQ_OK) return st;
+  if (!d_W || !d_prepared) return SVDQ_ERR_INVALID_ARGUMENT;
+  if (!(desc->flags & SVDQ_F_NO_SMOOTHING) && !d_act_absmax) return SVDQ_ERR_INVALID_ARGUMENT;
+  if ((desc->flags & SVDQ_F_HAS_BIAS) && !d_bias) return SVDQ_ERR_INVALID_ARGUMENT;
+  if ((desc->flags & SVDQ_F_FACTORS_GIVEN) && desc->rank > 0 && (!d_L1 || !d_L2)) return SVDQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(d_prepared) || !aligned16(d_W)) return SVDQ_ERR_MISALIGNED;
+  if (prepared_bytes < layout_of(*desc).total) return SVDQ_ERR_BUFFER_TOO_SMALL;
+  if ((st = check_device()) != SVDQ_OK) return st;
+  PrepOptions opt;
+  if (const char* e = std::getenv("SVDQ_PREP_ITERS")) opt.iterations = std::atoi(e);
+  return prepare_impl(*desc, static_cast<const uint16_t*>(d_W), d_act_absmax, static_cast<const uint16_t*>(d_bias),
+                      static_cast<const uint16_t*>(d_L1), static_cast<const uint16_t*>(d_L2),
+                      static_cast<uint8_t*>(d_prepared), as_stream(stream), opt);
+}
+
+svdq_status svdq_check_blob(const svdq_layer_desc* desc, const void* d_prepared, void* stream) {
+  svdq_status st = validate_desc(desc);
+  if (st != SVDQ_OK) return st;
+  if (!d_prepared) return SVDQ_ERR_INVALID_ARGUMENT;
+  if ((st = check_device()) != SVDQ_OK) return st;
+  BlobHeader h;
+  if (hipMemcpyAsync(&h, d_prepared, sizeof(h), hipMemcpyDeviceToHost, as_stream(stream)) != hipSuccess ||
+      hipStreamSynchronize(as_stream(stream)) != hipSuccess)
+    return SVDQ_ERR_HIP;
+  if (h.magic != kMagic || h.version != kVersion || h.fmt != desc->fmt || h.K != desc->K || h.N != desc->N ||
+      h.rank != desc->rank || h.flags != desc->flags)
+    return SVDQ_ERR_BAD_BLOB;
+  return SVDQ_OK;
+}
+
+svdq_status svdq_quantize_act(const svdq_layer_desc* desc, const void* d_prepared, const void* d_X, int M,
+                              void* d_codes, void* d_scales, void* d_T, void* stream) {
+  svdq_status st = validate_runtime(desc, d_prepared, d_X, M);
+  if (st != SVDQ_OK) return st;
+  if (!d_codes || !d_scales || (desc->rank > 0 && !d_T)) return SVDQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(d_codes) || !aligned16(d_scales) || (d_T && !aligned16(d_T))) return SVDQ_ERR_MISALIGNED;
+  if ((st = check_device()) != SVDQ_OK) return st;
+  const BlobPtrs bp = blob_ptrs(*desc, d_prepared);
+  ActArgs a;
+  a.X = static_cast<const uint16_t*>(d_X);
+  a.M = M;
+  a.K = desc->K;
+  a.rank = desc->rank;
+  a.inv_lam = bp.inv_lam;
+  a.l1t = bp.l1t;
+  a.codes = static_cast<uint8_t*>(d_codes);
+  a.scales = d_scales;
+  a.Tb = static_cast<uint16_t*>(d_T);
+  return from_hip(launch_act(desc->fmt, true, desc->rank > 0, a, as_stream(stream)));
+}
+
+svdq_status svdq_linear(const svdq_layer_desc* desc, const void* d_prepared, const void* d_X, int M, void* d_Y,
+                        int out_dtype, void* d_workspace, size_t ws_bytes, void* stream) {
+  return run_layer(desc, d_prepared, d_X, M, d_Y, out_dtype, d_workspace, ws_bytes, stream, false);
+}
+
+svdq_status svdq_linear_unfused(const svdq_layer_desc* desc, const void* d_prepared, const void* d_X, int M,
+                                void* d_Y, int out_dtype, void* d_workspace, size_t ws_bytes, void* stream) {
+  return run_layer(desc, d_prepared, d_X, M, d_Y, out_dtype, d_workspace, ws_bytes, stream, true);
+}
+
+}  // extern "C"

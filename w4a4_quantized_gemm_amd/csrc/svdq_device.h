@@ -1,0 +1,64 @@
+// Device-side helpers shared by the HIP kernels of libsvdq (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <cstdint>
+
+namespace svdq {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Round-half-even of the exact quotient x / s for s > 0 with |x / s| <= 16,
+// given r = 1/s correctly rounded.  y = x * r is within 2^-19 of x / s, so
+// rint(y) is the answer unless y is within 2^-18 of a half-integer; then the
+// sign of x - (q +- 1/2) s, which one fma gives exactly, decides.
+__device__ __forceinline__ float rne_quotient(float x, float s, float r) {
+  const float y = x * r;
+  float q = __builtin_rintf(y);
+  if (__builtin_fabsf(y - q) > 0.5f - 0x1p-18f) {
+    const float dhi = __builtin_fmaf(-(q + 0.5f), s, x);
+    const float dlo = __builtin_fmaf(-(q - 0.5f), s, x);
+    const bool odd = (static_cast<int>(q) & 1) != 0;
+    if (dhi > 0.f || (dhi == 0.f && odd)) q += 1.f;
+    else if (dlo < 0.f || (dlo == 0.f && odd)) q -= 1.f;
+  }
+  return q;
+}
+
+// Smallest e with a <= 6 * 2^e for a finite a >= 0, clamped to [-127, 127];
+// a = 0 (or below 2^-126) gives -127.  Exact integer arithmetic on the bits:
+// a = 1.f * 2^(eb-127); 6 * 2^e >= a  <=>  e >= eb - 129 + (1.f > 1.5).
+__device__ __forceinline__ int e8m0_exponent(float a) {
+  const uint32_t b = __float_as_uint(a);
+  const int eb = static_cast<int>((b >> 23) & 0xFFu);
+  if (eb == 0) return -127;
+  const int e = eb - 129 + ((b & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// 4-bit float (E2M1) code of y, |y| <= 6: nearest of 0, .5, 1, 1.5, 2, 3, 4,
+// 6 with ties to the even code; a value that rounds to zero gives +0.
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+  const float m = __builtin_fabsf(y);
+  uint32_t idx = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) +
+                 (m >= 3.5f) + (m > 5.0f);
+  return idx | ((y < 0.f && idx != 0u) ? 8u : 0u);
+}
+
+}  // namespace svdq

@@ -1,0 +1,52 @@
+// Internal declarations shared by the host translation units of libsvdq.
+// Nothing here includes HIP headers, so the validation and layout logic can
+// be compiled and unit-tested by a plain C++ compiler.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "svdq.h"
+
+namespace svdq {
+
+constexpr uint32_t kMagic = 0x51445653u;  // "SVDQ" little-endian
+constexpr uint32_t kVersion = 1u;
+constexpr uint32_t kKnownFlags = SVDQ_F_NO_SMOOTHING | SVDQ_F_FACTORS_GIVEN | SVDQ_F_HAS_BIAS;
+constexpr int kMaxRank = 128;
+constexpr int kMaxDim = 65536;
+constexpr int kMaxM = 1 << 22;
+
+// 256-byte header at offset 0 of every prepared blob.
+struct BlobHeader {
+  uint32_t magic;
+  uint32_t version;
+  int32_t fmt, K, N, rank;
+  uint32_t flags;
+  int32_t group;
+  float alpha;
+  uint32_t reserved0;
+  svdq_blob_layout layout;     // 9 x uint64
+  uint8_t pad[256 - 40 - sizeof(svdq_blob_layout)];
+};
+static_assert(sizeof(BlobHeader) == 256, "blob header must be 256 bytes");
+
+inline int group_of(int fmt) { return fmt == SVDQ_INT4_G64_FP16 ? 64 : 32; }
+// bytes of one activation/weight scale entry
+inline int scale_bytes_of(int fmt) { return fmt == SVDQ_INT4_G64_FP16 ? 2 : 1; }
+
+inline uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
+
+svdq_status validate_desc(const svdq_layer_desc* d);
+svdq_status validate_m(int M);
+bool aligned16(const void* p);
+svdq_blob_layout layout_of(const svdq_layer_desc& d);
+
+// Activation-side buffers inside a workspace: packed codes, scales, Tb.
+struct ActLayout {
+  uint64_t codes, scales, tb, total;
+  uint64_t codes_bytes, scales_bytes, tb_bytes;
+};
+ActLayout act_layout(const svdq_layer_desc& d, int M);
+
+}  // namespace svdq

@@ -1,0 +1,45 @@
+// Launchers of the libsvdq HIP kernels (internal; host-callable).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "svdq.h"
+
+namespace svdq {
+
+struct ActArgs {
+  const uint16_t* X;      // M x K bf16
+  int M, K, rank;
+  const float* inv_lam;   // K
+  const uint16_t* l1t;    // rank x K bf16
+  uint8_t* codes;         // M x K/2
+  void* scales;           // M x K/g (fp16 bits or E8M0 bytes)
+  uint16_t* Tb;           // M x rank bf16
+};
+
+// quant: write codes + scales; down: write Tb.
+hipError_t launch_act(int fmt, bool quant, bool down, const ActArgs& a, hipStream_t st);
+hipError_t launch_absmax(const uint16_t* X, int M, int K, float* out, bool accumulate, hipStream_t st);
+
+struct GemmArgs {
+  const uint8_t* acodes;  // M x K/2
+  const void* ascales;    // M x K/g
+  const uint8_t* wcodes;  // N x K/2
+  const void* wscales;    // K/g x N
+  const uint16_t* Tb;     // M x rank (slab A operand), may be null if rank == 0 or !slab
+  const uint16_t* l2t;    // N x rank (slab B operand)
+  const float* bias;      // N or null
+  void* Y;                // M x N, bf16 bits or fp32
+  int M, K, N, rank;
+};
+
+// slab: append the rank-r bf16 K-slab Tb L2b before the epilogue.
+hipError_t launch_gemm(int fmt, bool slab, int out_dtype, const GemmArgs& g, hipStream_t st);
+
+// Unfused up-projection: Y = round(Y + Tb L2b) in place.
+hipError_t launch_up(int out_dtype, const uint16_t* Tb, const uint16_t* l2t, void* Y, int M, int N,
+                     int rank, hipStream_t st);
+
+}  // namespace svdq

@@ -1,0 +1,63 @@
+// Small dense symmetric eigensolver for the offline SVD (host, no HIP).
+#include <algorithm>
+#include <cmath>
+#include <numeric>
+#include <vector>
+
+namespace svdq {
+
+void jacobi_eigh(int n, std::vector<double>& A, std::vector<double>& V, std::vector<double>& w) {
+  V.assign(static_cast<size_t>(n) * n, 0.0);
+  for (int i = 0; i < n; i++) V[static_cast<size_t>(i) * n + i] = 1.0;
+  auto a = [&](int i, int j) -> double& { return A[static_cast<size_t>(i) * n + j]; };
+  double diag2 = 0.0;
+  for (int i = 0; i < n; i++) diag2 += a(i, i) * a(i, i);
+  for (int sweep = 0; sweep < 100; sweep++) {
+    double off = 0.0, tot = diag2;
+    for (int p = 0; p < n; p++)
+      for (int q = p + 1; q < n; q++) off += a(p, q) * a(p, q);
+    tot = 0.0;
+    for (int i = 0; i < n; i++) tot += a(i, i) * a(i, i);
+    if (off <= 1e-32 * (tot + 2.0 * off) || off == 0.0) break;
+    for (int p = 0; p < n; p++) {
+      for (int q = p + 1; q < n; q++) {
+        const double apq = a(p, q);
+        if (apq == 0.0) continue;
+        const double theta = (a(q, q) - a(p, p)) / (2.0 * apq);
+        const double t = (theta >= 0 ? 1.0 : -1.0) / (std::fabs(theta) + std::sqrt(theta * theta + 1.0));
+        const double c = 1.0 / std::sqrt(t * t + 1.0), s = t * c;
+        for (int k = 0; k < n; k++) {  // columns p, q
+          const double akp = a(k, p), akq = a(k, q);
+          a(k, p) = c * akp - s * akq;
+          a(k, q) = s * akp + c * akq;
+        }
+        for (int k = 0; k < n; k++) {  // rows p, q
+          const double apk = a(p, k), aqk = a(q, k);
+          a(p, k) = c * apk - s * aqk;
+          a(q, k) = s * apk + c * aqk;
+        }
+        a(p, q) = 0.0;
+        a(q, p) = 0.0;
+        for (int k = 0; k < n; k++) {
+          double& vkp = V[static_cast<size_t>(k) * n + p];
+          double& vkq = V[static_cast<size_t>(k) * n + q];
+          const double x = vkp, y = vkq;
+          vkp = c * x - s * y;
+          vkq = s * x + c * y;
+        }
+      }
+    }
+  }
+  std::vector<int> order(n);
+  std::iota(order.begin(), order.end(), 0);
+  std::sort(order.begin(), order.end(), [&](int x, int y) { return a(x, x) > a(y, y); });
+  std::vector<double> Vs(static_cast<size_t>(n) * n);
+  w.resize(n);
+  for (int c = 0; c < n; c++) {
+    w[c] = a(order[c], order[c]);
+    for (int k = 0; k < n; k++) Vs[static_cast<size_t>(k) * n + c] = V[static_cast<size_t>(k) * n + order[c]];
+  }
+  V.swap(Vs);
+}
+
+}  // namespace svdq

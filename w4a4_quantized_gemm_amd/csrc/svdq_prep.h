@@ -1,0 +1,31 @@
+// Offline-preparation internals (host side).
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include "svdq.h"
+
+namespace svdq {
+
+struct PrepOptions {
+  int oversample = 64;    // extra subspace columns beyond the rank
+  int iterations = 32;    // subspace (power) iterations
+  uint64_t seed = 0x5344;  // seed of the Gaussian start block
+};
+
+// Symmetric eigendecomposition by cyclic Jacobi rotations.  A is n x n
+// row-major and is overwritten.  On return w holds the eigenvalues in
+// descending order and V (n x n row-major) the matching eigenvectors as
+// columns.
+void jacobi_eigh(int n, std::vector<double>& A, std::vector<double>& V, std::vector<double>& w);
+
+}  // namespace svdq
+
+#include <hip/hip_runtime.h>
+
+namespace svdq {
+svdq_status prepare_impl(const svdq_layer_desc& d, const uint16_t* W, const float* act_absmax,
+                         const uint16_t* bias, const uint16_t* L1, const uint16_t* L2, uint8_t* blob,
+                         hipStream_t st, const PrepOptions& opt);
+}  // namespace svdq

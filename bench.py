@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Benchmark of the SVDQuant W4A4 linear layer (fused low-rank branch) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--sweep]
+
+One step = one forward pass of the layer over one batch: the fused
+activation pass (smoothing + group quantization + rank-r down-projection)
+followed by the 4-bit GEMM with the low-rank slab and bias epilogue, i.e. one
+``svdq_linear`` call.  Offline weight preparation runs once, before timing.
+Inputs and prepared weights are resident in HBM when timing starts; every
+step works on the next of several copies of (X, blob, workspace, Y) whose
+total exceeds the 256 MB Infinity Cache, so no step is served from a warm
+last-level cache.
+
+Printed: one JSON line with the effective TOPS of the layer (2 M K N per
+layer time), the kernel roofline of the dominant kernel (the 4-bit GEMM,
+timed with HIP events on the stream it is launched on), the activation
+kernel's HBM roofline, the fused-versus-unfused speedup, and the CPU oracle's
+throughput on a bounded row sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks (dense)
+PEAK_TFLOPS = {"int4": 5000.0, "fp4": 10100.0}   # int8 MFMA (INT4 runs on it) / FP4 MFMA
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+INFINITY_CACHE = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2_qkv_4608x3072x9216_int4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="oracle row sample (0: automatic)")
+    ap.add_argument("--sweep", action="store_true", help="also time the shape sweep (one line each, to stderr)")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="short run for profilers: warmup + steps of the fused layer, no baseline")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "w4a4_quantized_gemm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(cfg):
+    """Algorithmic work of one layer call (per-unit figures x units)."""
+    M, K, N, r = cfg.M, cfg.K, cfg.N, cfg.rank
+    g = 64 if cfg.fmt == "int4" else 32
+    sbytes = 2 if cfg.fmt == "int4" else 1
+    q_bytes = 2 * M * K + M * K // 2 + M * (K // g) * sbytes + 2 * M * r + 2 * K * r + 4 * K
+    gemm_ops = 2 * M * K * N
+    slab_flops = 2 * M * r * N
+    gemm_bytes = (M * K // 2 + M * (K // g) * sbytes + N * K // 2 + (K // g) * N * sbytes
+                  + 2 * M * r + 2 * N * r + 2 * M * N + (4 * N if cfg.has_bias else 0))
+    return dict(q_bytes=q_bytes, gemm_ops=gemm_ops, slab_flops=slab_flops, gemm_bytes=gemm_bytes)
+
+
+class Rig:
+    """Device buffers for one workload, replicated to defeat the Infinity Cache."""
+
+    def __init__(self, cfg, torch, S, WL, O_bits_to_tensor):
+        self.cfg = cfg
+        dev = "cuda:0"
+        X_bits, W_bits, b_bits = WL.make_layer(cfg)
+        self.X_bits, self.W_bits, self.b_bits = X_bits, W_bits, b_bits
+        X = O_bits_to_tensor(X_bits, dev)
+        W = O_bits_to_tensor(W_bits, dev)
+        bias = None if b_bits is None else O_bits_to_tensor(b_bits, dev)
+        a = torch.empty(cfg.K, dtype=torch.float32, device=dev)
+        S.svdq_act_absmax(X, a)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        layer = S.SVDQLinear.prepare(W, a, cfg.rank, cfg.fmt, cfg.alpha, bias=bias)
+        torch.cuda.synchronize()
+        self.prep_s = time.perf_counter() - t0
+        self.layer = layer
+        del W
+        M, N = cfg.M, cfg.N
+        per_set = (X.numel() * 2 + layer.blob.numel() + S.svdq_workspace_bytes(layer.desc, M) + M * N * 2)
+        self.nsets = max(2, -(-2 * INFINITY_CACHE // per_set))
+        self.sets = []
+        c_b, s_b, t_b = S.svdq_act_sizes(layer.desc, M)
+        for i in range(self.nsets):
+            Xi = X if i == 0 else X.clone()
+            bi = layer.blob if i == 0 else layer.blob.clone()
+            ws = torch.empty(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev)
+            Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            codes = torch.empty(c_b, dtype=torch.uint8, device=dev)
+            scales = torch.empty(s_b, dtype=torch.uint8, device=dev)
+            T = torch.empty(max(t_b // 2, 1), dtype=torch.bfloat16, device=dev)
+            self.sets.append(dict(X=Xi, blob=bi, ws=ws, Y=Y, codes=codes, scales=scales, T=T))
+        self.working_set = per_set * self.nsets
+        torch.cuda.synchronize()
+
+
+def time_fused(torch, S, rig, steps, warmup, unfused=False):
+    d = rig.layer.desc
+    fn = S.svdq_linear_unfused if unfused else S.svdq_linear
+    n = rig.nsets
+    for k in range(warmup):
+        s = rig.sets[k % n]
+        fn(d, s["blob"], s["X"], s["Y"], s["ws"], S.OUT_BF16)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for k in range(steps):
+        s = rig.sets[k % n]
+        fn(d, s["blob"], s["X"], s["Y"], s["ws"], S.OUT_BF16)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def time_kernels(torch, S, rig, steps, warmup):
+    """Per-kernel durations with events on the launch stream: the activation
+    pass (svdq_quantize_act) and the GEMM (svdq_gemm), which together are the
+    same two launches as svdq_linear."""
+    d = rig.layer.desc
+    n = rig.nsets
+    M = rig.cfg.M
+
+    def one(s, evs=None):
+        if evs:
+            evs[0].record()
+        S.svdq_quantize_act(d, s["blob"], s["X"], s["codes"], s["scales"], s["T"] if d.rank else None)
+        if evs:
+            evs[1].record()
+        S.svdq_gemm(d, s["blob"], s["codes"], s["scales"], s["T"] if d.rank else None, M, s["Y"], S.OUT_BF16)
+        if evs:
+            evs[2].record()
+
+    for k in range(warmup):
+        one(rig.sets[k % n])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for k in range(steps):
+        one(rig.sets[k % n], evs[k])
+    torch.cuda.synchronize()
+    tq = [e[0].elapsed_time(e[1]) for e in evs]
+    tg = [e[1].elapsed_time(e[2]) for e in evs]
+    return tq, tg
+
+
+def cpu_baseline(rig, rows_req):
+    """The oracle as it stands, on a row sample of the same workload."""
+    import numpy as np
+    import oracle as O
+    from threadpoolctl import threadpool_info
+    cfg = rig.cfg
+    sec = rig.layer.blob.cpu().numpy()
+    import w4a4_quantized_gemm_amd as S
+    L = S.svdq_blob_layout_of(rig.layer.desc)
+    r, K, N = cfg.rank, cfg.K, cfg.N
+    l1t = sec[L.l1t:L.l1t + 2 * r * K].view(np.uint16).reshape(r, K)
+    l2t = sec[L.l2t:L.l2t + 2 * N * r].view(np.uint16).reshape(N, r)
+    factors = (O.bf16_bits_to_f64(l1t).T.copy(), O.bf16_bits_to_f64(l2t).T.copy())
+    t0 = time.perf_counter()
+    prep = O.prepare(rig.W_bits, O.act_absmax(rig.X_bits), alpha=cfg.alpha, rank=r, fmt=cfg.fmt,
+                     bias_bits=rig.b_bits, factors=factors)
+    prep_s = time.perf_counter() - t0
+    rows = rows_req
+    if rows <= 0:
+        # size the sample for roughly 10-20 s of oracle work: time a small probe first
+        probe = 64
+        t0 = time.perf_counter()
+        O.linear(prep, rig.X_bits[:probe], "bf16")
+        dt = time.perf_counter() - t0
+        rows = int(min(cfg.M, max(probe, 12.0 / max(dt, 1e-3) * probe)))
+    t0 = time.perf_counter()
+    O.linear(prep, rig.X_bits[:rows], "bf16")
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    tops = 2.0 * rows * K * N / dt / 1e12
+    return {"value": tops, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {cfg.M} token rows of the same layer (oracle.linear: act quantization, "
+                      f"down-projection, fp64 dequantized product, low-rank, bias); weight prep "
+                      f"({prep_s:.1f} s) excluded",
+            "seconds": dt, "cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def load_traffic(workload, src_hash):
+    """HBM traffic of the GEMM kernel from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"gemm_{workload}_hbm_counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != src_hash:
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def run_config(args, cfg, torch, S, WL, to_tensor, with_cpu):
+    rig = Rig(cfg, torch, S, WL, to_tensor)
+    ms_fused, wall = time_fused(torch, S, rig, args.steps, args.warmup)
+    tq, tg = time_kernels(torch, S, rig, args.steps, args.warmup)
+    ms_unfused, _ = time_fused(torch, S, rig, args.steps, args.warmup, unfused=True)
+    A = algorithmic(cfg)
+    tq_ms, tg_ms = statistics.mean(tq), statistics.mean(tg)
+    out = dict(rig=rig, ms_fused=ms_fused, wall=wall, ms_unfused=ms_unfused, tq=tq, tg=tg, A=A,
+               tq_ms=tq_ms, tg_ms=tg_ms)
+    if with_cpu:
+        out["cpu"] = cpu_baseline(rig, args.cpu_rows)
+    return out
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world > 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the layer's multi-GPU "
+                                   "sharding is a design note, not built (use --gpus 1)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import w4a4_quantized_gemm_amd as S
+    import workloads as WL
+    import numpy as np
+
+    def to_tensor(bits, dev):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    S.load()
+    cfgs = {c.name: c for c in list(WL.CONFIGS.values()) + WL.sweep_configs()}
+    cfg = cfgs[args.workload]
+
+    if args.profile_only:
+        rig = Rig(cfg, torch, S, WL, to_tensor)
+        ms, _ = time_fused(torch, S, rig, args.steps, args.warmup)
+        tq, tg = time_kernels(torch, S, rig, args.steps, args.warmup)
+        print(json.dumps({"workload": cfg.name, "ms_per_step": ms, "quant_ms": statistics.mean(tq),
+                          "gemm_ms": statistics.mean(tg)}), flush=True)
+        return
+
+    r = run_config(args, cfg, torch, S, WL, to_tensor, with_cpu=not args.no_cpu_baseline)
+    A, rig = r["A"], r["rig"]
+    fmt = cfg.fmt
+    t_layer_s = r["ms_fused"] / 1e3
+    tops = A["gemm_ops"] / t_layer_s / 1e12
+    gemm_tops = A["gemm_ops"] / (r["tg_ms"] / 1e3) / 1e12
+    q_gbs = A["q_bytes"] / (r["tq_ms"] / 1e3) / 1e9
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(cfg.name, src_hash)
+    line = {
+        "metric": "W4A4+low-rank linear effective TOPS & % MFMA peak; fused vs unfused speedup",
+        "value": tops,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_fused"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4" if fmt == "int4" else "fp4-e2m1",
+        "data": "synthetic (seeded generators with the workload's shapes and outlier structure; no checkpoint)",
+        "config": {"workload": cfg.name, "M": cfg.M, "K": cfg.K, "N": cfg.N, "rank": cfg.rank,
+                   "format": "int4_g64_fp16" if fmt == "int4" else "fp4_e2m1_g32_e8m0",
+                   "bias": cfg.has_bias, "out": "bf16"},
+        "roofline": {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_TFLOPS[fmt], "unit": "TFLOP/s",
+                     "frac": gemm_tops / PEAK_TFLOPS[fmt], "traffic": traffic,
+                     "kernel": f"gemm_kernel<{fmt}> (4-bit GEMM + rank-{cfg.rank} bf16 slab + bias)",
+                     "avg_us": r["tg_ms"] * 1e3},
+        "roofline_quant": {"bound": "hbm", "achieved": q_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": q_gbs / PEAK_HBM_GBS, "kernel": "act_kernel (smooth + quantize + down-proj)",
+                           "avg_us": r["tq_ms"] * 1e3, "bytes": A["q_bytes"]},
+        "us_per_layer": r["ms_fused"] * 1e3,
+        "us_per_layer_unfused": r["ms_unfused"] * 1e3,
+        "fused_vs_unfused_speedup": r["ms_unfused"] / r["ms_fused"],
+        "gemm_effective_tops": gemm_tops,
+        "slab_share_of_ops": A["slab_flops"] / A["gemm_ops"],
+        "prep_seconds": rig.prep_s,
+        "working_set_mb": rig.working_set / 2 ** 20,
+        "buffer_sets": rig.nsets,
+        "kernel_source_hash": src_hash,
+        "blob_bytes": int(rig.layer.blob.numel()),
+        "blob_vs_bf16_weight": rig.layer.blob.numel() / (2 * cfg.K * cfg.N),
+    }
+    if "cpu" in r:
+        line["cpu_baseline"] = r["cpu"]
+    print(json.dumps(line), flush=True)
+
+    if args.sweep:
+        for c in WL.sweep_configs():
+            rr = run_config(args, c, torch, S, WL, to_tensor, with_cpu=False)
+            A = rr["A"]
+            rec = {"workload": c.name, "us_per_layer": rr["ms_fused"] * 1e3,
+                   "us_unfused": rr["ms_unfused"] * 1e3, "speedup": rr["ms_unfused"] / rr["ms_fused"],
+                   "effective_tops": A["gemm_ops"] / (rr["ms_fused"] / 1e3) / 1e12,
+                   "gemm_frac_int8_peak": A["gemm_ops"] / (rr["tg_ms"] / 1e3) / 1e12 / PEAK_TFLOPS["int4"],
+                   "quant_gbs": A["q_bytes"] / (rr["tq_ms"] / 1e3) / 1e9}
+            print(json.dumps(rec), file=sys.stderr, flush=True)
+            del rr
+            torch.cuda.empty_cache()
+
+
+if __name__ == "__main__":
+    main()

@@ -182,6 +182,16 @@ svdq_status svdq_linear(const svdq_layer_desc* desc, const void* d_prepared, con
                         int M, void* d_Y, int out_dtype, void* d_workspace, size_t ws_bytes,
                         void* stream);
 
+/* The GEMM stage of svdq_linear on its own: Y = Q(x_hat) Q(R) + Tb L2b + b
+ * from activations already produced by svdq_quantize_act with the same blob
+ * (d_codes, d_scales, d_T in its output layouts; d_T may be NULL when
+ * rank == 0).  svdq_linear is svdq_quantize_act followed by this call; the
+ * split lets a caller time, overlap or reorder the two stages.
+ * Asynchronous. */
+svdq_status svdq_gemm(const svdq_layer_desc* desc, const void* d_prepared, const void* d_codes,
+                      const void* d_scales, const void* d_T, int M, void* d_Y, int out_dtype,
+                      void* stream);
+
 /* The same layer computed the naive way, as separate kernels (walkthrough,
  * Nunchaku section: a separately run low-rank branch re-reads the 16-bit
  * activation and writes a 16-bit output again; Table 4's "SVDQuant" column):

@@ -35,7 +35,7 @@ STATUS_NAMES = {
 EXPORTED = (
     "svdq_status_string", "svdq_version", "svdq_prepared_bytes", "svdq_workspace_bytes",
     "svdq_act_sizes", "svdq_act_absmax", "svdq_prepare_weights", "svdq_check_blob",
-    "svdq_quantize_act", "svdq_linear", "svdq_linear_unfused", "svdq_blob_layout_of",
+    "svdq_quantize_act", "svdq_gemm", "svdq_linear", "svdq_linear_unfused", "svdq_blob_layout_of",
 )
 
 
@@ -82,6 +82,7 @@ def _lib() -> ctypes.CDLL:
             "svdq_prepare_weights": ([D, P, P, P, P, P, P, Z, P], S),
             "svdq_check_blob": ([D, P, P], S),
             "svdq_quantize_act": ([D, P, P, I, P, P, P, P], S),
+            "svdq_gemm": ([D, P, P, P, P, I, P, I, P], S),
             "svdq_linear": ([D, P, P, I, P, I, P, Z, P], S),
             "svdq_linear_unfused": ([D, P, P, I, P, I, P, Z, P], S),
             "svdq_blob_layout_of": ([D, ctypes.POINTER(BlobLayout)], S),
@@ -169,6 +170,13 @@ def svdq_quantize_act(desc: LayerDesc, prepared, X, codes, scales, T=None, strea
     M = X.shape[0]
     _check(_lib().svdq_quantize_act(ctypes.byref(desc), _ptr(prepared), _ptr(X), M, _ptr(codes),
                                     _ptr(scales), _ptr(T), _stream(stream)), "svdq_quantize_act")
+
+
+def svdq_gemm(desc: LayerDesc, prepared, codes, scales, T, M: int, Y, out_dtype: int = OUT_BF16,
+              stream=None):
+    """The GEMM stage alone, on the outputs of svdq_quantize_act."""
+    _check(_lib().svdq_gemm(ctypes.byref(desc), _ptr(prepared), _ptr(codes), _ptr(scales), _ptr(T), M,
+                            _ptr(Y), out_dtype, _stream(stream)), "svdq_gemm")
 
 
 def svdq_linear(desc: LayerDesc, prepared, X, Y, workspace, out_dtype: int = OUT_BF16, stream=None):

@@ -192,6 +192,31 @@ svdq_status svdq_quantize_act(const svdq_layer_desc* desc, const void* d_prepare
   return from_hip(launch_act(desc->fmt, true, desc->rank > 0, a, as_stream(stream)));
 }
 
+svdq_status svdq_gemm(const svdq_layer_desc* desc, const void* d_prepared, const void* d_codes,
+                      const void* d_scales, const void* d_T, int M, void* d_Y, int out_dtype, void* stream) {
+  svdq_status st = validate_runtime(desc, d_prepared, d_codes, M);
+  if (st != SVDQ_OK) return st;
+  if (!d_scales || !d_Y || (desc->rank > 0 && !d_T)) return SVDQ_ERR_INVALID_ARGUMENT;
+  if (out_dtype != SVDQ_OUT_BF16 && out_dtype != SVDQ_OUT_F32) return SVDQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(d_scales) || !aligned16(d_Y) || (d_T && !aligned16(d_T))) return SVDQ_ERR_MISALIGNED;
+  if ((st = check_device()) != SVDQ_OK) return st;
+  const BlobPtrs bp = blob_ptrs(*desc, d_prepared);
+  GemmArgs g;
+  g.acodes = static_cast<const uint8_t*>(d_codes);
+  g.ascales = d_scales;
+  g.wcodes = bp.wcodes;
+  g.wscales = bp.wscales;
+  g.Tb = static_cast<const uint16_t*>(d_T);
+  g.l2t = bp.l2t;
+  g.bias = bp.bias;
+  g.Y = d_Y;
+  g.M = M;
+  g.K = desc->K;
+  g.N = desc->N;
+  g.rank = desc->rank;
+  return from_hip(launch_gemm(desc->fmt, desc->rank > 0, out_dtype, g, as_stream(stream)));
+}
+
 svdq_status svdq_linear(const svdq_layer_desc* desc, const void* d_prepared, const void* d_X, int M, void* d_Y,
                         int out_dtype, void* d_workspace, size_t ws_bytes, void* stream) {
   return run_layer(desc, d_prepared, d_X, M, d_Y, out_dtype, d_workspace, ws_bytes, stream, false);

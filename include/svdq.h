@@ -211,7 +211,7 @@ svdq_status svdq_linear_unfused(const svdq_layer_desc* desc, const void* d_prepa
  *   l1t         bf16[rank][K]    (L1 transposed: row t holds column t of L1)
  *   l2t         bf16[N][rank]    (L2 transposed: row n holds column n of L2)
  *   wcodes      u8[N][K/2]       (column n's K residual codes, packed)
- *   wscales     INT4: u16 fp16 bits [K/64][N]; FP4: u8 E8M0 [K/32][N]
+ *   wscales     INT4: u16 fp16 bits [N][K/64]; FP4: u8 E8M0 [N][K/32]
  *   bias        fp32[N]          (offset 0 when the layer has no bias) */
 typedef struct svdq_blob_layout {
   uint64_t header, lambda, inv_lambda, l1t, l2t, wcodes, wscales, bias, total;

@@ -51,11 +51,11 @@ def blob_sections(layer):
     nib = O.unpack_nibbles(raw_codes)                       # N x K
     if d.fmt == INT4:
         codes = O.nibble_to_int4(nib).T.copy()
-        raw_scales = sec(L.wscales, 2 * (K // g) * N).view(np.uint16).reshape(K // g, N)
+        raw_scales = sec(L.wscales, 2 * (K // g) * N).view(np.uint16).reshape(N, K // g).T
         scales = O.fp16_bits_to_f64(raw_scales)
     else:
         codes = nib.T.copy()
-        raw_scales = sec(L.wscales, (K // g) * N).reshape(K // g, N)
+        raw_scales = sec(L.wscales, (K // g) * N).reshape(N, K // g).T
         scales = raw_scales.astype(np.int32) - 127
     bias = None
     if d.flags & 4:

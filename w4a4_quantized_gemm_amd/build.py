@@ -29,8 +29,10 @@ ARCH = "gfx950"
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall"]
 # packed fp32 VALU ops are disabled for every device compilation
+# private arrays stay in registers/scratch rather than being promoted into
+# LDS, which the GEMM kernels size and use themselves
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-fno-gpu-rdc", "-ffp-contract=off"]
+             "-fno-gpu-rdc", "-ffp-contract=off", "-mllvm", "-disable-promote-alloca-to-lds"]
 
 
 def _compile(src: str) -> str:

@@ -1,27 +1,37 @@
 // Kernel G: the 4-bit GEMM of the SVDQuant layer with the low-rank
 // up-projection appended as an extra bf16 K-slab and a fused bias epilogue.
 //
-//   acc[i, n]  = sum_g s_x[i, g] s_w[g, n] sum_{k in g} q_x[i, k] q_w[k, n]
-//                                              (walkthrough eq. (2) per group)
-//   acc[i, n] += sum_t Tb[i, t] L2b[t, n]      (eq. (5) low-rank branch, Fig. 6:
-//                                               it shares the 4-bit branch's output)
+//   acc[i, n]  = sum_t Tb[i, t] L2b[t, n]      (eq. (5) low-rank branch; the
+//                                               walkthrough's Fig. 6: it shares
+//                                               the 4-bit branch's output)
+//   acc[i, n] += sum_g s_x[i, g] s_w[g, n] sum_{k in g} q_x[i, k] q_w[k, n]
+//                                              (eq. (2) per group)
 //   Y[i, n]    = round(acc[i, n] + b[n])
 //
-// INT4 (group 64, fp16 scales): the packed nibbles of a 64-wide K step are
-// moved to LDS, and on the way from LDS to the registers each nibble is
-// widened to a byte holding 16 * q (shift into the high half of the byte, so
-// the sign comes for free); two 32x32x32 i8 MFMAs give 256 * P_g exactly in
-// int32 and the group is dequantized into fp32 accumulators with
-// s_x * s_w / 256.
+// INT4 (group 64, fp16 scales): the packed nibbles of each K stage are moved
+// to LDS; on the way from LDS to the registers each nibble is widened to a
+// byte holding 16 * q (shifted into the high half of the byte, so the sign
+// comes for free); two 32x32x32 i8 MFMAs give 256 * P_g exactly in int32 and
+// the group is dequantized into the fp32 accumulators with s_x * s_w / 256.
+// The MFMAs of the next output tile are issued before the dequantization of
+// the current one, so the matrix core and the VALU overlap.
 // FP4 (group 32, E8M0 scales): the E2M1 nibbles and the power-of-two scales
 // are the native operands of the gfx950 block-scaled MFMA (32x32x64), which
 // accumulates in fp32 directly; there is no dequantization work.
 //
-// Tiling: 128 x 128 output tile per workgroup, 4 waves in a 2 x 2 grid, each
-// wave 64 x 64 = 2 x 2 MFMA tiles of 32 x 32; K step 64; LDS double buffer
-// with one barrier per step.  In every MFMA, lane l owns row (or column)
-// l % 32 and the 16-byte half l / 32 of the K step, for A and B alike, so
-// both operands enumerate K in the same order.
+// Tiling (see Shape): 4 waves per workgroup, FP4 256 x 256, INT4 128 x 128;
+// 32 x 32 MFMA tiles.  A K stage is 128 wide (two
+// 64-wide MFMA steps); the LDS holds two stages, the global loads of a stage
+// are issued three stages before its MFMAs (two register sets), and each
+// stage has one barrier.  In every
+// MFMA, lane l owns row (column) l % 32 and the 16-byte half l / 32 of the
+// 64-wide K step, for A and B alike, so both operands enumerate K in the same
+// order.  Workgroups are mapped to tiles so that the workgroups resident on
+// one XCD (the hardware deals them round-robin to the 8 XCDs) cover a
+// compact block of tiles that shares rows of A and columns of B in that
+// XCD's L2.
+#include <type_traits>
+
 #include "svdq_device.h"
 #include "svdq_kernels.h"
 
@@ -29,15 +39,15 @@ namespace svdq {
 
 namespace {
 
-constexpr int BM = 128;
-constexpr int BN = 128;
-constexpr int LDS_STRIDE = 48;  // 32 data bytes per row + 16 pad bytes (bank spread)
+constexpr int BKB = 64;          // code bytes per row per stage (128 K values)
+constexpr int NXCD = 8;
+constexpr int GROUP_TM = 4;      // tile rows per L2 group
 
 __device__ __forceinline__ uint32_t lo_nib_bytes(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
 __device__ __forceinline__ uint32_t hi_nib_bytes(uint32_t w) { return w & 0xF0F0F0F0u; }
 
-template <int OUT>
-__device__ __forceinline__ void store_out(void* Y, long idx, float v) {
+template <int OUT, typename I>
+__device__ __forceinline__ void store_out(void* Y, I idx, float v) {
   if constexpr (OUT == SVDQ_OUT_F32) {
     reinterpret_cast<float*>(Y)[idx] = v;
   } else {
@@ -45,8 +55,8 @@ __device__ __forceinline__ void store_out(void* Y, long idx, float v) {
   }
 }
 
-template <int OUT>
-__device__ __forceinline__ float load_out(const void* Y, long idx) {
+template <int OUT, typename I>
+__device__ __forceinline__ float load_out(const void* Y, I idx) {
   if constexpr (OUT == SVDQ_OUT_F32) {
     return reinterpret_cast<const float*>(Y)[idx];
   } else {
@@ -54,198 +64,331 @@ __device__ __forceinline__ float load_out(const void* Y, long idx) {
   }
 }
 
+// workgroup id -> (tile_m, tile_n): contiguous tile ranges per XCD, grouped
+// GROUP_TM tile rows at a time inside each range.
+__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int T = tiles_m * tiles_n;
+  const int q = T / NXCD, rem = T % NXCD;
+  const int x = b % NXCD, j = b / NXCD;
+  const int t = x * q + (x < rem ? x : rem) + j;
+  const int per_group = GROUP_TM * tiles_n;
+  const int grp = t / per_group;
+  const int first = grp * GROUP_TM;
+  const int gm = min(GROUP_TM, tiles_m - first);
+  const int w = t - grp * per_group;
+  tm = first + w % gm;
+  tn = w / gm;
+}
+
 }  // namespace
+
+// Per-format tile shape, all with 4 waves in a 2 x 2 grid:
+//  FP4: each wave owns 128 x 128 (4 x 4 MFMA tiles, 256 fp32 accumulators
+//       that only the MFMAs touch, so they live in AGPRs); 256 x 256 per
+//       workgroup.
+//  INT4: the per-group dequantization updates the accumulators with VALU
+//       fma, so they must be VGPRs; each wave owns 64 x 64 (2 x 2 tiles);
+//       128 x 128 per workgroup.
+template <int FMT>
+struct Shape {
+  static constexpr bool I4 = FMT == SVDQ_INT4_G64_FP16;
+  static constexpr int RB = I4 ? 2 : 4;   // 32-row blocks per wave
+  static constexpr int CB = I4 ? 2 : 4;   // 32-column blocks per wave
+  static constexpr int NTHREADS = 256;
+  static constexpr int BM = 2 * RB * 32;
+  static constexpr int BN = 2 * CB * 32;
+};
+
+// LDS layout of one K stage (128 K values = 64 code bytes per row): the
+// 16-byte chunk c (0..3) of row r lives in the 1 KB block of MFMA operand
+// (r / 32, step c / 2), at slot 32 * (c % 2) + ((r % 32) ^ (2 * c)).  Lane
+// l of an MFMA reads slot l ^ (2 * c) of its block: every group of 8 lanes
+// covers the 8 distinct 16-byte bank positions of a 128-byte window, and so
+// do the 8 chunks (4 per row, 2 rows) that 8 consecutive threads store.
+__device__ __forceinline__ int lds_chunk_offset(int row, int c) {
+  return (((row >> 5) * 2 + (c >> 1)) << 10) + ((((c & 1) << 5) | ((row & 31) ^ (2 * c))) << 4);
+}
 
 template <int FMT, bool SLAB, int OUT>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) float sSA[2][BM];   // INT4: s_x of the step's group
-  __shared__ __attribute__((aligned(16))) float sSB[2][BN];   // INT4: s_w / 256
-  __shared__ __attribute__((aligned(16))) uint8_t sEA[2][BM * 2];  // FP4: E8M0 [row][block]
-  __shared__ __attribute__((aligned(16))) uint8_t sEB[2][BN * 2];
+  using SH = Shape<FMT>;
+  constexpr int BM = SH::BM, BN = SH::BN, RB = SH::RB, CB = SH::CB;
+  constexpr int NTHREADS = SH::NTHREADS;
+  constexpr int A_CH = BM * 4 / NTHREADS, B_CH = BN * 4 / NTHREADS;   // 16-byte chunks per thread
+  constexpr bool I4 = SH::I4;
+  // LDS: two stage buffers of A and B codes plus their scales; the
+  // epilogue reuses the code buffers to stage the output tile.
+  // INT4 scales: [stage][group][row] fp32 (B pre-divided by 256); FP4: the
+  // 4 E8M0 bytes of a row (column) per stage as one word, in [.][0][row].
+  constexpr int NSG = I4 ? 2 : 1;
+  constexpr int LDS_A = 2 * BM * BKB, LDS_B = 2 * BN * BKB;
+  constexpr int LDS_SA = 2 * NSG * BM * 4, LDS_SB = 2 * NSG * BN * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_A + LDS_B + LDS_SA + LDS_SB];
+  auto sA = reinterpret_cast<uint8_t(*)[BM * BKB]>(smem);
+  auto sB = reinterpret_cast<uint8_t(*)[BN * BKB]>(smem + LDS_A);
+  auto sSA = reinterpret_cast<uint32_t(*)[NSG][BM]>(smem + LDS_A + LDS_B);
+  auto sSB = reinterpret_cast<uint32_t(*)[NSG][BN]>(smem + LDS_A + LDS_B + LDS_SA);
 
-  const int M = g.M, K = g.K, N = g.N;
-  const int tiles_n = (N + BN - 1) / BN;
-  const int tile_m = blockIdx.x / tiles_n;
-  const int tile_n = blockIdx.x % tiles_n;
-  const long m0 = static_cast<long>(tile_m) * BM;
-  const long n0 = static_cast<long>(tile_n) * BN;
+  // kernel arguments in registers (a lambda capturing g would read them
+  // from the argument segment with vector loads)
+  const int M = g.M, K = g.K, N = g.N, rank = g.rank;
+  const uint8_t* __restrict__ acodes = g.acodes;
+  const uint8_t* __restrict__ wcodes = g.wcodes;
+  const uint32_t* __restrict__ ascales = static_cast<const uint32_t*>(g.ascales);
+  const uint32_t* __restrict__ wscales = static_cast<const uint32_t*>(g.wscales);
+  const uint16_t* __restrict__ Tb = g.Tb;
+  const uint16_t* __restrict__ l2t = g.l2t;
+  const float* __restrict__ bias = g.bias;
+  void* __restrict__ Yout = g.Y;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const long m0 = static_cast<long>(tm) * BM;
+  const long n0 = static_cast<long>(tn) * BN;
 
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, lh = lane >> 5;
-  const int ld_r = t >> 1, ld_h = t & 1;
-  const long KB = K / 2;             // bytes per code row
-  const int steps = K / 64;
+  const long KB = K / 2;                         // code bytes per row
+  const int SW = K / 128;                        // scale words (4 bytes) per row
+  const int stages = K / 128;
+  const int wrow0 = wm * (RB * 32), wcol0 = wn * (CB * 32);
 
-  f32x16 acc[2][2];
+  f32x16 acc[RB][CB];
 #pragma unroll
-  for (int i = 0; i < 2; i++)
+  for (int i = 0; i < RB; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++)
+    for (int j = 0; j < CB; j++)
 #pragma unroll
       for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
-  // ---- global -> registers for one K step
-  uint4 ra, rb;
-  uint32_t rs0 = 0, rs1 = 0;
-  auto load_step = [&](int s) {
-    const long am = m0 + ld_r, bn = n0 + ld_r;
-    ra = am < M ? *reinterpret_cast<const uint4*>(g.acodes + am * KB + s * 32 + ld_h * 16)
-                : make_uint4(0u, 0u, 0u, 0u);
-    rb = bn < N ? *reinterpret_cast<const uint4*>(g.wcodes + bn * KB + s * 32 + ld_h * 16)
-                : make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (FMT == SVDQ_INT4_G64_FP16) {
-      if (t < BM) {
-        const long r = m0 + t;
-        rs0 = r < M ? reinterpret_cast<const uint16_t*>(g.ascales)[r * (K / 64) + s] : 0u;
-      } else {
-        const long c = n0 + (t - BM);
-        rs0 = c < N ? reinterpret_cast<const uint16_t*>(g.wscales)[static_cast<long>(s) * N + c] : 0u;
+  // ---- low-rank up-projection first (K = rank, bf16 MFMA).  Rows
+  // (columns) past M (N) are clamped to the last valid one: their outputs
+  // are computed from real data and never stored, and every load stays
+  // unconditional.
+  if constexpr (SLAB) {
+    for (int tb = 0; tb < rank / 16; tb++) {
+      bf16x8 b[CB];
+#pragma unroll
+      for (int j = 0; j < CB; j++) {
+        const long c = min(n0 + wcol0 + j * 32 + l32, static_cast<long>(N - 1));
+        b[j] = *reinterpret_cast<const bf16x8*>(l2t + c * rank + tb * 16 + lh * 8);
       }
-    } else {
-      if (t < BM) {
-        const long r = m0 + t;
-        rs0 = r < M ? reinterpret_cast<const uint16_t*>(g.ascales)[(r * (K / 32) + 2 * s) / 2] : 0x7F7Fu;
-      } else {
-        const long c = n0 + (t - BM);
-        const uint8_t* ws = reinterpret_cast<const uint8_t*>(g.wscales);
-        rs0 = c < N ? ws[static_cast<long>(2 * s) * N + c] : 127u;
-        rs1 = c < N ? ws[static_cast<long>(2 * s + 1) * N + c] : 127u;
+#pragma unroll
+      for (int i = 0; i < RB; i++) {
+        const long r = min(m0 + wrow0 + i * 32 + l32, static_cast<long>(M - 1));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Tb + r * rank + tb * 16 + lh * 8);
+#pragma unroll
+        for (int j = 0; j < CB; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[j], acc[i][j], 0, 0, 0);
       }
     }
+  }
+
+  // ---- global -> registers -> LDS.  Thread t loads chunks q = t + 256 i:
+  // row q / 4, chunk q % 4 (four consecutive threads read one row's 64
+  // contiguous bytes), plus one scale word of an A row (t < BM) or of a B
+  // column (t >= BM; FP4 tiles have BM = 256 = all threads, so their B word
+  // is a second load).
+  struct Regs {
+    u32x4 a[A_CH], b[B_CH];
+    uint32_t sa, sb;
   };
-  auto store_step = [&](int buf) {
-    *reinterpret_cast<uint4*>(&sA[buf][ld_r * LDS_STRIDE + ld_h * 16]) = ra;
-    *reinterpret_cast<uint4*>(&sB[buf][ld_r * LDS_STRIDE + ld_h * 16]) = rb;
-    if constexpr (FMT == SVDQ_INT4_G64_FP16) {
-      const float f = __half2float(__ushort_as_half(static_cast<unsigned short>(rs0)));
-      if (t < BM) sSA[buf][t] = f;
-      else sSB[buf][t - BM] = f * (1.0f / 256.0f);
+  auto load_stage = [&](Regs& r, int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < A_CH; i++) {
+      const int q = t + i * NTHREADS;
+      const long row = min(m0 + (q >> 2), static_cast<long>(M - 1));
+      r.a[i] = *reinterpret_cast<const u32x4*>(acodes + row * KB + st * BKB + (q & 3) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; i++) {
+      const int q = t + i * NTHREADS;
+      const long row = min(n0 + (q >> 2), static_cast<long>(N - 1));
+      r.b[i] = *reinterpret_cast<const u32x4*>(wcodes + row * KB + st * BKB + (q & 3) * 16);
+    }
+    if constexpr (I4) {
+      // 128 threads per operand
+      const bool is_a = t < BM;
+      const long row = is_a ? min(m0 + t, static_cast<long>(M - 1)) : min(n0 + (t - BM), static_cast<long>(N - 1));
+      r.sa = (is_a ? ascales : wscales)[row * SW + st];
     } else {
-      if (t < BM) {
-        sEA[buf][2 * t] = static_cast<uint8_t>(rs0 & 0xFFu);
-        sEA[buf][2 * t + 1] = static_cast<uint8_t>(rs0 >> 8);
-      } else {
-        sEB[buf][2 * (t - BM)] = static_cast<uint8_t>(rs0);
-        sEB[buf][2 * (t - BM) + 1] = static_cast<uint8_t>(rs1);
-      }
+      r.sa = ascales[min(m0 + t, static_cast<long>(M - 1)) * SW + st];
+      r.sb = wscales[min(n0 + t, static_cast<long>(N - 1)) * SW + st];
+    }
+  };
+  auto store_stage = [&](const Regs& r, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < A_CH; i++) {
+      const int q = t + i * NTHREADS;
+      *reinterpret_cast<u32x4*>(&sA[buf][lds_chunk_offset(q >> 2, q & 3)]) = r.a[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; i++) {
+      const int q = t + i * NTHREADS;
+      *reinterpret_cast<u32x4*>(&sB[buf][lds_chunk_offset(q >> 2, q & 3)]) = r.b[i];
+    }
+    if constexpr (I4) {
+      const float mul = t < BM ? 1.0f : 1.0f / 256.0f;
+      uint32_t(*ss)[BM] = t < BM ? sSA[buf] : sSB[buf];
+      const int idx = t < BM ? t : t - BM;
+      ss[0][idx] = __float_as_uint(__half2float(__ushort_as_half(static_cast<unsigned short>(r.sa & 0xFFFFu))) * mul);
+      ss[1][idx] = __float_as_uint(__half2float(__ushort_as_half(static_cast<unsigned short>(r.sa >> 16))) * mul);
+    } else {
+      sSA[buf][0][t] = r.sa;
+      sSB[buf][0][t] = r.sb;
     }
   };
 
-  load_step(0);
-  store_step(0);
+  // Stage k's codes are loaded into register set R[k % 2].  Schedule of
+  // stage s: (1) store register set R[(s + 1) % 2] (stage s + 1, loaded two
+  // stages earlier) to the other LDS buffer, (2) reuse that set for the
+  // global loads of stage s + 3, (3) run the MFMAs of stage s, (4) barrier.
+  // Loads past the last stage re-read the last stage (their data is never
+  // used), so that every stage issues the same loads and the compiler's
+  // wait counts stay exact across the loop.
+  Regs R0, R1;
+  const int last = stages - 1;
+  load_stage(R0, 0);
+  load_stage(R1, min(1, last));
+  store_stage(R0, 0);
+  load_stage(R0, min(2, last));
   __syncthreads();
 
-  for (int s = 0; s < steps; s++) {
-    const int buf = s & 1;
-    if (s + 1 < steps) load_step(s + 1);
+  auto stage_body = [&](int s, Regs& Rn, auto BUF) __attribute__((always_inline)) {
+    constexpr int buf = decltype(BUF)::value;
+    store_stage(Rn, buf ^ 1);
+    load_stage(Rn, min(s + 3, last));
+    __builtin_amdgcn_sched_barrier(0);
 
-    uint4 av[2], bv[2];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
-      av[i] = *reinterpret_cast<const uint4*>(&sA[buf][(wm * 64 + i * 32 + l32) * LDS_STRIDE + lh * 16]);
+    for (int j = 0; j < 2; j++) {          // two 64-wide MFMA steps per stage
+      const int c = 2 * j + lh;            // this lane's chunk of the stage
+      u32x4 av[RB], bv[CB];
 #pragma unroll
-    for (int j = 0; j < 2; j++)
-      bv[j] = *reinterpret_cast<const uint4*>(&sB[buf][(wn * 64 + j * 32 + l32) * LDS_STRIDE + lh * 16]);
+      for (int rb = 0; rb < RB; rb++)
+        av[rb] = *reinterpret_cast<const u32x4*>(&sA[buf][lds_chunk_offset(wrow0 + rb * 32 + l32, c)]);
+#pragma unroll
+      for (int cb = 0; cb < CB; cb++)
+        bv[cb] = *reinterpret_cast<const u32x4*>(&sB[buf][lds_chunk_offset(wcol0 + cb * 32 + l32, c)]);
 
-    if constexpr (FMT == SVDQ_INT4_G64_FP16) {
-      i32x4 a0[2], a1[2], b0[2], b1[2];
+      if constexpr (I4) {
+        i32x4 a0[RB], a1[RB], b0[CB], b1[CB];
+        float sw[CB];
 #pragma unroll
-      for (int i = 0; i < 2; i++) {
-        a0[i] = i32x4{(int)lo_nib_bytes(av[i].x), (int)hi_nib_bytes(av[i].x), (int)lo_nib_bytes(av[i].y),
-                      (int)hi_nib_bytes(av[i].y)};
-        a1[i] = i32x4{(int)lo_nib_bytes(av[i].z), (int)hi_nib_bytes(av[i].z), (int)lo_nib_bytes(av[i].w),
-                      (int)hi_nib_bytes(av[i].w)};
-        b0[i] = i32x4{(int)lo_nib_bytes(bv[i].x), (int)hi_nib_bytes(bv[i].x), (int)lo_nib_bytes(bv[i].y),
-                      (int)hi_nib_bytes(bv[i].y)};
-        b1[i] = i32x4{(int)lo_nib_bytes(bv[i].z), (int)hi_nib_bytes(bv[i].z), (int)lo_nib_bytes(bv[i].w),
-                      (int)hi_nib_bytes(bv[i].w)};
-      }
-      float4 sx[2][4];
-#pragma unroll
-      for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int j4 = 0; j4 < 4; j4++)
-          sx[i][j4] = *reinterpret_cast<const float4*>(&sSA[buf][wm * 64 + i * 32 + 8 * j4 + 4 * lh]);
-      float sw[2];
-#pragma unroll
-      for (int j = 0; j < 2; j++) sw[j] = sSB[buf][wn * 64 + j * 32 + l32];
-#pragma unroll
-      for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-          i32x16 p;
-#pragma unroll
-          for (int v = 0; v < 16; v++) p[v] = 0;
-          p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[i], b0[j], p, 0, 0, 0);
-          p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[i], b1[j], p, 0, 0, 0);
-#pragma unroll
-          for (int v = 0; v < 16; v++) {
-            const float4 s4 = sx[i][v >> 2];
-            const float sxv = (v & 3) == 0 ? s4.x : (v & 3) == 1 ? s4.y : (v & 3) == 2 ? s4.z : s4.w;
-            acc[i][j][v] = __builtin_fmaf(static_cast<float>(p[v]), sxv * sw[j], acc[i][j][v]);
-          }
+        for (int cb = 0; cb < CB; cb++) {
+          b0[cb] = i32x4{(int)lo_nib_bytes(bv[cb].x), (int)hi_nib_bytes(bv[cb].x), (int)lo_nib_bytes(bv[cb].y),
+                         (int)hi_nib_bytes(bv[cb].y)};
+          b1[cb] = i32x4{(int)lo_nib_bytes(bv[cb].z), (int)hi_nib_bytes(bv[cb].z), (int)lo_nib_bytes(bv[cb].w),
+                         (int)hi_nib_bytes(bv[cb].w)};
+          sw[cb] = __uint_as_float(sSB[buf][j][wcol0 + cb * 32 + l32]);
         }
-    } else {
-      i32x8 a[2], b[2];
-      int sa[2], sb[2];
 #pragma unroll
-      for (int i = 0; i < 2; i++) {
-        a[i] = i32x8{(int)av[i].x, (int)av[i].y, (int)av[i].z, (int)av[i].w, 0, 0, 0, 0};
-        b[i] = i32x8{(int)bv[i].x, (int)bv[i].y, (int)bv[i].z, (int)bv[i].w, 0, 0, 0, 0};
-        sa[i] = sEA[buf][(wm * 64 + i * 32 + l32) * 2 + lh];
-        sb[i] = sEB[buf][(wn * 64 + i * 32 + l32) * 2 + lh];
+        for (int rb = 0; rb < RB; rb++) {
+          a0[rb] = i32x4{(int)lo_nib_bytes(av[rb].x), (int)hi_nib_bytes(av[rb].x), (int)lo_nib_bytes(av[rb].y),
+                         (int)hi_nib_bytes(av[rb].y)};
+          a1[rb] = i32x4{(int)lo_nib_bytes(av[rb].z), (int)hi_nib_bytes(av[rb].z), (int)lo_nib_bytes(av[rb].w),
+                         (int)hi_nib_bytes(av[rb].w)};
+        }
+        // software pipeline over the wave's output tiles: the MFMAs of tile
+        // u + 1 are in flight while tile u is dequantized
+        constexpr int NT = RB * CB;
+        i32x16 p[2];
+        auto mma = [&](int u, i32x16& dst) __attribute__((always_inline)) {
+          const int rb = u / CB, cb = u % CB;
+          i32x16 z16;
+#pragma unroll
+          for (int v = 0; v < 16; v++) z16[v] = 0;
+          dst = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[rb], b0[cb], z16, 0, 0, 0);
+          dst = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[rb], b1[cb], dst, 0, 0, 0);
+        };
+        mma(0, p[0]);
+        f32x4 sx[4];
+#pragma unroll
+        for (int u = 0; u < NT; u++) {
+          const int rb = u / CB, cb = u % CB;
+          if (u + 1 < NT) mma(u + 1, p[(u + 1) & 1]);
+          if (cb == 0) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; q4++)
+              sx[q4] = *reinterpret_cast<const f32x4*>(&sSA[buf][j][wrow0 + rb * 32 + 8 * q4 + 4 * lh]);
+          }
+          const i32x16& pp = p[u & 1];
+#pragma unroll
+          for (int v = 0; v < 16; v++)
+            acc[rb][cb][v] = __builtin_fmaf(static_cast<float>(pp[v]), sx[v >> 2][v & 3] * sw[cb], acc[rb][cb][v]);
+        }
+      } else {
+        i32x8 a[RB], b[CB];
+        int sa[RB], sb[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; cb++) {
+          b[cb] = i32x8{(int)bv[cb].x, (int)bv[cb].y, (int)bv[cb].z, (int)bv[cb].w, 0, 0, 0, 0};
+          sb[cb] = (sSB[buf][0][wcol0 + cb * 32 + l32] >> (8 * c)) & 0xFF;
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; rb++) {
+          a[rb] = i32x8{(int)av[rb].x, (int)av[rb].y, (int)av[rb].z, (int)av[rb].w, 0, 0, 0, 0};
+          sa[rb] = (sSA[buf][0][wrow0 + rb * 32 + l32] >> (8 * c)) & 0xFF;
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+          for (int cb = 0; cb < CB; cb++)
+            acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[rb], b[cb], acc[rb][cb], 4, 4, 0, sa[rb],
+                                                                          0, sb[cb]);
       }
-#pragma unroll
-      for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int j = 0; j < 2; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 4, 4, 0, sa[i], 0,
-                                                                        sb[j]);
     }
-
-    if (s + 1 < steps) store_step(buf ^ 1);
     __syncthreads();
+  };
+  int s = 0;
+  for (; s + 1 < stages; s += 2) {
+    stage_body(s, R1, std::integral_constant<int, 0>{});
+    stage_body(s + 1, R0, std::integral_constant<int, 1>{});
   }
+  if (s < stages) stage_body(s, R1, std::integral_constant<int, 0>{});
 
-  // ---- low-rank up-projection as one more K slab (K = rank), bf16 MFMA
-  if constexpr (SLAB) {
-    for (int tb = 0; tb < g.rank / 16; tb++) {
-      bf16x8 a[2], b[2];
+  // ---- epilogue: bias, rounding, store.  Each wave stages one 32-row
+  // slice of its tile at a time in its own LDS region (row-major, output
+  // type), then writes whole rows with 16-byte stores.
+  {
+    constexpr int OB = OUT == SVDQ_OUT_F32 ? 4 : 2;     // output bytes per element
+    constexpr int ROWB = CB * 32 * OB;                  // bytes of one slice row
+    constexpr int SLICE = 32 * ROWB;
+    static_assert(4 * SLICE <= LDS_A + LDS_B, "epilogue staging must fit the stage buffers");
+    uint8_t* stage = smem + wave * SLICE;
+    float bv[CB];
 #pragma unroll
-      for (int i = 0; i < 2; i++) {
-        const long r = m0 + wm * 64 + i * 32 + l32;
-        const long c = n0 + wn * 64 + i * 32 + l32;
-        bf16x8 z;
-#pragma unroll
-        for (int e = 0; e < 8; e++) z[e] = static_cast<__bf16>(0.f);
-        a[i] = r < M ? *reinterpret_cast<const bf16x8*>(g.Tb + r * g.rank + tb * 16 + lh * 8) : z;
-        b[i] = c < N ? *reinterpret_cast<const bf16x8*>(g.l2t + c * g.rank + tb * 16 + lh * 8) : z;
-      }
-#pragma unroll
-      for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int j = 0; j < 2; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int cb = 0; cb < CB; cb++) {
+      const long c = min(n0 + wcol0 + cb * 32 + l32, static_cast<long>(N - 1));
+      bv[cb] = bias ? bias[c] : 0.f;
     }
-  }
-
-  // ---- epilogue: bias, rounding, store
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const long c = n0 + wn * 64 + j * 32 + l32;
-    if (c >= N) continue;
-    const float bv = g.bias ? g.bias[c] : 0.f;
+    for (int rb = 0; rb < RB; rb++) {
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
+      for (int cb = 0; cb < CB; cb++)
 #pragma unroll
-      for (int v = 0; v < 16; v++) {
-        const long r = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-        if (r < M) store_out<OUT>(g.Y, r * N + c, acc[i][j][v] + bv);
+        for (int v = 0; v < 16; v++) {
+          const int row = 8 * (v >> 2) + 4 * lh + (v & 3);
+          const int off = row * ROWB + (cb * 32 + l32) * OB;
+          const float y = acc[rb][cb][v] + bv[cb];
+          if constexpr (OUT == SVDQ_OUT_F32) *reinterpret_cast<float*>(stage + off) = y;
+          else *reinterpret_cast<uint16_t*>(stage + off) = static_cast<uint16_t>(f32_to_bf16_bits(y));
+        }
+      __builtin_amdgcn_wave_barrier();
+      constexpr int CHUNKS = SLICE / 16;                // 16-byte chunks per slice
+      constexpr int PER_ROW = ROWB / 16;
+#pragma unroll
+      for (int i = 0; i < CHUNKS / 64; i++) {
+        const int q = lane + 64 * i;
+        const int row = q / PER_ROW, cc = q % PER_ROW;
+        const long grow = m0 + wrow0 + rb * 32 + row;
+        const long gcol = n0 + wcol0 + cc * (16 / OB);
+        const u32x4 d = *reinterpret_cast<const u32x4*>(stage + row * ROWB + cc * 16);
+        if (grow < M && gcol < N)
+          *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(Yout) + (grow * N + gcol) * OB) = d;
       }
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }
@@ -284,6 +427,8 @@ __global__ __launch_bounds__(256) void up_kernel(const uint16_t* __restrict__ Tb
 }
 
 hipError_t launch_gemm(int fmt, bool slab, int out_dtype, const GemmArgs& g, hipStream_t st) {
+  const int BM = fmt == SVDQ_INT4_G64_FP16 ? Shape<SVDQ_INT4_G64_FP16>::BM : Shape<SVDQ_FP4_E2M1_G32_E8M0>::BM;
+  const int BN = fmt == SVDQ_INT4_G64_FP16 ? Shape<SVDQ_INT4_G64_FP16>::BN : Shape<SVDQ_FP4_E2M1_G32_E8M0>::BN;
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   dim3 grid(tiles), block(256);
 #define SVDQ_G(F, S, O) hipLaunchKernelGGL((gemm_kernel<F, S, O>), grid, block, 0, st, g)

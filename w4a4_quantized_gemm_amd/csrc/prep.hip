@@ -11,7 +11,7 @@
 //           and the Rayleigh-Ritz step run on the host (cyclic Jacobi)
 //   R     = W_hat - sum_t L1b[:, t] L2b[t, :]  (fp64, t increasing)
 //   group quantization of R along K for every output column; packing into
-//   the blob (codes N x K/2, scales K/g x N).
+//   the blob (codes N x K/2, scales N x K/g).
 #include <cmath>
 #include <cstring>
 #include <random>
@@ -241,14 +241,14 @@ __global__ void wquant_kernel(const double* __restrict__ R, int K, int N, uint8_
         words[k >> 3] |= (static_cast<uint32_t>(static_cast<int>(q)) & 0xFu) << (4 * (k & 7));
       }
     }
-    reinterpret_cast<uint16_t*>(wscales)[g * N + n] = static_cast<uint16_t>(sbits);
+    reinterpret_cast<uint16_t*>(wscales)[n * groups + g] = static_cast<uint16_t>(sbits);
   } else {
     const int e = e8m0_exponent_f64(a);
     for (int k = 0; k < G; k++) {
       const double y = ldexp(col[static_cast<long>(k) * N], -e);
       words[k >> 3] |= e2m1_code_f64(y) << (4 * (k & 7));
     }
-    reinterpret_cast<uint8_t*>(wscales)[g * N + n] = static_cast<uint8_t>(e + 127);
+    reinterpret_cast<uint8_t*>(wscales)[n * groups + g] = static_cast<uint8_t>(e + 127);
   }
   uint4* dst = reinterpret_cast<uint4*>(wcodes + n * static_cast<long>(K / 2) + g * (G / 2));
 #pragma unroll

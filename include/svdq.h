@@ -71,7 +71,15 @@ typedef enum svdq_status {
  *    e the smallest integer with max|v| <= 6 * 2^e (clamped to [-127, 127];
  *    an all-zero group has e = -127); codes round to nearest, ties to the
  *    even code, and a value that rounds to zero is encoded +0.
- * Two codes per byte; the even-K element is in the low nibble. */
+ * Two codes per byte; the even-K element is in the low nibble.
+ *
+ * Code matrices (activation codes, M rows; weight codes, N rows; K codes
+ * per row) are stored in MFMA operand-block order: 1 KB blocks, each holding
+ * the codes of 32 rows x 64 consecutive K values in the order the 64 lanes
+ * of a 32x32x64 MFMA read them.  The byte holding codes (k, k + 1), k even,
+ * of row i is at
+ *     ((i / 32) * (K / 64) + k / 64) * 1024 + (i % 32 + 32 * ((k % 64) / 32)) * 16 + (k % 32) / 2
+ * Rows are padded to a multiple of 32; the padding bytes are unspecified. */
 typedef enum svdq_format {
   SVDQ_INT4_G64_FP16 = 0,
   SVDQ_FP4_E2M1_G32_E8M0 = 1
@@ -112,7 +120,7 @@ int svdq_version(void);
 size_t svdq_prepared_bytes(const svdq_layer_desc* desc);
 
 /* Device workspace that svdq_linear / svdq_linear_unfused need for M tokens:
- * the packed activation codes (M x K/2 bytes), the activation scales and the
+ * the packed activation codes (ceil(M/32)*32 x K/2 bytes), the scales and the
  * bf16 down-projection (M x rank); 0 if arguments are invalid. */
 size_t svdq_workspace_bytes(const svdq_layer_desc* desc, int M, int unfused);
 
@@ -162,8 +170,9 @@ svdq_status svdq_check_blob(const svdq_layer_desc* desc, const void* d_prepared,
  * quantization share one input"; handbook timestep section: dynamic scales):
  *   x_hat = fp32(X * inv_lambda)                         (X: M x K bf16)
  *   per token row and K group: scale and 4-bit codes of x_hat in desc->fmt
- *     -> d_codes: M x K/2 bytes; d_scales: M x K/64 fp16 (INT4) or
- *        M x K/32 E8M0 bytes (FP4)
+ *     -> d_codes: ceil(M/32)*32 x K/2 bytes in MFMA operand-block order;
+ *        d_scales: M x K/64 fp16 (INT4) or M x K/32 E8M0 bytes (FP4),
+ *        row-major
  *   T = bf16(x_hat) L1b accumulated in fp32, rounded once to bf16
  *     -> d_T: M x rank bf16 (may be NULL when rank == 0).
  * X is read from HBM once.  `desc` must be the descriptor the blob was
@@ -210,7 +219,8 @@ svdq_status svdq_linear_unfused(const svdq_layer_desc* desc, const void* d_prepa
  *   inv_lambda  fp32[K]
  *   l1t         bf16[rank][K]    (L1 transposed: row t holds column t of L1)
  *   l2t         bf16[N][rank]    (L2 transposed: row n holds column n of L2)
- *   wcodes      u8[N][K/2]       (column n's K residual codes, packed)
+ *   wcodes      u8, N x K/2      (residual codes of output column n as row n,
+ *                                 in MFMA operand-block order)
  *   wscales     INT4: u16 fp16 bits [N][K/64]; FP4: u8 E8M0 [N][K/32]
  *   bias        fp32[N]          (offset 0 when the layer has no bias) */
 typedef struct svdq_blob_layout {

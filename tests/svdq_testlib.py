@@ -24,6 +24,18 @@ def np_bits_to_bf16_tensor(bits: np.ndarray, device):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
 
 
+def untile_codes(raw: np.ndarray, rows: int, K: int) -> np.ndarray:
+    """Code bytes stored in the MFMA operand-block order of include/svdq.h ->
+    row-major [rows][K/2].  The byte of codes (k, k+1) of row i sits at
+    ((i/32)*(K/64) + k/64)*1024 + (i%32 + 32*((k%64)/32))*16 + (k%32)/2."""
+    raw = np.asarray(raw).reshape(-1)
+    i = np.arange(rows, dtype=np.int64)[:, None]
+    k = 2 * np.arange(K // 2, dtype=np.int64)[None, :]
+    off = ((i // 32) * (K // 64) + k // 64) * 1024 + (i % 32 + 32 * ((k % 64) // 32)) * 16 + (k % 32) // 2
+    assert off.max() < raw.size, "code buffer smaller than the block layout needs"
+    return raw[off]
+
+
 def blob_sections(layer):
     """Canonical numpy views of a prepared blob.
 
@@ -47,7 +59,7 @@ def blob_sections(layer):
     l2t = sec(L.l2t, 2 * N * r).view(np.uint16).reshape(N, r)
     L1b = O.bf16_bits_to_f64(l1t).T.copy()
     L2b = O.bf16_bits_to_f64(l2t).T.copy()
-    raw_codes = sec(L.wcodes, N * K // 2).reshape(N, K // 2)
+    raw_codes = untile_codes(sec(L.wcodes, N * K // 2), N, K)
     nib = O.unpack_nibbles(raw_codes)                       # N x K
     if d.fmt == INT4:
         codes = O.nibble_to_int4(nib).T.copy()
@@ -89,7 +101,7 @@ def oracle_prep_from_blob(sections, W_bits, fmt: str, bias_bits=None, cols=None)
 def decode_act(codes_t, scales_t, fmt_id: int, M: int, K: int):
     """Packed activation codes / scales from the GPU -> (codes M x K, scale values)."""
     from w4a4_quantized_gemm_amd import INT4
-    raw = to_np(codes_t).reshape(M, K // 2)
+    raw = untile_codes(to_np(codes_t), M, K)
     nib = O.unpack_nibbles(raw)
     if fmt_id == INT4:
         sc = to_np(scales_t).view(np.uint16).reshape(M, K // 64)

@@ -99,15 +99,11 @@ struct Shape {
   static constexpr int BN = 2 * CB * 32;
 };
 
-// LDS layout of one K stage (128 K values = 64 code bytes per row): the
-// 16-byte chunk c (0..3) of row r lives in the 1 KB block of MFMA operand
-// (r / 32, step c / 2), at slot 32 * (c % 2) + ((r % 32) ^ (2 * c)).  Lane
-// l of an MFMA reads slot l ^ (2 * c) of its block: every group of 8 lanes
-// covers the 8 distinct 16-byte bank positions of a 128-byte window, and so
-// do the 8 chunks (4 per row, 2 rows) that 8 consecutive threads store.
-__device__ __forceinline__ int lds_chunk_offset(int row, int c) {
-  return (((row >> 5) * 2 + (c >> 1)) << 10) + ((((c & 1) << 5) | ((row & 31) ^ (2 * c))) << 4);
-}
+// LDS layout of one K stage (128 K values): the code tiles are kept in the
+// MFMA operand-block order of global memory, so block (row block rb, step
+// j) of the stage sits at ((rb * 2 + j) * 1 KB) and lane l of an MFMA reads
+// the 16 bytes at lane * 16 inside it: copies and reads are contiguous.
+__device__ __forceinline__ int lds_block(int rowblk, int j) { return (rowblk * 2 + j) << 10; }
 
 template <int FMT, bool SLAB, int OUT>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
@@ -150,7 +146,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const int lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, lh = lane >> 5;
-  const long KB = K / 2;                         // code bytes per row
   const int SW = K / 128;                        // scale words (4 bytes) per row
   const int stages = K / 128;
   const int wrow0 = wm * (RB * 32), wcol0 = wn * (CB * 32);
@@ -185,27 +180,30 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     }
   }
 
-  // ---- global -> registers -> LDS.  Thread t loads chunks q = t + 256 i:
-  // row q / 4, chunk q % 4 (four consecutive threads read one row's 64
-  // contiguous bytes), plus one scale word of an A row (t < BM) or of a B
-  // column (t >= BM; FP4 tiles have BM = 256 = all threads, so their B word
-  // is a second load).
+  // ---- global -> registers -> LDS.  A stage of the A (B) tile is BM / 16
+  // (BN / 16) operand blocks of 1 KB; thread t copies 16-byte pieces q =
+  // t + 256 i: block q / 64, lane slot q % 64 (64 threads cover one block
+  // contiguously).  Row blocks past the matrix are clamped to its last one
+  // (their outputs are never stored).  Thread t < BM also loads the scale
+  // word of A row t, thread t >= BM that of B column t - BM.
   struct Regs {
     u32x4 a[A_CH], b[B_CH];
     uint32_t sa, sb;
   };
+  const long KBLK = K / 64;                       // 1 KB blocks per 32-row block
+  const long last_ablk = (M + 31) / 32 - 1, last_bblk = N / 32 - 1;
   auto load_stage = [&](Regs& r, int st) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < A_CH; i++) {
-      const int q = t + i * NTHREADS;
-      const long row = min(m0 + (q >> 2), static_cast<long>(M - 1));
-      r.a[i] = *reinterpret_cast<const u32x4*>(acodes + row * KB + st * BKB + (q & 3) * 16);
+      const int q = t + i * NTHREADS, blk = q >> 6;
+      const long rb = min(m0 / 32 + (blk >> 1), last_ablk);
+      r.a[i] = *reinterpret_cast<const u32x4*>(acodes + ((rb * KBLK + 2 * st + (blk & 1)) << 10) + (q & 63) * 16);
     }
 #pragma unroll
     for (int i = 0; i < B_CH; i++) {
-      const int q = t + i * NTHREADS;
-      const long row = min(n0 + (q >> 2), static_cast<long>(N - 1));
-      r.b[i] = *reinterpret_cast<const u32x4*>(wcodes + row * KB + st * BKB + (q & 3) * 16);
+      const int q = t + i * NTHREADS, blk = q >> 6;
+      const long rb = min(n0 / 32 + (blk >> 1), last_bblk);
+      r.b[i] = *reinterpret_cast<const u32x4*>(wcodes + ((rb * KBLK + 2 * st + (blk & 1)) << 10) + (q & 63) * 16);
     }
     if constexpr (I4) {
       // 128 threads per operand
@@ -221,12 +219,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < A_CH; i++) {
       const int q = t + i * NTHREADS;
-      *reinterpret_cast<u32x4*>(&sA[buf][lds_chunk_offset(q >> 2, q & 3)]) = r.a[i];
+      *reinterpret_cast<u32x4*>(&sA[buf][q * 16]) = r.a[i];
     }
 #pragma unroll
     for (int i = 0; i < B_CH; i++) {
       const int q = t + i * NTHREADS;
-      *reinterpret_cast<u32x4*>(&sB[buf][lds_chunk_offset(q >> 2, q & 3)]) = r.b[i];
+      *reinterpret_cast<u32x4*>(&sB[buf][q * 16]) = r.b[i];
     }
     if constexpr (I4) {
       const float mul = t < BM ? 1.0f : 1.0f / 256.0f;
@@ -263,14 +261,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 
 #pragma unroll
     for (int j = 0; j < 2; j++) {          // two 64-wide MFMA steps per stage
-      const int c = 2 * j + lh;            // this lane's chunk of the stage
+      const int c = 2 * j + lh;            // this lane's 16-byte chunk of the stage
       u32x4 av[RB], bv[CB];
 #pragma unroll
       for (int rb = 0; rb < RB; rb++)
-        av[rb] = *reinterpret_cast<const u32x4*>(&sA[buf][lds_chunk_offset(wrow0 + rb * 32 + l32, c)]);
+        av[rb] = *reinterpret_cast<const u32x4*>(&sA[buf][lds_block(wrow0 / 32 + rb, j) + lane * 16]);
 #pragma unroll
       for (int cb = 0; cb < CB; cb++)
-        bv[cb] = *reinterpret_cast<const u32x4*>(&sB[buf][lds_chunk_offset(wcol0 + cb * 32 + l32, c)]);
+        bv[cb] = *reinterpret_cast<const u32x4*>(&sB[buf][lds_block(wcol0 / 32 + cb, j) + lane * 16]);
 
       if constexpr (I4) {
         i32x4 a0[RB], a1[RB], b0[CB], b1[CB];
@@ -393,6 +391,210 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// FP4 GEMM with direct global->LDS loads.
+//
+// The operands go from global memory straight into LDS (global_load_lds,
+// 16 bytes per lane), without passing through registers.  The LDS is a ring
+// of NBUF stages; each stage holds, for 128 K values, the A and B code tiles
+// as 1 KB MFMA operand blocks (block (rb, j) holds, in lane order, the 16
+// bytes that lane l of the 32x32x64 MFMA reads: row rb * 32 + l % 32, chunk
+// 2 j + l / 32) and one E8M0 scale word per row (column).  Each wave issues
+// 10 block loads per stage; loads run three stages ahead of the MFMAs, and a
+// stage is published by waiting until this wave's loads of it completed
+// (vmcnt) followed by a workgroup barrier.  MFMA operands are read from LDS
+// one 64-wide step before the MFMAs that use them.
+namespace {
+constexpr int F_BM = 256, F_BN = 256, F_RB = 4, F_CB = 4, F_NBUF = 4;
+constexpr int F_A = F_BM * 64, F_B = F_BN * 64, F_S = 256 * 4;          // bytes per stage
+constexpr int F_STAGE = F_A + F_B + 2 * F_S;
+// each wave issues 10 loads per stage: 4 A blocks, 4 B blocks, 2 scale words
+
+// wait until at most n vector-memory operations of this wave are
+// outstanding, then barrier; a compiler memory barrier as well
+#define SVDQ_WAIT_VM_BARRIER(n) asm volatile("s_waitcnt vmcnt(" #n ")\n\ts_barrier" ::: "memory")
+}  // namespace
+
+template <bool SLAB, int OUT>
+__global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[F_NBUF * F_STAGE];
+
+  const int M = g.M, K = g.K, N = g.N, rank = g.rank;
+  const uint8_t* __restrict__ acodes = g.acodes;
+  const uint8_t* __restrict__ wcodes = g.wcodes;
+  const uint32_t* __restrict__ ascales = static_cast<const uint32_t*>(g.ascales);
+  const uint32_t* __restrict__ wscales = static_cast<const uint32_t*>(g.wscales);
+  const uint16_t* __restrict__ Tb = g.Tb;
+  const uint16_t* __restrict__ l2t = g.l2t;
+  const float* __restrict__ bias = g.bias;
+  void* __restrict__ Yout = g.Y;
+  const int tiles_m = (M + F_BM - 1) / F_BM, tiles_n = (N + F_BN - 1) / F_BN;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const long m0 = static_cast<long>(tm) * F_BM;
+  const long n0 = static_cast<long>(tn) * F_BN;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int SW = K / 128;
+  const int stages = K / 128;
+  const int last = stages - 1;
+  const int wrow0 = wm * (F_RB * 32), wcol0 = wn * (F_CB * 32);
+
+  f32x16 acc[F_RB][F_CB];
+#pragma unroll
+  for (int i = 0; i < F_RB; i++)
+#pragma unroll
+    for (int j = 0; j < F_CB; j++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+
+  // low-rank up-projection first (K = rank, bf16 MFMA); rows (columns) past
+  // M (N) are clamped to the last valid one and never stored
+  if constexpr (SLAB) {
+    for (int tb = 0; tb < rank / 16; tb++) {
+      bf16x8 b[F_CB];
+#pragma unroll
+      for (int j = 0; j < F_CB; j++) {
+        const long c = min(n0 + wcol0 + j * 32 + l32, static_cast<long>(N - 1));
+        b[j] = *reinterpret_cast<const bf16x8*>(l2t + c * rank + tb * 16 + lh * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < F_RB; i++) {
+        const long r = min(m0 + wrow0 + i * 32 + l32, static_cast<long>(M - 1));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Tb + r * rank + tb * 16 + lh * 8);
+#pragma unroll
+        for (int j = 0; j < F_CB; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  // global sources of the blocks this wave copies: blocks 4 * wave + i
+  // (i = 0..3) of the A and B stage tiles, block (rb, j) = (blk / 2, blk % 2),
+  // each a contiguous 1 KB of the operand-block-ordered code matrix; row
+  // blocks past the matrix are clamped to its last one
+  const long KBLK = K / 64;
+  const long last_ablk = (M + 31) / 32 - 1, last_bblk = N / 32 - 1;
+  const uint8_t* asrc[4];
+  const uint8_t* bsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int blk = wave * 4 + i, rb = blk >> 1, j = blk & 1;
+    const long ab = min(m0 / 32 + rb, last_ablk), bb = min(n0 / 32 + rb, last_bblk);
+    asrc[i] = acodes + ((ab * KBLK + j) << 10) + lane * 16;
+    bsrc[i] = wcodes + ((bb * KBLK + j) << 10) + lane * 16;
+  }
+  const uint32_t* sasrc = ascales + min(m0 + wave * 64 + lane, static_cast<long>(M - 1)) * SW;
+  const uint32_t* sbsrc = wscales + min(n0 + wave * 64 + lane, static_cast<long>(N - 1)) * SW;
+
+  auto issue_stage = [&](int st) __attribute__((always_inline)) {
+    uint8_t* base = smem + (st % F_NBUF) * F_STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      __builtin_amdgcn_global_load_lds(asrc[i] + st * 2048, base + (wave * 4 + i) * 1024, 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      __builtin_amdgcn_global_load_lds(bsrc[i] + st * 2048, base + F_A + (wave * 4 + i) * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(sasrc + st, base + F_A + F_B + wave * 256, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(sbsrc + st, base + F_A + F_B + F_S + wave * 256, 4, 0, 0);
+  };
+
+  struct Ops {
+    u32x4 a[F_RB], b[F_CB];
+    uint32_t sa[F_RB], sb[F_CB];
+  };
+  // operands of MFMA step j of stage st
+  auto read_ops = [&](Ops& o, int st, int j) __attribute__((always_inline)) {
+    const uint8_t* base = smem + (st % F_NBUF) * F_STAGE;
+    const int c = 2 * j + lh;
+#pragma unroll
+    for (int rb = 0; rb < F_RB; rb++) {
+      o.a[rb] = *reinterpret_cast<const u32x4*>(base + ((wm * F_RB + rb) * 2 + j) * 1024 + lane * 16);
+      o.sa[rb] = (reinterpret_cast<const uint32_t*>(base + F_A + F_B)[wrow0 + rb * 32 + l32] >> (8 * c)) & 0xFFu;
+    }
+#pragma unroll
+    for (int cb = 0; cb < F_CB; cb++) {
+      o.b[cb] = *reinterpret_cast<const u32x4*>(base + F_A + ((wn * F_CB + cb) * 2 + j) * 1024 + lane * 16);
+      o.sb[cb] = (reinterpret_cast<const uint32_t*>(base + F_A + F_B + F_S)[wcol0 + cb * 32 + l32] >> (8 * c)) & 0xFFu;
+    }
+  };
+  auto mfmas = [&](const Ops& o) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < F_RB; rb++) {
+      const i32x8 a = i32x8{(int)o.a[rb].x, (int)o.a[rb].y, (int)o.a[rb].z, (int)o.a[rb].w, 0, 0, 0, 0};
+#pragma unroll
+      for (int cb = 0; cb < F_CB; cb++) {
+        const i32x8 b = i32x8{(int)o.b[cb].x, (int)o.b[cb].y, (int)o.b[cb].z, (int)o.b[cb].w, 0, 0, 0, 0};
+        acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[rb][cb], 4, 4, 0, (int)o.sa[rb], 0,
+                                                                      (int)o.sb[cb]);
+      }
+    }
+  };
+
+  // prologue: stages 0..2 in flight (clamped past the end: the extra loads
+  // re-read the last stage into a buffer nobody reads)
+  issue_stage(0);
+  issue_stage(min(1, last));
+  issue_stage(min(2, last));
+  SVDQ_WAIT_VM_BARRIER(20);
+  Ops o0, o1;
+  read_ops(o0, 0, 0);
+  for (int s = 0; s < stages; s++) {
+    read_ops(o1, s, 1);
+    mfmas(o0);
+    // stage s + 1 complete for every wave (its newer stage s + 2 may still
+    // be in flight); buffer (s + 3) % 4 = (s - 1) % 4 is no longer read
+    SVDQ_WAIT_VM_BARRIER(10);
+    issue_stage(min(s + 3, last));
+    mfmas(o1);
+    read_ops(o0, min(s + 1, last), 0);
+  }
+  SVDQ_WAIT_VM_BARRIER(0);
+
+  // epilogue: bias, rounding, LDS-staged 16-byte row stores (one 32-row
+  // slice of the wave's tile at a time, in the wave's own LDS region)
+  {
+    constexpr int OB = OUT == SVDQ_OUT_F32 ? 4 : 2;
+    constexpr int ROWB = F_CB * 32 * OB;
+    constexpr int SLICE = 32 * ROWB;
+    uint8_t* stage = smem + wave * SLICE;
+    float bv[F_CB];
+#pragma unroll
+    for (int cb = 0; cb < F_CB; cb++) {
+      const long c = min(n0 + wcol0 + cb * 32 + l32, static_cast<long>(N - 1));
+      bv[cb] = bias ? bias[c] : 0.f;
+    }
+#pragma unroll
+    for (int rb = 0; rb < F_RB; rb++) {
+#pragma unroll
+      for (int cb = 0; cb < F_CB; cb++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+          const int row = 8 * (v >> 2) + 4 * lh + (v & 3);
+          const int off = row * ROWB + (cb * 32 + l32) * OB;
+          const float y = acc[rb][cb][v] + bv[cb];
+          if constexpr (OUT == SVDQ_OUT_F32) *reinterpret_cast<float*>(stage + off) = y;
+          else *reinterpret_cast<uint16_t*>(stage + off) = static_cast<uint16_t>(f32_to_bf16_bits(y));
+        }
+      __builtin_amdgcn_wave_barrier();
+      constexpr int PER_ROW = ROWB / 16;
+#pragma unroll
+      for (int i = 0; i < SLICE / 16 / 64; i++) {
+        const int q = lane + 64 * i;
+        const int row = q / PER_ROW, cc = q % PER_ROW;
+        const long grow = m0 + wrow0 + rb * 32 + row;
+        const long gcol = n0 + wcol0 + cc * (16 / OB);
+        const u32x4 d = *reinterpret_cast<const u32x4*>(stage + row * ROWB + cc * 16);
+        if (grow < M && gcol < N)
+          *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(Yout) + (grow * N + gcol) * OB) = d;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
 // Unfused up-projection: Y = round(Y + Tb L2b), 64 x 64 tile per workgroup.
 template <int OUT>
 __global__ __launch_bounds__(256) void up_kernel(const uint16_t* __restrict__ Tb, const uint16_t* __restrict__ l2t,
@@ -437,8 +639,10 @@ hipError_t launch_gemm(int fmt, bool slab, int out_dtype, const GemmArgs& g, hip
     if (slab) { if (f32) SVDQ_G(SVDQ_INT4_G64_FP16, true, SVDQ_OUT_F32); else SVDQ_G(SVDQ_INT4_G64_FP16, true, SVDQ_OUT_BF16); }
     else      { if (f32) SVDQ_G(SVDQ_INT4_G64_FP16, false, SVDQ_OUT_F32); else SVDQ_G(SVDQ_INT4_G64_FP16, false, SVDQ_OUT_BF16); }
   } else {
-    if (slab) { if (f32) SVDQ_G(SVDQ_FP4_E2M1_G32_E8M0, true, SVDQ_OUT_F32); else SVDQ_G(SVDQ_FP4_E2M1_G32_E8M0, true, SVDQ_OUT_BF16); }
-    else      { if (f32) SVDQ_G(SVDQ_FP4_E2M1_G32_E8M0, false, SVDQ_OUT_F32); else SVDQ_G(SVDQ_FP4_E2M1_G32_E8M0, false, SVDQ_OUT_BF16); }
+#define SVDQ_F(S, O) hipLaunchKernelGGL((gemm_fp4_kernel<S, O>), grid, block, 0, st, g)
+    if (slab) { if (f32) SVDQ_F(true, SVDQ_OUT_F32); else SVDQ_F(true, SVDQ_OUT_BF16); }
+    else      { if (f32) SVDQ_F(false, SVDQ_OUT_F32); else SVDQ_F(false, SVDQ_OUT_BF16); }
+#undef SVDQ_F
   }
 #undef SVDQ_G
   return hipGetLastError();

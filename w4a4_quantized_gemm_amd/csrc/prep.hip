@@ -250,9 +250,10 @@ __global__ void wquant_kernel(const double* __restrict__ R, int K, int N, uint8_
     }
     reinterpret_cast<uint8_t*>(wscales)[n * groups + g] = static_cast<uint8_t>(e + 127);
   }
-  uint4* dst = reinterpret_cast<uint4*>(wcodes + n * static_cast<long>(K / 2) + g * (G / 2));
 #pragma unroll
-  for (int w = 0; w < G / 32; w++) dst[w] = make_uint4(words[4 * w], words[4 * w + 1], words[4 * w + 2], words[4 * w + 3]);
+  for (int w = 0; w < G / 32; w++)
+    *reinterpret_cast<u32x4*>(wcodes + code_chunk_offset(n, static_cast<int>(g * G + 32 * w), K)) =
+        u32x4{words[4 * w], words[4 * w + 1], words[4 * w + 2], words[4 * w + 3]};
 }
 
 __global__ void bias_kernel(const uint16_t* __restrict__ b, int N, float* __restrict__ out) {

@@ -94,8 +94,8 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
         if (valid) reinterpret_cast<uint8_t*>(scales)[grow * (K / 32) + kb / 32] = static_cast<uint8_t>(ex + 127);
       }
       if (valid)
-        *reinterpret_cast<uint4*>(codes + grow * (K / 2) + kb / 2) =
-            make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        *reinterpret_cast<u32x4*>(codes + code_chunk_offset(grow, kb, K)) =
+            u32x4{packed[0], packed[1], packed[2], packed[3]};
     }
 
     if constexpr (DOWN && RB > 0) {

@@ -62,4 +62,11 @@ __device__ __forceinline__ uint32_t e2m1_code(float y) {
   return idx | ((y < 0.f && idx != 0u) ? 8u : 0u);
 }
 
+// Byte offset of the 16-byte chunk holding codes k .. k + 31 (k % 32 == 0)
+// of row `row` in a code matrix with K codes per row, stored in MFMA
+// operand-block order (1 KB blocks of 32 rows x 64 codes, lane-ordered).
+__device__ __forceinline__ long code_chunk_offset(long row, int k, int K) {
+  return ((row >> 5) * (K >> 6) + (k >> 6)) * 1024 + (((row & 31) + (((k >> 5) & 1) << 5)) << 4);
+}
+
 }  // namespace svdq

@@ -57,7 +57,7 @@ svdq_blob_layout layout_of(const svdq_layer_desc& d) {
 ActLayout act_layout(const svdq_layer_desc& d, int M) {
   ActLayout A{};
   const uint64_t m = M, K = d.K;
-  A.codes_bytes = m * (K / 2);
+  A.codes_bytes = ((m + 31) / 32) * 32 * (K / 2);   // rows padded to whole 32-row blocks
   A.scales_bytes = m * (K / group_of(d.fmt)) * scale_bytes_of(d.fmt);
   A.tb_bytes = m * uint64_t(d.rank) * 2;
   uint64_t off = 0;

@@ -79,7 +79,19 @@ typedef enum svdq_status {
  * of a 32x32x64 MFMA read them.  The byte holding codes (k, k + 1), k even,
  * of row i is at
  *     ((i / 32) * (K / 64) + k / 64) * 1024 + (i % 32 + 32 * ((k % 64) / 32)) * 16 + (k % 32) / 2
- * Rows are padded to a multiple of 32; the padding bytes are unspecified. */
+ * Rows are padded to a multiple of 32; the padding bytes are unspecified.
+ *
+ * FP4 scale matrices (E8M0 bytes, one per row and 32-wide group) follow the
+ * same blocking: for each 32-row block and 64-wide K step, 64 bytes, row
+ * i % 32 at byte 2 (i % 32) + (k / 32) % 2:
+ *     ((i / 32) * (K / 64) + k / 64) * 64 + (i % 32) * 2 + (k / 32) % 2
+ * INT4 scales (fp16) are row-major [rows][K / 64].
+ *
+ * bf16 low-rank matrices with `cols` columns (cols % 16 == 0: T, M x rank,
+ * and L2 transposed, N x rank) are stored in 1 KB blocks of 32 rows x 16
+ * columns in the lane order of a 32x32x16 bf16 MFMA; element (i, t) is at
+ *     ((i / 32) * (cols / 16) + t / 16) * 512 + (i % 32 + 32 * ((t % 16) / 8)) * 8 + t % 8
+ * (in elements), rows again padded to a multiple of 32. */
 typedef enum svdq_format {
   SVDQ_INT4_G64_FP16 = 0,
   SVDQ_FP4_E2M1_G32_E8M0 = 1
@@ -121,7 +133,7 @@ size_t svdq_prepared_bytes(const svdq_layer_desc* desc);
 
 /* Device workspace that svdq_linear / svdq_linear_unfused need for M tokens:
  * the packed activation codes (ceil(M/32)*32 x K/2 bytes), the scales and the
- * bf16 down-projection (M x rank); 0 if arguments are invalid. */
+ * bf16 down-projection (ceil(M/32)*32 x rank); 0 if arguments are invalid. */
 size_t svdq_workspace_bytes(const svdq_layer_desc* desc, int M, int unfused);
 
 /* Byte sizes of svdq_quantize_act's three outputs for M tokens (codes,
@@ -171,10 +183,12 @@ svdq_status svdq_check_blob(const svdq_layer_desc* desc, const void* d_prepared,
  *   x_hat = fp32(X * inv_lambda)                         (X: M x K bf16)
  *   per token row and K group: scale and 4-bit codes of x_hat in desc->fmt
  *     -> d_codes: ceil(M/32)*32 x K/2 bytes in MFMA operand-block order;
- *        d_scales: M x K/64 fp16 (INT4) or M x K/32 E8M0 bytes (FP4),
- *        row-major
+ *        d_scales: M x K/64 fp16, row-major (INT4), or ceil(M/32)*32 x K/32
+ *        E8M0 bytes in the FP4 scale block order
  *   T = bf16(x_hat) L1b accumulated in fp32, rounded once to bf16
- *     -> d_T: M x rank bf16 (may be NULL when rank == 0).
+ *     -> d_T: ceil(M/32)*32 x rank bf16 in the bf16 block order (may be
+ *        NULL when rank == 0).
+ * Padding rows of the outputs are left unwritten.
  * X is read from HBM once.  `desc` must be the descriptor the blob was
  * prepared with.  Asynchronous. */
 svdq_status svdq_quantize_act(const svdq_layer_desc* desc, const void* d_prepared,
@@ -218,10 +232,12 @@ svdq_status svdq_linear_unfused(const svdq_layer_desc* desc, const void* d_prepa
  *   lambda      fp32[K]
  *   inv_lambda  fp32[K]
  *   l1t         bf16[rank][K]    (L1 transposed: row t holds column t of L1)
- *   l2t         bf16[N][rank]    (L2 transposed: row n holds column n of L2)
+ *   l2t         bf16, N x rank   (L2 transposed: row n holds column n of L2;
+ *                                 bf16 block order)
  *   wcodes      u8, N x K/2      (residual codes of output column n as row n,
  *                                 in MFMA operand-block order)
- *   wscales     INT4: u16 fp16 bits [N][K/64]; FP4: u8 E8M0 [N][K/32]
+ *   wscales     INT4: u16 fp16 bits [N][K/64] row-major; FP4: u8 E8M0,
+ *               N x K/32 in the FP4 scale block order
  *   bias        fp32[N]          (offset 0 when the layer has no bias) */
 typedef struct svdq_blob_layout {
   uint64_t header, lambda, inv_lambda, l1t, l2t, wcodes, wscales, bias, total;

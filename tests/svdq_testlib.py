@@ -36,6 +36,31 @@ def untile_codes(raw: np.ndarray, rows: int, K: int) -> np.ndarray:
     return raw[off]
 
 
+def untile_bf16(raw_u16: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """bf16 matrix (as uint16) stored in the operand-block order of
+    include/svdq.h -> row-major [rows][cols].  Element (i, t) sits at
+    ((i/32)*(cols/16) + t/16)*512 + (i%32 + 32*((t%16)/8))*8 + t%8."""
+    raw = np.asarray(raw_u16).reshape(-1)
+    i = np.arange(rows, dtype=np.int64)[:, None]
+    t = np.arange(cols, dtype=np.int64)[None, :]
+    off = ((i // 32) * (cols // 16) + t // 16) * 512 + (i % 32 + 32 * ((t % 16) // 8)) * 8 + t % 8
+    if off.size == 0:
+        return np.zeros((rows, cols), dtype=raw.dtype)
+    assert off.max() < raw.size, "bf16 buffer smaller than the block layout needs"
+    return raw[off]
+
+
+def untile_fp4_scales(raw: np.ndarray, rows: int, K: int) -> np.ndarray:
+    """FP4 E8M0 scale bytes in operand-block order -> [rows][K/32].  The byte
+    of (row i, group k/32) sits at ((i/32)*(K/64) + k/64)*64 + (i%32)*2 + (k/32)%2."""
+    raw = np.asarray(raw).reshape(-1)
+    i = np.arange(rows, dtype=np.int64)[:, None]
+    grp = np.arange(K // 32, dtype=np.int64)[None, :]
+    off = ((i // 32) * (K // 64) + grp // 2) * 64 + (i % 32) * 2 + grp % 2
+    assert off.max() < raw.size, "scale buffer smaller than the block layout needs"
+    return raw[off]
+
+
 def blob_sections(layer):
     """Canonical numpy views of a prepared blob.
 
@@ -56,7 +81,7 @@ def blob_sections(layer):
     lam32 = sec(L.lambda_, 4 * K).view(np.float32).astype(np.float64)
     inv32 = sec(L.inv_lambda, 4 * K).view(np.float32).astype(np.float64)
     l1t = sec(L.l1t, 2 * r * K).view(np.uint16).reshape(r, K)
-    l2t = sec(L.l2t, 2 * N * r).view(np.uint16).reshape(N, r)
+    l2t = untile_bf16(sec(L.l2t, 2 * N * r).view(np.uint16), N, r)
     L1b = O.bf16_bits_to_f64(l1t).T.copy()
     L2b = O.bf16_bits_to_f64(l2t).T.copy()
     raw_codes = untile_codes(sec(L.wcodes, N * K // 2), N, K)
@@ -67,7 +92,7 @@ def blob_sections(layer):
         scales = O.fp16_bits_to_f64(raw_scales)
     else:
         codes = nib.T.copy()
-        raw_scales = sec(L.wscales, (K // g) * N).reshape(N, K // g).T
+        raw_scales = untile_fp4_scales(sec(L.wscales, (K // g) * N), N, K).T
         scales = raw_scales.astype(np.int32) - 127
     bias = None
     if d.flags & 4:
@@ -106,5 +131,5 @@ def decode_act(codes_t, scales_t, fmt_id: int, M: int, K: int):
     if fmt_id == INT4:
         sc = to_np(scales_t).view(np.uint16).reshape(M, K // 64)
         return O.nibble_to_int4(nib), O.fp16_bits_to_f64(sc), raw, sc
-    sc = to_np(scales_t).reshape(M, K // 32)
+    sc = untile_fp4_scales(to_np(scales_t), M, K)
     return nib, sc.astype(np.int32) - 127, raw, sc

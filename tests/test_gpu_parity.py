@@ -21,7 +21,7 @@ import pytest
 
 import oracle as O
 import workloads as WL
-from svdq_testlib import (blob_sections, decode_act, np_bits_to_bf16_tensor, oracle_prep_from_blob, to_np,
+from svdq_testlib import (blob_sections, decode_act, np_bits_to_bf16_tensor, oracle_prep_from_blob, to_np, untile_bf16,
                           u16_tensor_to_np)
 
 pytestmark = pytest.mark.gpu
@@ -110,7 +110,7 @@ def _check_act(torch_dev, layer, X, X_bits, ref_prep, rows=None):
     assert np.array_equal(sraw[sel], ref["scale_bytes"]), "activation scales differ"
     if layer.desc.rank:
         r = layer.desc.rank
-        Tg = O.bf16_bits_to_f64(u16_tensor_to_np(T[: M * r]).reshape(M, r))[sel]
+        Tg = O.bf16_bits_to_f64(untile_bf16(u16_tensor_to_np(T), M, r))[sel]
         _, Tref = O.down_proj(ref["xhat"], ref_prep["L1b"])
         # within one bf16 ulp of the fp64-accumulated value
         ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(Tref), 1e-30))) - 7)

@@ -186,19 +186,21 @@ __global__ void store_l1t_kernel(const double* __restrict__ L1, int K, int r, ui
   l1t[idx] = static_cast<uint16_t>(f64_round_bits(L1[j * r + t], 7, 8));
 }
 
-// l2t[n][t] = bf16(L2t[n][t]) from an fp64 N x r matrix
-__global__ void store_l2t_kernel(const double* __restrict__ L2t, long count, uint16_t* __restrict__ l2t) {
+// l2t = bf16(L2t) from an fp64 N x r matrix, stored in operand-block order
+__global__ void store_l2t_kernel(const double* __restrict__ L2t, long count, int r, uint16_t* __restrict__ l2t) {
   const long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= count) return;
-  l2t[idx] = static_cast<uint16_t>(f64_round_bits(L2t[idx], 7, 8));
+  l2t[bf16_block_index(idx / r, static_cast<int>(idx % r), r)] = static_cast<uint16_t>(f64_round_bits(L2t[idx], 7, 8));
 }
 
-// Caller-supplied factors: L1 (K x r) -> l1t (r x K); L2 (r x N) -> l2t (N x r)
-__global__ void transpose_u16_kernel(const uint16_t* __restrict__ src, int rows, int cols, uint16_t* __restrict__ dst) {
+// Caller-supplied factors: L1 (K x r) -> l1t (r x K, row-major); L2 (r x N)
+// -> l2t (N x r, operand-block order when `block`)
+__global__ void transpose_u16_kernel(const uint16_t* __restrict__ src, int rows, int cols, bool block,
+                                     uint16_t* __restrict__ dst) {
   const long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= static_cast<long>(rows) * cols) return;
   const long i = idx / cols, j = idx % cols;
-  dst[j * rows + i] = src[idx];
+  dst[block ? bf16_block_index(j, static_cast<int>(i), rows) : j * rows + i] = src[idx];
 }
 
 // R = W_hat - sum_t L1b[j][t] L2b[t][n], in place, t increasing.
@@ -210,7 +212,7 @@ __global__ void residual_kernel(double* __restrict__ What, const uint16_t* __res
   double s = 0.0;
   for (int t = 0; t < r; t++) {
     const double a = __uint_as_float(static_cast<uint32_t>(l1t[static_cast<long>(t) * K + j]) << 16);
-    const double b = __uint_as_float(static_cast<uint32_t>(l2t[n * r + t]) << 16);
+    const double b = __uint_as_float(static_cast<uint32_t>(l2t[bf16_block_index(n, t, r)]) << 16);
     s = fma(a, b, s);  // the product of two bf16 numbers is exact in fp64
   }
   What[idx] = What[idx] - s;
@@ -248,7 +250,7 @@ __global__ void wquant_kernel(const double* __restrict__ R, int K, int N, uint8_
       const double y = ldexp(col[static_cast<long>(k) * N], -e);
       words[k >> 3] |= e2m1_code_f64(y) << (4 * (k & 7));
     }
-    reinterpret_cast<uint8_t*>(wscales)[n * groups + g] = static_cast<uint8_t>(e + 127);
+    reinterpret_cast<uint8_t*>(wscales)[fp4_scale_offset(n, static_cast<int>(g * G), K)] = static_cast<uint8_t>(e + 127);
   }
 #pragma unroll
   for (int w = 0; w < G / 32; w++)
@@ -346,9 +348,9 @@ svdq_status prepare_impl(const svdq_layer_desc& d, const uint16_t* W, const floa
   // low-rank factors
   if (r > 0) {
     if (d.flags & SVDQ_F_FACTORS_GIVEN) {
-      hipLaunchKernelGGL(transpose_u16_kernel, dim3(blocks_for(static_cast<long>(K) * r)), dim3(256), 0, st, L1, K, r, l1t);
+      hipLaunchKernelGGL(transpose_u16_kernel, dim3(blocks_for(static_cast<long>(K) * r)), dim3(256), 0, st, L1, K, r, false, l1t);
       SVDQ_TRY(hipGetLastError());
-      hipLaunchKernelGGL(transpose_u16_kernel, dim3(blocks_for(static_cast<long>(r) * N)), dim3(256), 0, st, L2, r, N, l2t);
+      hipLaunchKernelGGL(transpose_u16_kernel, dim3(blocks_for(static_cast<long>(r) * N)), dim3(256), 0, st, L2, r, N, true, l2t);
       SVDQ_TRY(hipGetLastError());
     } else {
       const int b = r + opt.oversample > (K < N ? K : N) ? (K < N ? K : N) : r + opt.oversample;
@@ -405,7 +407,7 @@ svdq_status prepare_impl(const svdq_layer_desc& d, const uint16_t* W, const floa
       hipLaunchKernelGGL(store_l1t_kernel, dim3(blocks_for(static_cast<long>(K) * r)), dim3(256), 0, st, dL1.d(), K, r, l1t);
       SVDQ_TRY(hipGetLastError());
       hipLaunchKernelGGL(store_l2t_kernel, dim3(blocks_for(static_cast<long>(N) * r)), dim3(256), 0, st, dL2t.d(),
-                         static_cast<long>(N) * r, l2t);
+                         static_cast<long>(N) * r, r, l2t);
       SVDQ_TRY(hipGetLastError());
       SVDQ_TRY(hipStreamSynchronize(st));
     }

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
           const float y = __builtin_amdgcn_ldexpf(xh[e], -ex);
           packed[e >> 3] |= e2m1_code(y) << (4 * (e & 7));
         }
-        if (valid) reinterpret_cast<uint8_t*>(scales)[grow * (K / 32) + kb / 32] = static_cast<uint8_t>(ex + 127);
+        if (valid) reinterpret_cast<uint8_t*>(scales)[fp4_scale_offset(grow, kb, K)] = static_cast<uint8_t>(ex + 127);
       }
       if (valid)
         *reinterpret_cast<u32x4*>(codes + code_chunk_offset(grow, kb, K)) =
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
       const float s = ((red[(0 * 16 + rr) * R + t] + red[(1 * 16 + rr) * R + t]) + red[(2 * 16 + rr) * R + t]) +
                       red[(3 * 16 + rr) * R + t];
       const long gr = static_cast<long>(blockIdx.x) * 16 + rr;
-      if (gr < M) Tb[gr * R + t] = static_cast<uint16_t>(f32_to_bf16_bits(s));
+      if (gr < M) Tb[bf16_block_index(gr, t, R)] = static_cast<uint16_t>(f32_to_bf16_bits(s));
     }
   }
 }

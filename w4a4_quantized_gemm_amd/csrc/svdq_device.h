@@ -16,6 +16,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
+// A value the compiler cannot see is uniform across the wave, made scalar.
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -67,6 +70,21 @@ __device__ __forceinline__ uint32_t e2m1_code(float y) {
 // operand-block order (1 KB blocks of 32 rows x 64 codes, lane-ordered).
 __device__ __forceinline__ long code_chunk_offset(long row, int k, int K) {
   return ((row >> 5) * (K >> 6) + (k >> 6)) * 1024 + (((row & 31) + (((k >> 5) & 1) << 5)) << 4);
+}
+
+// Byte offset of the E8M0 scale of (row `row`, group k / 32) of an FP4 scale
+// matrix in operand-block order: for each 32-row block and 64-wide K step,
+// 64 bytes holding (row % 32) * 2 + (k / 32) % 2.
+__device__ __forceinline__ long fp4_scale_offset(long row, int k, int K) {
+  return ((row >> 5) * (K >> 6) + (k >> 6)) * 64 + ((row & 31) << 1) + ((k >> 5) & 1);
+}
+
+// Element offset of (row i, column t) of a bf16 matrix with `cols` columns
+// (cols % 16 == 0) in MFMA operand-block order: 1 KB blocks of 32 rows x 16
+// columns; inside a block, the 16-byte slot of lane (i % 32) + 32 * ((t % 16) / 8)
+// holds columns 8 * (t / 8) .. + 7 of row i.
+__device__ __forceinline__ long bf16_block_index(long i, int t, int cols) {
+  return (((i >> 5) * (cols >> 4) + (t >> 4)) << 9) + (((i & 31) + (((t >> 3) & 1) << 5)) << 3) + (t & 7);
 }
 
 }  // namespace svdq

@@ -49,6 +49,14 @@ def parse():
     ap.add_argument("--sweep", action="store_true", help="also time the shape sweep (one line each, to stderr)")
     ap.add_argument("--profile-only", action="store_true",
                     help="short run for profilers: warmup + steps of the fused layer, no baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="with --profile-only: first run a plain device copy of known size, the "
+                         "reference that scales the HBM byte counters")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/gemm_<workload>_hbm_counters.json from two rocprofv3 --pmc "
+                         "runs (FETCH_SIZE, WRITE_SIZE) of --profile-only --calibrate-copy")
+    ap.add_argument("--extra", default="c3_fc1_4608x3072x12288_fp4",
+                    help="comma-separated further workloads reported in the same line ('' for none)")
     return ap.parse_args()
 
 
@@ -174,7 +182,11 @@ def cpu_baseline(rig, rows_req):
     L = S.svdq_blob_layout_of(rig.layer.desc)
     r, K, N = cfg.rank, cfg.K, cfg.N
     l1t = sec[L.l1t:L.l1t + 2 * r * K].view(np.uint16).reshape(r, K)
-    l2t = sec[L.l2t:L.l2t + 2 * N * r].view(np.uint16).reshape(N, r)
+    # L2 (N x r) is stored in 1 KB operand blocks: element (n, t) at
+    # ((n/32)*(r/16) + t/16)*512 + (n%32 + 32*((t%16)/8))*8 + t%8
+    n_i, t_i = np.arange(N)[:, None], np.arange(r)[None, :]
+    off = ((n_i // 32) * (r // 16) + t_i // 16) * 512 + (n_i % 32 + 32 * ((t_i % 16) // 8)) * 8 + t_i % 8
+    l2t = sec[L.l2t:L.l2t + 2 * N * r].view(np.uint16)[off]
     factors = (O.bf16_bits_to_f64(l1t).T.copy(), O.bf16_bits_to_f64(l2t).T.copy())
     t0 = time.perf_counter()
     prep = O.prepare(rig.W_bits, O.act_absmax(rig.X_bits), alpha=cfg.alpha, rank=r, fmt=cfg.fmt,
@@ -188,15 +200,19 @@ def cpu_baseline(rig, rows_req):
         O.linear(prep, rig.X_bits[:probe], "bf16")
         dt = time.perf_counter() - t0
         rows = int(min(cfg.M, max(probe, 12.0 / max(dt, 1e-3) * probe)))
-    t0 = time.perf_counter()
-    O.linear(prep, rig.X_bits[:rows], "bf16")
-    dt = time.perf_counter() - t0
+    # repeat the sample until about 10 s of oracle work have been timed
+    reps, dt = 0, 0.0
+    while dt < 10.0 and reps < 50:
+        t0 = time.perf_counter()
+        O.linear(prep, rig.X_bits[:rows], "bf16")
+        dt += time.perf_counter() - t0
+        reps += 1
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    tops = 2.0 * rows * K * N / dt / 1e12
+    tops = 2.0 * rows * K * N * reps / dt / 1e12
     return {"value": tops, "unit": "TOPS", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} of {cfg.M} token rows of the same layer (oracle.linear: act quantization, "
-                      f"down-projection, fp64 dequantized product, low-rank, bias); weight prep "
-                      f"({prep_s:.1f} s) excluded",
+            "sample": f"{rows} of {cfg.M} token rows of the same layer, {reps} times (oracle.linear: act "
+                      f"quantization, down-projection, fp64 dequantized product, low-rank, bias); weight "
+                      f"prep ({prep_s:.1f} s) excluded",
             "seconds": dt, "cpu": _cpu_model()}
 
 
@@ -223,6 +239,77 @@ def load_traffic(workload, src_hash):
     if d.get("kernel_source_hash") != src_hash:
         return None
     return d.get("traffic_bytes_per_launch")
+
+
+COPY_BYTES = 1 << 30          # the calibration copy moves this many bytes each way
+
+
+def calibration_copy(torch):
+    """A plain device-to-device copy of COPY_BYTES (read COPY_BYTES, write
+    COPY_BYTES): the reference the HBM byte counters are scaled by."""
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
+
+
+def summarize_counters(fetch_dir, write_dir, cfg, src_hash):
+    """Per-dispatch HBM traffic of the GEMM kernel from two rocprofv3 --pmc
+    runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), each scaled by the ratio
+    of the calibration copy's known bytes to what the same counter read for
+    it.  Writes profiles/gemm_<workload>_hbm_counters.json."""
+    import csv
+    import glob
+
+    def read(d, counter):
+        rows = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                rows.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return rows
+
+    def pick(rows, pred):
+        vals = [v for k, vs in rows.items() if pred(k) for v in vs]
+        return vals
+
+    is_gemm = (lambda k: k.startswith("void svdq::gemm_fp4_kernel<")) if cfg.fmt == "fp4" else \
+        (lambda k: k.startswith("void svdq::gemm_kernel<"))
+    # torch's copy kernel of the calibration: the largest elementwise-copy dispatch
+    is_copy = lambda k: "copy" in k.lower() and not k.startswith("void svdq::")
+    out = {"workload": cfg.name, "kernel_source_hash": src_hash, "copy_bytes": COPY_BYTES,
+           "commands": [f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{c}_{cfg.name} -o run -- "
+                        f"python3 bench.py --profile-only --calibrate-copy --steps 4 --warmup 1 --workload {cfg.name}"
+                        for c in ("FETCH_SIZE", "WRITE_SIZE")] +
+                       [f"python3 bench.py --summarize-counters gpurun_out/pmc_FETCH_SIZE_{cfg.name} "
+                        f"gpurun_out/pmc_WRITE_SIZE_{cfg.name} --workload {cfg.name}"],
+           "note": "FETCH_SIZE / WRITE_SIZE per dispatch of the GEMM kernel, each scaled by the ratio of "
+                   "the calibration copy's known bytes (torch copy of copy_bytes, one read and one write) "
+                   "to what the same counter read for that copy"}
+    total = 0.0
+    for name, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        rows = read(d, counter)
+        g = pick(rows, is_gemm)
+        c = pick(rows, is_copy)
+        if not g or not c:
+            raise SystemExit(f"no {counter} rows for the GEMM or the calibration copy in {d}")
+        copy_kib = max(c)                                  # the 1 GiB copy is the largest copy dispatch
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        gemm_kib = statistics.mean(g)
+        out[name] = {"counter": counter, "gemm_kib_per_dispatch": gemm_kib, "dispatches": len(g),
+                     "copy_kib": copy_kib, "scale": factor, "gemm_bytes_per_launch": gemm_kib * 1024.0 * factor}
+        total += gemm_kib * 1024.0 * factor
+    out["traffic_bytes_per_launch"] = total
+    path = os.path.join(ROOT, "profiles", f"gemm_{cfg.name}_hbm_counters.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def run_config(args, cfg, torch, S, WL, to_tensor, with_cpu):
@@ -259,7 +346,13 @@ def main():
     cfgs = {c.name: c for c in list(WL.CONFIGS.values()) + WL.sweep_configs()}
     cfg = cfgs[args.workload]
 
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], cfg, kernel_source_hash())
+        return
+
     if args.profile_only:
+        if args.calibrate_copy:
+            calibration_copy(torch)
         rig = Rig(cfg, torch, S, WL, to_tensor)
         ms, _ = time_fused(torch, S, rig, args.steps, args.warmup)
         tq, tg = time_kernels(torch, S, rig, args.steps, args.warmup)
@@ -294,7 +387,8 @@ def main():
                    "bias": cfg.has_bias, "out": "bf16"},
         "roofline": {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_TFLOPS[fmt], "unit": "TFLOP/s",
                      "frac": gemm_tops / PEAK_TFLOPS[fmt], "traffic": traffic,
-                     "kernel": f"gemm_kernel<{fmt}> (4-bit GEMM + rank-{cfg.rank} bf16 slab + bias)",
+                     "kernel": ("gemm_fp4_kernel (FP4 block-scaled MFMA GEMM" if fmt == "fp4" else
+                                "gemm_kernel (INT4 on the i8 MFMA GEMM") + f" + rank-{cfg.rank} bf16 slab + bias)",
                      "avg_us": r["tg_ms"] * 1e3},
         "roofline_quant": {"bound": "hbm", "achieved": q_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": q_gbs / PEAK_HBM_GBS, "kernel": "act_kernel (smooth + quantize + down-proj)",
@@ -313,6 +407,22 @@ def main():
     }
     if "cpu" in r:
         line["cpu_baseline"] = r["cpu"]
+    extra = {}
+    for name in [n for n in args.extra.split(",") if n and n != cfg.name]:
+        c = cfgs[name]
+        rr = run_config(args, c, torch, S, WL, to_tensor, with_cpu=False)
+        Ax = rr["A"]
+        gt = Ax["gemm_ops"] / (rr["tg_ms"] / 1e3) / 1e12
+        extra[name] = {"us_per_layer": rr["ms_fused"] * 1e3, "us_per_layer_unfused": rr["ms_unfused"] * 1e3,
+                       "fused_vs_unfused_speedup": rr["ms_unfused"] / rr["ms_fused"],
+                       "effective_tops": Ax["gemm_ops"] / (rr["ms_fused"] / 1e3) / 1e12,
+                       "gemm_us": rr["tg_ms"] * 1e3, "gemm_tops": gt, "gemm_frac_peak": gt / PEAK_TFLOPS[c.fmt],
+                       "peak_tops": PEAK_TFLOPS[c.fmt], "quant_us": rr["tq_ms"] * 1e3,
+                       "quant_frac_hbm": Ax["q_bytes"] / (rr["tq_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS}
+        del rr
+        torch.cuda.empty_cache()
+    if extra:
+        line["extra_workloads"] = extra
     print(json.dumps(line), flush=True)
 
     if args.sweep:

@@ -82,9 +82,10 @@ typedef enum svdq_status {
  * Rows are padded to a multiple of 32; the padding bytes are unspecified.
  *
  * FP4 scale matrices (E8M0 bytes, one per row and 32-wide group) follow the
- * same blocking: for each 32-row block and 64-wide K step, 64 bytes, row
- * i % 32 at byte 2 (i % 32) + (k / 32) % 2:
- *     ((i / 32) * (K / 64) + k / 64) * 64 + (i % 32) * 2 + (k / 32) % 2
+ * same blocking: for each 32-row block and 128-wide K stage, 128 bytes; the
+ * 2-byte slot of lane (i % 32) + 32 ((k / 32) % 2) holds the scales of the
+ * stage's two 64-wide steps:
+ *     ((i / 32) * (K / 128) + k / 128) * 128 + (i % 32 + 32 * ((k / 32) % 2)) * 2 + (k / 64) % 2
  * INT4 scales (fp16) are row-major [rows][K / 64].
  *
  * bf16 low-rank matrices with `cols` columns (cols % 16 == 0: T, M x rank,

@@ -52,11 +52,12 @@ def untile_bf16(raw_u16: np.ndarray, rows: int, cols: int) -> np.ndarray:
 
 def untile_fp4_scales(raw: np.ndarray, rows: int, K: int) -> np.ndarray:
     """FP4 E8M0 scale bytes in operand-block order -> [rows][K/32].  The byte
-    of (row i, group k/32) sits at ((i/32)*(K/64) + k/64)*64 + (i%32)*2 + (k/32)%2."""
+    of (row i, group k/32) sits at
+    ((i/32)*(K/128) + k/128)*128 + (i%32 + 32*((k/32)%2))*2 + (k/64)%2."""
     raw = np.asarray(raw).reshape(-1)
     i = np.arange(rows, dtype=np.int64)[:, None]
-    grp = np.arange(K // 32, dtype=np.int64)[None, :]
-    off = ((i // 32) * (K // 64) + grp // 2) * 64 + (i % 32) * 2 + grp % 2
+    k = 32 * np.arange(K // 32, dtype=np.int64)[None, :]
+    off = ((i // 32) * (K // 128) + k // 128) * 128 + (i % 32 + 32 * ((k // 32) % 2)) * 2 + (k // 64) % 2
     assert off.max() < raw.size, "scale buffer smaller than the block layout needs"
     return raw[off]
 

@@ -1,5 +1,6 @@
-// Kernel G: the 4-bit GEMM of the SVDQuant layer with the low-rank
-// up-projection appended as an extra bf16 K-slab and a fused bias epilogue.
+// Kernel G, INT4 variant: the 4-bit GEMM of the SVDQuant layer with the
+// low-rank up-projection appended as an extra bf16 K-slab and a fused bias
+// epilogue.  (The FP4 variant is in gemm_fp4.hip.)
 //
 //   acc[i, n]  = sum_t Tb[i, t] L2b[t, n]      (eq. (5) low-rank branch; the
 //                                               walkthrough's Fig. 6: it shares
@@ -8,28 +9,24 @@
 //                                              (eq. (2) per group)
 //   Y[i, n]    = round(acc[i, n] + b[n])
 //
-// INT4 (group 64, fp16 scales): the packed nibbles of each K stage are moved
-// to LDS; on the way from LDS to the registers each nibble is widened to a
-// byte holding 16 * q (shifted into the high half of the byte, so the sign
-// comes for free); two 32x32x32 i8 MFMAs give 256 * P_g exactly in int32 and
-// the group is dequantized into the fp32 accumulators with s_x * s_w / 256.
-// The MFMAs of the next output tile are issued before the dequantization of
-// the current one, so the matrix core and the VALU overlap.
-// FP4 (group 32, E8M0 scales): the E2M1 nibbles and the power-of-two scales
-// are the native operands of the gfx950 block-scaled MFMA (32x32x64), which
-// accumulates in fp32 directly; there is no dequantization work.
+// Group 64, fp16 scales: the packed nibbles of each K stage are moved to
+// LDS; on the way from LDS to the registers each nibble is widened to a byte
+// holding 16 * q (shifted into the high half of the byte, so the sign comes
+// for free); two 32x32x32 i8 MFMAs give 256 * P_g exactly in int32 and the
+// group is dequantized into the fp32 accumulators with s_x * s_w / 256.  The
+// MFMAs of the next output tile are issued before the dequantization of the
+// current one, so the matrix core and the VALU overlap.
 //
-// Tiling (see Shape): 4 waves per workgroup, FP4 256 x 256, INT4 128 x 128;
-// 32 x 32 MFMA tiles.  A K stage is 128 wide (two
-// 64-wide MFMA steps); the LDS holds two stages, the global loads of a stage
-// are issued three stages before its MFMAs (two register sets), and each
-// stage has one barrier.  In every
-// MFMA, lane l owns row (column) l % 32 and the 16-byte half l / 32 of the
-// 64-wide K step, for A and B alike, so both operands enumerate K in the same
-// order.  Workgroups are mapped to tiles so that the workgroups resident on
-// one XCD (the hardware deals them round-robin to the 8 XCDs) cover a
-// compact block of tiles that shares rows of A and columns of B in that
-// XCD's L2.
+// Tiling: 4 waves per workgroup in a 2 x 2 grid, 128 x 128 per workgroup,
+// 32 x 32 MFMA tiles.  A K stage is 128 wide (two 64-wide MFMA steps); the
+// LDS holds two stages, the global loads of a stage are issued three stages
+// before its MFMAs (two register sets), and each stage has one barrier.  In
+// every MFMA, lane l owns row (column) l % 32 and the 16-byte half l / 32 of
+// the 64-wide K step, for A and B alike, so both operands enumerate K in the
+// same order.  Workgroups are mapped to tiles so that the workgroups
+// resident on one XCD (the hardware deals them round-robin to the 8 XCDs)
+// cover a compact block of tiles that shares rows of A and columns of B in
+// that XCD's L2.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
@@ -42,8 +39,6 @@ namespace svdq {
 namespace {
 
 constexpr int BKB = 64;          // code bytes per row per stage (128 K values)
-constexpr int NXCD = 8;
-constexpr int GROUP_TM = 4;      // tile rows per L2 group
 
 __device__ __forceinline__ uint32_t lo_nib_bytes(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
 __device__ __forceinline__ uint32_t hi_nib_bytes(uint32_t w) { return w & 0xF0F0F0F0u; }
@@ -64,22 +59,6 @@ __device__ __forceinline__ float load_out(const void* Y, I idx) {
   } else {
     return __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(Y)[idx]) << 16);
   }
-}
-
-// workgroup id -> (tile_m, tile_n): contiguous tile ranges per XCD, grouped
-// GROUP_TM tile rows at a time inside each range.
-__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int T = tiles_m * tiles_n;
-  const int q = T / NXCD, rem = T % NXCD;
-  const int x = b % NXCD, j = b / NXCD;
-  const int t = x * q + (x < rem ? x : rem) + j;
-  const int per_group = GROUP_TM * tiles_n;
-  const int grp = t / per_group;
-  const int first = grp * GROUP_TM;
-  const int gm = min(GROUP_TM, tiles_m - first);
-  const int w = t - grp * per_group;
-  tm = first + w % gm;
-  tn = w / gm;
 }
 
 }  // namespace
@@ -393,412 +372,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// FP4 GEMM: gfx950 block-scaled MFMA, persistent workgroups of 8 waves, a
-// deep ring of direct global->LDS copies.
-//
-// Operand roles: the MFMA's A operand is the weight tile (its rows are output
-// columns n) and its B operand the activation tile (output rows m).  A 32x32
-// accumulator then gives lane l output row m = l % 32 and, for element v,
-// column 8 (v / 4) + 4 (l / 32) + v % 4.
-//
-// Waves: 8 per workgroup, two per SIMD (so one wave's waits hide behind the
-// other's MFMAs, and twice as many waves keep copies in flight: the copy
-// throughput of a wave is limited, not the bytes in flight).  The 256 x 256
-// output tile is split 2 (m) x 4 (n): each wave owns 128 rows x 64 columns,
-// 4 x 2 MFMA tiles, 128 fp32 accumulators.
-//
-// Stages: the reduction of one output tile is a sequence of stages, first
-// rank / 16 low-rank stages (16 ranks of Tb and L2b, bf16 32x32x16 MFMA),
-// then K / 64 FP4 stages (32x32x64 block-scaled MFMA).  Both kinds move 8 KB
-// of activation-side and 8 KB of weight-side operand blocks (1 KB = 32 rows
-// in MFMA lane order, contiguous in global memory) plus 1 KB of E8M0 scale
-// bytes straight from global memory into a ring of LDS stage
-// buffers; copies run P_AHEAD stages ahead of the MFMAs.  A wave completes
-// copy instructions at a limited rate whatever their size, so every copy
-// moves 16 bytes per lane: each wave copies one activation and one weight
-// block per stage, the scale kilobyte of a stage is copied by one wave in
-// turn, and a tile's bias (1 KB) once per tile.  Each workgroup walks its
-// tiles in sequence and the stage stream continues across tile boundaries.
-// One barrier per stage publishes the next stage (wait for this wave's
-// copies of it, then s_barrier) and frees the buffer the new copies go to.
-//
-// Epilogue: bias, rounding, and 16-row slices staged in the X/W part of the
-// just-consumed stage buffer (free until the next stage's barrier), read
-// back as whole rows and stored 16 bytes per lane, contiguous.
-namespace {
-constexpr int P_TILE = 256;                        // output tile P_TILE x P_TILE
-constexpr int P_X = 0, P_W = 8192, P_S = 16384;    // parts of a stage buffer
-constexpr int P_STAGE = 17408;                     // + 1 KB of scales: 8 x 64 activation, 8 x 64 weight
-
-// wait until at most n vector-memory operations of this wave are
-// outstanding, then barrier; a compiler memory barrier as well
-#define SVDQ_WAIT_VM_BARRIER(n) asm volatile("s_waitcnt vmcnt(" #n ")\n\ts_barrier" ::: "memory")
-}  // namespace
-
-// BIG: every tile has more than P_AHEAD stages, so the copies run at most
-// one tile ahead and their source follows from the consumed stage without a
-// separate cursor.  RS_ODD: rank / 16 is odd (decides how many stages of a
-// tile are peeled off its even-length loops).
-template <bool SLAB, int OUT, bool RS_ODD, bool BIG>
-__global__ __launch_bounds__(512) void gemm_fp4_kernel(GemmArgs g) {
-  // Ring of P_NBUF stage buffers (P_AHEAD = P_NBUF - 1 stages in flight),
-  // then P_NBIAS tile bias buffers of 1 KB (by turn % P_NBIAS).  The copies
-  // run at most P_AHEAD stages ahead, so with 8 bias buffers a tile's bias
-  // is not overwritten before its epilogue for any tile of 2 stages or more.
-  // (A ninth stage buffer measured slower.)
-  constexpr int P_NBUF = 8;
-  constexpr int P_AHEAD = P_NBUF - 1;
-  constexpr int P_NBIAS = 8;
-  constexpr int P_BIAS = P_NBUF * P_STAGE;
-  constexpr int P_LDS = P_BIAS + P_NBIAS * 1024;   // 147456 bytes
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[P_LDS];
-
-  const int M = g.M, K = g.K, N = g.N;
-  const int RS = SLAB ? g.rank / 16 : 0;        // low-rank stages per tile
-  const int KS = K / 64;                         // FP4 stages per tile
-  const int S = RS + KS;
-  const uint8_t* __restrict__ acodes = g.acodes;
-  const uint8_t* __restrict__ wcodes = g.wcodes;
-  const uint8_t* __restrict__ ascales = static_cast<const uint8_t*>(g.ascales);
-  const uint8_t* __restrict__ wscales = static_cast<const uint8_t*>(g.wscales);
-  const uint8_t* __restrict__ tbb = reinterpret_cast<const uint8_t*>(g.Tb);
-  const uint8_t* __restrict__ l2b = reinterpret_cast<const uint8_t*>(g.l2t);
-  const bool has_bias = g.bias != nullptr;
-  const float* __restrict__ bias = g.bias;
-  void* __restrict__ Yout = g.Y;
-
-  const int tiles_m = (M + P_TILE - 1) / P_TILE, tiles_n = (N + P_TILE - 1) / P_TILE;
-  const int ntiles = tiles_m * tiles_n;
-  const int grid = static_cast<int>(gridDim.x), wg = static_cast<int>(blockIdx.x);
-  const int my_tiles = (ntiles - wg + grid - 1) / grid;   // >= 1: the grid never exceeds the tile count
-  const int last_ablk = (M + 31) / 32 - 1, last_bblk = N / 32 - 1;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = wave_uniform(threadIdx.x >> 6);
-  const int wm = wave >> 2, wn = wave & 3;       // 128-row half, 64-column quarter
-  const int l32 = lane & 31, lh = lane >> 5;
-
-  // 32-row block indices of the tile a workgroup handles in its seq-th turn
-  auto tile_blocks = [&](int seq, int& mb0, int& nb0) __attribute__((always_inline)) {
-    int tm, tn;
-    tile_of(wg + seq * grid, tiles_m, tiles_n, tm, tn);
-    mb0 = tm * (P_TILE / 32);
-    nb0 = tn * (P_TILE / 32);
-  };
-
-  // ---- copy side.  For stage C, wave w copies activation block w and
-  // weight block w (1 KB each); wave C % 8 also copies the stage's scale
-  // kilobyte (lanes 0-31: 64 bytes per activation block, 4 lanes each;
-  // lanes 32-63 the weight blocks); on the last stage of a tile with a bias,
-  // wave 0 also copies the tile's 256 bias values into bias buffer
-  // turn % P_NBIAS (a tile's bias buffer is not reused before its epilogue:
-  // the copies run at most P_AHEAD stages ahead).  Blocks past the matrix are clamped to its last
-  // block; copies past the last stage repeat the last stage.  Sources are
-  // byte offsets turned into pointers at the copy (plain locals are the form
-  // the host compilation pass of this kernel also accepts).
-  struct Src {
-    long x, w, sc, b;      // operand blocks, this lane's scale bytes, this lane's bias values
-    bool lr;               // low-rank stage (Tb / L2b bases)
-    bool scales, bias;     // this wave copies the scales / the bias of the stage
-    uint32_t dst, bdst;    // LDS byte offsets of the stage buffer and the bias buffer
-  };
-  auto stage_src = [&](int seq, int st, long C, int mb0, int nb0) __attribute__((always_inline)) {
-    Src q;
-    q.lr = SLAB && st < RS;
-    const int ks = q.lr ? st : st - RS;           // stage index inside its matrix
-    const long stride = q.lr ? RS : KS;           // 1 KB blocks per 32-row block
-    q.x = (min(mb0 + wave, last_ablk) * stride + ks) << 10;
-    q.w = (min(nb0 + wave, last_bblk) * stride + ks) << 10;
-    const int kst = q.lr ? 0 : ks;                // low-rank stages copy (unused) scales of stage 0
-    const int sblk = (lane >> 2) & 7;
-    const long srow = lh ? min(nb0 + sblk, last_bblk) : min(mb0 + sblk, last_ablk);
-    q.sc = (srow * KS + kst) * 64 + (lane & 3) * 16;
-    q.b = min(nb0 * 32 + lane * 4, N - 4);
-    q.scales = wave == static_cast<int>(C & 7);     // the 8 waves take turns
-    q.bias = wave == 0 && has_bias && st == S - 1;
-    q.dst = static_cast<uint32_t>(C % P_NBUF) * P_STAGE;
-    q.bdst = P_BIAS + (seq & (P_NBIAS - 1)) * 1024;
-    return q;
-  };
-  auto copy = [&](const Src& q, int i) __attribute__((always_inline)) {
-    if (i < 2) {
-      const uint8_t* src = (i == 0 ? (q.lr ? tbb : acodes) + q.x : (q.lr ? l2b : wcodes) + q.w) + lane * 16;
-      uint8_t* dst = smem + q.dst + (i == 0 ? P_X : P_W) + wave * 1024;
-      __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-    } else if (i == 2) {
-      if (q.scales) {
-        const uint8_t* src = (lh ? wscales : ascales) + q.sc;
-        uint8_t* dst = smem + q.dst + P_S;
-        __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-      }
-    } else {
-      if (q.bias) {
-        const float* src = bias + q.b;
-        uint8_t* dst = smem + q.bdst;
-        __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-      }
-    }
-  };
-  constexpr int NCOPY = 4;                        // copy slots per stage (the last two conditional)
-
-  // tile being consumed, and the next one (BIG: the copies' only other tile)
-  int seq = 0, mb0, nb0, nmb0, nnb0;
-  tile_blocks(0, mb0, nb0);
-  nmb0 = mb0;
-  nnb0 = nb0;
-  // general cursor (small tiles): the next stage to copy
-  int iseq = 0, ist = 0, imb0 = mb0, inb0 = nb0;
-  // sources of the copies issued while stage st of the current tile is consumed
-  auto ahead_src = [&](int st, long G) __attribute__((always_inline)) {
-    if constexpr (BIG) {
-      const int t = st + P_AHEAD;
-      const bool wrap = t >= S, has_next = seq + 1 < my_tiles;
-      const bool nxt = wrap && has_next;
-      // past the last tile: repeat its last stage
-      const int cst = wrap ? (has_next ? t - S : S - 1) : t;
-      return stage_src(nxt ? seq + 1 : seq, cst, G + P_AHEAD, nxt ? nmb0 : mb0, nxt ? nnb0 : nb0);
-    } else {
-      const bool past = iseq >= my_tiles;
-      const Src q = stage_src(past ? my_tiles - 1 : iseq, past ? S - 1 : ist, G + P_AHEAD, imb0, inb0);
-      if (!past && ++ist == S) {
-        ist = 0;
-        if (++iseq < my_tiles) tile_blocks(iseq, imb0, inb0);
-      }
-      return q;
-    }
-  };
-
-  // ---- compute side: operand piece p of a stage (p = 0: weight block 0,
-  // 1..4: activation blocks 0..3, 5: weight block 1, the order the 8 MFMAs
-  // first need them), with its scale byte.  A stage's reads use four
-  // per-lane base addresses (the ring offset is uniform, the lane part
-  // loop-invariant) and constant offsets.
-  struct Ops {
-    u32x4 w[2], x[4];
-    uint32_t sw[2], sx[4];
-  };
-  struct Addr {
-    uint32_t x, w, sx, sw;
-  };
-  const uint32_t lane16 = lane * 16, lanes = l32 * 2 + lh;
-  auto addr_of = [&](long G) __attribute__((always_inline)) {
-    const uint32_t b = static_cast<uint32_t>(G % P_NBUF) * P_STAGE;
-    Addr a;
-    a.x = b + P_X + wm * 4096 + lane16;           // activation blocks 4 wm + j
-    a.w = b + P_W + wn * 2048 + lane16;           // weight blocks 2 wn + i
-    a.sx = b + P_S + wm * 256 + lanes;            // scales of activation block 4 wm + j: + j * 64
-    a.sw = b + P_S + 512 + wn * 128 + lanes;      // scales of weight block 2 wn + i: + i * 64
-    return a;
-  };
-  auto read_piece = [&](Ops& o, const Addr& a, int p) __attribute__((always_inline)) {
-    if (p == 0 || p == 5) {
-      const int i = p == 0 ? 0 : 1;
-      o.w[i] = *reinterpret_cast<const u32x4*>(smem + a.w + i * 1024);
-      o.sw[i] = smem[a.sw + i * 64];
-    } else {
-      const int j = p - 1;
-      o.x[j] = *reinterpret_cast<const u32x4*>(smem + a.x + j * 1024);
-      o.sx[j] = smem[a.sx + j * 64];
-    }
-  };
-
-  f32x16 acc[2][4];
-  // MFMA k of a stage: weight block i = k / 4, activation block j = k % 4.
-  // The first stage of a tile adds to a constant zero instead of the
-  // accumulators (which therefore never need clearing).
-  auto mfma = [&](const Ops& o, int k, auto LR, auto FIRST) __attribute__((always_inline)) {
-    const int i = k >> 2, j = k & 3;
-    f32x16 c = acc[i][j];
-    if constexpr (decltype(FIRST)::value) {
-#pragma unroll
-      for (int v = 0; v < 16; v++) c[v] = 0.f;
-    }
-    if constexpr (decltype(LR)::value) {
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, o.w[i]),
-                                                         __builtin_bit_cast(bf16x8, o.x[j]), c, 0, 0, 0);
-    } else {
-      const i32x8 av = i32x8{(int)o.w[i].x, (int)o.w[i].y, (int)o.w[i].z, (int)o.w[i].w, 0, 0, 0, 0};
-      const i32x8 bv = i32x8{(int)o.x[j].x, (int)o.x[j].y, (int)o.x[j].z, (int)o.x[j].w, 0, 0, 0, 0};
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 0, (int)o.sw[i], 0, (int)o.sx[j]);
-    }
-  };
-
-  // One stage (index st of the tile, G overall): 8 MFMAs on `cur`; between
-  // them the reads of stage G + 1 into `nxt` and the copies of stage
-  // G + P_AHEAD.  The wait at the top publishes stage G + 1: at least the
-  // block copies of the P_AHEAD - 2 stages issued after it may stay in flight (the
-  // occasional scale or bias copy among them only makes the wait slightly
-  // longer), and in the first P_AHEAD - 1 stages of a tile also the
-  // previous tile's epilogue stores, which were issued after them.  It also
-  // frees the buffer of stage G - 1.  The order is fixed with scheduling
-  // fences.
-  constexpr int NSTORE = OUT == SVDQ_OUT_F32 ? 32 : 16;   // epilogue stores per wave
-  auto stage = [&](const Ops& cur, Ops& nxt, long G, int st, auto LR, auto FIRST) __attribute__((always_inline)) {
-    const Src q = ahead_src(st, G);
-    const Addr an = addr_of(G + 1);
-    mfma(cur, 0, LR, FIRST);
-    // 5 stages of 2 block copies after stage G + 1 (+ the epilogue stores)
-    if (BIG && seq > 0 && st <= P_AHEAD - 2) {
-      if constexpr (NSTORE == 32) SVDQ_WAIT_VM_BARRIER(42);
-      else SVDQ_WAIT_VM_BARRIER(26);
-    } else {
-      SVDQ_WAIT_VM_BARRIER(10);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 1; k < 8; k++) {
-      mfma(cur, k, LR, FIRST);
-      if (k <= 6) read_piece(nxt, an, k - 1);
-      if (k >= 3 && k - 3 < NCOPY) copy(q, k - 3);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // Epilogue of the tile at (mb0, nb0), after its last stage G: bias,
-  // rounding, then per 16-row (bf16) or 8-row (fp32) slice: the lanes holding
-  // those rows write them into this wave's 2 KB of the X/W part of stage
-  // buffer G (16-byte chunks XOR-swizzled by row against bank conflicts),
-  // and the wave reads whole rows back and stores them 16 bytes per lane.
-  // The bias of the tile was copied into the tail of the same buffer.  The
-  // stores are bounds-checked buffer stores over the tile's rows: rows past
-  // M and columns past N get an offset past the buffer and are dropped, so
-  // every store instruction issues (the waits count them).
-  auto epilogue = [&](long G) __attribute__((always_inline)) {
-    // lane indices recomputed here through an opaque move, so that the
-    // compiler does not hoist the epilogue's per-lane addresses out of the
-    // tile loop (they would stay live through the main loops and spill)
-    int lane_e;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(lane_e) : "v"(lane));
-    const int l32 = lane_e & 31, lh = lane_e >> 5, lane = lane_e;
-    constexpr int OB = OUT == SVDQ_OUT_F32 ? 4 : 2;
-    constexpr int CPR = 64 * OB / 16;             // 16-byte chunks per staged row
-    constexpr int RPS = 2048 / (64 * OB);         // rows per slice
-    const uint32_t buf = static_cast<uint32_t>(G % P_NBUF) * P_STAGE;
-    uint8_t* stg = smem + buf + wave * 2048;
-    const float* bl = reinterpret_cast<const float*>(smem + P_BIAS + (seq & (P_NBIAS - 1)) * 1024);
-    const long col0 = static_cast<long>(nb0) * 32 + wn * 64;
-    const bool cols_ok = col0 < N;                // N % 64 == 0: all 64 columns or none
-    const long m0 = static_cast<long>(mb0) * 32;
-    const uint32_t rowb = static_cast<uint32_t>(N * OB);                     // output row bytes
-    const uint32_t nrec = static_cast<uint32_t>(min(static_cast<long>(M) - m0, static_cast<long>(P_TILE))) * rowb;
-    const __amdgpu_buffer_rsrc_t yr =
-        __builtin_amdgcn_make_buffer_rsrc(static_cast<uint8_t*>(Yout) + m0 * rowb, 0, static_cast<int>(nrec), 0x00020000);
-    // read-back position of this lane's two chunks: slice row rr[q2], chunk kk[q2]
-    const int rr0 = lane / CPR, rr1 = (lane + 64) / CPR, kk0 = lane % CPR, kk1 = (lane + 64) % CPR;
-    const uint32_t coff = static_cast<uint32_t>(col0 * OB);
-    const uint32_t loff0 = rr0 * rowb + coff + kk0 * 16, loff1 = rr1 * rowb + coff + kk1 * 16;
-    const int valid_rows = static_cast<int>(min(static_cast<long>(M) - m0, static_cast<long>(P_TILE)));
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-#pragma unroll
-      for (int h = 0; h < 32 / RPS; h++) {
-        // rows 32 j + RPS h .. of the wave's 128: held by lanes with l32 / RPS == h
-        if (l32 / RPS == h) {
-          const int r = l32 % RPS;
-#pragma unroll
-          for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int gq = 0; gq < 4; gq++) {
-              // bias of tile columns 64 wn + 32 i + 8 gq + 4 lh .. + 3
-              f32x4 b4 = f32x4{0.f, 0.f, 0.f, 0.f};
-              if (has_bias) b4 = *reinterpret_cast<const f32x4*>(bl + wn * 64 + i * 32 + 8 * gq + 4 * lh);
-              const float y0 = acc[i][j][4 * gq] + b4.x, y1 = acc[i][j][4 * gq + 1] + b4.y;
-              const float y2 = acc[i][j][4 * gq + 2] + b4.z, y3 = acc[i][j][4 * gq + 3] + b4.w;
-              if constexpr (OUT == SVDQ_OUT_F32) {
-                const int ch = i * 8 + gq * 2 + lh;  // 16-byte chunk of the 256-byte row
-                *reinterpret_cast<f32x4*>(stg + r * 256 + ((ch ^ (r % CPR)) << 4)) = f32x4{y0, y1, y2, y3};
-              } else {
-                const int ch = i * 4 + gq;           // 16-byte chunk of the 128-byte row; lh picks its half
-                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                *reinterpret_cast<u32x2*>(stg + r * 128 + ((ch ^ (r % CPR)) << 4) + lh * 8) =
-                    u32x2{f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16),
-                          f32_to_bf16_bits(y2) | (f32_to_bf16_bits(y3) << 16)};
-              }
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
-        // 2 KB slice: 128 chunks of 16 bytes, two per lane
-        const int srow = (wm * 4 + j) * 32 + h * RPS;                       // first slice row in the tile
-        const uint32_t soff = static_cast<uint32_t>(srow) * rowb;
-#pragma unroll
-        for (int q2 = 0; q2 < 2; q2++) {
-          const int r = q2 ? rr1 : rr0, k = q2 ? kk1 : kk0;
-          const u32x4 d = *reinterpret_cast<const u32x4*>(stg + r * (CPR * 16) + ((k ^ (r % CPR)) << 4));
-          const uint32_t off = cols_ok && srow + r < valid_rows ? soff + (q2 ? loff1 : loff0) : nrec;
-          __builtin_amdgcn_raw_buffer_store_b128(d, yr, static_cast<int>(off), 0, 0);
-        }
-        __builtin_amdgcn_wave_barrier();
-      }
-    }
-  };
-
-  // ---- prologue: P_AHEAD stages in flight, stage 0 published and read
-  Ops oa, ob;
-  if constexpr (BIG) {
-#pragma unroll 1
-    for (int st = 0; st < P_AHEAD; st++) {
-      const Src q = stage_src(0, st, st, mb0, nb0);
-#pragma unroll
-      for (int i = 0; i < NCOPY; i++) copy(q, i);
-    }
-  } else {
-#pragma unroll 1
-    for (int st = 0; st < P_AHEAD; st++) {
-      const Src q = ahead_src(0, st - P_AHEAD);
-#pragma unroll
-      for (int i = 0; i < NCOPY; i++) copy(q, i);
-    }
-  }
-  // stage 0 complete: at least the block copies of the P_AHEAD - 1 stages
-  // after it may stay in flight
-  SVDQ_WAIT_VM_BARRIER(12);
-#pragma unroll
-  for (int p = 0; p < 6; p++) read_piece(oa, addr_of(0), p);
-
-  // ---- per tile: S stages (the first starts the accumulators), then the
-  // epilogue.  The copies run P_AHEAD stages ahead, across tile boundaries.
-  long G = 0;
-#pragma unroll 1
-  for (; seq < my_tiles; seq++) {
-    if (seq > 0) {
-      mb0 = nmb0;
-      nb0 = nnb0;
-    }
-    if (seq + 1 < my_tiles) tile_blocks(seq + 1, nmb0, nnb0);
-    // Stages [from, to) of one kind, two per trip (the operand register sets
-    // alternate: `c` holds the current stage's operands on entry and again
-    // on exit); every run has an even length, so there is no odd tail whose
-    // join would force the accumulators through VGPRs.
-    auto run = [&](Ops& c, Ops& d, int from, int to, auto LR) __attribute__((always_inline)) {
-#pragma unroll 1
-      for (int st = from; st < to; st += 2) {
-        stage(c, d, G, st, LR, std::false_type{});
-        stage(d, c, G + 1, st + 1, LR, std::false_type{});
-        G += 2;
-      }
-    };
-    // One stage is peeled when rank / 16 is odd, two otherwise, which leaves
-    // even-length runs (K / 64 is even).
-    stage(oa, ob, G, 0, std::bool_constant<SLAB>{}, std::true_type{});
-    G++;
-    if constexpr (SLAB && RS_ODD) {
-      run(ob, oa, 1, RS, std::true_type{});
-      run(ob, oa, RS, S, std::false_type{});
-    } else {
-      stage(ob, oa, G, 1, std::bool_constant<SLAB>{}, std::false_type{});
-      G++;
-      if constexpr (SLAB) run(oa, ob, 2, RS, std::true_type{});
-      run(oa, ob, SLAB ? RS : 2, S, std::false_type{});
-    }
-    epilogue(G - 1);
-    // with one peeled stage the next tile's operands were read into ob
-    if constexpr (SLAB && RS_ODD) oa = ob;
-  }
-  // no copy may still be writing this workgroup's LDS when it exits
-  SVDQ_WAIT_VM_BARRIER(0);
-}
-
 // Unfused up-projection: Y = round(Y + Tb L2b), 64 x 64 tile per workgroup.
 template <int OUT>
 __global__ __launch_bounds__(256) void up_kernel(const uint16_t* __restrict__ Tb, const uint16_t* __restrict__ l2t,
@@ -832,20 +405,6 @@ __global__ __launch_bounds__(256) void up_kernel(const uint16_t* __restrict__ Tb
   }
 }
 
-// Compute units of the current device (cached per device): the persistent
-// FP4 kernel launches at most one workgroup per CU.
-static int cu_count() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cache[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 hipError_t launch_gemm(int fmt, bool slab, int out_dtype, const GemmArgs& g, hipStream_t st) {
   const bool f32 = out_dtype == SVDQ_OUT_F32;
   if (fmt == SVDQ_INT4_G64_FP16) {
@@ -858,21 +417,7 @@ hipError_t launch_gemm(int fmt, bool slab, int out_dtype, const GemmArgs& g, hip
 #undef SVDQ_G
     return hipGetLastError();
   }
-  const int tiles = ((g.M + P_TILE - 1) / P_TILE) * ((g.N + P_TILE - 1) / P_TILE);
-  dim3 grid(std::min(tiles, cu_count())), block(512);
-  const bool odd = slab && ((g.rank / 16) & 1);
-  const bool big = (slab ? g.rank / 16 : 0) + g.K / 64 > 7;     // more stages than the ring has in flight
-#define SVDQ_F(S, O, R, B) hipLaunchKernelGGL((gemm_fp4_kernel<S, O, R, B>), grid, block, 0, st, g)
-#define SVDQ_F2(S, O, R) do { if (big) SVDQ_F(S, O, R, true); else SVDQ_F(S, O, R, false); } while (0)
-  if (slab) {
-    if (odd) { if (f32) SVDQ_F2(true, SVDQ_OUT_F32, true); else SVDQ_F2(true, SVDQ_OUT_BF16, true); }
-    else     { if (f32) SVDQ_F2(true, SVDQ_OUT_F32, false); else SVDQ_F2(true, SVDQ_OUT_BF16, false); }
-  } else {
-    if (f32) SVDQ_F2(false, SVDQ_OUT_F32, false); else SVDQ_F2(false, SVDQ_OUT_BF16, false);
-  }
-#undef SVDQ_F2
-#undef SVDQ_F
-  return hipGetLastError();
+  return launch_gemm_fp4(slab, out_dtype, g, st);
 }
 
 hipError_t launch_up(int out_dtype, const uint16_t* Tb, const uint16_t* l2t, void* Y, int M, int N, int rank,

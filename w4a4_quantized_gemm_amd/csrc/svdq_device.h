@@ -73,10 +73,11 @@ __device__ __forceinline__ long code_chunk_offset(long row, int k, int K) {
 }
 
 // Byte offset of the E8M0 scale of (row `row`, group k / 32) of an FP4 scale
-// matrix in operand-block order: for each 32-row block and 64-wide K step,
-// 64 bytes holding (row % 32) * 2 + (k / 32) % 2.
+// matrix in operand-block order: for each 32-row block and 128-wide K stage,
+// 128 bytes; the 2-byte slot of MFMA lane (row % 32) + 32 ((k / 32) % 2)
+// holds the scales of the stage's two 64-wide steps, (k / 64) % 2.
 __device__ __forceinline__ long fp4_scale_offset(long row, int k, int K) {
-  return ((row >> 5) * (K >> 6) + (k >> 6)) * 64 + ((row & 31) << 1) + ((k >> 5) & 1);
+  return ((row >> 5) * (K >> 7) + (k >> 7)) * 128 + (((row & 31) + (((k >> 5) & 1) << 5)) << 1) + ((k >> 6) & 1);
 }
 
 // Element offset of (row i, column t) of a bf16 matrix with `cols` columns
@@ -85,6 +86,25 @@ __device__ __forceinline__ long fp4_scale_offset(long row, int k, int K) {
 // holds columns 8 * (t / 8) .. + 7 of row i.
 __device__ __forceinline__ long bf16_block_index(long i, int t, int cols) {
   return (((i >> 5) * (cols >> 4) + (t >> 4)) << 9) + (((i & 31) + (((t >> 3) & 1) << 5)) << 3) + (t & 7);
+}
+
+// Workgroup (or persistent turn) id b -> output tile (tm, tn).  The hardware
+// deals workgroups round-robin to the 8 XCDs, so b % 8 is the XCD; each XCD
+// gets a contiguous range of tiles, walked 4 tile rows at a time so that the
+// workgroups resident on one XCD share rows of A and columns of B in its L2.
+__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int NXCD = 8, GROUP_TM = 4;
+  const int T = tiles_m * tiles_n;
+  const int q = T / NXCD, rem = T % NXCD;
+  const int x = b % NXCD, j = b / NXCD;
+  const int t = x * q + (x < rem ? x : rem) + j;
+  const int per_group = GROUP_TM * tiles_n;
+  const int grp = t / per_group;
+  const int first = grp * GROUP_TM;
+  const int gm = min(GROUP_TM, tiles_m - first);
+  const int w = t - grp * per_group;
+  tm = first + w % gm;
+  tn = w / gm;
 }
 
 }  // namespace svdq

@@ -37,6 +37,8 @@ struct GemmArgs {
 
 // slab: append the rank-r bf16 K-slab Tb L2b before the epilogue.
 hipError_t launch_gemm(int fmt, bool slab, int out_dtype, const GemmArgs& g, hipStream_t st);
+// the FP4 variant (persistent, block-scaled MFMA); launch_gemm dispatches to it
+hipError_t launch_gemm_fp4(bool slab, int out_dtype, const GemmArgs& g, hipStream_t st);
 
 // Unfused up-projection: Y = round(Y + Tb L2b) in place.
 hipError_t launch_up(int out_dtype, const uint16_t* Tb, const uint16_t* l2t, void* Y, int M, int N,

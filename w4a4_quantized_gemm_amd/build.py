@@ -35,10 +35,17 @@ HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", 
              "-fno-gpu-rdc", "-ffp-contract=off", "-mllvm", "-disable-promote-alloca-to-lds"]
 
 
+# per-file device flags: the INT4 GEMM dequantizes the i8 MFMA's int32 results
+# with VALU code, so its MFMAs write VGPRs directly (otherwise every result
+# would be read out of the accumulation registers first)
+FILE_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     if src.endswith(".hip"):
-        cmd = [HIPCC, *HIP_FLAGS, *COMMON, "-x", "hip", "-c", src, "-o", obj]
+        extra = FILE_FLAGS.get(os.path.basename(src), [])
+        cmd = [HIPCC, *HIP_FLAGS, *extra, *COMMON, "-x", "hip", "-c", src, "-o", obj]
     else:
         cmd = ["g++", *COMMON, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

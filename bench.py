@@ -152,7 +152,7 @@ def time_kernels(torch, S, rig, steps, warmup):
     def one(s, evs=None):
         if evs:
             evs[0].record()
-        S.svdq_quantize_act(d, s["blob"], s["X"], s["codes"], s["scales"], s["T"] if d.rank else None)
+        S.svdq_quantize_act(d, s["blob"], s["X"], s["codes"], s["scales"], s["T"] if d.rank else None, s["ws"])
         if evs:
             evs[1].record()
         S.svdq_gemm(d, s["blob"], s["codes"], s["scales"], s["T"] if d.rank else None, M, s["Y"], S.OUT_BF16)
@@ -181,12 +181,7 @@ def cpu_baseline(rig, rows_req):
     import w4a4_quantized_gemm_amd as S
     L = S.svdq_blob_layout_of(rig.layer.desc)
     r, K, N = cfg.rank, cfg.K, cfg.N
-    l1t = sec[L.l1t:L.l1t + 2 * r * K].view(np.uint16).reshape(r, K)
-    # L2 (N x r) is stored in 1 KB operand blocks: element (n, t) at
-    # ((n/32)*(r/16) + t/16)*512 + (n%32 + 32*((t%16)/8))*8 + t%8
-    n_i, t_i = np.arange(N)[:, None], np.arange(r)[None, :]
-    off = ((n_i // 32) * (r // 16) + t_i // 16) * 512 + (n_i % 32 + 32 * ((t_i % 16) // 8)) * 8 + t_i % 8
-    l2t = sec[L.l2t:L.l2t + 2 * N * r].view(np.uint16)[off]
+    l1t, l2t = S.blob_factors(rig.layer.desc, sec)
     factors = (O.bf16_bits_to_f64(l1t).T.copy(), O.bf16_bits_to_f64(l2t).T.copy())
     t0 = time.perf_counter()
     prep = O.prepare(rig.W_bits, O.act_absmax(rig.X_bits), alpha=cfg.alpha, rank=r, fmt=cfg.fmt,

@@ -92,7 +92,14 @@ typedef enum svdq_status {
  * and L2 transposed, N x rank) are stored in 1 KB blocks of 32 rows x 16
  * columns in the lane order of a 32x32x16 bf16 MFMA; element (i, t) is at
  *     ((i / 32) * (cols / 16) + t / 16) * 512 + (i % 32 + 32 * ((t % 16) / 8)) * 8 + t % 8
- * (in elements), rows again padded to a multiple of 32. */
+ * (in elements), rows again padded to a multiple of 32.
+ *
+ * L1 transposed (rank x K bf16, the down-projection's operand) is stored in
+ * 1 KB blocks in the lane order of a 16x16x32 bf16 MFMA: per 128-wide K chunk,
+ * 16-row block and 8-wide step j = (k % 32) / 8; element (t, k) is at
+ *     (((k / 128) * (rank / 16) + t / 16) * 4 + (k % 32) / 8) * 512
+ *       + (t % 16 + 16 * ((k % 128) / 32)) * 8 + k % 8
+ * (in elements). */
 typedef enum svdq_format {
   SVDQ_INT4_G64_FP16 = 0,
   SVDQ_FP4_E2M1_G32_E8M0 = 1
@@ -133,8 +140,10 @@ int svdq_version(void);
 size_t svdq_prepared_bytes(const svdq_layer_desc* desc);
 
 /* Device workspace that svdq_linear / svdq_linear_unfused need for M tokens:
- * the packed activation codes (ceil(M/32)*32 x K/2 bytes), the scales and the
- * bf16 down-projection (ceil(M/32)*32 x rank); 0 if arguments are invalid. */
+ * the packed activation codes (ceil(M/32)*32 x K/2 bytes), the scales, the
+ * bf16 down-projection (ceil(M/32)*32 x rank) and, for M <= 16384, room for
+ * the fp32 partial down-projections of a K-split activation pass
+ * (8 x M x rank x 4 bytes); 0 if arguments are invalid. */
 size_t svdq_workspace_bytes(const svdq_layer_desc* desc, int M, int unfused);
 
 /* Byte sizes of svdq_quantize_act's three outputs for M tokens (codes,
@@ -191,10 +200,17 @@ svdq_status svdq_check_blob(const svdq_layer_desc* desc, const void* d_prepared,
  *        NULL when rank == 0).
  * Padding rows of the outputs are left unwritten.
  * X is read from HBM once.  `desc` must be the descriptor the blob was
- * prepared with.  Asynchronous. */
+ * prepared with.  d_workspace (optional, NULL allowed) is a buffer of
+ * ws_bytes >= svdq_workspace_bytes(desc, M, 0) bytes, as svdq_linear takes:
+ * with it, the pass may split K over several workgroups per row block and
+ * add their fp32 partial T in a second kernel, in a fixed order (codes and
+ * scales do not depend on the split; T is the same sum in another fp32
+ * order, and is deterministic for a given device); without it, and with
+ * rank > 0, each row block's T is accumulated by one workgroup.
+ * Asynchronous. */
 svdq_status svdq_quantize_act(const svdq_layer_desc* desc, const void* d_prepared,
                               const void* d_X, int M, void* d_codes, void* d_scales,
-                              void* d_T, void* stream);
+                              void* d_T, void* d_workspace, size_t ws_bytes, void* stream);
 
 /* The fused layer: Y = Q(x_hat) Q(R) + Tb L2b + b, M x N in `out_dtype`.
  * Two kernels: the activation pass above (into d_workspace), then the 4-bit
@@ -232,7 +248,8 @@ svdq_status svdq_linear_unfused(const svdq_layer_desc* desc, const void* d_prepa
  * tests).  All offsets are multiples of 256.
  *   lambda      fp32[K]
  *   inv_lambda  fp32[K]
- *   l1t         bf16[rank][K]    (L1 transposed: row t holds column t of L1)
+ *   l1t         bf16, rank x K   (L1 transposed: row t holds column t of L1;
+ *                                 L1 operand order)
  *   l2t         bf16, N x rank   (L2 transposed: row n holds column n of L2;
  *                                 bf16 block order)
  *   wcodes      u8, N x K/2      (residual codes of output column n as row n,

@@ -62,6 +62,20 @@ def untile_fp4_scales(raw: np.ndarray, rows: int, K: int) -> np.ndarray:
     return raw[off]
 
 
+def untile_l1(raw_u16: np.ndarray, r: int, K: int) -> np.ndarray:
+    """r x K matrix from the L1 operand order (1 KB blocks per 128-wide K
+    chunk, 16-row block and 8-wide step, in 16x16x32 MFMA lane order)."""
+    out = np.empty((r, K), dtype=raw_u16.dtype)
+    blocks = raw_u16.reshape(K // 128, r // 16, 4, 4, 16, 8)   # chunk, t block, step j, kq, t % 16, k % 8
+    for c in range(K // 128):
+        for nb in range(r // 16):
+            for j in range(4):
+                for kq in range(4):
+                    k0 = c * 128 + kq * 32 + j * 8
+                    out[nb * 16:nb * 16 + 16, k0:k0 + 8] = blocks[c, nb, j, kq]
+    return out
+
+
 def blob_sections(layer):
     """Canonical numpy views of a prepared blob.
 
@@ -81,7 +95,7 @@ def blob_sections(layer):
 
     lam32 = sec(L.lambda_, 4 * K).view(np.float32).astype(np.float64)
     inv32 = sec(L.inv_lambda, 4 * K).view(np.float32).astype(np.float64)
-    l1t = sec(L.l1t, 2 * r * K).view(np.uint16).reshape(r, K)
+    l1t = untile_l1(sec(L.l1t, 2 * r * K).view(np.uint16), r, K)
     l2t = untile_bf16(sec(L.l2t, 2 * N * r).view(np.uint16), N, r)
     L1b = O.bf16_bits_to_f64(l1t).T.copy()
     L2b = O.bf16_bits_to_f64(l2t).T.copy()

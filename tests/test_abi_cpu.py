@@ -95,7 +95,7 @@ def test_runtime_validation_before_device():
     dg = _desc(flags=S.F_FACTORS_GIVEN)
     assert lib.svdq_prepare_weights(ctypes.byref(dg), good, good, None, None, None, good, pb, None) == 1
     # quantize_act: T required when rank > 0
-    assert lib.svdq_quantize_act(ctypes.byref(d), good, good, 16, good, good, None, None) == 1
+    assert lib.svdq_quantize_act(ctypes.byref(d), good, good, 16, good, good, None, None, 0, None) == 1
 
 
 def _has_gpu():

@@ -87,21 +87,29 @@ def _check_lambda(sec, X_bits, W_bits, alpha, no_smoothing=False):
     return int((ulps > 0).sum())
 
 
-def _run_act(torch_dev, layer, X, M):
+def _run_act(torch_dev, layer, X, M, with_ws):
+    """The activation pass alone; with the workspace it may split K."""
     import w4a4_quantized_gemm_amd as S
     torch, dev = torch_dev
     cb, sb, tb = S.svdq_act_sizes(layer.desc, M)
     codes = torch.empty(cb, dtype=torch.uint8, device=dev)
     scales = torch.empty(sb, dtype=torch.uint8, device=dev)
     T = torch.empty(max(tb // 2, 1), dtype=torch.bfloat16, device=dev)
-    S.svdq_quantize_act(layer.desc, layer.blob, X, codes, scales, T if layer.desc.rank else None)
+    ws = torch.empty(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev) if with_ws else None
+    S.svdq_quantize_act(layer.desc, layer.blob, X, codes, scales, T if layer.desc.rank else None, ws)
     torch.cuda.synchronize()
     return codes, scales, T
 
 
 def _check_act(torch_dev, layer, X, X_bits, ref_prep, rows=None):
+    for with_ws in (True, False):
+        out = _check_act_once(torch_dev, layer, X, X_bits, ref_prep, rows, with_ws)
+    return out
+
+
+def _check_act_once(torch_dev, layer, X, X_bits, ref_prep, rows, with_ws):
     M, K = X_bits.shape
-    codes, scales, T = _run_act(torch_dev, layer, X, M)
+    codes, scales, T = _run_act(torch_dev, layer, X, M, with_ws)
     q, s, raw, sraw = decode_act(codes, scales, layer.desc.fmt, M, K)
     Xr = X_bits if rows is None else X_bits[rows]
     ref = O.quantize_act(Xr, ref_prep["inv32"], ref_prep["fmt"])

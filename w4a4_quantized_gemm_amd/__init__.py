@@ -81,7 +81,7 @@ def _lib() -> ctypes.CDLL:
             "svdq_act_absmax": ([P, I, I, P, I, P], S),
             "svdq_prepare_weights": ([D, P, P, P, P, P, P, Z, P], S),
             "svdq_check_blob": ([D, P, P], S),
-            "svdq_quantize_act": ([D, P, P, I, P, P, P, P], S),
+            "svdq_quantize_act": ([D, P, P, I, P, P, P, P, Z, P], S),
             "svdq_gemm": ([D, P, P, P, P, I, P, I, P], S),
             "svdq_linear": ([D, P, P, I, P, I, P, Z, P], S),
             "svdq_linear_unfused": ([D, P, P, I, P, I, P, Z, P], S),
@@ -166,10 +166,13 @@ def svdq_check_blob(desc: LayerDesc, prepared, stream=None):
     _check(_lib().svdq_check_blob(ctypes.byref(desc), _ptr(prepared), _stream(stream)), "svdq_check_blob")
 
 
-def svdq_quantize_act(desc: LayerDesc, prepared, X, codes, scales, T=None, stream=None):
+def svdq_quantize_act(desc: LayerDesc, prepared, X, codes, scales, T=None, workspace=None, stream=None):
+    """The activation pass; `workspace` (optional, svdq_workspace_bytes(desc, M) bytes) lets it split K."""
     M = X.shape[0]
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_lib().svdq_quantize_act(ctypes.byref(desc), _ptr(prepared), _ptr(X), M, _ptr(codes),
-                                    _ptr(scales), _ptr(T), _stream(stream)), "svdq_quantize_act")
+                                    _ptr(scales), _ptr(T), _ptr(workspace), ws_bytes, _stream(stream)),
+           "svdq_quantize_act")
 
 
 def svdq_gemm(desc: LayerDesc, prepared, codes, scales, T, M: int, Y, out_dtype: int = OUT_BF16,
@@ -193,6 +196,25 @@ def svdq_linear_unfused(desc: LayerDesc, prepared, X, Y, workspace, out_dtype: i
 
 
 # ----------------------------------------------------------------- convenience
+def blob_factors(desc: LayerDesc, blob_bytes):
+    """The stored bf16 factor bits of a prepared blob (a host uint8 array):
+    L1 transposed (rank x K) and L2 transposed (N x rank), each as uint16,
+    row-major, undoing the blob's operand orders (layouts documented in
+    include/svdq.h)."""
+    import numpy as np
+    L = svdq_blob_layout_of(desc)
+    K, N, r = desc.K, desc.N, desc.rank
+    t = np.arange(r)[:, None]
+    k = np.arange(K)[None, :]
+    off1 = (((k // 128) * (r // 16) + t // 16) * 4 + (k % 32) // 8) * 512 + (t % 16 + 16 * ((k % 128) // 32)) * 8 + k % 8
+    l1t = blob_bytes[L.l1t:L.l1t + 2 * r * K].view(np.uint16)[off1]
+    n = np.arange(N)[:, None]
+    t2 = np.arange(r)[None, :]
+    off2 = ((n // 32) * (r // 16) + t2 // 16) * 512 + (n % 32 + 32 * ((t2 % 16) // 8)) * 8 + t2 % 8
+    l2t = blob_bytes[L.l2t:L.l2t + 2 * N * r].view(np.uint16)[off2]
+    return l1t, l2t
+
+
 class SVDQLinear:
     """A prepared layer held on the GPU: the blob plus its descriptor.
 

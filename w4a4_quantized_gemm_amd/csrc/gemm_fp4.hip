@@ -581,7 +581,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
 
 // Compute units of the current device (cached per device): the persistent
 // kernel launches at most one workgroup per CU.
-static int cu_count() {
+int device_cu_count() {
   static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -598,7 +598,7 @@ hipError_t launch_gemm_fp4(bool slab, int out_dtype, const GemmArgs& g, hipStrea
   // a workgroup walks several tiles only when a tile has at least 3 stages,
   // so that the copies (3 stages ahead) never run more than one tile ahead
   const int stages = (slab ? (g.rank / 16 + 1) / 2 : 0) + g.K / 128;
-  dim3 grid(stages >= 3 ? std::min(tiles, cu_count()) : tiles), block(256);
+  dim3 grid(stages >= 3 ? std::min(tiles, device_cu_count()) : tiles), block(256);
   const bool f32 = out_dtype == SVDQ_OUT_F32;
   const int rs = slab ? (g.rank / 16 + 1) / 2 : 0;
   const bool general = rs > 3 || stages < rs + 3;

@@ -178,12 +178,14 @@ __global__ __launch_bounds__(256) void dgemm_kernel(int M, int N, int K, const d
     }
 }
 
-// l1t[t][j] = bf16(L1[j][t]) from an fp64 K x r matrix
+// bf16(L1[j][t]) from an fp64 K x r matrix, into the down-projection
+// operand order (l1_operand_index)
 __global__ void store_l1t_kernel(const double* __restrict__ L1, int K, int r, uint16_t* __restrict__ l1t) {
   const long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= static_cast<long>(K) * r) return;
-  const long t = idx / K, j = idx % K;
-  l1t[idx] = static_cast<uint16_t>(f64_round_bits(L1[j * r + t], 7, 8));
+  const long j = idx / r;
+  const int t = static_cast<int>(idx % r);
+  l1t[l1_operand_index(t, j, r)] = static_cast<uint16_t>(f64_round_bits(L1[idx], 7, 8));
 }
 
 // l2t = bf16(L2t) from an fp64 N x r matrix, stored in operand-block order
@@ -193,14 +195,19 @@ __global__ void store_l2t_kernel(const double* __restrict__ L2t, long count, int
   l2t[bf16_block_index(idx / r, static_cast<int>(idx % r), r)] = static_cast<uint16_t>(f64_round_bits(L2t[idx], 7, 8));
 }
 
-// Caller-supplied factors: L1 (K x r) -> l1t (r x K, row-major); L2 (r x N)
-// -> l2t (N x r, operand-block order when `block`)
-__global__ void transpose_u16_kernel(const uint16_t* __restrict__ src, int rows, int cols, bool block,
-                                     uint16_t* __restrict__ dst) {
+// Caller-supplied factors: L1 (K x r, row-major) -> l1t in the
+// down-projection operand order
+__global__ void store_given_l1_kernel(const uint16_t* __restrict__ L1, int K, int r, uint16_t* __restrict__ l1t) {
   const long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= static_cast<long>(rows) * cols) return;
-  const long i = idx / cols, j = idx % cols;
-  dst[block ? bf16_block_index(j, static_cast<int>(i), rows) : j * rows + i] = src[idx];
+  if (idx >= static_cast<long>(K) * r) return;
+  l1t[l1_operand_index(static_cast<int>(idx % r), idx / r, r)] = L1[idx];
+}
+
+// Caller-supplied factors: L2 (r x N, row-major) -> l2t (N x r, operand-block order)
+__global__ void store_given_l2_kernel(const uint16_t* __restrict__ L2, int r, int N, uint16_t* __restrict__ l2t) {
+  const long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<long>(r) * N) return;
+  l2t[bf16_block_index(idx % N, static_cast<int>(idx / N), r)] = L2[idx];
 }
 
 // R = W_hat - sum_t L1b[j][t] L2b[t][n], in place, t increasing.
@@ -211,7 +218,7 @@ __global__ void residual_kernel(double* __restrict__ What, const uint16_t* __res
   const long j = idx / N, n = idx % N;
   double s = 0.0;
   for (int t = 0; t < r; t++) {
-    const double a = __uint_as_float(static_cast<uint32_t>(l1t[static_cast<long>(t) * K + j]) << 16);
+    const double a = __uint_as_float(static_cast<uint32_t>(l1t[l1_operand_index(t, j, r)]) << 16);
     const double b = __uint_as_float(static_cast<uint32_t>(l2t[bf16_block_index(n, t, r)]) << 16);
     s = fma(a, b, s);  // the product of two bf16 numbers is exact in fp64
   }
@@ -348,9 +355,9 @@ svdq_status prepare_impl(const svdq_layer_desc& d, const uint16_t* W, const floa
   // low-rank factors
   if (r > 0) {
     if (d.flags & SVDQ_F_FACTORS_GIVEN) {
-      hipLaunchKernelGGL(transpose_u16_kernel, dim3(blocks_for(static_cast<long>(K) * r)), dim3(256), 0, st, L1, K, r, false, l1t);
+      hipLaunchKernelGGL(store_given_l1_kernel, dim3(blocks_for(static_cast<long>(K) * r)), dim3(256), 0, st, L1, K, r, l1t);
       SVDQ_TRY(hipGetLastError());
-      hipLaunchKernelGGL(transpose_u16_kernel, dim3(blocks_for(static_cast<long>(r) * N)), dim3(256), 0, st, L2, r, N, true, l2t);
+      hipLaunchKernelGGL(store_given_l2_kernel, dim3(blocks_for(static_cast<long>(r) * N)), dim3(256), 0, st, L2, r, N, l2t);
       SVDQ_TRY(hipGetLastError());
     } else {
       const int b = r + opt.oversample > (K < N ? K : N) ? (K < N ? K : N) : r + opt.oversample;

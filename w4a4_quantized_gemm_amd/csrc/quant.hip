@@ -6,62 +6,132 @@
 //   per token row and K group: absmax scale and 4-bit codes (eq. (1))
 //   T = bf16(x_hat) L1b on the bf16 MFMA, fp32 accumulation -> bf16
 //
-// Work split: a workgroup owns 16 token rows; its 4 waves take interleaved
-// 128-wide K chunks (wave w: chunks w, w+4, ...).  In a chunk, lane l holds
-// row l % 16 and the 32 consecutive K elements 32 * (l / 16) .. + 31, loaded as
-// four 16-byte vectors.  An INT4 group (64) is the lane pair (l, l ^ 16); an
-// FP4 group (32) is one lane.  The 32 values are also the A operands of four
+// Work split: a workgroup owns 16 token rows and one of `kparts` equal
+// parts of the 128-wide K chunks (the launch splits K so that there are
+// about four workgroups per CU: with one workgroup per 16-row block the M
+// of a layer would leave most of the chip idle); its 4 waves take
+// interleaved chunks of the part.  In a chunk, lane l holds row l % 16 and
+// the 32 consecutive K elements 32 * (l / 16) .. + 31, loaded as four
+// 16-byte vectors.  An INT4 group (64) is the lane pair (l, l ^ 16); an FP4
+// group (32) is one lane.  The 32 values are also the A operands of four
 // 16x16x32 bf16 MFMAs (8 consecutive K per MFMA), whose B operands come from
 // L1 stored transposed (L1t[t][k]), so the k index sets of A and B match.
 // The per-wave partial T tiles are summed across the 4 waves in LDS in a
-// fixed order, so T is deterministic.
+// fixed order; with several K parts each part writes its fp32 partial and
+// t_reduce_kernel adds the parts in order and rounds once, so T is
+// deterministic.
 #include "svdq_device.h"
 #include "svdq_kernels.h"
 
 namespace svdq {
 
+// Clears the sign of E2M1 codes that encode zero (the hardware conversion
+// keeps the sign of a negative value that rounds to zero; the format here
+// encodes every zero as +0): for each nibble, bit 3 survives only if one of
+// bits 0-2 is set (nibble + 7 carries into bit 3 exactly then, and never into
+// the next nibble).
+__device__ __forceinline__ uint32_t e2m1_plus_zero(uint32_t w) {
+  const uint32_t nz = ((w & 0x77777777u) + 0x77777777u) & 0x88888888u;
+  return w & (nz | 0x77777777u);
+}
+
 template <int FMT, bool QUANT, bool DOWN, int RB>
 __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X, int M, int K,
                                                   const float* __restrict__ inv_lam,
-                                                  const uint16_t* __restrict__ l1t,
+                                                  const uint16_t* __restrict__ l1op,
                                                   uint8_t* __restrict__ codes,
                                                   void* __restrict__ scales,
-                                                  uint16_t* __restrict__ Tb) {
+                                                  uint16_t* __restrict__ Tb, int kparts,
+                                                  float* __restrict__ tpart) {
   constexpr int R = RB * 16;
-  __shared__ float red[(DOWN && RB > 0) ? 4 * 16 * R : 1];
+  constexpr bool LR = DOWN && RB > 0;
+  // per wave: the 16 x 128 bf16 X chunk (4 KB, rows of 256 B whose 16-byte
+  // pieces are XOR-swizzled by the row index) and the chunk's 128 inverse
+  // smoothing factors (512 B); after the loop the same memory holds the
+  // cross-wave T reduction
+  constexpr int WSTAGE = 4096 + 512;
+  constexpr int LDS_BYTES = (LR && 256 * R > 4 * WSTAGE) ? 256 * R : 4 * WSTAGE;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_uniform(threadIdx.x >> 6);
   const int row = lane & 15;
   const int kq = lane >> 4;
-  const long grow = static_cast<long>(blockIdx.x) * 16 + row;
+  const int rblk = static_cast<int>(blockIdx.x) / kparts, part = static_cast<int>(blockIdx.x) - rblk * kparts;
+  const long grow = static_cast<long>(rblk) * 16 + row;
   const bool valid = grow < M;
-  const int iters = K >> 7;
+  const int cpp = (K >> 7) / kparts;              // chunks per part (kparts divides K / 128)
+  const int c_end = (part + 1) * cpp;
+  uint8_t* xs = lds + wave * WSTAGE;             // this wave's X chunk
+  const float* ils = reinterpret_cast<const float*>(xs + 4096);
 
-  f32x4 acc[RB > 0 ? RB : 1];
+  f32x4 acc[LR ? RB : 1];
 #pragma unroll
-  for (int nb = 0; nb < (RB > 0 ? RB : 1); nb++) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < (LR ? RB : 1); nb++) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int it = wave; it < iters; it += 4) {
+  // Loads are row-contiguous: load c of a lane takes the 16-byte piece l % 16
+  // of row 4c + l / 16 (four whole 256-byte rows per instruction; rows past
+  // M read row M - 1, whose results are not stored), and lane l < 32 takes
+  // inverse factors 4l .. 4l + 3.  The next chunk of the wave is requested
+  // before the current one is processed.
+  const int lrow = lane >> 4, piece = lane & 15;
+  const u32x4* xsrc[4];
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    const long r = static_cast<long>(rblk) * 16 + 4 * c + lrow;
+    xsrc[c] = reinterpret_cast<const u32x4*>(X + (r < M ? r : static_cast<long>(M) - 1) * K) + piece;
+  }
+  const f32x4* isrc = reinterpret_cast<const f32x4*>(inv_lam) + (lane & 31);
+  int it = part * cpp + wave;
+  u32x4 nx[4] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+  f32x4 ni = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (it < c_end) {
+#pragma unroll
+    for (int c = 0; c < 4; c++) nx[c] = xsrc[c][it * 16];
+    ni = isrc[it * 32];
+  }
+  for (; it < c_end; it += 4) {
     const int kb = it * 128 + kq * 32;
+    // stage the chunk: piece p of row r goes to slot p ^ r of the row, so
+    // that both these writes and the reads below touch 16 distinct 16-byte
+    // bank groups per 16 lanes
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      const int r = 4 * c + lrow;
+      *reinterpret_cast<u32x4*>(xs + r * 256 + ((piece ^ r) << 4)) = nx[c];
+    }
+    if (lane < 32) *reinterpret_cast<f32x4*>(xs + 4096 + lane * 16) = ni;
+    if (it + 4 < c_end) {
+#pragma unroll
+      for (int c = 0; c < 4; c++) nx[c] = xsrc[c][(it + 4) * 16];
+      ni = isrc[(it + 4) * 32];
+    }
+    // L1 operands of the chunk: one contiguous 1 KB block per (t block,
+    // step), requested before the quantization work (for up to 4 t blocks;
+    // wider ranks load them next to their MFMAs)
+    constexpr bool LT_EARLY = LR && RB <= 4;
+    const bf16x8* lp = reinterpret_cast<const bf16x8*>(l1op) + static_cast<long>(it) * RB * 256 + lane;
+    bf16x8 lt[LT_EARLY ? RB : 1][4];
+    if constexpr (LT_EARLY) {
+#pragma unroll
+      for (int nb = 0; nb < RB; nb++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) lt[nb][j] = lp[(nb * 4 + j) * 64];
+    }
+    // lane (row, kq): elements kq * 32 .. + 31 of its row = pieces 4 kq .. 4 kq + 3
     float xh[32];
-    {
-      uint4 raw[4];
-      const uint4* src = reinterpret_cast<const uint4*>(X + grow * K + kb);
 #pragma unroll
-      for (int c = 0; c < 4; c++) raw[c] = valid ? src[c] : make_uint4(0u, 0u, 0u, 0u);
-      const float4* il = reinterpret_cast<const float4*>(inv_lam + kb);
-#pragma unroll
-      for (int c = 0; c < 4; c++) {
-        const float4 i0 = il[2 * c], i1 = il[2 * c + 1];
-        xh[8 * c + 0] = bf16_lo(raw[c].x) * i0.x;
-        xh[8 * c + 1] = bf16_hi(raw[c].x) * i0.y;
-        xh[8 * c + 2] = bf16_lo(raw[c].y) * i0.z;
-        xh[8 * c + 3] = bf16_hi(raw[c].y) * i0.w;
-        xh[8 * c + 4] = bf16_lo(raw[c].z) * i1.x;
-        xh[8 * c + 5] = bf16_hi(raw[c].z) * i1.y;
-        xh[8 * c + 6] = bf16_lo(raw[c].w) * i1.z;
-        xh[8 * c + 7] = bf16_hi(raw[c].w) * i1.w;
-      }
+    for (int c = 0; c < 4; c++) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(xs + row * 256 + (((4 * kq + c) ^ row) << 4));
+      const f32x4 i0 = *reinterpret_cast<const f32x4*>(ils + kq * 32 + 8 * c);
+      const f32x4 i1 = *reinterpret_cast<const f32x4*>(ils + kq * 32 + 8 * c + 4);
+      xh[8 * c + 0] = bf16_lo(v.x) * i0.x;
+      xh[8 * c + 1] = bf16_hi(v.x) * i0.y;
+      xh[8 * c + 2] = bf16_lo(v.y) * i0.z;
+      xh[8 * c + 3] = bf16_hi(v.y) * i0.w;
+      xh[8 * c + 4] = bf16_lo(v.z) * i1.x;
+      xh[8 * c + 5] = bf16_hi(v.z) * i1.y;
+      xh[8 * c + 6] = bf16_lo(v.w) * i1.z;
+      xh[8 * c + 7] = bf16_hi(v.w) * i1.w;
     }
 
     if constexpr (QUANT) {
@@ -85,11 +155,28 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
         if (valid && (kq & 1) == 0)
           reinterpret_cast<uint16_t*>(scales)[grow * (K / 64) + kb / 64] = __half_as_ushort(sh);
       } else {
+        // E2M1 of x / 2^ex, rounded to nearest even by the conversion
+        // instruction (|x / 2^ex| <= 6 by the choice of ex), two codes per
+        // instruction into byte e / 2 % 4 of word e / 8.  Groups whose scale
+        // is below 2^-120 (absmax under ~5e-36, all-zero groups included)
+        // take the exact bit-level rounding instead, so that no denormal
+        // scale or input reaches the conversion.
         const int ex = e8m0_exponent(amax);
+        if (ex >= -120) {
+          const float sc = __builtin_amdgcn_ldexpf(1.0f, ex);
 #pragma unroll
-        for (int e = 0; e < 32; e++) {
-          const float y = __builtin_amdgcn_ldexpf(xh[e], -ex);
-          packed[e >> 3] |= e2m1_code(y) << (4 * (e & 7));
+          for (int w = 0; w < 4; w++) {
+            uint32_t v = 0u;
+            v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, xh[8 * w + 0], xh[8 * w + 1], sc, 0);
+            v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, xh[8 * w + 2], xh[8 * w + 3], sc, 1);
+            v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, xh[8 * w + 4], xh[8 * w + 5], sc, 2);
+            v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, xh[8 * w + 6], xh[8 * w + 7], sc, 3);
+            packed[w] = e2m1_plus_zero(v);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 32; e++)
+            packed[e >> 3] |= e2m1_code(__builtin_amdgcn_ldexpf(xh[e], -ex)) << (4 * (e & 7));
         }
         if (valid) reinterpret_cast<uint8_t*>(scales)[fp4_scale_offset(grow, kb, K)] = static_cast<uint8_t>(ex + 127);
       }
@@ -98,24 +185,34 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
             u32x4{packed[0], packed[1], packed[2], packed[3]};
     }
 
-    if constexpr (DOWN && RB > 0) {
+    if constexpr (LR) {
+      // bf16 of x_hat, rounded to nearest even (v_cvt_pk_bf16_f32)
+      typedef float f32x2 __attribute__((ext_vector_type(2)));
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
       bf16x8 a[4];
 #pragma unroll
       for (int j = 0; j < 4; j++)
 #pragma unroll
-        for (int e = 0; e < 8; e++) a[j][e] = static_cast<__bf16>(xh[8 * j + e]);
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 p2 = __builtin_convertvector(f32x2{xh[8 * j + e], xh[8 * j + e + 1]}, bf16x2);
+          a[j][e] = p2[0];
+          a[j][e + 1] = p2[1];
+        }
 #pragma unroll
-      for (int nb = 0; nb < RB; nb++) {
-        const bf16x8* lp = reinterpret_cast<const bf16x8*>(l1t + static_cast<long>(nb * 16 + row) * K + kb);
+      for (int nb = 0; nb < RB; nb++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], lp[j], acc[nb], 0, 0, 0);
-      }
+        for (int j = 0; j < 4; j++) {
+          if constexpr (LT_EARLY) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], lt[nb][j], acc[nb], 0, 0, 0);
+          else acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], lp[(nb * 4 + j) * 64], acc[nb], 0, 0, 0);
+        }
     }
   }
 
-  if constexpr (DOWN && RB > 0) {
-    // acc[nb][v] is this wave's partial T[4 * kq + v][nb * 16 + (lane & 15)]
+  if constexpr (LR) {
+    // acc[nb][v] is this wave's partial T[4 * kq + v][nb * 16 + (lane & 15)];
+    // the staging memory is reused once every wave has left the loop
+    float* red = reinterpret_cast<float*>(lds);
+    __syncthreads();
 #pragma unroll
     for (int nb = 0; nb < RB; nb++)
 #pragma unroll
@@ -125,19 +222,55 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
       const int rr = idx / R, t = idx % R;
       const float s = ((red[(0 * 16 + rr) * R + t] + red[(1 * 16 + rr) * R + t]) + red[(2 * 16 + rr) * R + t]) +
                       red[(3 * 16 + rr) * R + t];
-      const long gr = static_cast<long>(blockIdx.x) * 16 + rr;
-      if (gr < M) Tb[bf16_block_index(gr, t, R)] = static_cast<uint16_t>(f32_to_bf16_bits(s));
+      const long gr = static_cast<long>(rblk) * 16 + rr;
+      if (gr < M) {
+        if (kparts == 1) Tb[bf16_block_index(gr, t, R)] = static_cast<uint16_t>(f32_to_bf16_bits(s));
+        else tpart[(static_cast<long>(part) * M + gr) * R + t] = s;
+      }
     }
   }
 }
 
+// T = sum over the K parts (in part order) of the fp32 partials, rounded once
+// to bf16 into the block layout; one thread per element of rows < M.
+__global__ __launch_bounds__(256) void t_reduce_kernel(const float* __restrict__ tpart, int kparts, int M, int R,
+                                                       uint16_t* __restrict__ Tb) {
+  const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<long>(M) * R) return;
+  const long row = idx / R;
+  const int t = static_cast<int>(idx - row * R);
+  float s = tpart[idx];
+  for (int p = 1; p < kparts; p++) s += tpart[static_cast<long>(p) * M * R + idx];
+  Tb[bf16_block_index(row, t, R)] = static_cast<uint16_t>(f32_to_bf16_bits(s));
+}
+
+// K parts: the fewest (dividing K / 128, at most kMaxKParts) that give about
+// four workgroups per CU; parts whose chunk count is a multiple of 4 (an even
+// split over the 4 waves) are preferred.  Without a partial-T buffer (or for
+// M above kSplitMaxM, where the workspace holds none) a pass with a
+// down-projection runs in one part.
+static int choose_kparts(int M, int K, bool down, bool have_tpart) {
+  if (down && (!have_tpart || M > kSplitMaxM)) return 1;
+  const int nchunks = K >> 7, nrb = (M + 15) / 16;
+  const long target = 4L * device_cu_count();
+  int best = 1;
+  for (int d = 1; d <= kMaxKParts; d++) {
+    if (nchunks % d) continue;
+    if ((nchunks / d) % 4 != 0 && nchunks % 4 == 0) continue;
+    best = d;
+    if (static_cast<long>(nrb) * d >= target) break;
+  }
+  return best;
+}
+
 template <int FMT, bool QUANT, bool DOWN>
 static hipError_t launch_act_rb(int rb, const ActArgs& a, hipStream_t st) {
-  dim3 grid((a.M + 15) / 16), block(256);
+  const int kparts = choose_kparts(a.M, a.K, DOWN && rb > 0, a.tpart != nullptr);
+  dim3 grid(((a.M + 15) / 16) * kparts), block(256);
 #define SVDQ_ACT_CASE(RBV)                                                                              \
   case RBV:                                                                                           \
     hipLaunchKernelGGL((act_kernel<FMT, QUANT, DOWN, RBV>), grid, block, 0, st, a.X, a.M, a.K, a.inv_lam, \
-                       a.l1t, a.codes, a.scales, a.Tb);                                              \
+                       a.l1t, a.codes, a.scales, a.Tb, kparts, a.tpart);                             \
     break;
   switch (rb) {
     SVDQ_ACT_CASE(0) SVDQ_ACT_CASE(1) SVDQ_ACT_CASE(2) SVDQ_ACT_CASE(3) SVDQ_ACT_CASE(4)
@@ -145,6 +278,11 @@ static hipError_t launch_act_rb(int rb, const ActArgs& a, hipStream_t st) {
     default: return hipErrorInvalidValue;
   }
 #undef SVDQ_ACT_CASE
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !DOWN || rb == 0 || kparts == 1) return e;
+  const long n = static_cast<long>(a.M) * rb * 16;
+  hipLaunchKernelGGL(t_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, a.tpart, kparts,
+                     a.M, rb * 16, a.Tb);
   return hipGetLastError();
 }
 

@@ -98,6 +98,7 @@ svdq_status run_layer(const svdq_layer_desc* desc, const void* prepared, const v
   a.codes = w + A.codes;
   a.scales = w + A.scales;
   a.Tb = reinterpret_cast<uint16_t*>(w + A.tb);
+  a.tpart = reinterpret_cast<float*>(w + A.tpart);
 
   GemmArgs g;
   g.acodes = a.codes;
@@ -172,11 +173,14 @@ svdq_status svdq_check_blob(const svdq_layer_desc* desc, const void* d_prepared,
 }
 
 svdq_status svdq_quantize_act(const svdq_layer_desc* desc, const void* d_prepared, const void* d_X, int M,
-                              void* d_codes, void* d_scales, void* d_T, void* stream) {
+                              void* d_codes, void* d_scales, void* d_T, void* d_workspace, size_t ws_bytes,
+                              void* stream) {
   svdq_status st = validate_runtime(desc, d_prepared, d_X, M);
   if (st != SVDQ_OK) return st;
   if (!d_codes || !d_scales || (desc->rank > 0 && !d_T)) return SVDQ_ERR_INVALID_ARGUMENT;
   if (!aligned16(d_codes) || !aligned16(d_scales) || (d_T && !aligned16(d_T))) return SVDQ_ERR_MISALIGNED;
+  if (d_workspace && !aligned16(d_workspace)) return SVDQ_ERR_MISALIGNED;
+  if (d_workspace && ws_bytes < svdq_workspace_bytes(desc, M, 0)) return SVDQ_ERR_BUFFER_TOO_SMALL;
   if ((st = check_device()) != SVDQ_OK) return st;
   const BlobPtrs bp = blob_ptrs(*desc, d_prepared);
   ActArgs a;
@@ -189,6 +193,9 @@ svdq_status svdq_quantize_act(const svdq_layer_desc* desc, const void* d_prepare
   a.codes = static_cast<uint8_t*>(d_codes);
   a.scales = d_scales;
   a.Tb = static_cast<uint16_t*>(d_T);
+  // the workspace's partial-T section (if any) lets the pass split K
+  a.tpart = d_workspace ? reinterpret_cast<float*>(static_cast<uint8_t*>(d_workspace) + act_layout(*desc, M).tpart)
+                        : nullptr;
   return from_hip(launch_act(desc->fmt, true, desc->rank > 0, a, as_stream(stream)));
 }
 

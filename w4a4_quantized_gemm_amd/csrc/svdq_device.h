@@ -88,6 +88,16 @@ __device__ __forceinline__ long bf16_block_index(long i, int t, int cols) {
   return (((i >> 5) * (cols >> 4) + (t >> 4)) << 9) + (((i & 31) + (((t >> 3) & 1) << 5)) << 3) + (t & 7);
 }
 
+// Element offset of L1t[t][k] (t < R, R % 16 == 0, k < K) in the
+// down-projection operand order: per 128-wide K chunk c = k / 128, column
+// block nb = t / 16 and step j = (k % 32) / 8, a 1 KB block (blocks ordered
+// by c, then nb, then j) whose 16-byte slot of lane (t % 16) + 16 ((k % 128) / 32)
+// holds k - k % 8 .. + 7, the B operand of a 16x16x32 bf16 MFMA.
+__host__ __device__ __forceinline__ long l1_operand_index(int t, long k, int R) {
+  return ((((k >> 7) * (R >> 4) + (t >> 4)) * 4 + ((k >> 3) & 3)) << 9) + (((t & 15) + (((k >> 5) & 3) << 4)) << 3) +
+         (k & 7);
+}
+
 // Workgroup (or persistent turn) id b -> output tile (tm, tn).  The hardware
 // deals workgroups round-robin to the 8 XCDs, so b % 8 is the XCD; each XCD
 // gets a contiguous range of tiles, walked 4 tile rows at a time so that the

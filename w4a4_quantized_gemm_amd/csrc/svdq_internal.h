@@ -11,11 +11,16 @@
 namespace svdq {
 
 constexpr uint32_t kMagic = 0x51445653u;  // "SVDQ" little-endian
-constexpr uint32_t kVersion = 1u;
+constexpr uint32_t kVersion = 2u;
 constexpr uint32_t kKnownFlags = SVDQ_F_NO_SMOOTHING | SVDQ_F_FACTORS_GIVEN | SVDQ_F_HAS_BIAS;
 constexpr int kMaxRank = 128;
 constexpr int kMaxDim = 65536;
 constexpr int kMaxM = 1 << 22;
+// The activation pass splits K into at most kMaxKParts parts, and only for
+// M <= kSplitMaxM (larger M fills the chip with row blocks alone); the
+// workspace holds the fp32 partial T of the parts.
+constexpr int kMaxKParts = 8;
+constexpr int kSplitMaxM = 16384;
 
 // 256-byte header at offset 0 of every prepared blob.
 struct BlobHeader {
@@ -44,7 +49,7 @@ svdq_blob_layout layout_of(const svdq_layer_desc& d);
 
 // Activation-side buffers inside a workspace: packed codes, scales, Tb.
 struct ActLayout {
-  uint64_t codes, scales, tb, total;
+  uint64_t codes, scales, tb, tpart, total;
   uint64_t codes_bytes, scales_bytes, tb_bytes;
 };
 ActLayout act_layout(const svdq_layer_desc& d, int M);

@@ -6,6 +6,7 @@
 #include <cstdint>
 
 #include "svdq.h"
+#include "svdq_internal.h"
 
 namespace svdq {
 
@@ -17,7 +18,11 @@ struct ActArgs {
   uint8_t* codes;         // M x K/2
   void* scales;           // M x K/g (fp16 bits or E8M0 bytes)
   uint16_t* Tb;           // M x rank bf16
+  float* tpart;           // kMaxKParts x M x rank fp32 partial T (workspace), or null: K is not split
 };
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
 
 // quant: write codes + scales; down: write Tb.
 hipError_t launch_act(int fmt, bool quant, bool down, const ActArgs& a, hipStream_t st);

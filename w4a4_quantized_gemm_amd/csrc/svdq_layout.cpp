@@ -70,6 +70,9 @@ ActLayout act_layout(const svdq_layer_desc& d, int M) {
   off = align256(off + A.scales_bytes);
   A.tb = off;
   off = align256(off + A.tb_bytes);
+  // fp32 partial T of the K parts of the activation pass (at most kMaxKParts)
+  A.tpart = off;
+  off = align256(off + (m <= kSplitMaxM ? uint64_t(kMaxKParts) * m * uint64_t(d.rank) * 4 : 0));
   A.total = off;
   return A;
 }

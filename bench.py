@@ -350,6 +350,7 @@ def main():
             calibration_copy(torch)
         rig = Rig(cfg, torch, S, WL, to_tensor)
         ms, _ = time_fused(torch, S, rig, args.steps, args.warmup)
+        time_fused(torch, S, rig, args.steps, args.warmup, unfused=True)
         tq, tg = time_kernels(torch, S, rig, args.steps, args.warmup)
         print(json.dumps({"workload": cfg.name, "ms_per_step": ms, "quant_ms": statistics.mean(tq),
                           "gemm_ms": statistics.mean(tg)}), flush=True)

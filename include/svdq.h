@@ -86,7 +86,11 @@ typedef enum svdq_status {
  * 2-byte slot of lane (i % 32) + 32 ((k / 32) % 2) holds the scales of the
  * stage's two 64-wide steps:
  *     ((i / 32) * (K / 128) + k / 128) * 128 + (i % 32 + 32 * ((k / 32) % 2)) * 2 + (k / 64) % 2
- * INT4 scales (fp16) are row-major [rows][K / 64].
+ * INT4 activation scales (fp16, one per row and 64-wide group) are blocked
+ * the same way: for each 32-row block and 128-wide K stage, 128 bytes; the
+ * 4-byte word of row i % 32 holds the stage's two groups:
+ *     ((i / 32) * (K / 128) + k / 128) * 128 + (i % 32) * 4 + ((k / 64) % 2) * 2
+ * INT4 weight scales are row-major [N][K / 64].
  *
  * bf16 low-rank matrices with `cols` columns (cols % 16 == 0: T, M x rank,
  * and L2 transposed, N x rank) are stored in 1 KB blocks of 32 rows x 16
@@ -193,8 +197,9 @@ svdq_status svdq_check_blob(const svdq_layer_desc* desc, const void* d_prepared,
  *   x_hat = fp32(X * inv_lambda)                         (X: M x K bf16)
  *   per token row and K group: scale and 4-bit codes of x_hat in desc->fmt
  *     -> d_codes: ceil(M/32)*32 x K/2 bytes in MFMA operand-block order;
- *        d_scales: M x K/64 fp16, row-major (INT4), or ceil(M/32)*32 x K/32
- *        E8M0 bytes in the FP4 scale block order
+ *        d_scales: ceil(M/32)*32 x K/64 fp16 in the INT4 activation scale
+ *        block order, or ceil(M/32)*32 x K/32 E8M0 bytes in the FP4 scale
+ *        block order
  *   T = bf16(x_hat) L1b accumulated in fp32, rounded once to bf16
  *     -> d_T: ceil(M/32)*32 x rank bf16 in the bf16 block order (may be
  *        NULL when rank == 0).

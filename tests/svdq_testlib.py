@@ -138,13 +138,23 @@ def oracle_prep_from_blob(sections, W_bits, fmt: str, bias_bits=None, cols=None)
                 w_scales=w_scales, bias=bias)
 
 
+def untile_int4_act_scales(raw_u16: np.ndarray, M: int, K: int) -> np.ndarray:
+    """M x K/64 fp16 bits from the INT4 activation scale blocks: per 32-row
+    block and 128-wide stage, 32 words of the stage's two groups."""
+    i = np.arange(M)[:, None]
+    g = np.arange(K // 64)[None, :]
+    off = ((i // 32) * (K // 128) + g // 2) * 64 + (i % 32) * 2 + g % 2
+    assert off.max() < raw_u16.size, "scale buffer smaller than the block layout needs"
+    return raw_u16[off]
+
+
 def decode_act(codes_t, scales_t, fmt_id: int, M: int, K: int):
     """Packed activation codes / scales from the GPU -> (codes M x K, scale values)."""
     from w4a4_quantized_gemm_amd import INT4
     raw = untile_codes(to_np(codes_t), M, K)
     nib = O.unpack_nibbles(raw)
     if fmt_id == INT4:
-        sc = to_np(scales_t).view(np.uint16).reshape(M, K // 64)
+        sc = untile_int4_act_scales(to_np(scales_t).view(np.uint16), M, K)
         return O.nibble_to_int4(nib), O.fp16_bits_to_f64(sc), raw, sc
     sc = untile_fp4_scales(to_np(scales_t), M, K)
     return nib, sc.astype(np.int32) - 127, raw, sc

@@ -134,10 +134,9 @@ def test_blob_layout_and_sizes():
             c, s, t = S.svdq_act_sizes(d, 4608)
             assert (c, s, t) == (4608 * 1536, 4608 * (3072 // g) * sb, 4608 * 32 * 2)
             assert S.svdq_workspace_bytes(d, 4608) >= c + s + t
-            # codes, T and FP4 scales are padded to whole 32-row operand blocks
+            # codes, scales and T of both formats are padded to whole 32-row blocks
             c, s, t = S.svdq_act_sizes(d, 100)
-            srows = 100 if fmt == S.INT4 else 128
-            assert (c, s, t) == (128 * 1536, srows * (3072 // g) * sb, 128 * 32 * 2)
+            assert (c, s, t) == (128 * 1536, 128 * (3072 // g) * sb, 128 * 32 * 2)
     # compression: the 4-bit blob is ~0.27-0.28x the bf16 weight
     d = _desc(K=3072, N=12288, r=32, fmt=S.FP4)
     ratio = S.svdq_prepared_bytes(d) / (3072 * 12288 * 2)

@@ -171,6 +171,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     u32x4 a[A_CH], b[B_CH];
     uint32_t sa, sb;
   };
+  // INT4 scale word of this thread's row (t < BM: A row t, else B column
+  // t - BM) for stage st: sc_base[sc_off + st * sc_step].  Activation scales
+  // are in 32-row blocks (word (row, st) at ((row / 32) * SW + st) * 32 +
+  // row % 32), weight scales row-major.
+  const bool sc_is_a = t < BM;
+  const long sc_row = sc_is_a ? min(m0 + t, static_cast<long>(M - 1)) : min(n0 + (t - BM), static_cast<long>(N - 1));
+  const uint32_t* __restrict__ sc_base = sc_is_a ? ascales : wscales;
+  const long sc_off = sc_is_a ? (sc_row >> 5) * SW * 32 + (sc_row & 31) : sc_row * SW;
+  const int sc_step = sc_is_a ? 32 : 1;
   const long KBLK = K / 64;                       // 1 KB blocks per 32-row block
   const long last_ablk = (M + 31) / 32 - 1, last_bblk = N / 32 - 1;
   auto load_stage = [&](Regs& r, int st) __attribute__((always_inline)) {
@@ -188,9 +197,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     }
     if constexpr (I4) {
       // 128 threads per operand
-      const bool is_a = t < BM;
-      const long row = is_a ? min(m0 + t, static_cast<long>(M - 1)) : min(n0 + (t - BM), static_cast<long>(N - 1));
-      r.sa = (is_a ? ascales : wscales)[row * SW + st];
+      r.sa = sc_base[sc_off + st * sc_step];
     } else {
       r.sa = ascales[min(m0 + t, static_cast<long>(M - 1)) * SW + st];
       r.sb = wscales[min(n0 + t, static_cast<long>(N - 1)) * SW + st];

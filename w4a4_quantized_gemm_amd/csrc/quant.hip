@@ -57,39 +57,66 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
   const int row = lane & 15;
   const int kq = lane >> 4;
   const int rblk = static_cast<int>(blockIdx.x) / kparts, part = static_cast<int>(blockIdx.x) - rblk * kparts;
-  const long grow = static_cast<long>(rblk) * 16 + row;
-  const bool valid = grow < M;
+  const long row0 = static_cast<long>(rblk) * 16;
+  const bool valid = row0 + row < M;
+  const int nrows = static_cast<int>(min(static_cast<long>(M) - row0, 16L));
   const int cpp = (K >> 7) / kparts;              // chunks per part (kparts divides K / 128)
   const int c_end = (part + 1) * cpp;
   uint8_t* xs = lds + wave * WSTAGE;             // this wave's X chunk
   const float* ils = reinterpret_cast<const float*>(xs + 4096);
+  const uint32_t rowb = static_cast<uint32_t>(K) * 2;
+
+  // Buffer resources of the workgroup's rows: X (rows past M read as 0; their
+  // results are not stored), codes and scales; L1 and the inverse factors.
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(X) + row0 * K, 0, static_cast<int>(static_cast<uint32_t>(nrows) * rowb), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ir =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(inv_lam), 0, K * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(l1op), 0, static_cast<int>(static_cast<uint32_t>(K) * R * 2), 0x00020000);
+  // the 16 rows lie in one 32-row block of the code and FP4 scale layouts
+  const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+      codes + (row0 >> 5) * (K >> 6) * 1024, 0, (K >> 6) * 1024, 0x00020000);
+  // (both scale layouts give each 32-row block and 128-wide stage 128 bytes)
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<uint8_t*>(scales) + (row0 >> 5) * (K >> 7) * 128, 0, (K >> 7) * 128, 0x00020000);
+  const int r32 = static_cast<int>(row0 & 31) + row;   // the lane's row within its 32-row block
+  // store offsets past the end of cr / sr: such stores write nothing
+  const uint32_t c_oob = static_cast<uint32_t>(K >> 6) * 1024;
+  const uint32_t s_oob = static_cast<uint32_t>(K >> 7) * 128;
 
   f32x4 acc[LR ? RB : 1];
 #pragma unroll
   for (int nb = 0; nb < (LR ? RB : 1); nb++) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Loads are row-contiguous: load c of a lane takes the 16-byte piece l % 16
-  // of row 4c + l / 16 (four whole 256-byte rows per instruction; rows past
-  // M read row M - 1, whose results are not stored), and lane l < 32 takes
-  // inverse factors 4l .. 4l + 3.  The next chunk of the wave is requested
-  // before the current one is processed.
+  // of row 4c + l / 16 (four whole 256-byte rows per instruction), and lane
+  // l < 32 takes inverse factors 4l .. 4l + 3.  The next chunk of the wave is
+  // requested before the current one is processed.
   const int lrow = lane >> 4, piece = lane & 15;
-  const u32x4* xsrc[4];
+  const uint32_t xoff = static_cast<uint32_t>(lrow) * rowb + piece * 16;
+  const uint32_t ioff = static_cast<uint32_t>(lane & 31) * 16;
+  // Two chunks of each wave are in flight while it processes a third: chunk
+  // it + 8 is requested into the registers chunk it arrived in.
+  const int it0 = part * cpp + wave;
+  const u32x4 z4 = u32x4{0u, 0u, 0u, 0u};
+  u32x4 xa[4] = {z4, z4, z4, z4}, xb[4] = {z4, z4, z4, z4};
+  u32x4 ia = z4, ib = z4;
+  // Every fetch is issued, also past the part's last chunk: there its offset
+  // lies past the buffer's end, so it reads nothing and returns zeros.  The
+  // compiler then counts the same number of loads in flight on every path and
+  // its waits for the L1 operands never include a prefetch.
+  const int x_oob = nrows * static_cast<int>(rowb), i_oob = K * 4;
+  auto fetch = [&](int c0, u32x4 (&x)[4], u32x4& iv) __attribute__((always_inline)) {
+    const bool ok = c0 < c_end;
 #pragma unroll
-  for (int c = 0; c < 4; c++) {
-    const long r = static_cast<long>(rblk) * 16 + 4 * c + lrow;
-    xsrc[c] = reinterpret_cast<const u32x4*>(X + (r < M ? r : static_cast<long>(M) - 1) * K) + piece;
-  }
-  const f32x4* isrc = reinterpret_cast<const f32x4*>(inv_lam) + (lane & 31);
-  int it = part * cpp + wave;
-  u32x4 nx[4] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
-  f32x4 ni = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (it < c_end) {
-#pragma unroll
-    for (int c = 0; c < 4; c++) nx[c] = xsrc[c][it * 16];
-    ni = isrc[it * 32];
-  }
-  for (; it < c_end; it += 4) {
+    for (int c = 0; c < 4; c++)
+      x[c] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, ok ? static_cast<int>(4 * c * rowb + c0 * 256) : x_oob, 0);
+    iv = __builtin_amdgcn_raw_buffer_load_b128(ir, ioff, ok ? c0 * 512 : i_oob, 0);
+  };
+  fetch(it0, xa, ia);
+  fetch(it0 + 4, xb, ib);
+  auto body = [&](int it, u32x4 (&x)[4], u32x4& iv) __attribute__((always_inline)) {
     const int kb = it * 128 + kq * 32;
     // stage the chunk: piece p of row r goes to slot p ^ r of the row, so
     // that both these writes and the reads below touch 16 distinct 16-byte
@@ -97,26 +124,31 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
 #pragma unroll
     for (int c = 0; c < 4; c++) {
       const int r = 4 * c + lrow;
-      *reinterpret_cast<u32x4*>(xs + r * 256 + ((piece ^ r) << 4)) = nx[c];
+      *reinterpret_cast<u32x4*>(xs + r * 256 + ((piece ^ r) << 4)) = x[c];
     }
-    if (lane < 32) *reinterpret_cast<f32x4*>(xs + 4096 + lane * 16) = ni;
-    if (it + 4 < c_end) {
-#pragma unroll
-      for (int c = 0; c < 4; c++) nx[c] = xsrc[c][(it + 4) * 16];
-      ni = isrc[(it + 4) * 32];
-    }
+    if (lane < 32) *reinterpret_cast<u32x4*>(xs + 4096 + lane * 16) = iv;
     // L1 operands of the chunk: one contiguous 1 KB block per (t block,
-    // step), requested before the quantization work (for up to 4 t blocks;
-    // wider ranks load them next to their MFMAs)
-    constexpr bool LT_EARLY = LR && RB <= 4;
-    const bf16x8* lp = reinterpret_cast<const bf16x8*>(l1op) + static_cast<long>(it) * RB * 256 + lane;
+    // step).  For FP4 and up to 4 t blocks they are requested before the
+    // quantization work; the INT4 quantizer needs the registers (holding
+    // them would cost a wave per SIMD), so INT4 and wider ranks load them
+    // next to their MFMAs.
+    constexpr bool LT_EARLY = LR && RB <= 4 && FMT == SVDQ_FP4_E2M1_G32_E8M0;
+    const int lbase = it * RB * 4096;
+    auto lt_load = [&](int nb, int j) __attribute__((always_inline)) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(lr, static_cast<uint32_t>(lane) * 16, lbase + (nb * 4 + j) * 1024, 0);
+      return __builtin_bit_cast(bf16x8, v);
+    };
     bf16x8 lt[LT_EARLY ? RB : 1][4];
     if constexpr (LT_EARLY) {
 #pragma unroll
       for (int nb = 0; nb < RB; nb++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) lt[nb][j] = lp[(nb * 4 + j) * 64];
+        for (int j = 0; j < 4; j++) lt[nb][j] = lt_load(nb, j);
     }
+    // The X prefetch is issued after the L1 loads: vector memory counters
+    // complete in issue order, so waiting for the L1 operands does not wait
+    // for the prefetch.
+    fetch(it + 8, x, iv);
     // lane (row, kq): elements kq * 32 .. + 31 of its row = pieces 4 kq .. 4 kq + 3
     float xh[32];
 #pragma unroll
@@ -134,6 +166,22 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
       xh[8 * c + 7] = bf16_hi(v.w) * i1.w;
     }
 
+    // bf16 of x_hat, rounded to nearest even (v_cvt_pk_bf16_f32): the A
+    // operands of the down-projection, formed before the quantizer reuses xh
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x8 a[LR ? 4 : 1];
+    if constexpr (LR) {
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 p2 = __builtin_convertvector(f32x2{xh[8 * j + e], xh[8 * j + e + 1]}, bf16x2);
+          a[j][e] = p2[0];
+          a[j][e + 1] = p2[1];
+        }
+    }
+
     if constexpr (QUANT) {
       float amax = 0.f;
 #pragma unroll
@@ -143,17 +191,54 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
         amax = fmaxf(amax, __shfl_xor(amax, 16));
         const __half sh = __float2half_rn(amax / 7.0f);
         const float s = __half2float(sh);
-        if (s > 0.f) {
-          const float r = 1.0f / s;
+        const float r = s > 0.f ? 1.0f / s : 0.f;
+        // t = x / s + 8 with one rounding (fma with the rounded reciprocal)
+        // is within 2^-20 of the exact value, so rint(t) = RNE(x / s) + 8
+        // unless t lies within 2^-18 of a half-integer; a lane with such a
+        // value redoes its 32 quotients exactly.  (s = 0 gives r = 0, t = 8.)
+        float dmax = 0.f;
 #pragma unroll
-          for (int e = 0; e < 32; e++) {
-            float q = rne_quotient(xh[e], s, r);
-            q = fminf(fmaxf(q, -7.f), 7.f);
-            packed[e >> 3] |= (static_cast<uint32_t>(static_cast<int>(q)) & 0xFu) << (4 * (e & 7));
+        for (int e = 0; e < 32; e++) {
+          const float t = __builtin_fmaf(xh[e], r, 8.0f);
+          const float q = __builtin_rintf(t);
+          dmax = fmaxf(dmax, __builtin_fabsf(t - q));
+          xh[e] = q;
+        }
+        if (dmax > 0.5f - 0x1p-18f) {
+          // xh holds rint(t) now: recompute x from the staged chunk
+#pragma unroll
+          for (int c = 0; c < 4; c++) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(xs + row * 256 + (((4 * kq + c) ^ row) << 4));
+            const f32x4 i0 = *reinterpret_cast<const f32x4*>(ils + kq * 32 + 8 * c);
+            const f32x4 i1 = *reinterpret_cast<const f32x4*>(ils + kq * 32 + 8 * c + 4);
+            const float xv[8] = {bf16_lo(v.x) * i0.x, bf16_hi(v.x) * i0.y, bf16_lo(v.y) * i0.z, bf16_hi(v.y) * i0.w,
+                                 bf16_lo(v.z) * i1.x, bf16_hi(v.z) * i1.y, bf16_lo(v.w) * i1.z, bf16_hi(v.w) * i1.w};
+#pragma unroll
+            for (int e = 0; e < 8; e++) xh[8 * c + e] = rne_quotient(xv[e], s, r) + 8.0f;
           }
         }
-        if (valid && (kq & 1) == 0)
-          reinterpret_cast<uint16_t*>(scales)[grow * (K / 64) + kb / 64] = __half_as_ushort(sh);
+        // codes: nibble = clamp(q, -7, 7) & 15 = clamp(q + 8, 1, 15) ^ 8; bytes
+        // of four values, then nibble pairs (byte j | byte j+1 << 4) at bytes
+        // 0 and 2 of each, gathered by one byte permute
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+          uint32_t d[2];
+#pragma unroll
+          for (int h = 0; h < 2; h++) {
+            uint32_t v = 0u;
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+              v = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(xh[8 * w + 4 * h + e], 1.0f, 15.0f), e, v);
+            d[h] = v | (v >> 4);
+          }
+          packed[w] = __builtin_amdgcn_perm(d[1], d[0], 0x06040200u) ^ 0x88888888u;
+        }
+        // INT4 scale block order within the 32-row block (the 4-byte word of
+        // row r32 holds the stage's two groups); rows past M and the odd lane
+        // of each pair store past the buffer's end: no write
+        __builtin_amdgcn_raw_buffer_store_b16(
+            __half_as_ushort(sh), sr,
+            valid && (kq & 1) == 0 ? static_cast<uint32_t>((kb >> 7) * 128 + r32 * 4 + ((kb >> 6) & 1) * 2) : s_oob, 0, 0);
       } else {
         // E2M1 of x / 2^ex, rounded to nearest even by the conversion
         // instruction (|x / 2^ex| <= 6 by the choice of ex), two codes per
@@ -178,35 +263,33 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
           for (int e = 0; e < 32; e++)
             packed[e >> 3] |= e2m1_code(__builtin_amdgcn_ldexpf(xh[e], -ex)) << (4 * (e & 7));
         }
-        if (valid) reinterpret_cast<uint8_t*>(scales)[fp4_scale_offset(grow, kb, K)] = static_cast<uint8_t>(ex + 127);
+        // FP4 scale block order within the 32-row block (fp4_scale_offset)
+        __builtin_amdgcn_raw_buffer_store_b8(
+            static_cast<uint8_t>(ex + 127), sr,
+            valid ? static_cast<uint32_t>((kb >> 7) * 128 + (r32 + 32 * ((kb >> 5) & 1)) * 2 + ((kb >> 6) & 1)) : s_oob, 0, 0);
       }
-      if (valid)
-        *reinterpret_cast<u32x4*>(codes + code_chunk_offset(grow, kb, K)) =
-            u32x4{packed[0], packed[1], packed[2], packed[3]};
+      // code block order within the 32-row block (code_chunk_offset)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          u32x4{packed[0], packed[1], packed[2], packed[3]}, cr,
+          valid ? static_cast<uint32_t>((kb >> 6) * 1024 + (r32 + 32 * ((kb >> 5) & 1)) * 16) : c_oob, 0, 0);
     }
 
     if constexpr (LR) {
-      // bf16 of x_hat, rounded to nearest even (v_cvt_pk_bf16_f32)
-      typedef float f32x2 __attribute__((ext_vector_type(2)));
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      bf16x8 a[4];
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 p2 = __builtin_convertvector(f32x2{xh[8 * j + e], xh[8 * j + e + 1]}, bf16x2);
-          a[j][e] = p2[0];
-          a[j][e + 1] = p2[1];
-        }
 #pragma unroll
       for (int nb = 0; nb < RB; nb++)
 #pragma unroll
         for (int j = 0; j < 4; j++) {
           if constexpr (LT_EARLY) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], lt[nb][j], acc[nb], 0, 0, 0);
-          else acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], lp[(nb * 4 + j) * 64], acc[nb], 0, 0, 0);
+          else acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], lt_load(nb, j), acc[nb], 0, 0, 0);
         }
     }
+  };
+  int it = it0;
+  for (; it + 4 < c_end; it += 8) {
+    body(it, xa, ia);
+    body(it + 4, xb, ib);
   }
+  if (it < c_end) body(it, xa, ia);
 
   if constexpr (LR) {
     // acc[nb][v] is this wave's partial T[4 * kq + v][nb * 16 + (lane & 15)];
@@ -232,33 +315,53 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
 }
 
 // T = sum over the K parts (in part order) of the fp32 partials, rounded once
-// to bf16 into the block layout; one thread per element of rows < M.
+// to bf16 into the block layout; one thread per 4 consecutive elements of a
+// row < M (R % 16 == 0, so the 4 are contiguous in the block layout too).
 __global__ __launch_bounds__(256) void t_reduce_kernel(const float* __restrict__ tpart, int kparts, int M, int R,
                                                        uint16_t* __restrict__ Tb) {
-  const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= static_cast<long>(M) * R) return;
+  const long idx = (static_cast<long>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  const long n = static_cast<long>(M) * R;
+  if (idx >= n) return;
   const long row = idx / R;
   const int t = static_cast<int>(idx - row * R);
-  float s = tpart[idx];
-  for (int p = 1; p < kparts; p++) s += tpart[static_cast<long>(p) * M * R + idx];
-  Tb[bf16_block_index(row, t, R)] = static_cast<uint16_t>(f32_to_bf16_bits(s));
+  // all loads first (kparts <= kMaxKParts), then the sum in part order
+  f32x4 v[kMaxKParts];
+#pragma unroll
+  for (int p = 0; p < kMaxKParts; p++)
+    if (p < kparts) v[p] = *reinterpret_cast<const f32x4*>(tpart + p * n + idx);
+  f32x4 s = v[0];
+#pragma unroll
+  for (int p = 1; p < kMaxKParts; p++)
+    if (p < kparts) s += v[p];
+  const uint32_t lo = f32_to_bf16_bits(s.x) | (f32_to_bf16_bits(s.y) << 16);
+  const uint32_t hi = f32_to_bf16_bits(s.z) | (f32_to_bf16_bits(s.w) << 16);
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  *reinterpret_cast<u32x2*>(Tb + bf16_block_index(row, t, R)) = u32x2{lo, hi};
 }
 
-// K parts: the fewest (dividing K / 128, at most kMaxKParts) that give about
-// four workgroups per CU; parts whose chunk count is a multiple of 4 (an even
-// split over the 4 waves) are preferred.  Without a partial-T buffer (or for
-// M above kSplitMaxM, where the workspace holds none) a pass with a
-// down-projection runs in one part.
+// K parts: balances the bytes each CU streams.  With d parts, the
+// ceil(row blocks * d / CUs) workgroups of the busiest CU each carry 1/d of a
+// row block's K; the waves of a workgroup share its chunks, so a chunk count
+// that is not a multiple of 4 leaves some idle; each part adds an fp32
+// partial T write and read (about 2% each).  d divides K / 128 and is at most
+// kMaxKParts.  Without a partial-T buffer (or for M above kSplitMaxM, where
+// the workspace holds none) a pass with a down-projection runs in one part.
 static int choose_kparts(int M, int K, bool down, bool have_tpart) {
   if (down && (!have_tpart || M > kSplitMaxM)) return 1;
   const int nchunks = K >> 7, nrb = (M + 15) / 16;
-  const long target = 4L * device_cu_count();
+  const long cus = device_cu_count();
   int best = 1;
+  double best_cost = 0.0;
   for (int d = 1; d <= kMaxKParts; d++) {
     if (nchunks % d) continue;
-    if ((nchunks / d) % 4 != 0 && nchunks % 4 == 0) continue;
-    best = d;
-    if (static_cast<long>(nrb) * d >= target) break;
+    const int cpp = nchunks / d;
+    const double per_cu = static_cast<double>((static_cast<long>(nrb) * d + cus - 1) / cus) / d;
+    const double waves = static_cast<double>((cpp + 3) / 4) / (cpp / 4.0);
+    const double cost = per_cu * waves * (1.0 + (down ? 0.02 * (d - 1) : 0.0));
+    if (d == 1 || cost < best_cost) {
+      best = d;
+      best_cost = cost;
+    }
   }
   return best;
 }
@@ -280,8 +383,8 @@ static hipError_t launch_act_rb(int rb, const ActArgs& a, hipStream_t st) {
 #undef SVDQ_ACT_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !DOWN || rb == 0 || kparts == 1) return e;
-  const long n = static_cast<long>(a.M) * rb * 16;
-  hipLaunchKernelGGL(t_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, a.tpart, kparts,
+  const long n4 = static_cast<long>(a.M) * rb * 4;   // groups of 4 elements
+  hipLaunchKernelGGL(t_reduce_kernel, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, st, a.tpart, kparts,
                      a.M, rb * 16, a.Tb);
   return hipGetLastError();
 }

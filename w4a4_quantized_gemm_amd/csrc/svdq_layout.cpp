@@ -59,9 +59,8 @@ ActLayout act_layout(const svdq_layer_desc& d, int M) {
   const uint64_t m = M, K = d.K;
   const uint64_t mp = ((m + 31) / 32) * 32;         // rows padded to whole 32-row blocks
   A.codes_bytes = mp * (K / 2);
-  // FP4 scales and T are stored in operand-block order too; INT4 scales are
-  // row-major [M][K/64]
-  A.scales_bytes = (d.fmt == SVDQ_FP4_E2M1_G32_E8M0 ? mp : m) * (K / group_of(d.fmt)) * scale_bytes_of(d.fmt);
+  // scales and T are stored in 32-row blocks too
+  A.scales_bytes = mp * (K / group_of(d.fmt)) * scale_bytes_of(d.fmt);
   A.tb_bytes = mp * uint64_t(d.rank) * 2;
   uint64_t off = 0;
   A.codes = off;

@@ -12,10 +12,16 @@
 // Group 64, fp16 scales: the packed nibbles of each K stage are moved to
 // LDS; on the way from LDS to the registers each nibble is widened to a byte
 // holding 16 * q (shifted into the high half of the byte, so the sign comes
-// for free); two 32x32x32 i8 MFMAs give 256 * P_g exactly in int32 and the
-// group is dequantized into the fp32 accumulators with s_x * s_w / 256.  The
-// MFMAs of the next output tile are issued before the dequantization of the
-// current one, so the matrix core and the VALU overlap.
+// for free); two 32x32x32 i8 MFMAs give 256 * P_g exactly in int32, a
+// 32x32x8 f16 MFMA with one nonzero K slot gives the tile's scale products
+// s_x[i] s_w[j] (exact in fp32, in the accumulator layout), and the group is
+// dequantized with one convert and one fma per accumulator.  The
+// accumulators carry 256 x the result (the slab is scaled up to match and
+// the epilogue scales down; powers of two, so every rounding is unchanged).
+// The dequantization is VALU work (about 3 instructions per accumulator per
+// group against 1/16 cycle of i8 MFMA), which bounds this variant well below
+// the i8 MFMA peak.  The MFMAs of the next output tile are issued before the
+// dequantization of the current one, so the matrix core and the VALU overlap.
 //
 // Tiling: 4 waves per workgroup in a 2 x 2 grid, 128 x 128 per workgroup,
 // 32 x 32 MFMA tiles.  A K stage is 128 wide (two 64-wide MFMA steps); the
@@ -39,6 +45,8 @@ namespace svdq {
 namespace {
 
 constexpr int BKB = 64;          // code bytes per row per stage (128 K values)
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t lo_nib_bytes(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
 __device__ __forceinline__ uint32_t hi_nib_bytes(uint32_t w) { return w & 0xF0F0F0F0u; }
@@ -159,6 +167,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         for (int j = 0; j < CB; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[j], acc[i][j], 0, 0, 0);
       }
     }
+    if constexpr (I4) {
+      // the INT4 groups accumulate 256 x their value (codes widened to 16 q);
+      // the slab is scaled to match and the epilogue divides by 256 (powers
+      // of two: every rounding is the same as without the factor)
+#pragma unroll
+      for (int i = 0; i < RB; i++)
+#pragma unroll
+        for (int j = 0; j < CB; j++)
+#pragma unroll
+          for (int v = 0; v < 16; v++) acc[i][j][v] *= 256.0f;
+    }
   }
 
   // ---- global -> registers -> LDS.  A stage of the A (B) tile is BM / 16
@@ -215,11 +234,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       *reinterpret_cast<u32x4*>(&sB[buf][q * 16]) = r.b[i];
     }
     if constexpr (I4) {
-      const float mul = t < BM ? 1.0f : 1.0f / 256.0f;
+      // fp16 bits of the two groups' scales, as the f16 MFMA operands take them
       uint32_t(*ss)[BM] = t < BM ? sSA[buf] : sSB[buf];
       const int idx = t < BM ? t : t - BM;
-      ss[0][idx] = __float_as_uint(__half2float(__ushort_as_half(static_cast<unsigned short>(r.sa & 0xFFFFu))) * mul);
-      ss[1][idx] = __float_as_uint(__half2float(__ushort_as_half(static_cast<unsigned short>(r.sa >> 16))) * mul);
+      ss[0][idx] = r.sa & 0xFFFFu;
+      ss[1][idx] = r.sa >> 16;
     } else {
       sSA[buf][0][t] = r.sa;
       sSB[buf][0][t] = r.sb;
@@ -260,14 +279,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 
       if constexpr (I4) {
         i32x4 a0[RB], a1[RB], b0[CB], b1[CB];
-        float sw[CB];
+        // scale operands of the f16 MFMA that forms s_x[i] s_w[j] for a
+        // 32 x 32 tile: only K slot 0 (lanes 0-31, first element) is nonzero
+        // (every lane reads its word; lanes 32-63 mask it to zero, which
+        // keeps the reads unconditional)
+        f16x4 fa[RB], fb[CB];
 #pragma unroll
         for (int cb = 0; cb < CB; cb++) {
           b0[cb] = i32x4{(int)lo_nib_bytes(bv[cb].x), (int)hi_nib_bytes(bv[cb].x), (int)lo_nib_bytes(bv[cb].y),
                          (int)hi_nib_bytes(bv[cb].y)};
           b1[cb] = i32x4{(int)lo_nib_bytes(bv[cb].z), (int)hi_nib_bytes(bv[cb].z), (int)lo_nib_bytes(bv[cb].w),
                          (int)hi_nib_bytes(bv[cb].w)};
-          sw[cb] = __uint_as_float(sSB[buf][j][wcol0 + cb * 32 + l32]);
+          const uint32_t w = sSB[buf][j][wcol0 + cb * 32 + l32] & (lh ? 0u : 0xFFFFu);
+          fb[cb] = __builtin_bit_cast(f16x4, u32x2{w, 0u});
         }
 #pragma unroll
         for (int rb = 0; rb < RB; rb++) {
@@ -275,34 +299,37 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
                          (int)hi_nib_bytes(av[rb].y)};
           a1[rb] = i32x4{(int)lo_nib_bytes(av[rb].z), (int)hi_nib_bytes(av[rb].z), (int)lo_nib_bytes(av[rb].w),
                          (int)hi_nib_bytes(av[rb].w)};
+          const uint32_t w = sSA[buf][j][wrow0 + rb * 32 + l32] & (lh ? 0u : 0xFFFFu);
+          fa[rb] = __builtin_bit_cast(f16x4, u32x2{w, 0u});
         }
         // software pipeline over the wave's output tiles: the MFMAs of tile
-        // u + 1 are in flight while tile u is dequantized
+        // u + 1 (the group's 256 P_g in int32 and the scale products
+        // s_x s_w, exact in fp32) are in flight while tile u is dequantized
         constexpr int NT = RB * CB;
         i32x16 p[2];
-        auto mma = [&](int u, i32x16& dst) __attribute__((always_inline)) {
+        f32x16 sp[2];
+        auto mma = [&](int u, i32x16& dst, f32x16& sdst) __attribute__((always_inline)) {
           const int rb = u / CB, cb = u % CB;
           i32x16 z16;
+          f32x16 zf;
 #pragma unroll
-          for (int v = 0; v < 16; v++) z16[v] = 0;
+          for (int v = 0; v < 16; v++) {
+            z16[v] = 0;
+            zf[v] = 0.f;
+          }
           dst = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[rb], b0[cb], z16, 0, 0, 0);
           dst = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[rb], b1[cb], dst, 0, 0, 0);
+          sdst = __builtin_amdgcn_mfma_f32_32x32x8f16(fa[rb], fb[cb], zf, 0, 0, 0);
         };
-        mma(0, p[0]);
-        f32x4 sx[4];
+        mma(0, p[0], sp[0]);
 #pragma unroll
         for (int u = 0; u < NT; u++) {
           const int rb = u / CB, cb = u % CB;
-          if (u + 1 < NT) mma(u + 1, p[(u + 1) & 1]);
-          if (cb == 0) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; q4++)
-              sx[q4] = *reinterpret_cast<const f32x4*>(&sSA[buf][j][wrow0 + rb * 32 + 8 * q4 + 4 * lh]);
-          }
+          if (u + 1 < NT) mma(u + 1, p[(u + 1) & 1], sp[(u + 1) & 1]);
           const i32x16& pp = p[u & 1];
+          const f32x16& ss = sp[u & 1];
 #pragma unroll
-          for (int v = 0; v < 16; v++)
-            acc[rb][cb][v] = __builtin_fmaf(static_cast<float>(pp[v]), sx[v >> 2][v & 3] * sw[cb], acc[rb][cb][v]);
+          for (int v = 0; v < 16; v++) acc[rb][cb][v] = __builtin_fmaf(static_cast<float>(pp[v]), ss[v], acc[rb][cb][v]);
         }
       } else {
         i32x8 a[RB], b[CB];
@@ -357,7 +384,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         for (int v = 0; v < 16; v++) {
           const int row = 8 * (v >> 2) + 4 * lh + (v & 3);
           const int off = row * ROWB + (cb * 32 + l32) * OB;
-          const float y = acc[rb][cb][v] + bv[cb];
+          const float y = (I4 ? acc[rb][cb][v] * (1.0f / 256.0f) : acc[rb][cb][v]) + bv[cb];
           if constexpr (OUT == SVDQ_OUT_F32) *reinterpret_cast<float*>(stage + off) = y;
           else *reinterpret_cast<uint16_t*>(stage + off) = static_cast<uint16_t>(f32_to_bf16_bits(y));
         }

@@ -222,18 +222,19 @@ def _cpu_model():
 
 
 def load_traffic(workload, src_hash):
-    """HBM traffic of the GEMM kernel from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel sources."""
+    """HBM traffic per launch of the GEMM kernel and of the activation pass
+    from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel sources: (gemm_bytes, act_bytes), None where unknown."""
     path = os.path.join(ROOT, "profiles", f"gemm_{workload}_hbm_counters.json")
     if not os.path.exists(path):
-        return None
+        return None, None
     try:
         d = json.load(open(path))
     except (OSError, ValueError):
-        return None
+        return None, None
     if d.get("kernel_source_hash") != src_hash:
-        return None
-    return d.get("traffic_bytes_per_launch")
+        return None, None
+    return d.get("traffic_bytes_per_launch"), d.get("act_traffic_bytes_per_launch")
 
 
 COPY_BYTES = 1 << 30          # the calibration copy moves this many bytes each way
@@ -283,10 +284,16 @@ def summarize_counters(fetch_dir, write_dir, cfg, src_hash):
                         for c in ("FETCH_SIZE", "WRITE_SIZE")] +
                        [f"python3 bench.py --summarize-counters gpurun_out/pmc_FETCH_SIZE_{cfg.name} "
                         f"gpurun_out/pmc_WRITE_SIZE_{cfg.name} --workload {cfg.name}"],
-           "note": "FETCH_SIZE / WRITE_SIZE per dispatch of the GEMM kernel, each scaled by the ratio of "
-                   "the calibration copy's known bytes (torch copy of copy_bytes, one read and one write) "
-                   "to what the same counter read for that copy"}
+           "note": "FETCH_SIZE / WRITE_SIZE per dispatch of the GEMM kernel and of the activation pass "
+                   "(act_kernel + t_reduce_kernel), each scaled by the ratio of the calibration copy's known "
+                   "bytes (torch copy of copy_bytes, one read and one write) to what the same counter read "
+                   "for that copy"}
     total = 0.0
+    act_total = 0.0
+    # the fused path's activation pass: act_kernel with quantization and
+    # down-projection, then the partial-T reduction
+    is_act = lambda k: k.startswith("void svdq::act_kernel<") and ", true, true," in k
+    is_red = lambda k: k.startswith("svdq::t_reduce_kernel")
     for name, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         rows = read(d, counter)
         g = pick(rows, is_gemm)
@@ -299,7 +306,15 @@ def summarize_counters(fetch_dir, write_dir, cfg, src_hash):
         out[name] = {"counter": counter, "gemm_kib_per_dispatch": gemm_kib, "dispatches": len(g),
                      "copy_kib": copy_kib, "scale": factor, "gemm_bytes_per_launch": gemm_kib * 1024.0 * factor}
         total += gemm_kib * 1024.0 * factor
+        a, r = pick(rows, is_act), pick(rows, is_red)
+        if a:
+            ab = statistics.mean(a) * 1024.0 * factor
+            rb = statistics.mean(r) * 1024.0 * factor if r else 0.0
+            out[name].update({"act_kib_per_dispatch": statistics.mean(a), "act_bytes_per_launch": ab,
+                              "t_reduce_bytes_per_launch": rb})
+            act_total += ab + rb
     out["traffic_bytes_per_launch"] = total
+    out["act_traffic_bytes_per_launch"] = act_total
     path = os.path.join(ROOT, "profiles", f"gemm_{cfg.name}_hbm_counters.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
@@ -364,7 +379,7 @@ def main():
     gemm_tops = A["gemm_ops"] / (r["tg_ms"] / 1e3) / 1e12
     q_gbs = A["q_bytes"] / (r["tq_ms"] / 1e3) / 1e9
     src_hash = kernel_source_hash()
-    traffic = load_traffic(cfg.name, src_hash)
+    traffic, act_traffic = load_traffic(cfg.name, src_hash)
     line = {
         "metric": "W4A4+low-rank linear effective TOPS & % MFMA peak; fused vs unfused speedup",
         "value": tops,
@@ -387,7 +402,8 @@ def main():
                                 "gemm_kernel (INT4 on the i8 MFMA GEMM") + f" + rank-{cfg.rank} bf16 slab + bias)",
                      "avg_us": r["tg_ms"] * 1e3},
         "roofline_quant": {"bound": "hbm", "achieved": q_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                           "frac": q_gbs / PEAK_HBM_GBS, "kernel": "act_kernel (smooth + quantize + down-proj)",
+                           "frac": q_gbs / PEAK_HBM_GBS, "traffic": act_traffic,
+                           "kernel": "act_kernel (smooth + quantize + down-proj) + t_reduce_kernel",
                            "avg_us": r["tq_ms"] * 1e3, "bytes": A["q_bytes"]},
         "us_per_layer": r["ms_fused"] * 1e3,
         "us_per_layer_unfused": r["ms_unfused"] * 1e3,

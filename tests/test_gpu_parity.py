@@ -200,6 +200,7 @@ SMALL = [
     (129, 512, 448, 128, False, O.INT4),
     (64, 1024, 128, 32, True, O.INT4),
     (257, 640, 576, 64, False, O.FP4),
+    (16400, 256, 64, 16, False, O.FP4),    # M above the K-split limit: one part per row block
 ]
 
 
@@ -247,7 +248,8 @@ def test_factors_given_and_no_smoothing(torch_dev):
 
 def test_quantizer_edge_values(torch_dev):
     """Zero rows, exact ties of x/s, tiny values with subnormal fp16 scales,
-    E2M1 midpoints and large magnitudes, in both formats."""
+    E2M1 midpoints, large magnitudes, E8M0 exponents near -127 and bf16
+    subnormal inputs, in both formats."""
     import w4a4_quantized_gemm_amd as S
     torch, dev = torch_dev
     _say("case: quantizer edge values")
@@ -262,6 +264,9 @@ def test_quantizer_edge_values(torch_dev):
     x[4] = rng.standard_normal(K) * 3e3                   # large values
     x[5, :32] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 4)   # E2M1 midpoints (A = 6: e = 0)
     x[6] = -x[5]
+    x[7] = rng.standard_normal(K) * 2.0 ** -125           # E8M0 exponents near -127 (exact FP4 path)
+    x[8] = rng.standard_normal(K) * 2.0 ** -118           # around the -120 switch of the FP4 conversion
+    x[9] = (np.arange(K) % 7 - 3.0) * 2.0 ** -131         # bf16 subnormals
     X_bits = O.bf16_bits_of(O.to_bf16(x).astype(np.float32))
     W_bits = O.bf16_bits_of(O.to_bf16(rng.standard_normal((K, N)) * 0.05).astype(np.float32))
     X = np_bits_to_bf16_tensor(X_bits, dev)

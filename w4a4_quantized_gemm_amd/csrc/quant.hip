@@ -324,15 +324,18 @@ __global__ __launch_bounds__(256) void t_reduce_kernel(const float* __restrict__
   if (idx >= n) return;
   const long row = idx / R;
   const int t = static_cast<int>(idx - row * R);
-  // all loads first (kparts <= kMaxKParts), then the sum in part order
+  // all loads first, unconditionally (parts past kparts lie past the buffer
+  // resource's end and read as zeros), then the sum in part order
+  const __amdgpu_buffer_rsrc_t tr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(tpart), 0, static_cast<int>(static_cast<uint32_t>(kparts) * static_cast<uint32_t>(n) * 4), 0x00020000);
   f32x4 v[kMaxKParts];
 #pragma unroll
   for (int p = 0; p < kMaxKParts; p++)
-    if (p < kparts) v[p] = *reinterpret_cast<const f32x4*>(tpart + p * n + idx);
+    v[p] = __builtin_bit_cast(
+        f32x4, __builtin_amdgcn_raw_buffer_load_b128(tr, static_cast<uint32_t>(idx) * 4, static_cast<int>(p * n * 4), 0));
   f32x4 s = v[0];
 #pragma unroll
-  for (int p = 1; p < kMaxKParts; p++)
-    if (p < kparts) s += v[p];
+  for (int p = 1; p < kMaxKParts; p++) s += v[p];
   const uint32_t lo = f32_to_bf16_bits(s.x) | (f32_to_bf16_bits(s.y) << 16);
   const uint32_t hi = f32_to_bf16_bits(s.z) | (f32_to_bf16_bits(s.w) << 16);
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

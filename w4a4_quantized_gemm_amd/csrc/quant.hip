@@ -349,10 +349,15 @@ __global__ __launch_bounds__(256) void t_reduce_kernel(const float* __restrict__
 // partial T write and read (about 2% each).  d divides K / 128 and is at most
 // kMaxKParts.  Without a partial-T buffer (or for M above kSplitMaxM, where
 // the workspace holds none) a pass with a down-projection runs in one part.
-static int choose_kparts(int M, int K, bool down, bool have_tpart) {
+// The FP4 pass (light per-element work) over short rows (K <= 4096) with at
+// most two row blocks per CU also runs unsplit: there the reduction launch
+// costs more than the split gains (measured, 4608 x 3072 FP4: 11.6 us in one
+// part against 10.1 us split plus a 4.7 us reduction).
+static int choose_kparts(int M, int K, bool down, bool have_tpart, bool fp4) {
   if (down && (!have_tpart || M > kSplitMaxM)) return 1;
   const int nchunks = K >> 7, nrb = (M + 15) / 16;
   const long cus = device_cu_count();
+  if (down && fp4 && K <= 4096 && nrb <= 2 * cus) return 1;
   int best = 1;
   double best_cost = 0.0;
   for (int d = 1; d <= kMaxKParts; d++) {
@@ -371,7 +376,7 @@ static int choose_kparts(int M, int K, bool down, bool have_tpart) {
 
 template <int FMT, bool QUANT, bool DOWN>
 static hipError_t launch_act_rb(int rb, const ActArgs& a, hipStream_t st) {
-  const int kparts = choose_kparts(a.M, a.K, DOWN && rb > 0, a.tpart != nullptr);
+  const int kparts = choose_kparts(a.M, a.K, DOWN && rb > 0, a.tpart != nullptr, FMT == SVDQ_FP4_E2M1_G32_E8M0);
   dim3 grid(((a.M + 15) / 16) * kparts), block(256);
 #define SVDQ_ACT_CASE(RBV)                                                                              \
   case RBV:                                                                                           \

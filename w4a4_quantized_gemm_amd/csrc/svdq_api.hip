@@ -100,7 +100,7 @@ svdq_status run_layer(const svdq_layer_desc* desc, const void* prepared, const v
   a.Tb = reinterpret_cast<uint16_t*>(w + A.tb);
   a.tpart = reinterpret_cast<float*>(w + A.tpart);
 
-  GemmArgs g;
+  GemmArgs g{};
   g.acodes = a.codes;
   g.ascales = a.scales;
   g.wcodes = bp.wcodes;
@@ -208,7 +208,7 @@ svdq_status svdq_gemm(const svdq_layer_desc* desc, const void* d_prepared, const
   if (!aligned16(d_scales) || !aligned16(d_Y) || (d_T && !aligned16(d_T))) return SVDQ_ERR_MISALIGNED;
   if ((st = check_device()) != SVDQ_OK) return st;
   const BlobPtrs bp = blob_ptrs(*desc, d_prepared);
-  GemmArgs g;
+  GemmArgs g{};
   g.acodes = static_cast<const uint8_t*>(d_codes);
   g.ascales = d_scales;
   g.wcodes = bp.wcodes;

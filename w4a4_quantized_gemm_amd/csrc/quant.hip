@@ -128,11 +128,12 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
     }
     if (lane < 32) *reinterpret_cast<u32x4*>(xs + 4096 + lane * 16) = iv;
     // L1 operands of the chunk: one contiguous 1 KB block per (t block,
-    // step).  For FP4 and up to 4 t blocks they are requested before the
-    // quantization work; the INT4 quantizer needs the registers (holding
-    // them would cost a wave per SIMD), so INT4 and wider ranks load them
-    // next to their MFMAs.
-    constexpr bool LT_EARLY = LR && RB <= 4 && FMT == SVDQ_FP4_E2M1_G32_E8M0;
+    // step), requested before the X prefetch (for up to 4 t blocks; wider
+    // ranks load them next to their MFMAs).  The INT4 quantizer needs many
+    // registers, so for INT4 the down-projection's MFMAs run before the
+    // quantization and the L1 operands are dead by then.
+    constexpr bool LT_EARLY = LR && RB <= 4;
+    constexpr bool MFMA_FIRST = FMT == SVDQ_INT4_G64_FP16;
     const int lbase = it * RB * 4096;
     auto lt_load = [&](int nb, int j) __attribute__((always_inline)) {
       const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(lr, static_cast<uint32_t>(lane) * 16, lbase + (nb * 4 + j) * 1024, 0);
@@ -181,6 +182,19 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
           a[j][e + 1] = p2[1];
         }
     }
+
+    auto down = [&]() __attribute__((always_inline)) {
+      if constexpr (LR) {
+#pragma unroll
+        for (int nb = 0; nb < RB; nb++)
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            if constexpr (LT_EARLY) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], lt[nb][j], acc[nb], 0, 0, 0);
+            else acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], lt_load(nb, j), acc[nb], 0, 0, 0);
+          }
+      }
+    };
+    if constexpr (MFMA_FIRST) down();
 
     if constexpr (QUANT) {
       float amax = 0.f;
@@ -274,15 +288,7 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
           valid ? static_cast<uint32_t>((kb >> 6) * 1024 + (r32 + 32 * ((kb >> 5) & 1)) * 16) : c_oob, 0, 0);
     }
 
-    if constexpr (LR) {
-#pragma unroll
-      for (int nb = 0; nb < RB; nb++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          if constexpr (LT_EARLY) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], lt[nb][j], acc[nb], 0, 0, 0);
-          else acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], lt_load(nb, j), acc[nb], 0, 0, 0);
-        }
-    }
+    if constexpr (!MFMA_FIRST) down();
   };
   int it = it0;
   for (; it + 4 < c_end; it += 8) {

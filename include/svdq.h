@@ -64,20 +64,28 @@ typedef enum svdq_status {
  *    one fp16 scale per 64 consecutive K elements (the quantization handbook's
  *    "one scale per 64 elements"), s = fp16(max|v| / 7), codes
  *    clamp(round_half_even(v / s)) of the exact quotient; s = 0 -> codes 0.
- *    Codes are two's-complement nibbles.
+ *    Eight codes per 32-bit little-endian word (codes k .. k + 7, k % 8 ==
+ *    0): code j of the word is the byte c = (q < 0) << 7 | |q| (the FP8
+ *    E4M3 bits of q * 2^-9; zero is +0, c = 0); codes 0-3 occupy bits 7 and
+ *    0-2 of bytes 0-3, codes 4-7 the same positions rotated left by 4 bits:
+ *        word = C0123 | rotl32(C4567, 4)
+ *    so word & 0x87878787 and rotr32(word, 4) & 0x87878787 are the E4M3
+ *    bytes of codes 0-3 and 4-7.  The words sit where the block order below
+ *    puts the bytes of codes k .. k + 7.
  *  SVDQ_FP4_E2M1_G32_E8M0: 4-bit float codes (sign, 2 exponent bits, 1
  *    mantissa bit; q_max = 6 as the walkthrough states for 4-bit floats), one
  *    power-of-two scale 2^e per 32 K elements stored as an E8M0 byte e + 127,
  *    e the smallest integer with max|v| <= 6 * 2^e (clamped to [-127, 127];
  *    an all-zero group has e = -127); codes round to nearest, ties to the
- *    even code, and a value that rounds to zero is encoded +0.
- * Two codes per byte; the even-K element is in the low nibble.
+ *    even code, and a value that rounds to zero is encoded +0.  Two codes
+ *    per byte; the even-K element is in the low nibble.
  *
  * Code matrices (activation codes, M rows; weight codes, N rows; K codes
  * per row) are stored in MFMA operand-block order: 1 KB blocks, each holding
  * the codes of 32 rows x 64 consecutive K values in the order the 64 lanes
  * of a 32x32x64 MFMA read them.  The byte holding codes (k, k + 1), k even,
- * of row i is at
+ * of row i (for INT4: byte (k % 8) / 2 of the word that holds the eight
+ * codes from k - k % 8 on) is at
  *     ((i / 32) * (K / 64) + k / 64) * 1024 + (i % 32 + 32 * ((k % 64) / 32)) * 16 + (k % 32) / 2
  * Rows are padded to a multiple of 32; the padding bytes are unspecified.
  *

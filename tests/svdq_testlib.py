@@ -36,6 +36,41 @@ def untile_codes(raw: np.ndarray, rows: int, K: int) -> np.ndarray:
     return raw[off]
 
 
+def int4_words_to_q(raw: np.ndarray) -> np.ndarray:
+    """INT4 codes from code bytes in K order (rows x K/2, as untile_codes
+    returns them) -> rows x K int8, per the word format of include/svdq.h:
+    each little-endian 32-bit word holds codes k .. k+7; code j < 4 is byte
+    j of (word & 0x87878787), code j >= 4 byte j-4 of (rotr(word, 4) &
+    0x87878787); a byte is sign (bit 7) and magnitude (bits 0-2).  A
+    negative zero (byte 0x80) is rejected: zero must be encoded +0."""
+    raw = np.asarray(raw, dtype=np.uint8)
+    rows, half = raw.shape
+    b = raw.reshape(rows, half // 4, 4).astype(np.uint64)
+    w = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16) | (b[..., 3] << 24)
+    lo = w & 0x87878787
+    hi = ((w >> 4) | (w << 28)) & 0xFFFFFFFF & 0x87878787
+    c = np.empty((rows, half // 4, 8), dtype=np.int64)
+    for j in range(4):
+        c[..., j] = (lo >> (8 * j)) & 0xFF
+        c[..., 4 + j] = (hi >> (8 * j)) & 0xFF
+    assert not np.any(c == 0x80), "INT4 zero encoded with the sign bit set"
+    q = (c & 7) * np.where(c & 0x80, -1, 1)
+    return q.reshape(rows, 2 * half).astype(np.int8)
+
+
+def q_to_int4_words(q: np.ndarray) -> np.ndarray:
+    """Inverse of int4_words_to_q: rows x K integer codes in [-7, 7] -> rows x
+    K/2 code bytes in K order."""
+    q = np.asarray(q, dtype=np.int64)
+    rows, K = q.shape
+    assert np.all(np.abs(q) <= 7)
+    c = (np.where(q < 0, 0x80, 0) | np.abs(q)).astype(np.uint64).reshape(rows, K // 8, 8)
+    lo = c[..., 0] | (c[..., 1] << 8) | (c[..., 2] << 16) | (c[..., 3] << 24)
+    hi = c[..., 4] | (c[..., 5] << 8) | (c[..., 6] << 16) | (c[..., 7] << 24)
+    w = (lo | (((hi << 4) | (hi >> 28)) & 0xFFFFFFFF)).astype(np.uint32)
+    return w.view(np.uint8).reshape(rows, K // 2)
+
+
 def untile_bf16(raw_u16: np.ndarray, rows: int, cols: int) -> np.ndarray:
     """bf16 matrix (as uint16) stored in the operand-block order of
     include/svdq.h -> row-major [rows][cols].  Element (i, t) sits at
@@ -100,13 +135,14 @@ def blob_sections(layer):
     L1b = O.bf16_bits_to_f64(l1t).T.copy()
     L2b = O.bf16_bits_to_f64(l2t).T.copy()
     raw_codes = untile_codes(sec(L.wcodes, N * K // 2), N, K)
-    nib = O.unpack_nibbles(raw_codes)                       # N x K
     if d.fmt == INT4:
-        codes = O.nibble_to_int4(nib).T.copy()
+        q = int4_words_to_q(raw_codes)                       # N x K
+        codes = q.T.copy()
+        raw_codes = O.pack_nibbles(O.int4_nibble(q))         # the oracle's byte format
         raw_scales = sec(L.wscales, 2 * (K // g) * N).view(np.uint16).reshape(N, K // g).T
         scales = O.fp16_bits_to_f64(raw_scales)
     else:
-        codes = nib.T.copy()
+        codes = O.unpack_nibbles(raw_codes).T.copy()
         raw_scales = untile_fp4_scales(sec(L.wscales, (K // g) * N), N, K).T
         scales = raw_scales.astype(np.int32) - 127
     bias = None
@@ -149,12 +185,13 @@ def untile_int4_act_scales(raw_u16: np.ndarray, M: int, K: int) -> np.ndarray:
 
 
 def decode_act(codes_t, scales_t, fmt_id: int, M: int, K: int):
-    """Packed activation codes / scales from the GPU -> (codes M x K, scale values)."""
+    """Packed activation codes / scales from the GPU -> (codes M x K, scale
+    values, codes packed in the oracle's byte format, raw scale bits)."""
     from w4a4_quantized_gemm_amd import INT4
     raw = untile_codes(to_np(codes_t), M, K)
-    nib = O.unpack_nibbles(raw)
     if fmt_id == INT4:
+        q = int4_words_to_q(raw)
         sc = untile_int4_act_scales(to_np(scales_t).view(np.uint16), M, K)
-        return O.nibble_to_int4(nib), O.fp16_bits_to_f64(sc), raw, sc
+        return q, O.fp16_bits_to_f64(sc), O.pack_nibbles(O.int4_nibble(q)), sc
     sc = untile_fp4_scales(to_np(scales_t), M, K)
-    return nib, sc.astype(np.int32) - 127, raw, sc
+    return O.unpack_nibbles(raw), sc.astype(np.int32) - 127, raw, sc

@@ -143,6 +143,27 @@ def test_blob_layout_and_sizes():
     assert 0.26 < ratio < 0.30
 
 
+def test_int4_code_word_format():
+    """The INT4 word layout of include/svdq.h on a worked example and a round
+    trip: codes 1..7, -7 -> low bytes 01 02 03 04 and high bytes 05 06 07 87
+    rotated left by 4 -> 0x74736259."""
+    from svdq_testlib import int4_words_to_q, q_to_int4_words
+    q = np.array([[1, 2, 3, 4, 5, 6, 7, -7]])
+    raw = q_to_int4_words(q)
+    assert raw.tolist() == [[0x59, 0x62, 0x73, 0x74]]
+    assert int4_words_to_q(raw).tolist() == q.tolist()
+    # the E4M3 operand bytes: word & 0x87878787 and rotr(word, 4) & 0x87878787
+    w = 0x74736259
+    assert w & 0x87878787 == 0x04030201
+    assert (((w >> 4) | (w << 28)) & 0xFFFFFFFF) & 0x87878787 == 0x87070605
+    rng = np.random.default_rng(3)
+    q = rng.integers(-7, 8, size=(5, 128))
+    assert np.array_equal(int4_words_to_q(q_to_int4_words(q)), q)
+    # a negative zero is not a valid code
+    with pytest.raises(AssertionError):
+        int4_words_to_q(np.array([[0x80, 0, 0, 0]], dtype=np.uint8))
+
+
 JACOBI_MAIN = r"""
 #include <cstdio>
 #include <vector>

@@ -9,19 +9,20 @@
 //                                              (eq. (2) per group)
 //   Y[i, n]    = round(acc[i, n] + b[n])
 //
-// Group 64, fp16 scales: the packed nibbles of each K stage are moved to
-// LDS; on the way from LDS to the registers each nibble is widened to a byte
-// holding 16 * q (shifted into the high half of the byte, so the sign comes
-// for free); two 32x32x32 i8 MFMAs give 256 * P_g exactly in int32, a
-// 32x32x8 f16 MFMA with one nonzero K slot gives the tile's scale products
-// s_x[i] s_w[j] (exact in fp32, in the accumulator layout), and the group is
-// dequantized with one convert and one fma per accumulator.  The
-// accumulators carry 256 x the result (the slab is scaled up to match and
-// the epilogue scales down; powers of two, so every rounding is unchanged).
-// The dequantization is VALU work (about 3 instructions per accumulator per
-// group against 1/16 cycle of i8 MFMA), which bounds this variant well below
-// the i8 MFMA peak.  The MFMAs of the next output tile are issued before the
-// dequantization of the current one, so the matrix core and the VALU overlap.
+// Group 64, fp16 scales: the packed codes of each K stage are moved to LDS
+// as they are stored.  An INT4 code is kept as the E4M3 bits of q * 2^-9
+// (sign-magnitude: |q| <= 7 is a subnormal), two per byte, so that on the
+// way from LDS to the registers one AND (codes 0-3 of a word) or one rotate
+// and AND (codes 4-7) per 4 codes yields the 8-bit float operands.  One
+// block-scaled 32x32x64 MFMA with E4M3 operands and both block scales 2^9
+// then gives the group's P_g = sum_k q_x q_w exactly in fp32, a 32x32x8 f16
+// MFMA with one nonzero K slot gives the tile's scale products s_x[i]
+// s_w[j] (exact in fp32, in the accumulator layout), and the group is
+// dequantized with one fma per accumulator.  That fma (16 per 32 x 32 tile
+// and group) is VALU work, which bounds this variant below the 8-bit MFMA
+// peak.  The MFMAs of the next output tile are issued before the
+// dequantization of the current one, so the matrix core and the VALU
+// overlap.
 //
 // Tiling: 4 waves per workgroup in a 2 x 2 grid, 128 x 128 per workgroup,
 // 32 x 32 MFMA tiles.  A K stage is 128 wide (two 64-wide MFMA steps); the
@@ -44,12 +45,21 @@ namespace svdq {
 
 namespace {
 
-constexpr int BKB = 64;          // code bytes per row per stage (128 K values)
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t lo_nib_bytes(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
-__device__ __forceinline__ uint32_t hi_nib_bytes(uint32_t w) { return w & 0xF0F0F0F0u; }
+// E4M3 operand bytes of 16 bytes of INT4 codes: codes 0-3 of each word are
+// bits 7 and 0-2 of its bytes, codes 4-7 the same positions rotated left by
+// 4 bits.
+__device__ __forceinline__ u32x4 e4m3_lo(const u32x4& c) {
+  constexpr uint32_t MSK = 0x87878787u;
+  return u32x4{c.x & MSK, c.y & MSK, c.z & MSK, c.w & MSK};
+}
+__device__ __forceinline__ u32x4 e4m3_hi(const u32x4& c) {
+  constexpr uint32_t MSK = 0x87878787u;
+  return u32x4{__builtin_amdgcn_alignbit(c.x, c.x, 4) & MSK, __builtin_amdgcn_alignbit(c.y, c.y, 4) & MSK,
+               __builtin_amdgcn_alignbit(c.z, c.z, 4) & MSK, __builtin_amdgcn_alignbit(c.w, c.w, 4) & MSK};
+}
 
 template <int OUT, typename I>
 __device__ __forceinline__ void store_out(void* Y, I idx, float v) {
@@ -71,56 +81,39 @@ __device__ __forceinline__ float load_out(const void* Y, I idx) {
 
 }  // namespace
 
-// Per-format tile shape, all with 4 waves in a 2 x 2 grid:
-//  FP4: each wave owns 128 x 128 (4 x 4 MFMA tiles, 256 fp32 accumulators
-//       that only the MFMAs touch, so they live in AGPRs); 256 x 256 per
-//       workgroup.
-//  INT4: the per-group dequantization updates the accumulators with VALU
-//       fma, so they must be VGPRs; each wave owns 64 x 64 (2 x 2 tiles);
-//       128 x 128 per workgroup.
-template <int FMT>
-struct Shape {
-  static constexpr bool I4 = FMT == SVDQ_INT4_G64_FP16;
-  static constexpr int RB = I4 ? 2 : 4;   // 32-row blocks per wave
-  static constexpr int CB = I4 ? 2 : 4;   // 32-column blocks per wave
-  static constexpr int NTHREADS = 256;
-  static constexpr int BM = 2 * RB * 32;
-  static constexpr int BN = 2 * CB * 32;
-};
+// Tile: 4 waves in a 2 x 2 grid, each owning 64 x 64 (2 x 2 MFMA tiles).
+// The per-group dequantization updates the accumulators with VALU fma, so
+// they are VGPRs; 128 x 128 per workgroup, two workgroups per CU.
+constexpr int RB = 2, CB = 2;                      // 32-row (-column) blocks per wave
+constexpr int BM = 2 * RB * 32, BN = 2 * CB * 32;
+constexpr int NTHREADS = 256;
+constexpr int A_CH = BM * 4 / NTHREADS, B_CH = BN * 4 / NTHREADS;   // 16-byte code pieces per thread and stage
 
-// LDS layout of one K stage (128 K values): the code tiles are kept in the
-// MFMA operand-block order of global memory, so block (row block rb, step
-// j) of the stage sits at ((rb * 2 + j) * 1 KB) and lane l of an MFMA reads
-// the 16 bytes at lane * 16 inside it: copies and reads are contiguous.
-__device__ __forceinline__ int lds_block(int rowblk, int j) { return (rowblk * 2 + j) << 10; }
+// LDS layout of one K stage (128 K values) of one operand: the codes are
+// widened to E4M3 operand bytes once, as they are stored.  The 2 KB block of
+// (32-row block rb, 64-wide step j) sits at (rb * 2 + j) * 2 KB; lane l of an
+// MFMA finds the bytes of codes 0-3 of its four words at l * 16 and those of
+// codes 4-7 at 1 KB + l * 16, so stores and reads are contiguous.  Both
+// operands use the same byte order, which is all the MFMA's K sum needs.
+__device__ __forceinline__ int lds_block(int rowblk, int j) { return (rowblk * 2 + j) << 11; }
 
-template <int FMT, bool SLAB, int OUT>
+template <bool SLAB, int OUT>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
-  using SH = Shape<FMT>;
-  constexpr int BM = SH::BM, BN = SH::BN, RB = SH::RB, CB = SH::CB;
-  constexpr int NTHREADS = SH::NTHREADS;
-  constexpr int A_CH = BM * 4 / NTHREADS, B_CH = BN * 4 / NTHREADS;   // 16-byte chunks per thread
-  constexpr bool I4 = SH::I4;
-  // LDS: two stage buffers of A and B codes plus their scales; the
-  // epilogue reuses the code buffers to stage the output tile.
-  // INT4 scales: [stage][group][row] fp32 (B pre-divided by 256); FP4: the
-  // 4 E8M0 bytes of a row (column) per stage as one word, in [.][0][row].
-  constexpr int NSG = I4 ? 2 : 1;
-  constexpr int LDS_A = 2 * BM * BKB, LDS_B = 2 * BN * BKB;
-  constexpr int LDS_SA = 2 * NSG * BM * 4, LDS_SB = 2 * NSG * BN * 4;
+  constexpr int STAGE_A = (BM / 32) * 2 * 2048, STAGE_B = (BN / 32) * 2 * 2048;
+  // LDS: two stage buffers of A and B operands plus the scales as f16 MFMA
+  // operand words ([stage][group][row]: fp16 bits in the low half); the
+  // epilogue reuses the operand buffers to stage the output tile.
+  constexpr int LDS_A = 2 * STAGE_A, LDS_B = 2 * STAGE_B;
+  constexpr int LDS_SA = 2 * 2 * BM * 4, LDS_SB = 2 * 2 * BN * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_A + LDS_B + LDS_SA + LDS_SB];
-  auto sA = reinterpret_cast<uint8_t(*)[BM * BKB]>(smem);
-  auto sB = reinterpret_cast<uint8_t(*)[BN * BKB]>(smem + LDS_A);
-  auto sSA = reinterpret_cast<uint32_t(*)[NSG][BM]>(smem + LDS_A + LDS_B);
-  auto sSB = reinterpret_cast<uint32_t(*)[NSG][BN]>(smem + LDS_A + LDS_B + LDS_SA);
+  auto sA = reinterpret_cast<uint8_t(*)[STAGE_A]>(smem);
+  auto sB = reinterpret_cast<uint8_t(*)[STAGE_B]>(smem + LDS_A);
+  auto sSA = reinterpret_cast<uint32_t(*)[2][BM]>(smem + LDS_A + LDS_B);
+  auto sSB = reinterpret_cast<uint32_t(*)[2][BN]>(smem + LDS_A + LDS_B + LDS_SA);
 
   // kernel arguments in registers (a lambda capturing g would read them
   // from the argument segment with vector loads)
   const int M = g.M, K = g.K, N = g.N, rank = g.rank;
-  const uint8_t* __restrict__ acodes = g.acodes;
-  const uint8_t* __restrict__ wcodes = g.wcodes;
-  const uint32_t* __restrict__ ascales = static_cast<const uint32_t*>(g.ascales);
-  const uint32_t* __restrict__ wscales = static_cast<const uint32_t*>(g.wscales);
   const uint16_t* __restrict__ Tb = g.Tb;
   const uint16_t* __restrict__ l2t = g.l2t;
   const float* __restrict__ bias = g.bias;
@@ -132,9 +125,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const long n0 = static_cast<long>(tn) * BN;
 
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
+  const int lane = t & 63, wave = wave_uniform(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, lh = lane >> 5;
+  const int l32 = lane & 31;
+  const int lh = lane >> 5;
   const int SW = K / 128;                        // scale words (4 bytes) per row
   const int stages = K / 128;
   const int wrow0 = wm * (RB * 32), wcol0 = wn * (CB * 32);
@@ -167,82 +161,86 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         for (int j = 0; j < CB; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[j], acc[i][j], 0, 0, 0);
       }
     }
-    if constexpr (I4) {
-      // the INT4 groups accumulate 256 x their value (codes widened to 16 q);
-      // the slab is scaled to match and the epilogue divides by 256 (powers
-      // of two: every rounding is the same as without the factor)
-#pragma unroll
-      for (int i = 0; i < RB; i++)
-#pragma unroll
-        for (int j = 0; j < CB; j++)
-#pragma unroll
-          for (int v = 0; v < 16; v++) acc[i][j][v] *= 256.0f;
-    }
   }
 
-  // ---- global -> registers -> LDS.  A stage of the A (B) tile is BM / 16
-  // (BN / 16) operand blocks of 1 KB; thread t copies 16-byte pieces q =
-  // t + 256 i: block q / 64, lane slot q % 64 (64 threads cover one block
-  // contiguously).  Row blocks past the matrix are clamped to its last one
-  // (their outputs are never stored).  Thread t < BM also loads the scale
-  // word of A row t, thread t >= BM that of B column t - BM.
+  // ---- global -> registers -> LDS, through buffer resources over the
+  // workgroup's own row blocks (32-bit offsets; the stage is the scalar
+  // offset).  A stage of the A (B) tile is BM / 16 (BN / 16) operand blocks
+  // of 1 KB; thread t copies 16-byte pieces q = t + 256 i: block q / 64, lane
+  // slot q % 64 (64 threads cover one block contiguously).  Row blocks past
+  // the matrix are clamped to its last one (their outputs are never
+  // stored).  Waves 0-1 load the scale words of the 128 A rows, waves 2-3
+  // those of the 128 B columns.
   struct Regs {
     u32x4 a[A_CH], b[B_CH];
-    uint32_t sa, sb;
+    uint32_t sc;
   };
-  // INT4 scale word of this thread's row (t < BM: A row t, else B column
-  // t - BM) for stage st: sc_base[sc_off + st * sc_step].  Activation scales
-  // are in 32-row blocks (word (row, st) at ((row / 32) * SW + st) * 32 +
-  // row % 32), weight scales row-major.
-  const bool sc_is_a = t < BM;
-  const long sc_row = sc_is_a ? min(m0 + t, static_cast<long>(M - 1)) : min(n0 + (t - BM), static_cast<long>(N - 1));
-  const uint32_t* __restrict__ sc_base = sc_is_a ? ascales : wscales;
-  const long sc_off = sc_is_a ? (sc_row >> 5) * SW * 32 + (sc_row & 31) : sc_row * SW;
-  const int sc_step = sc_is_a ? 32 : 1;
   const long KBLK = K / 64;                       // 1 KB blocks per 32-row block
-  const long last_ablk = (M + 31) / 32 - 1, last_bblk = N / 32 - 1;
+  const int a_blks = static_cast<int>(min(static_cast<long>(BM / 32), (M + 31) / 32 - m0 / 32));
+  const int b_blks = static_cast<int>(min(static_cast<long>(BN / 32), N / 32 - n0 / 32));
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(g.acodes + (m0 / 32) * KBLK * 1024), 0, static_cast<int>(a_blks * KBLK * 1024), 0x00020000);
+  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(g.wcodes + (n0 / 32) * KBLK * 1024), 0, static_cast<int>(b_blks * KBLK * 1024), 0x00020000);
+  uint32_t aoff[A_CH], boff[B_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; i++) {
+    const int q = t + i * NTHREADS, blk = q >> 6;
+    aoff[i] = static_cast<uint32_t>(((min(blk >> 1, a_blks - 1) * KBLK + (blk & 1)) << 10) + (q & 63) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < B_CH; i++) {
+    const int q = t + i * NTHREADS, blk = q >> 6;
+    boff[i] = static_cast<uint32_t>(((min(blk >> 1, b_blks - 1) * KBLK + (blk & 1)) << 10) + (q & 63) * 16);
+  }
+  // scale words: activation scales in 32-row blocks (word (row, st) at
+  // ((row / 32) * SW + st) * 32 + row % 32), weight scales row-major
+  const bool sc_is_a = wave < 2;
+  __amdgpu_buffer_rsrc_t sr;
+  uint32_t soff;
+  int sstep;
+  if (sc_is_a) {
+    const long rows = min(static_cast<long>(BM), static_cast<long>(M) - m0);
+    const long r = min(static_cast<long>(t), rows - 1);
+    sr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(static_cast<const void*>(static_cast<const uint32_t*>(g.ascales) + (m0 >> 5) * SW * 32)), 0,
+        static_cast<int>(((rows + 31) >> 5) * SW * 128), 0x00020000);
+    soff = static_cast<uint32_t>(((r >> 5) * SW * 32 + (r & 31)) * 4);
+    sstep = 128;
+  } else {
+    const long cols = min(static_cast<long>(BN), static_cast<long>(N) - n0);
+    const long c = min(static_cast<long>(t - BM), cols - 1);
+    sr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(static_cast<const void*>(static_cast<const uint32_t*>(g.wscales) + n0 * SW)), 0,
+        static_cast<int>(cols * SW * 4), 0x00020000);
+    soff = static_cast<uint32_t>(c * SW * 4);
+    sstep = 4;
+  }
   auto load_stage = [&](Regs& r, int st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < A_CH; i++) {
-      const int q = t + i * NTHREADS, blk = q >> 6;
-      const long rb = min(m0 / 32 + (blk >> 1), last_ablk);
-      r.a[i] = *reinterpret_cast<const u32x4*>(acodes + ((rb * KBLK + 2 * st + (blk & 1)) << 10) + (q & 63) * 16);
-    }
+    for (int i = 0; i < A_CH; i++) r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff[i], st * 2048, 0);
 #pragma unroll
-    for (int i = 0; i < B_CH; i++) {
-      const int q = t + i * NTHREADS, blk = q >> 6;
-      const long rb = min(n0 / 32 + (blk >> 1), last_bblk);
-      r.b[i] = *reinterpret_cast<const u32x4*>(wcodes + ((rb * KBLK + 2 * st + (blk & 1)) << 10) + (q & 63) * 16);
-    }
-    if constexpr (I4) {
-      // 128 threads per operand
-      r.sa = sc_base[sc_off + st * sc_step];
-    } else {
-      r.sa = ascales[min(m0 + t, static_cast<long>(M - 1)) * SW + st];
-      r.sb = wscales[min(n0 + t, static_cast<long>(N - 1)) * SW + st];
-    }
+    for (int i = 0; i < B_CH; i++) r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(br, boff[i], st * 2048, 0);
+    r.sc = __builtin_amdgcn_raw_buffer_load_b32(sr, soff, st * sstep, 0);
   };
   auto store_stage = [&](const Regs& r, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < A_CH; i++) {
-      const int q = t + i * NTHREADS;
-      *reinterpret_cast<u32x4*>(&sA[buf][q * 16]) = r.a[i];
+      const int q = t + i * NTHREADS, off = ((q >> 6) << 11) + (q & 63) * 16;
+      *reinterpret_cast<u32x4*>(&sA[buf][off]) = e4m3_lo(r.a[i]);
+      *reinterpret_cast<u32x4*>(&sA[buf][off + 1024]) = e4m3_hi(r.a[i]);
     }
 #pragma unroll
     for (int i = 0; i < B_CH; i++) {
-      const int q = t + i * NTHREADS;
-      *reinterpret_cast<u32x4*>(&sB[buf][q * 16]) = r.b[i];
+      const int q = t + i * NTHREADS, off = ((q >> 6) << 11) + (q & 63) * 16;
+      *reinterpret_cast<u32x4*>(&sB[buf][off]) = e4m3_lo(r.b[i]);
+      *reinterpret_cast<u32x4*>(&sB[buf][off + 1024]) = e4m3_hi(r.b[i]);
     }
-    if constexpr (I4) {
-      // fp16 bits of the two groups' scales, as the f16 MFMA operands take them
-      uint32_t(*ss)[BM] = t < BM ? sSA[buf] : sSB[buf];
-      const int idx = t < BM ? t : t - BM;
-      ss[0][idx] = r.sa & 0xFFFFu;
-      ss[1][idx] = r.sa >> 16;
-    } else {
-      sSA[buf][0][t] = r.sa;
-      sSB[buf][0][t] = r.sb;
-    }
+    // fp16 bits of the two groups' scales, as the f16 MFMA operands take them
+    uint32_t(*ss)[BM] = sc_is_a ? sSA[buf] : sSB[buf];
+    const int idx = sc_is_a ? t : t - BM;
+    ss[0][idx] = r.sc & 0xFFFFu;
+    ss[1][idx] = r.sc >> 16;
   };
 
   // Stage k's codes are loaded into register set R[k % 2].  Schedule of
@@ -252,12 +250,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   // Loads past the last stage re-read the last stage (their data is never
   // used), so that every stage issues the same loads and the compiler's
   // wait counts stay exact across the loop.
+  // The prologue issues its loads stage by stage (no interleaving), in the
+  // same order as the loop, so that the compiler's load counters agree at
+  // the loop head and each wait covers exactly the stage it needs.
   Regs R0, R1;
   const int last = stages - 1;
   load_stage(R0, 0);
+  __builtin_amdgcn_sched_barrier(0);
   load_stage(R1, min(1, last));
+  __builtin_amdgcn_sched_barrier(0);
   store_stage(R0, 0);
   load_stage(R0, min(2, last));
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
 
   auto stage_body = [&](int s, Regs& Rn, auto BUF) __attribute__((always_inline)) {
@@ -268,88 +272,53 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 
 #pragma unroll
     for (int j = 0; j < 2; j++) {          // two 64-wide MFMA steps per stage
-      const int c = 2 * j + lh;            // this lane's 16-byte chunk of the stage
-      u32x4 av[RB], bv[CB];
+      // E4M3 operands (codes 0-3 of the lane's words, then codes 4-7) and
+      // the scale operands of the f16 MFMA that forms the tile's scale
+      // products: every lane holds its row's (column's) fp16 scale in its
+      // first element, so K slots 0 and 4 both carry s_x[i] s_w[j] and the
+      // MFMA gives 2 s_x[i] s_w[j] (exact); the E4M3 MFMA's block scales
+      // (2^9, 2^8) give P_g / 2 to match.
+      i32x8 a8[RB], b8[CB];
+      f16x4 fa[RB], fb[CB];
 #pragma unroll
-      for (int rb = 0; rb < RB; rb++)
-        av[rb] = *reinterpret_cast<const u32x4*>(&sA[buf][lds_block(wrow0 / 32 + rb, j) + lane * 16]);
+      for (int rb = 0; rb < RB; rb++) {
+        const int o = lds_block(wrow0 / 32 + rb, j) + lane * 16;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(&sA[buf][o]);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(&sA[buf][o + 1024]);
+        a8[rb] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        fa[rb] = __builtin_bit_cast(f16x4, u32x2{sSA[buf][j][wrow0 + rb * 32 + l32], 0u});
+      }
 #pragma unroll
-      for (int cb = 0; cb < CB; cb++)
-        bv[cb] = *reinterpret_cast<const u32x4*>(&sB[buf][lds_block(wcol0 / 32 + cb, j) + lane * 16]);
-
-      if constexpr (I4) {
-        i32x4 a0[RB], a1[RB], b0[CB], b1[CB];
-        // scale operands of the f16 MFMA that forms s_x[i] s_w[j] for a
-        // 32 x 32 tile: only K slot 0 (lanes 0-31, first element) is nonzero
-        // (every lane reads its word; lanes 32-63 mask it to zero, which
-        // keeps the reads unconditional)
-        f16x4 fa[RB], fb[CB];
+      for (int cb = 0; cb < CB; cb++) {
+        const int o = lds_block(wcol0 / 32 + cb, j) + lane * 16;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(&sB[buf][o]);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(&sB[buf][o + 1024]);
+        b8[cb] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        fb[cb] = __builtin_bit_cast(f16x4, u32x2{sSB[buf][j][wcol0 + cb * 32 + l32], 0u});
+      }
+      // software pipeline over the wave's output tiles: the MFMAs of tile
+      // u + 1 (P_g / 2 = sum q_x q_w / 2, exact in fp32: codes are q 2^-9;
+      // and 2 s_x s_w) are in flight while tile u is dequantized with one fma
+      // per accumulator (the product of the two is P_g s_x s_w exactly)
+      constexpr int NT = RB * CB;
+      f32x16 p[2], sp[2];
+      auto mma = [&](int u, f32x16& dst, f32x16& sdst) __attribute__((always_inline)) {
+        const int rb = u / CB, cb = u % CB;
+        f32x16 zf;
 #pragma unroll
-        for (int cb = 0; cb < CB; cb++) {
-          b0[cb] = i32x4{(int)lo_nib_bytes(bv[cb].x), (int)hi_nib_bytes(bv[cb].x), (int)lo_nib_bytes(bv[cb].y),
-                         (int)hi_nib_bytes(bv[cb].y)};
-          b1[cb] = i32x4{(int)lo_nib_bytes(bv[cb].z), (int)hi_nib_bytes(bv[cb].z), (int)lo_nib_bytes(bv[cb].w),
-                         (int)hi_nib_bytes(bv[cb].w)};
-          const uint32_t w = sSB[buf][j][wcol0 + cb * 32 + l32] & (lh ? 0u : 0xFFFFu);
-          fb[cb] = __builtin_bit_cast(f16x4, u32x2{w, 0u});
-        }
+        for (int v = 0; v < 16; v++) zf[v] = 0.f;
+        dst = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8[rb], b8[cb], zf, 0, 0, 0, 127 + 9, 0, 127 + 8);
+        sdst = __builtin_amdgcn_mfma_f32_32x32x8f16(fa[rb], fb[cb], zf, 0, 0, 0);
+      };
+      mma(0, p[0], sp[0]);
 #pragma unroll
-        for (int rb = 0; rb < RB; rb++) {
-          a0[rb] = i32x4{(int)lo_nib_bytes(av[rb].x), (int)hi_nib_bytes(av[rb].x), (int)lo_nib_bytes(av[rb].y),
-                         (int)hi_nib_bytes(av[rb].y)};
-          a1[rb] = i32x4{(int)lo_nib_bytes(av[rb].z), (int)hi_nib_bytes(av[rb].z), (int)lo_nib_bytes(av[rb].w),
-                         (int)hi_nib_bytes(av[rb].w)};
-          const uint32_t w = sSA[buf][j][wrow0 + rb * 32 + l32] & (lh ? 0u : 0xFFFFu);
-          fa[rb] = __builtin_bit_cast(f16x4, u32x2{w, 0u});
-        }
-        // software pipeline over the wave's output tiles: the MFMAs of tile
-        // u + 1 (the group's 256 P_g in int32 and the scale products
-        // s_x s_w, exact in fp32) are in flight while tile u is dequantized
-        constexpr int NT = RB * CB;
-        i32x16 p[2];
-        f32x16 sp[2];
-        auto mma = [&](int u, i32x16& dst, f32x16& sdst) __attribute__((always_inline)) {
-          const int rb = u / CB, cb = u % CB;
-          i32x16 z16;
-          f32x16 zf;
+      for (int u = 0; u < NT; u++) {
+        const int rb = u / CB, cb = u % CB;
+        if (u + 1 < NT) mma(u + 1, p[(u + 1) & 1], sp[(u + 1) & 1]);
+        const f32x16& pp = p[u & 1];
+        const f32x16& ss = sp[u & 1];
 #pragma unroll
-          for (int v = 0; v < 16; v++) {
-            z16[v] = 0;
-            zf[v] = 0.f;
-          }
-          dst = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[rb], b0[cb], z16, 0, 0, 0);
-          dst = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[rb], b1[cb], dst, 0, 0, 0);
-          sdst = __builtin_amdgcn_mfma_f32_32x32x8f16(fa[rb], fb[cb], zf, 0, 0, 0);
-        };
-        mma(0, p[0], sp[0]);
-#pragma unroll
-        for (int u = 0; u < NT; u++) {
-          const int rb = u / CB, cb = u % CB;
-          if (u + 1 < NT) mma(u + 1, p[(u + 1) & 1], sp[(u + 1) & 1]);
-          const i32x16& pp = p[u & 1];
-          const f32x16& ss = sp[u & 1];
-#pragma unroll
-          for (int v = 0; v < 16; v++) acc[rb][cb][v] = __builtin_fmaf(static_cast<float>(pp[v]), ss[v], acc[rb][cb][v]);
-        }
-      } else {
-        i32x8 a[RB], b[CB];
-        int sa[RB], sb[CB];
-#pragma unroll
-        for (int cb = 0; cb < CB; cb++) {
-          b[cb] = i32x8{(int)bv[cb].x, (int)bv[cb].y, (int)bv[cb].z, (int)bv[cb].w, 0, 0, 0, 0};
-          sb[cb] = (sSB[buf][0][wcol0 + cb * 32 + l32] >> (8 * c)) & 0xFF;
-        }
-#pragma unroll
-        for (int rb = 0; rb < RB; rb++) {
-          a[rb] = i32x8{(int)av[rb].x, (int)av[rb].y, (int)av[rb].z, (int)av[rb].w, 0, 0, 0, 0};
-          sa[rb] = (sSA[buf][0][wrow0 + rb * 32 + l32] >> (8 * c)) & 0xFF;
-        }
-#pragma unroll
-        for (int rb = 0; rb < RB; rb++)
-#pragma unroll
-          for (int cb = 0; cb < CB; cb++)
-            acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[rb], b[cb], acc[rb][cb], 4, 4, 0, sa[rb],
-                                                                          0, sb[cb]);
+        for (int v = 0; v < 16; v++) acc[rb][cb][v] = __builtin_fmaf(pp[v], ss[v], acc[rb][cb][v]);
       }
     }
     __syncthreads();
@@ -384,7 +353,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         for (int v = 0; v < 16; v++) {
           const int row = 8 * (v >> 2) + 4 * lh + (v & 3);
           const int off = row * ROWB + (cb * 32 + l32) * OB;
-          const float y = (I4 ? acc[rb][cb][v] * (1.0f / 256.0f) : acc[rb][cb][v]) + bv[cb];
+          const float y = acc[rb][cb][v] + bv[cb];
           if constexpr (OUT == SVDQ_OUT_F32) *reinterpret_cast<float*>(stage + off) = y;
           else *reinterpret_cast<uint16_t*>(stage + off) = static_cast<uint16_t>(f32_to_bf16_bits(y));
         }
@@ -442,10 +411,9 @@ __global__ __launch_bounds__(256) void up_kernel(const uint16_t* __restrict__ Tb
 hipError_t launch_gemm(int fmt, bool slab, int out_dtype, const GemmArgs& g, hipStream_t st) {
   const bool f32 = out_dtype == SVDQ_OUT_F32;
   if (fmt == SVDQ_INT4_G64_FP16) {
-    using SH = Shape<SVDQ_INT4_G64_FP16>;
-    const int tiles = ((g.M + SH::BM - 1) / SH::BM) * ((g.N + SH::BN - 1) / SH::BN);
+    const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
     dim3 grid(tiles), block(256);
-#define SVDQ_G(S, O) hipLaunchKernelGGL((gemm_kernel<SVDQ_INT4_G64_FP16, S, O>), grid, block, 0, st, g)
+#define SVDQ_G(S, O) hipLaunchKernelGGL((gemm_kernel<S, O>), grid, block, 0, st, g)
     if (slab) { if (f32) SVDQ_G(true, SVDQ_OUT_F32); else SVDQ_G(true, SVDQ_OUT_BF16); }
     else      { if (f32) SVDQ_G(false, SVDQ_OUT_F32); else SVDQ_G(false, SVDQ_OUT_BF16); }
 #undef SVDQ_G

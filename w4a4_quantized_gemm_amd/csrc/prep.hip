@@ -247,7 +247,7 @@ __global__ void wquant_kernel(const double* __restrict__ R, int K, int N, uint8_
       for (int k = 0; k < G; k++) {
         double q = rne_quotient_f64(col[static_cast<long>(k) * N], s);
         q = fmin(fmax(q, -7.0), 7.0);
-        words[k >> 3] |= (static_cast<uint32_t>(static_cast<int>(q)) & 0xFu) << (4 * (k & 7));
+        words[k >> 3] |= int4_code_bits(static_cast<int>(q), k & 7);
       }
     }
     reinterpret_cast<uint16_t*>(wscales)[n * groups + g] = static_cast<uint16_t>(sbits);

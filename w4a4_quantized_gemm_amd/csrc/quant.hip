@@ -35,6 +35,15 @@ __device__ __forceinline__ uint32_t e2m1_plus_zero(uint32_t w) {
   return w & (nz | 0x77777777u);
 }
 
+// The same for four E4M3 bytes of INT4 codes: bit 7 survives only if one of
+// bits 0-6 is set.
+__device__ __forceinline__ uint32_t e4m3_plus_zero(uint32_t w) {
+  const uint32_t nz = ((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) & 0x80808080u;
+  return w & (nz | 0x7F7F7F7Fu);
+}
+
+typedef short fp8x2 __attribute__((ext_vector_type(2)));
+
 template <int FMT, bool QUANT, bool DOWN, int RB>
 __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X, int M, int K,
                                                   const float* __restrict__ inv_lam,
@@ -206,14 +215,15 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
         const __half sh = __float2half_rn(amax / 7.0f);
         const float s = __half2float(sh);
         const float r = s > 0.f ? 1.0f / s : 0.f;
-        // t = x / s + 8 with one rounding (fma with the rounded reciprocal)
-        // is within 2^-20 of the exact value, so rint(t) = RNE(x / s) + 8
-        // unless t lies within 2^-18 of a half-integer; a lane with such a
-        // value redoes its 32 quotients exactly.  (s = 0 gives r = 0, t = 8.)
+        // t = x / s with one rounding (the product with the rounded
+        // reciprocal) is within 2^-20 of the exact quotient, so rint(t) is
+        // RNE(x / s) unless t lies within 2^-18 of a half-integer; a lane
+        // with such a value redoes its 32 quotients exactly.  (s = 0 gives
+        // r = 0 and all-zero codes.)
         float dmax = 0.f;
 #pragma unroll
         for (int e = 0; e < 32; e++) {
-          const float t = __builtin_fmaf(xh[e], r, 8.0f);
+          const float t = xh[e] * r;
           const float q = __builtin_rintf(t);
           dmax = fmaxf(dmax, __builtin_fabsf(t - q));
           xh[e] = q;
@@ -228,24 +238,28 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
             const float xv[8] = {bf16_lo(v.x) * i0.x, bf16_hi(v.x) * i0.y, bf16_lo(v.y) * i0.z, bf16_hi(v.y) * i0.w,
                                  bf16_lo(v.z) * i1.x, bf16_hi(v.z) * i1.y, bf16_lo(v.w) * i1.z, bf16_hi(v.w) * i1.w};
 #pragma unroll
-            for (int e = 0; e < 8; e++) xh[8 * c + e] = rne_quotient(xv[e], s, r) + 8.0f;
+            for (int e = 0; e < 8; e++) xh[8 * c + e] = rne_quotient(xv[e], s, r);
           }
         }
-        // codes: nibble = clamp(q, -7, 7) & 15 = clamp(q + 8, 1, 15) ^ 8; bytes
-        // of four values, then nibble pairs (byte j | byte j+1 << 4) at bytes
-        // 0 and 2 of each, gathered by one byte permute
+        // codes (sign-magnitude, the E4M3 bits of q * 2^-9; the format's
+        // word layout): the hardware conversion of clamp(q, -7, 7) / 2^9
+        // (exact: |q| <= 7 are E4M3 subnormals), zeros made +0, then the
+        // bytes of codes 4-7 of each word rotated left by 4 bits over those
+        // of codes 0-3
 #pragma unroll
         for (int w = 0; w < 4; w++) {
           uint32_t d[2];
 #pragma unroll
           for (int h = 0; h < 2; h++) {
-            uint32_t v = 0u;
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-              v = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(xh[8 * w + 4 * h + e], 1.0f, 15.0f), e, v);
-            d[h] = v | (v >> 4);
+            const float* qv = xh + 8 * w + 4 * h;
+            fp8x2 v = {0, 0};
+            v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v, __builtin_amdgcn_fmed3f(qv[0], -7.0f, 7.0f),
+                                                         __builtin_amdgcn_fmed3f(qv[1], -7.0f, 7.0f), 512.0f, false);
+            v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v, __builtin_amdgcn_fmed3f(qv[2], -7.0f, 7.0f),
+                                                         __builtin_amdgcn_fmed3f(qv[3], -7.0f, 7.0f), 512.0f, true);
+            d[h] = e4m3_plus_zero(__builtin_bit_cast(uint32_t, v));
           }
-          packed[w] = __builtin_amdgcn_perm(d[1], d[0], 0x06040200u) ^ 0x88888888u;
+          packed[w] = d[0] | __builtin_amdgcn_alignbit(d[1], d[1], 28);
         }
         // INT4 scale block order within the 32-row block (the 4-byte word of
         // row r32 holds the stage's two groups); rows past M and the odd lane

@@ -65,6 +65,18 @@ __device__ __forceinline__ uint32_t e2m1_code(float y) {
   return idx | ((y < 0.f && idx != 0u) ? 8u : 0u);
 }
 
+// Bits of INT4 code q (|q| <= 7) in the 32-bit word that holds codes
+// k .. k + 7 (k % 8 == 0), for code j = 0..7 of the word.  Each code is the
+// byte (q < 0) << 7 | |q|, the E4M3 bits of q * 2^-9 (a subnormal; zero is
+// +0); codes 0-3 fill bits 7 and 0-2 of bytes 0-3, codes 4-7 the same byte
+// positions rotated left by 4 bits.  So word & 0x87878787 and
+// rotr(word, 4) & 0x87878787 are the E4M3 bytes of codes 0-3 and 4-7.
+__host__ __device__ inline uint32_t int4_code_bits(int q, int j) {
+  const uint32_t b = (q < 0 ? 0x80u : 0u) | static_cast<uint32_t>(q < 0 ? -q : q);
+  const int sh = j < 4 ? 8 * j : 8 * (j - 4) + 4;
+  return sh == 0 ? b : (b << sh) | (b >> (32 - sh));
+}
+
 // Byte offset of the 16-byte chunk holding codes k .. k + 31 (k % 32 == 0)
 // of row `row` in a code matrix with K codes per row, stored in MFMA
 // operand-block order (1 KB blocks of 32 rows x 64 codes, lane-ordered).

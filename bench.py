@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/gemm_<workload>_hbm_counters.json from two rocprofv3 --pmc "
                          "runs (FETCH_SIZE, WRITE_SIZE) of --profile-only --calibrate-copy")
+    ap.add_argument("--summarize-util", nargs="+", metavar="PMC_DIR",
+                    help="write profiles/gemm_<workload>_mfma_counters.json from rocprofv3 --pmc runs of "
+                         "--profile-only (SQ / GRBM / TCC counters; one directory per pass)")
     ap.add_argument("--extra", default="c3_fc1_4608x3072x12288_fp4",
                     help="comma-separated further workloads reported in the same line ('' for none)")
     return ap.parse_args()
@@ -322,6 +325,80 @@ def summarize_counters(fetch_dir, write_dir, cfg, src_hash):
     print(json.dumps(out))
 
 
+UTIL_PASSES = (
+    "GRBM_GUI_ACTIVE SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_INSTS_VALU "
+    "SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT",
+    "GRBM_GUI_ACTIVE SQ_ACTIVE_INST_MFMA SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_VMEM "
+    "SQ_INST_LEVEL_VMEM SQ_INSTS_VMEM_RD SQ_ACTIVE_INST_LDS SQ_WAIT_ANY",
+    "TCC_HIT_sum TCC_MISS_sum TCP_PENDING_STALL_CYCLES_sum TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_READ_REQ_sum",
+)
+N_XCD, N_SIMD = 8, 1024      # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+
+
+def summarize_util(dirs, cfg, src_hash):
+    """MFMA / VALU / wait counters of the GEMM kernel and the activation pass
+    from rocprofv3 --pmc passes of --profile-only (per-dispatch means), with
+    the derived figures: the shader clock (GRBM_GUI_ACTIVE is summed over the
+    XCDs), the share of SIMD cycles the matrix core was busy, the MFMA
+    throughput and the wave time spent waiting.  Writes
+    profiles/gemm_<workload>_mfma_counters.json."""
+    import csv
+    import glob
+
+    kernels = {"gemm": ("void svdq::gemm_fp4_kernel<" if cfg.fmt == "fp4" else "void svdq::gemm_kernel<"),
+               "act": "void svdq::act_kernel<"}
+    vals = {k: {} for k in kernels}
+    durs = {k: [] for k in kernels}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            seen = set()
+            for r in csv.DictReader(open(f)):
+                for k, pre in kernels.items():
+                    name = r["Kernel_Name"]
+                    if not name.startswith(pre) or (k == "act" and ", true, true," not in name):
+                        continue
+                    vals[k].setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                    key = (f, r["Dispatch_Id"])
+                    if key not in seen:
+                        seen.add(key)
+                        durs[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    out = {"workload": cfg.name, "kernel_source_hash": src_hash,
+           "commands": [f"rocprofv3 --pmc {p} --output-format csv -d gpurun_out/pmc_{cfg.name}_{i + 1} -o run -- "
+                        f"python3 bench.py --profile-only --steps 4 --warmup 1 --workload {cfg.name}"
+                        for i, p in enumerate(UTIL_PASSES)] +
+                       [f"python3 bench.py --workload {cfg.name} --summarize-util " +
+                        " ".join(f"gpurun_out/pmc_{cfg.name}_{i + 1}" for i in range(len(UTIL_PASSES)))],
+           "note": "per-dispatch means; cycles = GRBM_GUI_ACTIVE / 8 XCDs; mfma_busy = "
+                   "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles); wave_wait = SQ_WAIT_INST_ANY / "
+                   "SQ_WAVE_CYCLES (share of wave lifetime stalled at s_waitcnt); l2_hit = TCC_HIT / "
+                   "(TCC_HIT + TCC_MISS); durations are the profiled dispatches' (counters slow them down)"}
+    for k in kernels:
+        v = {c: statistics.mean(x) for c, x in vals[k].items()}
+        if not v:
+            continue
+        rec = {"counters": v, "dispatch_us": statistics.mean(durs[k]) * 1e6 if durs[k] else None}
+        if "GRBM_GUI_ACTIVE" in v:
+            cyc = v["GRBM_GUI_ACTIVE"] / N_XCD
+            rec["cycles"] = cyc
+            if durs[k] and k == "gemm":      # long enough for the counter window to match the dispatch
+                rec["clock_ghz"] = cyc / statistics.mean(durs[k]) / 1e9
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in v:
+                rec["mfma_busy"] = v["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * cyc)
+            if "SQ_INSTS_VALU" in v:
+                rec["valu_insts_per_simd"] = (v["SQ_INSTS_VALU"] - v.get("SQ_INSTS_MFMA", 0.0)) / N_SIMD
+        if "SQ_WAIT_INST_ANY" in v and v.get("SQ_WAVE_CYCLES"):
+            rec["wave_wait"] = v["SQ_WAIT_INST_ANY"] / v["SQ_WAVE_CYCLES"]
+        if "TCC_HIT_sum" in v and "TCC_MISS_sum" in v:
+            rec["l2_hit"] = v["TCC_HIT_sum"] / max(1.0, v["TCC_HIT_sum"] + v["TCC_MISS_sum"])
+        out[k] = rec
+    path = os.path.join(ROOT, "profiles", f"gemm_{cfg.name}_mfma_counters.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps({k: {x: out[k][x] for x in ("clock_ghz", "mfma_busy", "wave_wait", "l2_hit") if x in out[k]}
+                      for k in kernels if k in out}))
+
+
 def run_config(args, cfg, torch, S, WL, to_tensor, with_cpu):
     rig = Rig(cfg, torch, S, WL, to_tensor)
     ms_fused, wall = time_fused(torch, S, rig, args.steps, args.warmup)
@@ -355,6 +432,10 @@ def main():
     S.load()
     cfgs = {c.name: c for c in list(WL.CONFIGS.values()) + WL.sweep_configs()}
     cfg = cfgs[args.workload]
+
+    if args.summarize_util:
+        summarize_util(args.summarize_util, cfg, kernel_source_hash())
+        return
 
     if args.summarize_counters:
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1], cfg, kernel_source_hash())

@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--summarize-util", nargs="+", metavar="PMC_DIR",
                     help="write profiles/gemm_<workload>_mfma_counters.json from rocprofv3 --pmc runs of "
                          "--profile-only (SQ / GRBM / TCC counters; one directory per pass)")
+    ap.add_argument("--lora", type=int, default=16,
+                    help="also time the main workload with an extra rank-LORA branch merged in (0: skip)")
     ap.add_argument("--extra", default="c3_fc1_4608x3072x12288_fp4",
                     help="comma-separated further workloads reported in the same line ('' for none)")
     return ap.parse_args()
@@ -89,7 +91,7 @@ def algorithmic(cfg):
 class Rig:
     """Device buffers for one workload, replicated to defeat the Infinity Cache."""
 
-    def __init__(self, cfg, torch, S, WL, O_bits_to_tensor):
+    def __init__(self, cfg, torch, S, WL, O_bits_to_tensor, lora: int = 0):
         self.cfg = cfg
         dev = "cuda:0"
         X_bits, W_bits, b_bits = WL.make_layer(cfg)
@@ -104,6 +106,14 @@ class Rig:
         layer = S.SVDQLinear.prepare(W, a, cfg.rank, cfg.fmt, cfg.alpha, bias=bias)
         torch.cuda.synchronize()
         self.prep_s = time.perf_counter() - t0
+        if lora:
+            # an extra low-rank branch (a LoRA update dW = A B) merged into the
+            # 16-bit branch: the residual codes are shared, the slab grows
+            g = torch.Generator(device="cpu").manual_seed(cfg.seed + 1)
+            A = (torch.randn(cfg.K, lora, generator=g) * 0.02).to(torch.bfloat16).to(dev)
+            B = (torch.randn(lora, cfg.N, generator=g) * 0.02).to(torch.bfloat16).to(dev)
+            layer = layer.merge_lowrank(A, B)
+            torch.cuda.synchronize()
         self.layer = layer
         del W
         M, N = cfg.M, cfg.N
@@ -399,8 +409,8 @@ def summarize_util(dirs, cfg, src_hash):
                       for k in kernels if k in out}))
 
 
-def run_config(args, cfg, torch, S, WL, to_tensor, with_cpu):
-    rig = Rig(cfg, torch, S, WL, to_tensor)
+def run_config(args, cfg, torch, S, WL, to_tensor, with_cpu, lora=0):
+    rig = Rig(cfg, torch, S, WL, to_tensor, lora)
     ms_fused, wall = time_fused(torch, S, rig, args.steps, args.warmup)
     tq, tg = time_kernels(torch, S, rig, args.steps, args.warmup)
     ms_unfused, _ = time_fused(torch, S, rig, args.steps, args.warmup, unfused=True)
@@ -512,6 +522,16 @@ def main():
                        "gemm_us": rr["tg_ms"] * 1e3, "gemm_tops": gt, "gemm_frac_peak": gt / PEAK_TFLOPS[c.fmt],
                        "peak_tops": PEAK_TFLOPS[c.fmt], "quant_us": rr["tq_ms"] * 1e3,
                        "quant_frac_hbm": Ax["q_bytes"] / (rr["tq_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS}
+        del rr
+        torch.cuda.empty_cache()
+    if args.lora:
+        rr = run_config(args, cfg, torch, S, WL, to_tensor, with_cpu=False, lora=args.lora)
+        extra[f"{cfg.name}+lora{args.lora}"] = {
+            "rank": cfg.rank + args.lora, "us_per_layer": rr["ms_fused"] * 1e3,
+            "us_per_layer_unfused": rr["ms_unfused"] * 1e3,
+            "fused_vs_unfused_speedup": rr["ms_unfused"] / rr["ms_fused"],
+            "overhead_vs_base": rr["ms_fused"] / r["ms_fused"] - 1.0, "gemm_us": rr["tg_ms"] * 1e3,
+            "quant_us": rr["tq_ms"] * 1e3}
         del rr
         torch.cuda.empty_cache()
     if extra:

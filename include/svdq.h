@@ -195,6 +195,25 @@ svdq_status svdq_prepare_weights(const svdq_layer_desc* desc, const void* d_W,
                                  const void* d_L1, const void* d_L2, void* d_prepared,
                                  size_t prepared_bytes, void* stream);
 
+/* An extra low-rank branch merged into the 16-bit branch of a prepared
+ * layer, without touching the quantized residual (walkthrough, Fig. 9 and
+ * Fig. 16 section: a LoRA runs as part of the low-rank branch, so a new
+ * LoRA needs no re-quantization).  For an update dW = A B of the original
+ * weight (d_A: K x r_extra, d_B: r_extra x N, bf16 row-major), X dW =
+ * X_hat diag(lambda) A B, so the merged factors are
+ *     L1' = [L1b | bf16(lambda32 (.) A)]   (row j scaled by lambda32_j; the
+ *                                           fp64 product rounded once)
+ *     L2' = [L2b ; B]
+ * and lambda, inv_lambda, the residual codes and scales and the bias are
+ * copied.  d_out receives the blob of the descriptor with rank
+ * desc->rank + r_extra (format, K, N, alpha and flags unchanged), so
+ * out_bytes >= svdq_prepared_bytes of that descriptor; d_out must not
+ * overlap d_prepared.  r_extra > 0, r_extra % 16 == 0 and desc->rank +
+ * r_extra <= 128, else SVDQ_ERR_UNSUPPORTED_SHAPE.  Synchronous.  Allocates
+ * nothing. */
+svdq_status svdq_merge_lowrank(const svdq_layer_desc* desc, const void* d_prepared, const void* d_A,
+                               const void* d_B, int r_extra, void* d_out, size_t out_bytes, void* stream);
+
 /* Reads the blob header back (synchronously) and checks it against `desc`:
  * magic, version, format, K, N, rank and flags.  SVDQ_ERR_BAD_BLOB if they
  * differ. */

@@ -351,6 +351,26 @@ def prepare(W_bits, a, *, alpha: float, rank: int, fmt: str, bias_bits=None,
 # ============================================================ runtime
 
 
+def merge_lowrank(prep: dict, A_bits, B_bits) -> dict:
+    """An extra low-rank branch dW = A B (A: K x r_e, B: r_e x N, bf16 bits)
+    merged into the 16-bit branch of a prepared layer.
+
+    [walkthrough] Fig. 9 / Fig. 16 section: a LoRA joins the existing
+    low-rank branch, so the quantized residual is not redone.  The layer
+    computes with X_hat = X diag(1/lambda), so X dW = X_hat diag(lambda) A B:
+    L1 gains the columns bf16(lambda32 * A) (row j times lambda32_j, exact in
+    fp64, rounded once) and L2 the rows B; R, its codes and scales, lambda and
+    the bias stay as they are.
+    """
+    A = bf16_bits_to_f64(A_bits)
+    B = bf16_bits_to_f64(B_bits)
+    out = dict(prep)
+    out["L1b"] = np.concatenate([prep["L1b"], to_bf16(prep["lam32"][:, None] * A)], axis=1)
+    out["L2b"] = np.concatenate([prep["L2b"], B], axis=0)
+    out["rank"] = out["L1b"].shape[1]
+    return out
+
+
 def smooth_act(X_bits, inv32) -> np.ndarray:
     """x_hat = fp32(x * inv_lambda) (the product of two fp32 numbers, rounded once)."""
     return to_fp32(bf16_bits_to_f64(X_bits) * np.asarray(inv32, dtype=np.float64)[None, :])

@@ -94,6 +94,20 @@ def test_runtime_validation_before_device():
     assert lib.svdq_prepare_weights(ctypes.byref(db), good, good, None, None, None, good, pb, None) == 1
     dg = _desc(flags=S.F_FACTORS_GIVEN)
     assert lib.svdq_prepare_weights(ctypes.byref(dg), good, good, None, None, None, good, pb, None) == 1
+    # merge_lowrank: r_extra a positive multiple of 16 with rank + r_extra <= 128;
+    # pointers, alignment, the output size and no overlap with the input
+    out = 1 << 30
+    d48 = _desc(r=48)
+    pb48 = S.svdq_prepared_bytes(d48)
+    merge = lib.svdq_merge_lowrank
+    assert merge(ctypes.byref(d), good, good, good, 0, out, pb48, None) == 2
+    assert merge(ctypes.byref(d), good, good, good, 8, out, pb48, None) == 2
+    assert merge(ctypes.byref(d), good, good, good, 112, out, 1 << 40, None) == 2
+    assert merge(ctypes.byref(d), good, None, good, 16, out, pb48, None) == 1
+    assert merge(ctypes.byref(d), good, good, good, 16, None, pb48, None) == 1
+    assert merge(ctypes.byref(d), good, good, good, 16, out + 8, pb48, None) == 7
+    assert merge(ctypes.byref(d), good, good, good, 16, out, pb48 - 1, None) == 4
+    assert merge(ctypes.byref(d), good, good, good, 16, good + 4096, pb48, None) == 1
     # quantize_act: T required when rank > 0
     assert lib.svdq_quantize_act(ctypes.byref(d), good, good, 16, good, good, None, None, 0, None) == 1
 
@@ -114,6 +128,9 @@ def test_device_check_without_gpu():
     good = 1 << 20
     assert lib.svdq_linear(ctypes.byref(d), good, good, 64, good, 0, good, ws, None) == 3
     assert lib.svdq_act_absmax(good, 64, 3072, good, 0, None) == 3
+    d48 = _desc(r=48)
+    assert lib.svdq_merge_lowrank(ctypes.byref(d), good, good, good, 16, 1 << 30, S.svdq_prepared_bytes(d48),
+                                  None) == 3
 
 
 def test_blob_layout_and_sizes():

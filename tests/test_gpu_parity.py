@@ -246,6 +246,40 @@ def test_factors_given_and_no_smoothing(torch_dev):
     _check_linear(torch_dev, layer, X, X_bits, ref3)
 
 
+@pytest.mark.parametrize("fmt,re", [(O.INT4, 16), (O.FP4, 32)])
+def test_merge_lowrank(torch_dev, fmt, re):
+    """An extra low-rank branch (a LoRA) merged into a prepared layer: lambda,
+    the residual codes and scales and the bias are copied, the merged
+    factors equal the oracle's merge bit for bit, the input blob is
+    untouched, and the merged layer matches the oracle's merged layer."""
+    import w4a4_quantized_gemm_amd as S
+    torch, dev = torch_dev
+    _say(f"case: merge low-rank fmt={fmt} r_extra={re}")
+    M, K, N, r = 200, 384, 320, 16
+    cfg = WL.C2.with_(name="merge", M=M, K=K, N=N, rank=r, fmt=fmt, w_std=1 / np.sqrt(K),
+                      n_outlier_channels=8, bias_std=0.02, seed=77)
+    X_bits, W_bits, b_bits = WL.make_layer(cfg)
+    layer, X, _ = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
+    sec, ref = _check_weights(layer, W_bits, fmt, b_bits)
+    rng = np.random.default_rng(78)
+    A_bits = O.bf16_bits_of(O.to_bf16(rng.standard_normal((K, re)) * 0.05).astype(np.float32))
+    B_bits = O.bf16_bits_of(O.to_bf16(rng.standard_normal((re, N)) * 0.05).astype(np.float32))
+    merged = layer.merge_lowrank(np_bits_to_bf16_tensor(A_bits, dev), np_bits_to_bf16_tensor(B_bits, dev))
+    torch.cuda.synchronize()
+    assert merged.desc.rank == r + re
+    S.svdq_check_blob(merged.desc, merged.blob)
+    msec = blob_sections(merged)
+    for k in ("lam32", "inv32", "w_codes", "w_scales", "bias", "raw_wcodes", "raw_wscales"):
+        assert np.array_equal(msec[k], sec[k]), k
+    after = blob_sections(layer)
+    assert all(np.array_equal(after[k], sec[k]) for k in ("L1b", "L2b", "raw_wcodes", "raw_wscales"))
+    mref = O.merge_lowrank(ref, A_bits, B_bits)
+    assert np.array_equal(msec["L1b"], mref["L1b"]) and np.array_equal(msec["L2b"], mref["L2b"])
+    _check_act(torch_dev, merged, X, X_bits, mref)
+    errs = _check_linear(torch_dev, merged, X, X_bits, mref)
+    _say(f"  rel errors {errs}")
+
+
 def test_quantizer_edge_values(torch_dev):
     """Zero rows, exact ties of x/s, tiny values with subnormal fp16 scales,
     E2M1 midpoints, large magnitudes, E8M0 exponents near -127 and bf16

@@ -429,3 +429,51 @@ def test_error_ordering_on_tiny_config():
         p = O.prepare(Wb, a, alpha=0.5, rank=r, fmt=O.INT4)
         errs.append(O.rel_fro(O.linear(p, X, "f32")["Y64"], y))
     assert all(errs[i] > errs[i + 1] for i in range(len(errs) - 1)), errs
+
+
+def test_merge_lowrank_exact_case():
+    """lambda = 1, no low-rank base, integer X and W whose 4-bit branch is
+    exact, and a LoRA whose A has one +-1 per column: the merged layer is
+    exactly X W + X A B (walkthrough, Fig. 9 / Fig. 16 section: the LoRA
+    joins the low-rank branch, the residual is untouched)."""
+    rng = np.random.default_rng(21)
+    M, K, N, re = 8, 128, 16, 16
+    X = rng.integers(-7, 8, (M, K)).astype(np.float64)
+    W = rng.integers(-7, 8, (K, N)).astype(np.float64)
+    X[:, ::64] = 7
+    W[::64, :] = -7
+    A = np.zeros((K, re))
+    A[rng.permutation(K)[:re], np.arange(re)] = rng.choice([-1.0, 1.0], re)
+    B = rng.integers(-3, 4, (re, N)).astype(np.float64)
+    Xb, Wb = O.bf16_bits_of(X.astype(np.float32)), O.bf16_bits_of(W.astype(np.float32))
+    Ab, Bb = O.bf16_bits_of(A.astype(np.float32)), O.bf16_bits_of(B.astype(np.float32))
+    prep = O.prepare(Wb, O.act_absmax(Xb), alpha=0.5, rank=0, fmt=O.INT4, no_smoothing=True)
+    merged = O.merge_lowrank(prep, Ab, Bb)
+    assert merged["rank"] == re and merged["L1b"].shape == (K, re) and merged["L2b"].shape == (re, N)
+    assert np.array_equal(merged["w_codes"], prep["w_codes"]) and np.array_equal(merged["w_scales"], prep["w_scales"])
+    assert np.array_equal(O.linear(merged, Xb, out="f32")["Y64"], X @ W + X @ A @ B)
+
+
+@pytest.mark.parametrize("fmt", [O.INT4, O.FP4])
+def test_merge_lowrank_adds_the_update(fmt):
+    """With smoothing and a real low-rank base, merging dW = A B changes the
+    layer by X A B up to the bf16 roundings of the 16-bit branch (x_hat, the
+    scaled A and T, each at most 2^-9 relative): |dY - X A B| <= 3.1 * 2^-9
+    |X| |A| |B| elementwise.  Scaling A by 1/lambda instead of lambda, or a
+    transposed B, breaks it."""
+    rng = np.random.default_rng(22)
+    M, K, N, r, re = 12, 256, 24, 8, 16
+    X, W = _c1_small()
+    X, W = X[:M, :K], W[:K, :N]
+    A = O.to_bf16(rng.standard_normal((K, re)) * 0.05)
+    B = O.to_bf16(rng.standard_normal((re, N)) * 0.05)
+    prep = O.prepare(W, O.act_absmax(X), alpha=0.5, rank=r, fmt=fmt)
+    assert np.ptp(prep["lam32"]) > 0.1                         # smoothing is active
+    merged = O.merge_lowrank(prep, O.bf16_bits_of(A.astype(np.float32)), O.bf16_bits_of(B.astype(np.float32)))
+    assert np.array_equal(merged["L1b"][:, :r], prep["L1b"]) and np.array_equal(merged["L2b"][:r], prep["L2b"])
+    assert np.array_equal(merged["L1b"][:, r:], O.to_bf16(prep["lam32"][:, None] * A))
+    dY = O.linear(merged, X, out="f32")["Y64"] - O.linear(prep, X, out="f32")["Y64"]
+    x = O.bf16_bits_to_f64(X)
+    bound = 3.1 * 2.0 ** -9 * (np.abs(x) @ np.abs(A) @ np.abs(B))
+    assert np.all(np.abs(dY - x @ A @ B) <= bound)
+    assert np.max(np.abs(x @ A @ B)) > 10 * np.max(bound)       # the update is well above the bound

@@ -34,7 +34,7 @@ STATUS_NAMES = {
 # every symbol include/svdq.h declares
 EXPORTED = (
     "svdq_status_string", "svdq_version", "svdq_prepared_bytes", "svdq_workspace_bytes",
-    "svdq_act_sizes", "svdq_act_absmax", "svdq_prepare_weights", "svdq_check_blob",
+    "svdq_act_sizes", "svdq_act_absmax", "svdq_prepare_weights", "svdq_merge_lowrank", "svdq_check_blob",
     "svdq_quantize_act", "svdq_gemm", "svdq_linear", "svdq_linear_unfused", "svdq_blob_layout_of",
 )
 
@@ -80,6 +80,7 @@ def _lib() -> ctypes.CDLL:
             "svdq_act_sizes": ([D, I, ctypes.POINTER(Z), ctypes.POINTER(Z), ctypes.POINTER(Z)], S),
             "svdq_act_absmax": ([P, I, I, P, I, P], S),
             "svdq_prepare_weights": ([D, P, P, P, P, P, P, Z, P], S),
+            "svdq_merge_lowrank": ([D, P, P, P, I, P, Z, P], S),
             "svdq_check_blob": ([D, P, P], S),
             "svdq_quantize_act": ([D, P, P, I, P, P, P, P, Z, P], S),
             "svdq_gemm": ([D, P, P, P, P, I, P, I, P], S),
@@ -162,6 +163,15 @@ def svdq_prepare_weights(desc: LayerDesc, W, act_absmax, prepared, bias=None, L1
                                        _stream(stream)), "svdq_prepare_weights")
 
 
+def svdq_merge_lowrank(desc: LayerDesc, prepared, A, B, out, stream=None):
+    """Merge an extra low-rank branch dW = A B (A: K x r_extra, B: r_extra x N,
+    bf16 tensors) into ``out``, the blob of ``desc`` with rank + r_extra
+    (synchronous)."""
+    r_extra = A.shape[1]
+    _check(_lib().svdq_merge_lowrank(ctypes.byref(desc), _ptr(prepared), _ptr(A), _ptr(B), r_extra, _ptr(out),
+                                     out.numel(), _stream(stream)), "svdq_merge_lowrank")
+
+
 def svdq_check_blob(desc: LayerDesc, prepared, stream=None):
     _check(_lib().svdq_check_blob(ctypes.byref(desc), _ptr(prepared), _stream(stream)), "svdq_check_blob")
 
@@ -242,6 +252,20 @@ class SVDQLinear:
         blob = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
         svdq_prepare_weights(desc, W, act_absmax, blob, bias=bias, L1=L1, L2=L2, stream=stream)
         return cls(desc, blob)
+
+    def merge_lowrank(self, A, B, stream=None) -> "SVDQLinear":
+        """A new layer with the extra low-rank branch dW = A B (e.g. a LoRA)
+        merged into the 16-bit branch; the quantized residual is shared
+        unchanged (copied)."""
+        import torch
+        d = self.desc
+        desc = make_desc(d.K, d.N, d.rank + A.shape[1], d.fmt, d.alpha, d.flags)
+        nbytes = svdq_prepared_bytes(desc)
+        if nbytes == 0:
+            raise SvdqError(2, "svdq_prepared_bytes")
+        blob = torch.empty(nbytes, dtype=torch.uint8, device=self.blob.device)
+        svdq_merge_lowrank(d, self.blob, A, B, blob, stream)
+        return SVDQLinear(desc, blob)
 
     def workspace(self, M: int, unfused: bool = False):
         import torch

@@ -265,6 +265,39 @@ __global__ void wquant_kernel(const double* __restrict__ R, int K, int N, uint8_
         u32x4{words[4 * w], words[4 * w + 1], words[4 * w + 2], words[4 * w + 3]};
 }
 
+// Merged low-rank factors for an extra branch dW = A B (A: K x re, B: re x
+// N, bf16 row-major): columns t < r of L1 and rows t < r of L2 are the old
+// blob's, the new ones are bf16(lambda32[k] A[k][t - r]) (the product is
+// exact in fp64, rounded once) and B[t - r][n].  Thread per element of the
+// merged factor, in the stored orders (l1_operand_index, bf16_block_index).
+__global__ void merge_l1_kernel(const uint16_t* __restrict__ old_l1t, const float* __restrict__ lam,
+                                const uint16_t* __restrict__ A, int K, int r, int re, uint16_t* __restrict__ l1t) {
+  const long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int R = r + re;
+  if (idx >= static_cast<long>(K) * R) return;
+  const long k = idx / R;
+  const int t = static_cast<int>(idx % R);
+  uint16_t v;
+  if (t < r) {
+    v = old_l1t[l1_operand_index(t, k, r)];
+  } else {
+    const double a = __uint_as_float(static_cast<uint32_t>(A[k * re + (t - r)]) << 16);
+    v = static_cast<uint16_t>(f64_round_bits(static_cast<double>(lam[k]) * a, 7, 8));
+  }
+  l1t[l1_operand_index(t, k, R)] = v;
+}
+
+__global__ void merge_l2_kernel(const uint16_t* __restrict__ old_l2t, const uint16_t* __restrict__ B, int N, int r,
+                                int re, uint16_t* __restrict__ l2t) {
+  const long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int R = r + re;
+  if (idx >= static_cast<long>(N) * R) return;
+  const long n = idx / R;
+  const int t = static_cast<int>(idx % R);
+  const uint16_t v = t < r ? old_l2t[bf16_block_index(n, t, r)] : B[static_cast<long>(t - r) * N + n];
+  l2t[bf16_block_index(n, t, R)] = v;
+}
+
 __global__ void bias_kernel(const uint16_t* __restrict__ b, int N, float* __restrict__ out) {
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
   if (n < N) out[n] = __uint_as_float(static_cast<uint32_t>(b[n]) << 16);
@@ -453,6 +486,50 @@ svdq_status prepare_impl(const svdq_layer_desc& d, const uint16_t* W, const floa
   h.group = group_of(d.fmt);
   h.alpha = d.alpha;
   h.layout = L;
+  SVDQ_TRY(hipMemcpyAsync(blob, &h, sizeof(h), hipMemcpyHostToDevice, st));
+  SVDQ_TRY(hipStreamSynchronize(st));
+  return SVDQ_OK;
+}
+
+svdq_status merge_impl(const svdq_layer_desc& d, const uint8_t* old_blob, const uint16_t* A, const uint16_t* B,
+                       int re, uint8_t* blob, hipStream_t st) {
+  svdq_layer_desc dn = d;
+  dn.rank = d.rank + re;
+  const svdq_blob_layout Lo = layout_of(d), Ln = layout_of(dn);
+  const int K = d.K, N = d.N, r = d.rank;
+  // sections that do not depend on the rank are copied as they are
+  SVDQ_TRY(hipMemcpyAsync(blob + Ln.lambda, old_blob + Lo.lambda, 4ul * K, hipMemcpyDeviceToDevice, st));
+  SVDQ_TRY(hipMemcpyAsync(blob + Ln.inv_lambda, old_blob + Lo.inv_lambda, 4ul * K, hipMemcpyDeviceToDevice, st));
+  SVDQ_TRY(hipMemcpyAsync(blob + Ln.wcodes, old_blob + Lo.wcodes, static_cast<size_t>(N) * K / 2,
+                          hipMemcpyDeviceToDevice, st));
+  SVDQ_TRY(hipMemcpyAsync(blob + Ln.wscales, old_blob + Lo.wscales,
+                          static_cast<size_t>(K / group_of(d.fmt)) * N * scale_bytes_of(d.fmt), hipMemcpyDeviceToDevice,
+                          st));
+  if (d.flags & SVDQ_F_HAS_BIAS)
+    SVDQ_TRY(hipMemcpyAsync(blob + Ln.bias, old_blob + Lo.bias, 4ul * N, hipMemcpyDeviceToDevice, st));
+  hipLaunchKernelGGL(merge_l1_kernel, dim3(blocks_for(static_cast<long>(K) * dn.rank)), dim3(256), 0, st,
+                     reinterpret_cast<const uint16_t*>(old_blob + Lo.l1t),
+                     reinterpret_cast<const float*>(old_blob + Lo.lambda), A, K, r, re,
+                     reinterpret_cast<uint16_t*>(blob + Ln.l1t));
+  SVDQ_TRY(hipGetLastError());
+  hipLaunchKernelGGL(merge_l2_kernel, dim3(blocks_for(static_cast<long>(N) * dn.rank)), dim3(256), 0, st,
+                     reinterpret_cast<const uint16_t*>(old_blob + Lo.l2t), B, N, r, re,
+                     reinterpret_cast<uint16_t*>(blob + Ln.l2t));
+  SVDQ_TRY(hipGetLastError());
+  BlobHeader h;
+  std::memset(&h, 0, sizeof(h));
+  h.magic = kMagic;
+  h.version = kVersion;
+  h.fmt = dn.fmt;
+  h.K = K;
+  h.N = N;
+  h.rank = dn.rank;
+  h.flags = dn.flags;
+  h.group = group_of(dn.fmt);
+  h.alpha = dn.alpha;
+  h.layout = Ln;
+  // header last, from host memory: the call returns after the stream has
+  // drained
   SVDQ_TRY(hipMemcpyAsync(blob, &h, sizeof(h), hipMemcpyHostToDevice, st));
   SVDQ_TRY(hipStreamSynchronize(st));
   return SVDQ_OK;

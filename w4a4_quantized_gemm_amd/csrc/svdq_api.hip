@@ -157,6 +157,26 @@ svdq_status svdq_prepare_weights(const svdq_layer_desc* desc, const void* d_W, c
                       static_cast<uint8_t*>(d_prepared), as_stream(stream), opt);
 }
 
+svdq_status svdq_merge_lowrank(const svdq_layer_desc* desc, const void* d_prepared, const void* d_A, const void* d_B,
+                               int r_extra, void* d_out, size_t out_bytes, void* stream) {
+  svdq_status st = validate_desc(desc);
+  if (st != SVDQ_OK) return st;
+  if (r_extra <= 0 || r_extra % 16 != 0 || desc->rank + r_extra > kMaxRank) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  if (!d_prepared || !d_A || !d_B || !d_out) return SVDQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(d_prepared) || !aligned16(d_out)) return SVDQ_ERR_MISALIGNED;
+  svdq_layer_desc dn = *desc;
+  dn.rank += r_extra;
+  const svdq_blob_layout L = layout_of(dn);
+  if (out_bytes < L.total) return SVDQ_ERR_BUFFER_TOO_SMALL;
+  const uint8_t* in = static_cast<const uint8_t*>(d_prepared);
+  const uint8_t* out = static_cast<const uint8_t*>(d_out);
+  const uint64_t in_bytes = layout_of(*desc).total;
+  if (out < in + in_bytes && in < out + L.total) return SVDQ_ERR_INVALID_ARGUMENT;   // overlap
+  if ((st = check_device()) != SVDQ_OK) return st;
+  return merge_impl(*desc, in, static_cast<const uint16_t*>(d_A), static_cast<const uint16_t*>(d_B), r_extra,
+                    static_cast<uint8_t*>(d_out), as_stream(stream));
+}
+
 svdq_status svdq_check_blob(const svdq_layer_desc* desc, const void* d_prepared, void* stream) {
   svdq_status st = validate_desc(desc);
   if (st != SVDQ_OK) return st;

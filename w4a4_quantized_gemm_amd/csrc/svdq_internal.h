@@ -11,7 +11,7 @@
 namespace svdq {
 
 constexpr uint32_t kMagic = 0x51445653u;  // "SVDQ" little-endian
-constexpr uint32_t kVersion = 2u;
+constexpr uint32_t kVersion = 3u;
 constexpr uint32_t kKnownFlags = SVDQ_F_NO_SMOOTHING | SVDQ_F_FACTORS_GIVEN | SVDQ_F_HAS_BIAS;
 constexpr int kMaxRank = 128;
 constexpr int kMaxDim = 65536;

@@ -28,4 +28,6 @@ namespace svdq {
 svdq_status prepare_impl(const svdq_layer_desc& d, const uint16_t* W, const float* act_absmax,
                          const uint16_t* bias, const uint16_t* L1, const uint16_t* L2, uint8_t* blob,
                          hipStream_t st, const PrepOptions& opt);
+svdq_status merge_impl(const svdq_layer_desc& d, const uint8_t* old_blob, const uint16_t* A, const uint16_t* B,
+                       int re, uint8_t* blob, hipStream_t st);
 }  // namespace svdq

@@ -32,7 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 # MI355X published peaks (dense)
-PEAK_TFLOPS = {"int4": 5000.0, "fp4": 10100.0}   # int8 MFMA (INT4 runs on it) / FP4 MFMA
+PEAK_TFLOPS = {"int4": 5000.0, "fp4": 10100.0}   # 8-bit MFMA (INT4 runs on the E4M3 one) / FP4 MFMA
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 INFINITY_CACHE = 256 << 20
@@ -490,7 +490,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_TFLOPS[fmt], "unit": "TFLOP/s",
                      "frac": gemm_tops / PEAK_TFLOPS[fmt], "traffic": traffic,
                      "kernel": ("gemm_fp4_kernel (FP4 block-scaled MFMA GEMM" if fmt == "fp4" else
-                                "gemm_kernel (INT4 on the i8 MFMA GEMM") + f" + rank-{cfg.rank} bf16 slab + bias)",
+                                "gemm_kernel (INT4 codes on the E4M3 block-scaled MFMA") + f" + rank-{cfg.rank} bf16 slab + bias)",
                      "avg_us": r["tg_ms"] * 1e3},
         "roofline_quant": {"bound": "hbm", "achieved": q_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": q_gbs / PEAK_HBM_GBS, "traffic": act_traffic,

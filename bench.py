@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--summarize-util", nargs="+", metavar="PMC_DIR",
                     help="write profiles/gemm_<workload>_mfma_counters.json from rocprofv3 --pmc runs of "
                          "--profile-only (SQ / GRBM / TCC counters; one directory per pass)")
+    ap.add_argument("--no-norm", dest="norm", action="store_false",
+                    help="skip timing the LayerNorm-fused layer against a separate norm pass")
     ap.add_argument("--lora", type=int, default=16,
                     help="also time the main workload with an extra rank-LORA branch merged in (0: skip)")
     ap.add_argument("--extra", default="c3_fc1_4608x3072x12288_fp4",
@@ -152,6 +154,40 @@ def time_fused(torch, S, rig, steps, warmup, unfused=False):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return e0.elapsed_time(e1) / steps, wall
+
+
+def time_norm(torch, S, rig, steps, warmup, eps=1e-6):
+    """The layer on a LayerNorm's input: the norm fused into the activation
+    pass (svdq_linear_ln) against the norm as its own pass (torch's
+    layer_norm writing the bf16 normalized activations) followed by
+    svdq_linear.  Returns (fused ms, separate ms) per step."""
+    d = rig.layer.desc
+    n = rig.nsets
+    g = torch.Generator(device="cpu").manual_seed(rig.cfg.seed + 2)
+    gamma = (1.0 + 0.1 * torch.randn(d.K, generator=g)).to(torch.bfloat16).to("cuda:0")
+    beta = (0.1 * torch.randn(d.K, generator=g)).to(torch.bfloat16).to("cuda:0")
+    F = torch.nn.functional
+
+    def fused(s):
+        S.svdq_linear_ln(d, s["blob"], s["X"], gamma, beta, eps, s["Y"], s["ws"], S.OUT_BF16)
+
+    def separate(s):
+        xn = F.layer_norm(s["X"], (d.K,), gamma, beta, eps)
+        S.svdq_linear(d, s["blob"], xn, s["Y"], s["ws"], S.OUT_BF16)
+
+    out = []
+    for fn in (fused, separate):
+        for k in range(warmup):
+            fn(rig.sets[k % n])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for k in range(steps):
+            fn(rig.sets[k % n])
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / steps)
+    return out[0], out[1]
 
 
 def time_kernels(torch, S, rig, steps, warmup):
@@ -409,15 +445,16 @@ def summarize_util(dirs, cfg, src_hash):
                       for k in kernels if k in out}))
 
 
-def run_config(args, cfg, torch, S, WL, to_tensor, with_cpu, lora=0):
+def run_config(args, cfg, torch, S, WL, to_tensor, with_cpu, lora=0, norm=False):
     rig = Rig(cfg, torch, S, WL, to_tensor, lora)
     ms_fused, wall = time_fused(torch, S, rig, args.steps, args.warmup)
     tq, tg = time_kernels(torch, S, rig, args.steps, args.warmup)
     ms_unfused, _ = time_fused(torch, S, rig, args.steps, args.warmup, unfused=True)
+    ms_norm = time_norm(torch, S, rig, args.steps, args.warmup) if norm else None
     A = algorithmic(cfg)
     tq_ms, tg_ms = statistics.mean(tq), statistics.mean(tg)
     out = dict(rig=rig, ms_fused=ms_fused, wall=wall, ms_unfused=ms_unfused, tq=tq, tg=tg, A=A,
-               tq_ms=tq_ms, tg_ms=tg_ms)
+               tq_ms=tq_ms, tg_ms=tg_ms, ms_norm=ms_norm)
     if with_cpu:
         out["cpu"] = cpu_baseline(rig, args.cpu_rows)
     return out
@@ -462,7 +499,7 @@ def main():
                           "gemm_ms": statistics.mean(tg)}), flush=True)
         return
 
-    r = run_config(args, cfg, torch, S, WL, to_tensor, with_cpu=not args.no_cpu_baseline)
+    r = run_config(args, cfg, torch, S, WL, to_tensor, with_cpu=not args.no_cpu_baseline, norm=args.norm)
     A, rig = r["A"], r["rig"]
     fmt = cfg.fmt
     t_layer_s = r["ms_fused"] / 1e3
@@ -510,10 +547,16 @@ def main():
     }
     if "cpu" in r:
         line["cpu_baseline"] = r["cpu"]
+    if r.get("ms_norm"):
+        nf, ns = r["ms_norm"]
+        line["layernorm_fused"] = {"us_per_layer_norm_fused": nf * 1e3, "us_per_layer_norm_separate": ns * 1e3,
+                                   "speedup": ns / nf,
+                                   "note": "svdq_linear_ln on the norm's input against torch layer_norm (bf16 "
+                                           "out) followed by svdq_linear"}
     extra = {}
     for name in [n for n in args.extra.split(",") if n and n != cfg.name]:
         c = cfgs[name]
-        rr = run_config(args, c, torch, S, WL, to_tensor, with_cpu=False)
+        rr = run_config(args, c, torch, S, WL, to_tensor, with_cpu=False, norm=args.norm)
         Ax = rr["A"]
         gt = Ax["gemm_ops"] / (rr["tg_ms"] / 1e3) / 1e12
         extra[name] = {"us_per_layer": rr["ms_fused"] * 1e3, "us_per_layer_unfused": rr["ms_unfused"] * 1e3,
@@ -522,6 +565,9 @@ def main():
                        "gemm_us": rr["tg_ms"] * 1e3, "gemm_tops": gt, "gemm_frac_peak": gt / PEAK_TFLOPS[c.fmt],
                        "peak_tops": PEAK_TFLOPS[c.fmt], "quant_us": rr["tq_ms"] * 1e3,
                        "quant_frac_hbm": Ax["q_bytes"] / (rr["tq_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS}
+        if rr.get("ms_norm"):
+            extra[name]["us_per_layer_norm_fused"] = rr["ms_norm"][0] * 1e3
+            extra[name]["us_per_layer_norm_separate"] = rr["ms_norm"][1] * 1e3
         del rr
         torch.cuda.empty_cache()
     if args.lora:

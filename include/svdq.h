@@ -254,6 +254,32 @@ svdq_status svdq_linear(const svdq_layer_desc* desc, const void* d_prepared, con
                         int M, void* d_Y, int out_dtype, void* d_workspace, size_t ws_bytes,
                         void* stream);
 
+/* Norm-fused activation pass: X is the input of the LayerNorm that precedes
+ * the layer, and the smoothing is folded into that norm's affine (handbook,
+ * SmoothQuant section: the smoothing factor is merged into the preceding
+ * normalization's weights, so no separate operator runs):
+ *   mu_i = mean_k x_ik,  rho_i = 1 / sqrt(mean_k (x_ik - mu_i)^2 + eps)
+ *     (fp32 sums in a fixed order, one kernel)
+ *   x_hat_ik = fma((x_ik - mu_i) rho_i, gamma'_k, beta'_k),
+ *     gamma' = fp32(gamma * inv_lambda), beta' = fp32(beta * inv_lambda)
+ * then the same quantization and down-projection as svdq_quantize_act, in
+ * the same output layouts; x_hat is never written to memory.  d_gamma,
+ * d_beta: bf16[K] (d_beta may be NULL: beta = 0); eps > 0 and finite.
+ * d_workspace (svdq_workspace_bytes(desc, M, 0) bytes) is required: it holds
+ * the row statistics and the folded affine.  Asynchronous. */
+svdq_status svdq_quantize_act_ln(const svdq_layer_desc* desc, const void* d_prepared, const void* d_X,
+                                 const void* d_gamma, const void* d_beta, float eps, int M,
+                                 void* d_codes, void* d_scales, void* d_T, void* d_workspace,
+                                 size_t ws_bytes, void* stream);
+
+/* The fused layer on the LayerNorm's input: svdq_linear with its activation
+ * pass replaced by svdq_quantize_act_ln's (one extra launch for the row
+ * statistics).  Y = Q(x_hat) Q(R) + Tb L2b + b with x_hat as above.
+ * Asynchronous. */
+svdq_status svdq_linear_ln(const svdq_layer_desc* desc, const void* d_prepared, const void* d_X,
+                           const void* d_gamma, const void* d_beta, float eps, int M, void* d_Y,
+                           int out_dtype, void* d_workspace, size_t ws_bytes, void* stream);
+
 /* The GEMM stage of svdq_linear on its own: Y = Q(x_hat) Q(R) + Tb L2b + b
  * from activations already produced by svdq_quantize_act with the same blob
  * (d_codes, d_scales, d_T in its output layouts; d_T may be NULL when

@@ -376,15 +376,37 @@ def smooth_act(X_bits, inv32) -> np.ndarray:
     return to_fp32(bf16_bits_to_f64(X_bits) * np.asarray(inv32, dtype=np.float64)[None, :])
 
 
-def quantize_act(X_bits, inv32, fmt: str) -> dict:
+def norm_act(X_bits, gamma_bits, beta_bits, eps: float, inv32) -> np.ndarray:
+    """x_hat of the norm-fused activation pass: LayerNorm over K of each row
+    with its affine, the smoothing folded into the affine.
+
+    [handbook] SmoothQuant section: the smoothing factor is merged into the
+    preceding normalization's weights, so inference has no separate
+    operator.  In fp64: mu = mean_k x, var = mean_k (x - mu)^2,
+    y = (x - mu) / sqrt(var + eps) * gamma + beta, x_hat = y * inv_lambda32;
+    returned rounded once to fp32, the precision in which the quantizer
+    decides.  beta_bits None means beta = 0.
+    """
+    x = bf16_bits_to_f64(X_bits)
+    g = bf16_bits_to_f64(gamma_bits)
+    b = np.zeros_like(g) if beta_bits is None else bf16_bits_to_f64(beta_bits)
+    mu = x.mean(axis=1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=1, keepdims=True)
+    y = (x - mu) / np.sqrt(var + eps) * g[None, :] + b[None, :]
+    return to_fp32(y * np.asarray(inv32, dtype=np.float64)[None, :])
+
+
+def quantize_act(X_bits, inv32, fmt: str, norm=None) -> dict:
     """Smoothing + dynamic per-token group quantization of the activations.
 
     [handbook] timestep section: dynamic scales computed from the current
     activation; groups along K per token row.  Returns the API byte formats
     (packed codes M x K/2, INT4 fp16 scale bits / FP4 E8M0 bytes M x K/g)
-    together with the unpacked codes, scale values and x_hat.
+    together with the unpacked codes, scale values and x_hat.  With ``norm``
+    = (gamma_bits, beta_bits, eps), X is the pre-norm input and x_hat comes
+    from ``norm_act``.
     """
-    xh = smooth_act(X_bits, inv32)
+    xh = smooth_act(X_bits, inv32) if norm is None else norm_act(X_bits, norm[0], norm[1], norm[2], inv32)
     if fmt == INT4:
         q, s = quantize_int4_groups(xh)
         nib = int4_nibble(q)
@@ -408,17 +430,17 @@ def _round_out(Y, out: str):
     return to_bf16(Y) if out == "bf16" else to_fp32(Y)
 
 
-def linear(prep: dict, X_bits, out: str = "bf16") -> dict:
+def linear(prep: dict, X_bits, out: str = "bf16", norm=None) -> dict:
     """Fused layer: Y = Q(x_hat) Q(R) + Tb L2b + b, then one rounding.
 
     [walkthrough] eq. (5): X W ~ X_hat L1 L2 + Q(X_hat) Q(R); eq. (2): the
     4-bit product is s_x s_w Q_x Q_w per group.  Dequantization is exact in
     fp64, so the 4-bit product is one fp64 matrix product of the dequantized
     operands.  Returns Y64 (unrounded), Y (rounded to ``out``) and the
-    activation-side intermediates.
+    activation-side intermediates.  ``norm`` as in ``quantize_act``.
     """
     fmt = prep["fmt"]
-    qa = quantize_act(X_bits, prep["inv32"], fmt)
+    qa = quantize_act(X_bits, prep["inv32"], fmt, norm)
     T, Tb = down_proj(qa["xhat"], prep["L1b"])
     Xdq = dequant_groups(qa["codes"], qa["scales"], fmt)
     Wdq = dequant_groups(prep["w_codes"].T, prep["w_scales"].T, fmt).T
@@ -429,9 +451,9 @@ def linear(prep: dict, X_bits, out: str = "bf16") -> dict:
     return dict(Y64=Y64, Y=_round_out(Y64, out), main=main, low=low, Tb=Tb, T=T, act=qa)
 
 
-def linear_unfused(prep: dict, X_bits, out: str = "bf16") -> dict:
+def linear_unfused(prep: dict, X_bits, out: str = "bf16", norm=None) -> dict:
     """Unfused rounding model: Yp = round(main + b); Y = round(Yp + Tb L2b)."""
-    r = linear(prep, X_bits, out)
+    r = linear(prep, X_bits, out, norm)
     bias = 0.0 if prep["bias"] is None else prep["bias"][None, :]
     Yp = _round_out(r["main"] + bias, out)
     r["Yp"] = Yp

@@ -108,6 +108,15 @@ def test_runtime_validation_before_device():
     assert merge(ctypes.byref(d), good, good, good, 16, out + 8, pb48, None) == 7
     assert merge(ctypes.byref(d), good, good, good, 16, out, pb48 - 1, None) == 4
     assert merge(ctypes.byref(d), good, good, good, 16, good + 4096, pb48, None) == 1
+    # the norm-fused calls: gamma required, eps > 0 and finite, workspace required
+    ln = lib.svdq_linear_ln
+    assert ln(ctypes.byref(d), good, good, None, None, 1e-5, 4608, good, 0, good, ws, None) == 1
+    assert ln(ctypes.byref(d), good, good, good, None, 0.0, 4608, good, 0, good, ws, None) == 1
+    assert ln(ctypes.byref(d), good, good, good, None, float("inf"), 4608, good, 0, good, ws, None) == 1
+    assert ln(ctypes.byref(d), good, good, good, None, 1e-5, 4608, good, 0, good, ws - 1, None) == 4
+    qln = lib.svdq_quantize_act_ln
+    assert qln(ctypes.byref(d), good, good, good, None, 1e-5, 16, good, good, good, None, ws, None) == 1
+    assert qln(ctypes.byref(d), good, good, good, None, 1e-5, 16, good, good, None, good, ws, None) == 1
     # quantize_act: T required when rank > 0
     assert lib.svdq_quantize_act(ctypes.byref(d), good, good, 16, good, good, None, None, 0, None) == 1
 

@@ -280,6 +280,83 @@ def test_merge_lowrank(torch_dev, fmt, re):
     _say(f"  rel errors {errs}")
 
 
+E2M1_MIDPOINTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+
+
+@pytest.mark.parametrize("fmt", [O.INT4, O.FP4])
+def test_norm_fused_pass(torch_dev, fmt):
+    """The LayerNorm-fused activation pass and layer against the oracle's
+    norm path.  x_hat comes from fp32 row statistics, so it may differ from
+    the oracle's by a few fp32 ulps: scales must be equal except in groups
+    whose absmax sits within 1e-5 of a scale rounding boundary, and in every
+    other group the codes must be equal except for elements within 1e-4 of a
+    rounding tie (where either neighbour is right); T within 2 bf16 ulps; Y to
+    the usual tolerance."""
+    import w4a4_quantized_gemm_amd as S
+    torch, dev = torch_dev
+    _say(f"case: norm-fused pass fmt={fmt}")
+    M, K, N, r, eps = 300, 384, 320, 16, 1e-5
+    cfg = WL.C2.with_(name="norm", M=M, K=K, N=N, rank=r, fmt=fmt, w_std=1 / np.sqrt(K),
+                      n_outlier_channels=8, bias_std=0.02, seed=91)
+    X_bits, W_bits, b_bits = WL.make_layer(cfg)
+    rng = np.random.default_rng(92)
+    # a per-row offset and scale, so that the norm has work to do
+    xf = O.bf16_bits_to_f64(X_bits) * rng.uniform(0.5, 3.0, (M, 1)) + rng.standard_normal((M, 1))
+    X_bits = O.bf16_bits_of(O.to_bf16(xf).astype(np.float32))
+    g_bits = O.bf16_bits_of(O.to_bf16(rng.uniform(0.5, 1.5, K)).astype(np.float32))
+    be_bits = O.bf16_bits_of(O.to_bf16(rng.standard_normal(K) * 0.1).astype(np.float32))
+    layer, X, _ = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
+    sec, ref = _check_weights(layer, W_bits, fmt, b_bits)
+    gamma, beta = np_bits_to_bf16_tensor(g_bits, dev), np_bits_to_bf16_tensor(be_bits, dev)
+    for beta_t, beta_b in ((beta, be_bits), (None, None)):
+        norm = (g_bits, beta_b, eps)
+        cb, sb, tb = S.svdq_act_sizes(layer.desc, M)
+        codes = torch.empty(cb, dtype=torch.uint8, device=dev)
+        scales = torch.empty(sb, dtype=torch.uint8, device=dev)
+        T = torch.empty(tb // 2, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev)
+        S.svdq_quantize_act_ln(layer.desc, layer.blob, X, gamma, beta_t, eps, codes, scales, T, ws)
+        torch.cuda.synchronize()
+        q, s, _, _ = decode_act(codes, scales, layer.desc.fmt, M, K)
+        qa = O.quantize_act(X_bits, ref["inv32"], fmt, norm)
+        g = 64 if fmt == O.INT4 else 32
+        xh = qa["xhat"].reshape(M, K // g, g)
+        if fmt == O.INT4:
+            same = s == qa["scales"]
+            a7 = np.abs(xh).max(axis=2) / 7.0
+            # fp16 rounding boundaries near a7: midpoints between neighbouring fp16 values
+            e = np.floor(np.log2(np.maximum(a7, 2.0 ** -24)))
+            ulp = 2.0 ** (np.maximum(e, -14) - 10)
+            near_b = np.abs(a7 / ulp - np.floor(a7 / ulp) - 0.5) < 1e-5 * a7 / ulp
+            t = xh / np.where(qa["scales"] > 0, qa["scales"], 1.0)[..., None]
+            near_tie = np.abs(np.abs(t - np.floor(t)) - 0.5) < 1e-4
+        else:
+            same = s == qa["scales"]
+            amax = np.abs(xh).max(axis=2)
+            near_b = np.abs(amax / (6.0 * np.exp2(qa["scales"])) - 1.0) < 1e-5
+            t = np.abs(xh) / np.exp2(qa["scales"])[..., None]
+            near_tie = np.min(np.abs(t[..., None] - E2M1_MIDPOINTS), axis=-1) < 1e-4
+        assert np.all(same | near_b), "scales differ away from a rounding boundary"
+        qg = q.reshape(M, K // g, g).astype(np.int64)
+        rg = qa["codes"].reshape(M, K // g, g).astype(np.int64)
+        bad = (qg != rg) & same[..., None] & ~near_tie
+        assert not np.any(bad), f"{int(bad.sum())} codes differ away from a rounding tie"
+        mism = float(np.mean((qg != rg) & same[..., None]))
+        assert mism < 1e-3, mism
+        _say(f"  beta={'yes' if beta_b is not None else 'no'}: scales differing {int((~same).sum())}, codes at ties "
+             f"differing {int(((qg != rg) & same[..., None]).sum())}")
+        Tg = O.bf16_bits_to_f64(untile_bf16(u16_tensor_to_np(T), M, r))
+        _, Tref = O.down_proj(qa["xhat"], ref["L1b"])
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(Tref), 1e-30))) - 7)
+        assert np.all(np.abs(Tg - Tref) <= 2 * ulp * 1.0001)
+        for out in (S.OUT_BF16, S.OUT_F32):
+            oname = "bf16" if out == S.OUT_BF16 else "f32"
+            Y = layer(X, out_dtype=out, norm=(gamma, beta_t, eps))
+            torch.cuda.synchronize()
+            e_rel = O.rel_fro(Y.float().cpu().numpy().astype(np.float64), O.linear(ref, X_bits, oname, norm)["Y"])
+            assert e_rel <= TOL, (oname, e_rel)
+
+
 def test_quantizer_edge_values(torch_dev):
     """Zero rows, exact ties of x/s, tiny values with subnormal fp16 scales,
     E2M1 midpoints, large magnitudes, E8M0 exponents near -127 and bf16

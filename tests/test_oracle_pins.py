@@ -477,3 +477,49 @@ def test_merge_lowrank_adds_the_update(fmt):
     bound = 3.1 * 2.0 ** -9 * (np.abs(x) @ np.abs(A) @ np.abs(B))
     assert np.all(np.abs(dY - x @ A @ B) <= bound)
     assert np.max(np.abs(x @ A @ B)) > 10 * np.max(bound)       # the update is well above the bound
+
+
+def _bits(a):
+    return O.bf16_bits_of(O.to_bf16(np.asarray(a, dtype=np.float64)).astype(np.float32))
+
+
+def test_norm_act_two_valued_rows_closed_form():
+    """Rows alternating a, b: mu = (a + b) / 2, var = ((a - b) / 2)^2, so with
+    gamma = 1, beta = 0 and lambda = 1 every x_hat is +-d / sqrt(d^2 + eps),
+    d = (a - b) / 2 (handbook SmoothQuant section: the norm that the
+    smoothing folds into)."""
+    K, eps = 256, 1e-6
+    ab = [(3.0, -1.0), (0.5, 0.25), (-7.0, 9.0)]
+    X = np.array([[a if k % 2 == 0 else b for k in range(K)] for a, b in ab])
+    xh = O.norm_act(_bits(X), _bits(np.ones(K)), None, eps, np.ones(K))
+    for i, (a, b) in enumerate(ab):
+        d = (a - b) / 2
+        v = d / np.sqrt(d * d + eps)
+        assert np.array_equal(xh[i], O.to_fp32(np.where(np.arange(K) % 2 == 0, v, -v)))
+
+
+def test_norm_act_invariances_and_fold():
+    """LayerNorm is invariant to a per-row shift and positive scale (up to
+    eps); its rows have zero mean and variance var / (var + eps); and the fold
+    keeps the layer: x_hat (lambda W) = norm(x) W."""
+    rng = np.random.default_rng(23)
+    M, K, N, eps = 6, 128, 8, 1e-5
+    x = rng.integers(-100, 101, (M, K)) / 8.0        # x, 4 x and 4 x + 3 are all exact in bf16
+    one = np.ones(K)
+    plain = O.norm_act(_bits(x), _bits(one), None, eps, one)
+    assert np.all(np.abs(plain.mean(axis=1)) < 1e-6)
+    var = x.var(axis=1)
+    assert np.allclose((plain ** 2).mean(axis=1), var / (var + eps), rtol=1e-6)
+    shifted = O.norm_act(_bits(x * 4 + 3), _bits(one), None, eps * 16, one)
+    assert np.allclose(shifted, plain, rtol=0, atol=1e-6)
+    g = O.to_bf16(rng.uniform(0.5, 1.5, K))
+    b = O.to_bf16(rng.standard_normal(K) * 0.1)
+    lam32 = O.to_fp32(rng.uniform(0.2, 5.0, K))
+    inv32 = O.to_fp32(1.0 / lam32)
+    W = rng.standard_normal((K, N))
+    xh = O.norm_act(_bits(x), _bits(g), _bits(b), eps, inv32)
+    y = (x - x.mean(axis=1, keepdims=True)) / np.sqrt(var[:, None] + eps) * g + b
+    lhs, rhs = xh @ (lam32[:, None] * W), y @ W
+    assert np.max(np.abs(lhs - rhs)) <= 1e-6 * np.max(np.abs(rhs))
+    # smoothing applied the other way round (times lambda) would break the fold
+    assert np.max(np.abs(O.norm_act(_bits(x), _bits(g), _bits(b), eps, lam32) @ (lam32[:, None] * W) - rhs)) > 0.1

@@ -35,7 +35,8 @@ STATUS_NAMES = {
 EXPORTED = (
     "svdq_status_string", "svdq_version", "svdq_prepared_bytes", "svdq_workspace_bytes",
     "svdq_act_sizes", "svdq_act_absmax", "svdq_prepare_weights", "svdq_merge_lowrank", "svdq_check_blob",
-    "svdq_quantize_act", "svdq_gemm", "svdq_linear", "svdq_linear_unfused", "svdq_blob_layout_of",
+    "svdq_quantize_act", "svdq_quantize_act_ln", "svdq_gemm", "svdq_linear", "svdq_linear_ln",
+    "svdq_linear_unfused", "svdq_blob_layout_of",
 )
 
 
@@ -70,7 +71,7 @@ def _lib() -> ctypes.CDLL:
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m w4a4_quantized_gemm_amd.build` (hipcc, gfx950)")
         lib = ctypes.CDLL(LIB_PATH)
-        P, I, Z, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_int
+        P, I, Z, S, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_int, ctypes.c_float
         D = ctypes.POINTER(LayerDesc)
         sig = {
             "svdq_status_string": ([I], ctypes.c_char_p),
@@ -83,7 +84,9 @@ def _lib() -> ctypes.CDLL:
             "svdq_merge_lowrank": ([D, P, P, P, I, P, Z, P], S),
             "svdq_check_blob": ([D, P, P], S),
             "svdq_quantize_act": ([D, P, P, I, P, P, P, P, Z, P], S),
+            "svdq_quantize_act_ln": ([D, P, P, P, P, F, I, P, P, P, P, Z, P], S),
             "svdq_gemm": ([D, P, P, P, P, I, P, I, P], S),
+            "svdq_linear_ln": ([D, P, P, P, P, F, I, P, I, P, Z, P], S),
             "svdq_linear": ([D, P, P, I, P, I, P, Z, P], S),
             "svdq_linear_unfused": ([D, P, P, I, P, I, P, Z, P], S),
             "svdq_blob_layout_of": ([D, ctypes.POINTER(BlobLayout)], S),
@@ -185,6 +188,25 @@ def svdq_quantize_act(desc: LayerDesc, prepared, X, codes, scales, T=None, works
            "svdq_quantize_act")
 
 
+def svdq_quantize_act_ln(desc: LayerDesc, prepared, X, gamma, beta, eps: float, codes, scales, T, workspace,
+                         stream=None):
+    """The norm-fused activation pass: X is the LayerNorm's input; gamma and
+    beta (bf16 [K], beta may be None) its affine; the workspace is required."""
+    M = X.shape[0]
+    _check(_lib().svdq_quantize_act_ln(ctypes.byref(desc), _ptr(prepared), _ptr(X), _ptr(gamma), _ptr(beta),
+                                       float(eps), M, _ptr(codes), _ptr(scales), _ptr(T), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)),
+           "svdq_quantize_act_ln")
+
+
+def svdq_linear_ln(desc: LayerDesc, prepared, X, gamma, beta, eps: float, Y, workspace, out_dtype: int = OUT_BF16,
+                   stream=None):
+    M = X.shape[0]
+    _check(_lib().svdq_linear_ln(ctypes.byref(desc), _ptr(prepared), _ptr(X), _ptr(gamma), _ptr(beta), float(eps),
+                                 M, _ptr(Y), out_dtype, _ptr(workspace), workspace.numel(), _stream(stream)),
+           "svdq_linear_ln")
+
+
 def svdq_gemm(desc: LayerDesc, prepared, codes, scales, T, M: int, Y, out_dtype: int = OUT_BF16,
               stream=None):
     """The GEMM stage alone, on the outputs of svdq_quantize_act."""
@@ -274,12 +296,19 @@ class SVDQLinear:
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.blob.device)
         return self._ws
 
-    def __call__(self, X, out_dtype: int = OUT_BF16, unfused: bool = False, Y=None, stream=None):
+    def __call__(self, X, out_dtype: int = OUT_BF16, unfused: bool = False, Y=None, stream=None, norm=None):
+        """Y = layer(X); with ``norm`` = (gamma, beta, eps), X is the input of
+        the preceding LayerNorm, which runs fused into the activation pass."""
         import torch
         M = X.shape[0]
         if Y is None:
             Y = torch.empty((M, self.desc.N), dtype=torch.bfloat16 if out_dtype == OUT_BF16 else torch.float32,
                             device=X.device)
+        if norm is not None:
+            if unfused:
+                raise ValueError("the norm-fused pass exists for the fused layer only")
+            svdq_linear_ln(self.desc, self.blob, X, norm[0], norm[1], norm[2], Y, self.workspace(M), out_dtype, stream)
+            return Y
         fn = svdq_linear_unfused if unfused else svdq_linear
         fn(self.desc, self.blob, X, Y, self.workspace(M, unfused), out_dtype, stream)
         return Y

@@ -44,9 +44,40 @@ __device__ __forceinline__ uint32_t e4m3_plus_zero(uint32_t w) {
 
 typedef short fp8x2 __attribute__((ext_vector_type(2)));
 
-template <int FMT, bool QUANT, bool DOWN, int RB>
+// x_hat of the 8 elements 8c .. 8c + 7 of a lane's 32 (row `row`, quarter
+// kq) from the staged chunk: x * inv_lambda, or with NORM
+// fma((x - mu) * rho, gamma', beta') (the staged factors are gamma' then
+// beta').  The exact-rounding path recomputes x_hat with this same code.
+template <bool NORM>
+__device__ __forceinline__ void x_hat8(const uint8_t* xs, const float* ils, int row, int kq, int c, float mu,
+                                       float rho, float* out) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(xs + row * 256 + (((4 * kq + c) ^ row) << 4));
+  const float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                      bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+  const f32x4 i0 = *reinterpret_cast<const f32x4*>(ils + kq * 32 + 8 * c);
+  const f32x4 i1 = *reinterpret_cast<const f32x4*>(ils + kq * 32 + 8 * c + 4);
+  const float f[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+  if constexpr (NORM) {
+    const f32x4 b0 = *reinterpret_cast<const f32x4*>(ils + 128 + kq * 32 + 8 * c);
+    const f32x4 b1 = *reinterpret_cast<const f32x4*>(ils + 128 + kq * 32 + 8 * c + 4);
+    const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+    for (int e = 0; e < 8; e++) out[e] = __builtin_fmaf((x[e] - mu) * rho, f[e], b[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; e++) out[e] = x[e] * f[e];
+  }
+}
+
+// NORM: X is the input of a LayerNorm whose affine carries the smoothing
+// (the norm-fused pass): x_hat = fma((x - mu) * rho, gamma', beta') with the
+// row's mean mu and 1/sqrt(var + eps) rho from `rowstat` (two floats per row)
+// and inv_lam pointing at gamma' = gamma * inv_lambda (K floats) followed by
+// beta' = beta * inv_lambda (K floats).
+template <int FMT, bool QUANT, bool DOWN, int RB, bool NORM>
 __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X, int M, int K,
                                                   const float* __restrict__ inv_lam,
+                                                  const float* __restrict__ rowstat,
                                                   const uint16_t* __restrict__ l1op,
                                                   uint8_t* __restrict__ codes,
                                                   void* __restrict__ scales,
@@ -56,9 +87,9 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
   constexpr bool LR = DOWN && RB > 0;
   // per wave: the 16 x 128 bf16 X chunk (4 KB, rows of 256 B whose 16-byte
   // pieces are XOR-swizzled by the row index) and the chunk's 128 inverse
-  // smoothing factors (512 B); after the loop the same memory holds the
-  // cross-wave T reduction
-  constexpr int WSTAGE = 4096 + 512;
+  // smoothing factors (512 B; NORM: 128 gamma' then 128 beta'); after the
+  // loop the same memory holds the cross-wave T reduction
+  constexpr int WSTAGE = 4096 + (NORM ? 1024 : 512);
   constexpr int LDS_BYTES = (LR && 256 * R > 4 * WSTAGE) ? 256 * R : 4 * WSTAGE;
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   const int lane = threadIdx.x & 63;
@@ -80,7 +111,7 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(X) + row0 * K, 0, static_cast<int>(static_cast<uint32_t>(nrows) * rowb), 0x00020000);
   const __amdgpu_buffer_rsrc_t ir =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(inv_lam), 0, K * 4, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(inv_lam), 0, (NORM ? 2 : 1) * K * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(l1op), 0, static_cast<int>(static_cast<uint32_t>(K) * R * 2), 0x00020000);
   // the 16 rows lie in one 32-row block of the code and FP4 scale layouts
@@ -104,7 +135,14 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
   // requested before the current one is processed.
   const int lrow = lane >> 4, piece = lane & 15;
   const uint32_t xoff = static_cast<uint32_t>(lrow) * rowb + piece * 16;
-  const uint32_t ioff = static_cast<uint32_t>(lane & 31) * 16;
+  const uint32_t ioff = static_cast<uint32_t>(lane & 31) * 16 + (NORM && lane >= 32 ? static_cast<uint32_t>(K) * 4 : 0u);
+  // NORM: the row's mean and reciprocal standard deviation
+  float mu = 0.f, rho = 0.f;
+  if constexpr (NORM) {
+    const long sr_row = min(row0 + row, static_cast<long>(M - 1));
+    mu = rowstat[2 * sr_row];
+    rho = rowstat[2 * sr_row + 1];
+  }
   // Two chunks of each wave are in flight while it processes a third: chunk
   // it + 8 is requested into the registers chunk it arrived in.
   const int it0 = part * cpp + wave;
@@ -115,7 +153,7 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
   // lies past the buffer's end, so it reads nothing and returns zeros.  The
   // compiler then counts the same number of loads in flight on every path and
   // its waits for the L1 operands never include a prefetch.
-  const int x_oob = nrows * static_cast<int>(rowb), i_oob = K * 4;
+  const int x_oob = nrows * static_cast<int>(rowb), i_oob = (NORM ? 2 : 1) * K * 4;
   auto fetch = [&](int c0, u32x4 (&x)[4], u32x4& iv) __attribute__((always_inline)) {
     const bool ok = c0 < c_end;
 #pragma unroll
@@ -135,7 +173,7 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
       const int r = 4 * c + lrow;
       *reinterpret_cast<u32x4*>(xs + r * 256 + ((piece ^ r) << 4)) = x[c];
     }
-    if (lane < 32) *reinterpret_cast<u32x4*>(xs + 4096 + lane * 16) = iv;
+    if (NORM || lane < 32) *reinterpret_cast<u32x4*>(xs + 4096 + lane * 16) = iv;
     // L1 operands of the chunk: one contiguous 1 KB block per (t block,
     // step), requested before the X prefetch (for up to 4 t blocks; wider
     // ranks load them next to their MFMAs).  The INT4 quantizer needs many
@@ -162,19 +200,7 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
     // lane (row, kq): elements kq * 32 .. + 31 of its row = pieces 4 kq .. 4 kq + 3
     float xh[32];
 #pragma unroll
-    for (int c = 0; c < 4; c++) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(xs + row * 256 + (((4 * kq + c) ^ row) << 4));
-      const f32x4 i0 = *reinterpret_cast<const f32x4*>(ils + kq * 32 + 8 * c);
-      const f32x4 i1 = *reinterpret_cast<const f32x4*>(ils + kq * 32 + 8 * c + 4);
-      xh[8 * c + 0] = bf16_lo(v.x) * i0.x;
-      xh[8 * c + 1] = bf16_hi(v.x) * i0.y;
-      xh[8 * c + 2] = bf16_lo(v.y) * i0.z;
-      xh[8 * c + 3] = bf16_hi(v.y) * i0.w;
-      xh[8 * c + 4] = bf16_lo(v.z) * i1.x;
-      xh[8 * c + 5] = bf16_hi(v.z) * i1.y;
-      xh[8 * c + 6] = bf16_lo(v.w) * i1.z;
-      xh[8 * c + 7] = bf16_hi(v.w) * i1.w;
-    }
+    for (int c = 0; c < 4; c++) x_hat8<NORM>(xs, ils, row, kq, c, mu, rho, xh + 8 * c);
 
     // bf16 of x_hat, rounded to nearest even (v_cvt_pk_bf16_f32): the A
     // operands of the down-projection, formed before the quantizer reuses xh
@@ -232,11 +258,8 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
           // xh holds rint(t) now: recompute x from the staged chunk
 #pragma unroll
           for (int c = 0; c < 4; c++) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(xs + row * 256 + (((4 * kq + c) ^ row) << 4));
-            const f32x4 i0 = *reinterpret_cast<const f32x4*>(ils + kq * 32 + 8 * c);
-            const f32x4 i1 = *reinterpret_cast<const f32x4*>(ils + kq * 32 + 8 * c + 4);
-            const float xv[8] = {bf16_lo(v.x) * i0.x, bf16_hi(v.x) * i0.y, bf16_lo(v.y) * i0.z, bf16_hi(v.y) * i0.w,
-                                 bf16_lo(v.z) * i1.x, bf16_hi(v.z) * i1.y, bf16_lo(v.w) * i1.z, bf16_hi(v.w) * i1.w};
+            float xv[8];
+            x_hat8<NORM>(xs, ils, row, kq, c, mu, rho, xv);
 #pragma unroll
             for (int e = 0; e < 8; e++) xh[8 * c + e] = rne_quotient(xv[e], s, r);
           }
@@ -394,14 +417,14 @@ static int choose_kparts(int M, int K, bool down, bool have_tpart, bool fp4) {
   return best;
 }
 
-template <int FMT, bool QUANT, bool DOWN>
+template <int FMT, bool QUANT, bool DOWN, bool NORM>
 static hipError_t launch_act_rb(int rb, const ActArgs& a, hipStream_t st) {
   const int kparts = choose_kparts(a.M, a.K, DOWN && rb > 0, a.tpart != nullptr, FMT == SVDQ_FP4_E2M1_G32_E8M0);
   dim3 grid(((a.M + 15) / 16) * kparts), block(256);
-#define SVDQ_ACT_CASE(RBV)                                                                              \
-  case RBV:                                                                                           \
-    hipLaunchKernelGGL((act_kernel<FMT, QUANT, DOWN, RBV>), grid, block, 0, st, a.X, a.M, a.K, a.inv_lam, \
-                       a.l1t, a.codes, a.scales, a.Tb, kparts, a.tpart);                             \
+#define SVDQ_ACT_CASE(RBV)                                                                                  \
+  case RBV:                                                                                               \
+    hipLaunchKernelGGL((act_kernel<FMT, QUANT, DOWN, RBV, NORM>), grid, block, 0, st, a.X, a.M, a.K, a.inv_lam, \
+                       a.rowstat, a.l1t, a.codes, a.scales, a.Tb, kparts, a.tpart);                      \
     break;
   switch (rb) {
     SVDQ_ACT_CASE(0) SVDQ_ACT_CASE(1) SVDQ_ACT_CASE(2) SVDQ_ACT_CASE(3) SVDQ_ACT_CASE(4)
@@ -419,14 +442,83 @@ static hipError_t launch_act_rb(int rb, const ActArgs& a, hipStream_t st) {
 
 hipError_t launch_act(int fmt, bool quant, bool down, const ActArgs& a, hipStream_t st) {
   const int rb = down ? a.rank / 16 : 0;
-  if (fmt == SVDQ_INT4_G64_FP16) {
-    if (quant && down) return launch_act_rb<SVDQ_INT4_G64_FP16, true, true>(rb, a, st);
-    if (quant) return launch_act_rb<SVDQ_INT4_G64_FP16, true, false>(0, a, st);
-    return launch_act_rb<SVDQ_INT4_G64_FP16, false, true>(rb, a, st);
+  if (a.rowstat) {
+    // the norm-fused pass exists with quantization (and the down-projection
+    // where the layer has a rank)
+    if (!quant) return hipErrorInvalidValue;
+    if (fmt == SVDQ_INT4_G64_FP16)
+      return down ? launch_act_rb<SVDQ_INT4_G64_FP16, true, true, true>(rb, a, st)
+                  : launch_act_rb<SVDQ_INT4_G64_FP16, true, false, true>(0, a, st);
+    return down ? launch_act_rb<SVDQ_FP4_E2M1_G32_E8M0, true, true, true>(rb, a, st)
+                : launch_act_rb<SVDQ_FP4_E2M1_G32_E8M0, true, false, true>(0, a, st);
   }
-  if (quant && down) return launch_act_rb<SVDQ_FP4_E2M1_G32_E8M0, true, true>(rb, a, st);
-  if (quant) return launch_act_rb<SVDQ_FP4_E2M1_G32_E8M0, true, false>(0, a, st);
-  return launch_act_rb<SVDQ_FP4_E2M1_G32_E8M0, false, true>(rb, a, st);
+  if (fmt == SVDQ_INT4_G64_FP16) {
+    if (quant && down) return launch_act_rb<SVDQ_INT4_G64_FP16, true, true, false>(rb, a, st);
+    if (quant) return launch_act_rb<SVDQ_INT4_G64_FP16, true, false, false>(0, a, st);
+    return launch_act_rb<SVDQ_INT4_G64_FP16, false, true, false>(rb, a, st);
+  }
+  if (quant && down) return launch_act_rb<SVDQ_FP4_E2M1_G32_E8M0, true, true, false>(rb, a, st);
+  if (quant) return launch_act_rb<SVDQ_FP4_E2M1_G32_E8M0, true, false, false>(0, a, st);
+  return launch_act_rb<SVDQ_FP4_E2M1_G32_E8M0, false, true, false>(rb, a, st);
+}
+
+// Row statistics of the norm-fused pass: blocks below ceil(M / 4) give each
+// wave one row: mu = (sum x) / K and rho = 1 / sqrt((sum (x - mu)^2) / K + eps),
+// fp32 sums of 16-byte loads per lane in a fixed order, then a fixed
+// butterfly across the wave; the remaining blocks fold the smoothing into the
+// norm's affine: gamma'[k] = gamma[k] * inv_lambda[k], beta'[k] = beta[k] *
+// inv_lambda[k] (beta = 0 when absent), each rounded once to fp32.
+__global__ __launch_bounds__(256) void norm_stats_kernel(const uint16_t* __restrict__ X, int M, int K, float eps,
+                                                         const uint16_t* __restrict__ gamma,
+                                                         const uint16_t* __restrict__ beta,
+                                                         const float* __restrict__ inv_lam, float* __restrict__ rowstat,
+                                                         float* __restrict__ fold) {
+  const int row_blocks = (M + 3) / 4;
+  if (static_cast<int>(blockIdx.x) >= row_blocks) {
+    const int k = (static_cast<int>(blockIdx.x) - row_blocks) * 256 + static_cast<int>(threadIdx.x);
+    if (k < K) {
+      const float inv = inv_lam[k];
+      fold[k] = __uint_as_float(static_cast<uint32_t>(gamma[k]) << 16) * inv;
+      fold[K + k] = beta ? __uint_as_float(static_cast<uint32_t>(beta[k]) << 16) * inv : 0.f;
+    }
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const long r = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= M) return;
+  const u32x4* xr = reinterpret_cast<const u32x4*>(X + r * K);
+  const int nv = K / 8;                          // 16-byte vectors per row
+  float s = 0.f;
+  for (int i = lane; i < nv; i += 64) {
+    const u32x4 v = xr[i];
+    s += bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) + bf16_lo(v.z) + bf16_hi(v.z) + bf16_lo(v.w) +
+         bf16_hi(v.w);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  const float mu = s / static_cast<float>(K);
+  float q = 0.f;
+  for (int i = lane; i < nv; i += 64) {
+    const u32x4 v = xr[i];
+    const float d[8] = {bf16_lo(v.x) - mu, bf16_hi(v.x) - mu, bf16_lo(v.y) - mu, bf16_hi(v.y) - mu,
+                        bf16_lo(v.z) - mu, bf16_hi(v.z) - mu, bf16_lo(v.w) - mu, bf16_hi(v.w) - mu};
+#pragma unroll
+    for (int e = 0; e < 8; e++) q = __builtin_fmaf(d[e], d[e], q);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) q += __shfl_xor(q, o);
+  if (lane == 0) {
+    rowstat[2 * r] = mu;
+    rowstat[2 * r + 1] = 1.0f / __builtin_sqrtf(q / static_cast<float>(K) + eps);
+  }
+}
+
+hipError_t launch_norm_stats(const uint16_t* X, int M, int K, float eps, const uint16_t* gamma, const uint16_t* beta,
+                             const float* inv_lam, float* rowstat, float* fold, hipStream_t st) {
+  const int blocks = (M + 3) / 4 + (K + 255) / 256;
+  hipLaunchKernelGGL(norm_stats_kernel, dim3(blocks), dim3(256), 0, st, X, M, K, eps, gamma, beta, inv_lam, rowstat,
+                     fold);
+  return hipGetLastError();
 }
 
 // Calibration statistic: absmax[j] = max_i |X[i, j]|.  Non-negative floats

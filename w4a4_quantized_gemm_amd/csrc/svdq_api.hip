@@ -75,8 +75,32 @@ BlobPtrs blob_ptrs(const svdq_layer_desc& d, const void* prepared) {
   return p;
 }
 
+// LayerNorm of the norm-fused pass (gamma == nullptr: none).
+struct NormArgs {
+  const void* gamma = nullptr;
+  const void* beta = nullptr;
+  float eps = 0.f;
+};
+
+bool norm_ok(const NormArgs& n) { return n.gamma && n.eps > 0.f && n.eps < 3.0e38f; }
+
+// The norm-fused pass's statistics and folded affine into the workspace;
+// points the activation arguments at them.
+svdq_status setup_norm(const svdq_layer_desc& d, const NormArgs& n, const void* X, int M, uint8_t* w,
+                       const ActLayout& A, ActArgs& a, hipStream_t s) {
+  float* rowstat = reinterpret_cast<float*>(w + A.rowstat);
+  float* fold = reinterpret_cast<float*>(w + A.fold);
+  svdq_status st = from_hip(launch_norm_stats(static_cast<const uint16_t*>(X), M, d.K, n.eps,
+                                              static_cast<const uint16_t*>(n.gamma),
+                                              static_cast<const uint16_t*>(n.beta), a.inv_lam, rowstat, fold, s));
+  a.rowstat = rowstat;
+  a.inv_lam = fold;
+  return st;
+}
+
 svdq_status run_layer(const svdq_layer_desc* desc, const void* prepared, const void* X, int M, void* Y,
-                      int out_dtype, void* ws, size_t ws_bytes, void* stream, bool unfused) {
+                      int out_dtype, void* ws, size_t ws_bytes, void* stream, bool unfused,
+                      const NormArgs& norm = NormArgs()) {
   svdq_status st = validate_runtime(desc, prepared, X, M);
   if (st != SVDQ_OK) return st;
   if (!Y || !ws) return SVDQ_ERR_INVALID_ARGUMENT;
@@ -99,6 +123,8 @@ svdq_status run_layer(const svdq_layer_desc* desc, const void* prepared, const v
   a.scales = w + A.scales;
   a.Tb = reinterpret_cast<uint16_t*>(w + A.tb);
   a.tpart = reinterpret_cast<float*>(w + A.tpart);
+  const hipStream_t s = as_stream(stream);
+  if (norm.gamma && (st = setup_norm(*desc, norm, X, M, w, A, a, s)) != SVDQ_OK) return st;
 
   GemmArgs g{};
   g.acodes = a.codes;
@@ -114,7 +140,6 @@ svdq_status run_layer(const svdq_layer_desc* desc, const void* prepared, const v
   g.N = desc->N;
   g.rank = desc->rank;
 
-  const hipStream_t s = as_stream(stream);
   if (!unfused) {
     if ((st = from_hip(launch_act(desc->fmt, true, desc->rank > 0, a, s))) != SVDQ_OK) return st;
     return from_hip(launch_gemm(desc->fmt, desc->rank > 0, out_dtype, g, s));
@@ -242,6 +267,52 @@ svdq_status svdq_gemm(const svdq_layer_desc* desc, const void* d_prepared, const
   g.N = desc->N;
   g.rank = desc->rank;
   return from_hip(launch_gemm(desc->fmt, desc->rank > 0, out_dtype, g, as_stream(stream)));
+}
+
+svdq_status svdq_quantize_act_ln(const svdq_layer_desc* desc, const void* d_prepared, const void* d_X,
+                                 const void* d_gamma, const void* d_beta, float eps, int M, void* d_codes,
+                                 void* d_scales, void* d_T, void* d_workspace, size_t ws_bytes, void* stream) {
+  svdq_status st = validate_runtime(desc, d_prepared, d_X, M);
+  if (st != SVDQ_OK) return st;
+  NormArgs n;
+  n.gamma = d_gamma;
+  n.beta = d_beta;
+  n.eps = eps;
+  if (!norm_ok(n) || !d_codes || !d_scales || !d_workspace || (desc->rank > 0 && !d_T)) return SVDQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(d_codes) || !aligned16(d_scales) || !aligned16(d_workspace) || (d_T && !aligned16(d_T)))
+    return SVDQ_ERR_MISALIGNED;
+  const ActLayout A = act_layout(*desc, M);
+  if (ws_bytes < A.total) return SVDQ_ERR_BUFFER_TOO_SMALL;
+  if ((st = check_device()) != SVDQ_OK) return st;
+  const BlobPtrs bp = blob_ptrs(*desc, d_prepared);
+  uint8_t* w = static_cast<uint8_t*>(d_workspace);
+  ActArgs a;
+  a.X = static_cast<const uint16_t*>(d_X);
+  a.M = M;
+  a.K = desc->K;
+  a.rank = desc->rank;
+  a.inv_lam = bp.inv_lam;
+  a.l1t = bp.l1t;
+  a.codes = static_cast<uint8_t*>(d_codes);
+  a.scales = d_scales;
+  a.Tb = static_cast<uint16_t*>(d_T);
+  a.tpart = reinterpret_cast<float*>(w + A.tpart);
+  const hipStream_t s = as_stream(stream);
+  if ((st = setup_norm(*desc, n, d_X, M, w, A, a, s)) != SVDQ_OK) return st;
+  return from_hip(launch_act(desc->fmt, true, desc->rank > 0, a, s));
+}
+
+svdq_status svdq_linear_ln(const svdq_layer_desc* desc, const void* d_prepared, const void* d_X, const void* d_gamma,
+                           const void* d_beta, float eps, int M, void* d_Y, int out_dtype, void* d_workspace,
+                           size_t ws_bytes, void* stream) {
+  NormArgs n;
+  n.gamma = d_gamma;
+  n.beta = d_beta;
+  n.eps = eps;
+  svdq_status st = validate_runtime(desc, d_prepared, d_X, M);
+  if (st != SVDQ_OK) return st;
+  if (!norm_ok(n)) return SVDQ_ERR_INVALID_ARGUMENT;
+  return run_layer(desc, d_prepared, d_X, M, d_Y, out_dtype, d_workspace, ws_bytes, stream, false, n);
 }
 
 svdq_status svdq_linear(const svdq_layer_desc* desc, const void* d_prepared, const void* d_X, int M, void* d_Y,

@@ -49,7 +49,7 @@ svdq_blob_layout layout_of(const svdq_layer_desc& d);
 
 // Activation-side buffers inside a workspace: packed codes, scales, Tb.
 struct ActLayout {
-  uint64_t codes, scales, tb, tpart, total;
+  uint64_t codes, scales, tb, tpart, rowstat, fold, total;
   uint64_t codes_bytes, scales_bytes, tb_bytes;
 };
 ActLayout act_layout(const svdq_layer_desc& d, int M);

@@ -19,6 +19,7 @@ struct ActArgs {
   void* scales;           // M x K/g (fp16 bits or E8M0 bytes)
   uint16_t* Tb;           // M x rank bf16
   float* tpart;           // kMaxKParts x M x rank fp32 partial T (workspace), or null: K is not split
+  const float* rowstat = nullptr;  // norm-fused pass: M x {mean, 1/std}; inv_lam then holds gamma', beta' (2K)
 };
 
 // Compute units of the current device (cached per device).
@@ -26,6 +27,10 @@ int device_cu_count();
 
 // quant: write codes + scales; down: write Tb.
 hipError_t launch_act(int fmt, bool quant, bool down, const ActArgs& a, hipStream_t st);
+// Row mean and 1/sqrt(var + eps) of X (M x {mu, rho}) and the norm's affine
+// with the smoothing folded in (gamma' then beta', 2K floats).
+hipError_t launch_norm_stats(const uint16_t* X, int M, int K, float eps, const uint16_t* gamma, const uint16_t* beta,
+                             const float* inv_lam, float* rowstat, float* fold, hipStream_t st);
 hipError_t launch_absmax(const uint16_t* X, int M, int K, float* out, bool accumulate, hipStream_t st);
 
 struct GemmArgs {

@@ -72,6 +72,11 @@ ActLayout act_layout(const svdq_layer_desc& d, int M) {
   // fp32 partial T of the K parts of the activation pass (at most kMaxKParts)
   A.tpart = off;
   off = align256(off + (m <= kSplitMaxM ? uint64_t(kMaxKParts) * m * uint64_t(d.rank) * 4 : 0));
+  // norm-fused pass: per-row mean and 1/std, then gamma' and beta'
+  A.rowstat = off;
+  off = align256(off + m * 8);
+  A.fold = off;
+  off = align256(off + K * 8);
   A.total = off;
   return A;
 }

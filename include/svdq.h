@@ -280,6 +280,19 @@ svdq_status svdq_linear_ln(const svdq_layer_desc* desc, const void* d_prepared, 
                            const void* d_gamma, const void* d_beta, float eps, int M, void* d_Y,
                            int out_dtype, void* d_workspace, size_t ws_bytes, void* stream);
 
+/* The weight-only 4-bit layer (4-bit weights, 16-bit activations) for a few
+ * token rows (diffusers page: the second operator, used for the
+ * adaptive-norm and modulation projections next to the W4A4 layers):
+ *   Y = round(x_hat dequant(Q(R)) + b),  x_hat = fp32(X * inv_lambda)
+ * on a blob prepared with rank 0 (R = W_hat: the smoothed weight itself);
+ * the activations are not quantized; accumulation in fp32 (deterministic
+ * order).  M <= 16 and desc->rank == 0, else SVDQ_ERR_UNSUPPORTED_SHAPE.
+ * d_workspace: svdq_workspace_bytes(desc, M, 0) bytes (partial outputs of a
+ * K split).  Asynchronous. */
+svdq_status svdq_linear_w4a16(const svdq_layer_desc* desc, const void* d_prepared, const void* d_X,
+                              int M, void* d_Y, int out_dtype, void* d_workspace, size_t ws_bytes,
+                              void* stream);
+
 /* The GEMM stage of svdq_linear on its own: Y = Q(x_hat) Q(R) + Tb L2b + b
  * from activations already produced by svdq_quantize_act with the same blob
  * (d_codes, d_scales, d_T in its output layouts; d_T may be NULL when

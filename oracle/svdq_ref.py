@@ -451,6 +451,23 @@ def linear(prep: dict, X_bits, out: str = "bf16", norm=None) -> dict:
     return dict(Y64=Y64, Y=_round_out(Y64, out), main=main, low=low, Tb=Tb, T=T, act=qa)
 
 
+def linear_w4a16(prep: dict, X_bits, out: str = "bf16") -> dict:
+    """Weight-only 4-bit layer (16-bit activations): Y = x_hat dequant(Q(R)) + b.
+
+    [diffusers] page: next to the W4A4 operator for the attention and MLP
+    layers, the engine runs a second one with 4-bit weights and 16-bit
+    activations for the adaptive-norm and modulation projections.  Reading: the prepared layer with rank 0 (R = W_hat), the same
+    smoothing x_hat = fp32(x * inv_lambda) and the same weight codes and
+    scales; the activations are not quantized; the product in fp64.
+    """
+    assert prep["rank"] == 0
+    xh = smooth_act(X_bits, prep["inv32"])
+    Wdq = dequant_groups(prep["w_codes"].T, prep["w_scales"].T, prep["fmt"]).T
+    bias = 0.0 if prep["bias"] is None else prep["bias"][None, :]
+    Y64 = xh @ Wdq + bias
+    return dict(Y64=Y64, Y=_round_out(Y64, out), xhat=xh)
+
+
 def linear_unfused(prep: dict, X_bits, out: str = "bf16", norm=None) -> dict:
     """Unfused rounding model: Yp = round(main + b); Y = round(Yp + Tb L2b)."""
     r = linear(prep, X_bits, out, norm)

@@ -108,6 +108,14 @@ def test_runtime_validation_before_device():
     assert merge(ctypes.byref(d), good, good, good, 16, out + 8, pb48, None) == 7
     assert merge(ctypes.byref(d), good, good, good, 16, out, pb48 - 1, None) == 4
     assert merge(ctypes.byref(d), good, good, good, 16, good + 4096, pb48, None) == 1
+    # the weight-only layer: rank-0 blobs and at most 16 rows
+    d0 = _desc(r=0)
+    ws0 = S.svdq_workspace_bytes(d0, 16)
+    w16 = lib.svdq_linear_w4a16
+    assert w16(ctypes.byref(d), good, good, 4, good, 0, good, ws, None) == 2
+    assert w16(ctypes.byref(d0), good, good, 17, good, 0, good, S.svdq_workspace_bytes(d0, 17), None) == 2
+    assert w16(ctypes.byref(d0), good, good, 16, None, 0, good, ws0, None) == 1
+    assert w16(ctypes.byref(d0), good, good, 16, good, 0, good, ws0 - 1, None) == 4
     # the norm-fused calls: gamma required, eps > 0 and finite, workspace required
     ln = lib.svdq_linear_ln
     assert ln(ctypes.byref(d), good, good, None, None, 1e-5, 4608, good, 0, good, ws, None) == 1

@@ -280,6 +280,31 @@ def test_merge_lowrank(torch_dev, fmt, re):
     _say(f"  rel errors {errs}")
 
 
+@pytest.mark.parametrize("fmt", [O.INT4, O.FP4])
+@pytest.mark.parametrize("M,K,N", [(1, 3072, 576), (3, 1024, 320), (16, 4096, 192), (16, 1024, 9216)])
+def test_w4a16(torch_dev, fmt, M, K, N):
+    """The weight-only 4-bit layer on a rank-0 blob against the oracle's
+    weight-only layer (x_hat unquantized, fp64 product): only the fp32
+    accumulation order differs, so the f32 output agrees to 1e-5."""
+    import w4a4_quantized_gemm_amd as S
+    torch, dev = torch_dev
+    _say(f"case: w4a16 fmt={fmt} M={M} K={K} N={N}")
+    cfg = WL.C2.with_(name="w4a16", M=max(M, 64), K=K, N=N, rank=0, fmt=fmt, w_std=1 / np.sqrt(K),
+                      n_outlier_channels=8, bias_std=0.02, seed=M + K)
+    X_bits, W_bits, b_bits = WL.make_layer(cfg)
+    layer, Xfull, _ = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
+    sec, ref = _check_weights(layer, W_bits, fmt, b_bits)
+    X = Xfull[:M].contiguous()
+    ws = torch.empty(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev)
+    for out, oname in ((S.OUT_F32, "f32"), (S.OUT_BF16, "bf16")):
+        Y = torch.empty((M, N), dtype=torch.float32 if out == S.OUT_F32 else torch.bfloat16, device=dev)
+        S.svdq_linear_w4a16(layer.desc, layer.blob, X, Y, ws, out)
+        torch.cuda.synchronize()
+        r = O.linear_w4a16(ref, X_bits[:M], oname)
+        e = O.rel_fro(Y.float().cpu().numpy().astype(np.float64), r["Y"])
+        assert e <= (1e-5 if oname == "f32" else TOL), (oname, e)
+
+
 E2M1_MIDPOINTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
 
 

@@ -523,3 +523,26 @@ def test_norm_act_invariances_and_fold():
     assert np.max(np.abs(lhs - rhs)) <= 1e-6 * np.max(np.abs(rhs))
     # smoothing applied the other way round (times lambda) would break the fold
     assert np.max(np.abs(O.norm_act(_bits(x), _bits(g), _bits(b), eps, lam32) @ (lam32[:, None] * W) - rhs)) > 0.1
+
+
+@pytest.mark.parametrize("fmt", [O.INT4, O.FP4])
+def test_w4a16_exact_when_weights_are_on_the_grid(fmt):
+    """Weights already on the 4-bit grid with a full-range element in every
+    group (so every scale is 1, or 2^e for FP4) and no smoothing: the
+    weight-only layer is exactly X W for any bf16 X, which the W4A4 layer
+    (activations rounded to 4 bits) is not."""
+    rng = np.random.default_rng(24)
+    M, K, N = 5, 128, 12
+    if fmt == O.INT4:
+        W = rng.integers(-7, 8, (K, N)).astype(np.float64)
+        W[::64, :] = 7
+    else:
+        W = rng.choice(np.concatenate([O.E2M1_GRID, -O.E2M1_GRID]), (K, N)) * 4.0
+        W[::32, :] = 24.0                          # 6 * 2^2: the group exponent is 2
+    X = O.to_bf16(rng.standard_normal((M, K)))
+    Wb = O.bf16_bits_of(W.astype(np.float32))
+    Xb = O.bf16_bits_of(X.astype(np.float32))
+    prep = O.prepare(Wb, O.act_absmax(Xb), alpha=0.5, rank=0, fmt=fmt, no_smoothing=True)
+    y = O.linear_w4a16(prep, Xb, out="f32")["Y64"]
+    assert np.allclose(y, X @ W, rtol=1e-13, atol=1e-12)
+    assert not np.allclose(O.linear(prep, Xb, out="f32")["Y64"], X @ W, rtol=1e-6, atol=1e-6)

@@ -35,7 +35,7 @@ STATUS_NAMES = {
 EXPORTED = (
     "svdq_status_string", "svdq_version", "svdq_prepared_bytes", "svdq_workspace_bytes",
     "svdq_act_sizes", "svdq_act_absmax", "svdq_prepare_weights", "svdq_merge_lowrank", "svdq_check_blob",
-    "svdq_quantize_act", "svdq_quantize_act_ln", "svdq_gemm", "svdq_linear", "svdq_linear_ln",
+    "svdq_quantize_act", "svdq_quantize_act_ln", "svdq_gemm", "svdq_linear", "svdq_linear_ln", "svdq_linear_w4a16",
     "svdq_linear_unfused", "svdq_blob_layout_of",
 )
 
@@ -87,6 +87,7 @@ def _lib() -> ctypes.CDLL:
             "svdq_quantize_act_ln": ([D, P, P, P, P, F, I, P, P, P, P, Z, P], S),
             "svdq_gemm": ([D, P, P, P, P, I, P, I, P], S),
             "svdq_linear_ln": ([D, P, P, P, P, F, I, P, I, P, Z, P], S),
+            "svdq_linear_w4a16": ([D, P, P, I, P, I, P, Z, P], S),
             "svdq_linear": ([D, P, P, I, P, I, P, Z, P], S),
             "svdq_linear_unfused": ([D, P, P, I, P, I, P, Z, P], S),
             "svdq_blob_layout_of": ([D, ctypes.POINTER(BlobLayout)], S),
@@ -205,6 +206,13 @@ def svdq_linear_ln(desc: LayerDesc, prepared, X, gamma, beta, eps: float, Y, wor
     _check(_lib().svdq_linear_ln(ctypes.byref(desc), _ptr(prepared), _ptr(X), _ptr(gamma), _ptr(beta), float(eps),
                                  M, _ptr(Y), out_dtype, _ptr(workspace), workspace.numel(), _stream(stream)),
            "svdq_linear_ln")
+
+
+def svdq_linear_w4a16(desc: LayerDesc, prepared, X, Y, workspace, out_dtype: int = OUT_BF16, stream=None):
+    """The weight-only 4-bit layer (rank-0 blob, M <= 16 rows, bf16 activations)."""
+    M = X.shape[0]
+    _check(_lib().svdq_linear_w4a16(ctypes.byref(desc), _ptr(prepared), _ptr(X), M, _ptr(Y), out_dtype,
+                                    _ptr(workspace), workspace.numel(), _stream(stream)), "svdq_linear_w4a16")
 
 
 def svdq_gemm(desc: LayerDesc, prepared, codes, scales, T, M: int, Y, out_dtype: int = OUT_BF16,

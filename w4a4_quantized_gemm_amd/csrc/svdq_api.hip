@@ -315,6 +315,33 @@ svdq_status svdq_linear_ln(const svdq_layer_desc* desc, const void* d_prepared, 
   return run_layer(desc, d_prepared, d_X, M, d_Y, out_dtype, d_workspace, ws_bytes, stream, false, n);
 }
 
+svdq_status svdq_linear_w4a16(const svdq_layer_desc* desc, const void* d_prepared, const void* d_X, int M,
+                              void* d_Y, int out_dtype, void* d_workspace, size_t ws_bytes, void* stream) {
+  svdq_status st = validate_runtime(desc, d_prepared, d_X, M);
+  if (st != SVDQ_OK) return st;
+  if (desc->rank != 0 || M > kW4A16MaxM) return SVDQ_ERR_UNSUPPORTED_SHAPE;
+  if (!d_Y || !d_workspace) return SVDQ_ERR_INVALID_ARGUMENT;
+  if (out_dtype != SVDQ_OUT_BF16 && out_dtype != SVDQ_OUT_F32) return SVDQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(d_Y) || !aligned16(d_workspace)) return SVDQ_ERR_MISALIGNED;
+  const ActLayout A = act_layout(*desc, M);
+  if (ws_bytes < A.total) return SVDQ_ERR_BUFFER_TOO_SMALL;
+  if ((st = check_device()) != SVDQ_OK) return st;
+  const BlobPtrs bp = blob_ptrs(*desc, d_prepared);
+  W4A16Args a;
+  a.X = static_cast<const uint16_t*>(d_X);
+  a.M = M;
+  a.K = desc->K;
+  a.N = desc->N;
+  a.inv_lam = bp.inv_lam;
+  a.wcodes = bp.wcodes;
+  a.wscales = bp.wscales;
+  a.bias = bp.bias;
+  a.Y = d_Y;
+  a.out_f32 = out_dtype == SVDQ_OUT_F32;
+  a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(d_workspace) + A.w4a16);
+  return from_hip(launch_w4a16(desc->fmt, a, as_stream(stream)));
+}
+
 svdq_status svdq_linear(const svdq_layer_desc* desc, const void* d_prepared, const void* d_X, int M, void* d_Y,
                         int out_dtype, void* d_workspace, size_t ws_bytes, void* stream) {
   return run_layer(desc, d_prepared, d_X, M, d_Y, out_dtype, d_workspace, ws_bytes, stream, false);

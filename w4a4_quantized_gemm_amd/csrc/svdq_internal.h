@@ -49,9 +49,18 @@ svdq_blob_layout layout_of(const svdq_layer_desc& d);
 
 // Activation-side buffers inside a workspace: packed codes, scales, Tb.
 struct ActLayout {
-  uint64_t codes, scales, tb, tpart, rowstat, fold, total;
+  uint64_t codes, scales, tb, tpart, rowstat, fold, w4a16, total;
   uint64_t codes_bytes, scales_bytes, tb_bytes;
 };
 ActLayout act_layout(const svdq_layer_desc& d, int M);
+
+// Weight-only (W4A16) layer for small M: rows are padded to kW4A16Rows[b]
+// (1, 2, 4, 8 or 16), K is split into w4a16_ksplit parts (a divisor of
+// K / 64) so that a part's fp32 activations fit the kernel's LDS and there
+// are enough workgroups; with more than one part the fp32 partial outputs
+// (parts x M x N) sit in the workspace.
+constexpr int kW4A16MaxM = 16;
+int w4a16_rows(int M);
+int w4a16_ksplit(int M, int K, int N);
 
 }  // namespace svdq

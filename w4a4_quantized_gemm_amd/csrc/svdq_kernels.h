@@ -50,6 +50,20 @@ hipError_t launch_gemm(int fmt, bool slab, int out_dtype, const GemmArgs& g, hip
 // the FP4 variant (persistent, block-scaled MFMA); launch_gemm dispatches to it
 hipError_t launch_gemm_fp4(bool slab, int out_dtype, const GemmArgs& g, hipStream_t st);
 
+struct W4A16Args {
+  const uint16_t* X;      // M x K bf16 (M <= kW4A16MaxM)
+  int M, K, N;
+  const float* inv_lam;   // K
+  const uint8_t* wcodes;  // N x K/2 (operand-block order)
+  const void* wscales;
+  const float* bias;      // N or null
+  void* Y;                // M x N
+  int out_f32;
+  float* part;            // fp32 partial outputs of the K parts (workspace), when w4a16_ksplit > 1
+};
+// The weight-only 4-bit layer (rank 0 blob), small M.
+hipError_t launch_w4a16(int fmt, const W4A16Args& a, hipStream_t st);
+
 // Unfused up-projection: Y = round(Y + Tb L2b) in place.
 hipError_t launch_up(int out_dtype, const uint16_t* Tb, const uint16_t* l2t, void* Y, int M, int N,
                      int rank, hipStream_t st);

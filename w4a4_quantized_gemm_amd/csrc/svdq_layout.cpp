@@ -77,8 +77,35 @@ ActLayout act_layout(const svdq_layer_desc& d, int M) {
   off = align256(off + m * 8);
   A.fold = off;
   off = align256(off + K * 8);
+  // weight-only layer: fp32 partial outputs of its K parts
+  A.w4a16 = off;
+  if (d.rank == 0 && M <= kW4A16MaxM) {
+    const int ks = w4a16_ksplit(M, d.K, d.N);
+    off = align256(off + (ks > 1 ? uint64_t(ks) * m * uint64_t(d.N) * 4 : 0));
+  }
   A.total = off;
   return A;
+}
+
+int w4a16_rows(int M) {
+  int r = 1;
+  while (r < M) r *= 2;
+  return r;
+}
+
+// The smallest number of parts (a divisor of K / 64) such that a part's fp32
+// activations (rows x K / parts) fit 64 KB of LDS and either there are at
+// least 512 workgroups of 32 columns or a part is at most 8 blocks of 64.
+int w4a16_ksplit(int M, int K, int N) {
+  const int rows = w4a16_rows(M), kb = K / 64, nb = N / 32;
+  int ks = 1;
+  for (int d = 1; d <= kb; d++) {
+    if (kb % d) continue;
+    ks = d;
+    const bool fits = static_cast<long>(kb / d) * 64 * rows * 4 <= 65536;
+    if (fits && (static_cast<long>(nb) * d >= 512 || kb / d <= 8)) break;
+  }
+  return ks;
 }
 
 }  // namespace svdq

@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--summarize-util", nargs="+", metavar="PMC_DIR",
                     help="write profiles/gemm_<workload>_mfma_counters.json from rocprofv3 --pmc runs of "
                          "--profile-only (SQ / GRBM / TCC counters; one directory per pass)")
+    ap.add_argument("--no-w4a16", dest="w4a16", action="store_false",
+                    help="skip timing the weight-only layer on the modulation projection's shape")
     ap.add_argument("--no-norm", dest="norm", action="store_false",
                     help="skip timing the LayerNorm-fused layer against a separate norm pass")
     ap.add_argument("--lora", type=int, default=16,
@@ -188,6 +190,56 @@ def time_norm(torch, S, rig, steps, warmup, eps=1e-6):
         torch.cuda.synchronize()
         out.append(e0.elapsed_time(e1) / steps)
     return out[0], out[1]
+
+
+W4A16_SHAPES = ((1, 3072, 18432), (16, 3072, 18432))   # AdaLN modulation projection: one sample / a batch of 16
+
+
+def time_w4a16(torch, S, WL, to_tensor, steps, warmup, fmt="int4"):
+    """The weight-only 4-bit layer on the modulation projection's shape
+    (3072 -> 6 x 3072), against torch's bf16 matmul of the same weights and
+    the W4A4 layer (rank 0) at the same M.  Enough blob copies rotate to
+    defeat the Infinity Cache.  Returns one dict per M."""
+    res = []
+    for M, K, N in W4A16_SHAPES:
+        cfg = WL.C2.with_(name="w4a16", M=64, K=K, N=N, rank=0, fmt=fmt, w_std=1 / K ** 0.5, bias_std=0.02, seed=5)
+        X_bits, W_bits, b_bits = WL.make_layer(cfg)
+        dev = "cuda:0"
+        Xf, W, b = to_tensor(X_bits, dev), to_tensor(W_bits, dev), to_tensor(b_bits, dev)
+        a = torch.empty(K, dtype=torch.float32, device=dev)
+        S.svdq_act_absmax(Xf, a)
+        layer = S.SVDQLinear.prepare(W, a, 0, fmt, cfg.alpha, bias=b)
+        X = Xf[:M].contiguous()
+        ncopy = max(2, -(-2 * INFINITY_CACHE // layer.blob.numel()))
+        blobs = [layer.blob] + [layer.blob.clone() for _ in range(ncopy - 1)]
+        nw = max(2, -(-2 * INFINITY_CACHE // (W.numel() * 2)))
+        Ws = [W] + [W.clone() for _ in range(nw - 1)]
+        ws = torch.empty(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev)
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+        def run(fn, n):
+            for k in range(warmup):
+                fn(k % n)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for k in range(steps):
+                fn(k % n)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / steps * 1e3
+
+        us = run(lambda i: S.svdq_linear_w4a16(layer.desc, blobs[i], X, Y, ws, S.OUT_BF16), len(blobs))
+        ws4 = torch.empty(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev)
+        us_w4a4 = run(lambda i: S.svdq_linear(layer.desc, blobs[i], X, Y, ws4, S.OUT_BF16), len(blobs))
+        us_bf16 = run(lambda i: torch.matmul(X, Ws[i]), len(Ws))
+        wbytes = K * N // 2 + (K // (64 if fmt == "int4" else 32)) * N * (2 if fmt == "int4" else 1)
+        res.append({"M": M, "K": K, "N": N, "format": fmt, "us": us, "weight_gbs": wbytes / (us * 1e-6) / 1e9,
+                    "frac_hbm": wbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, "us_bf16_matmul": us_bf16,
+                    "us_w4a4_rank0": us_w4a4})
+        del blobs, Ws, layer, W, Xf
+        torch.cuda.empty_cache()
+    return res
 
 
 def time_kernels(torch, S, rig, steps, warmup):
@@ -570,6 +622,8 @@ def main():
             extra[name]["us_per_layer_norm_separate"] = rr["ms_norm"][1] * 1e3
         del rr
         torch.cuda.empty_cache()
+    if args.w4a16:
+        line["w4a16_modulation"] = time_w4a16(torch, S, WL, to_tensor, min(args.steps, 200), args.warmup)
     if args.lora:
         rr = run_config(args, cfg, torch, S, WL, to_tensor, with_cpu=False, lora=args.lora)
         extra[f"{cfg.name}+lora{args.lora}"] = {

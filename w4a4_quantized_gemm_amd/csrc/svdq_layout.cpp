@@ -95,9 +95,9 @@ int w4a16_rows(int M) {
 
 // The smallest number of parts (a divisor of K / 64) such that a part's fp32
 // activations (rows x K / parts) fit 64 KB of LDS and either there are at
-// least 512 workgroups of 32 columns or a part is at most 8 blocks of 64.
+// least 512 workgroups of 128 columns or a part is at most 8 blocks of 64.
 int w4a16_ksplit(int M, int K, int N) {
-  const int rows = w4a16_rows(M), kb = K / 64, nb = N / 32;
+  const int rows = w4a16_rows(M), kb = K / 64, nb = (N / 32 + 3) / 4;   // workgroups of 4 x 32 columns
   int ks = 1;
   for (int d = 1; d <= kb; d++) {
     if (kb % d) continue;

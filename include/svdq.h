@@ -195,6 +195,26 @@ svdq_status svdq_prepare_weights(const svdq_layer_desc* desc, const void* d_W,
                                  const void* d_L1, const void* d_L2, void* d_prepared,
                                  size_t prepared_bytes, void* stream);
 
+/* svdq_prepare_weights with the residual quantized by GPTQ instead of
+ * round-to-nearest (walkthrough, Table 3 row: GPTQ on the residual gives a
+ * further gain).  H = x_hat^T x_hat of the calibration activations d_Xcal
+ * (bf16, M_cal x K, x_hat = fp32(x * inv_lambda) as at run time), a channel
+ * never active gets 1 on the diagonal, then damp * mean(diag H) is added to
+ * the diagonal; U = upper Cholesky factor of H^-1 (H^-1 = U^T U).  The rows
+ * k of R are quantized in increasing k; a group's scales (per output column)
+ * are computed from the current rows when k reaches the group's first row,
+ * with the same quantizer as round-to-nearest; the error of row k divided by
+ * U[k][k] is taken off the rows i > k with weights U[k][i].  Same blob
+ * format; a diagonal H gives the round-to-nearest blob exactly.  Synchronous;
+ * allocates temporary device memory (x_hat, H, U: (M_cal + 2 K) K doubles)
+ * and factors H on the host.  damp >= 0; SVDQ_ERR_INVALID_ARGUMENT also if H
+ * is not positive definite. */
+svdq_status svdq_prepare_weights_gptq(const svdq_layer_desc* desc, const void* d_W,
+                                      const float* d_act_absmax, const void* d_bias,
+                                      const void* d_L1, const void* d_L2, const void* d_Xcal,
+                                      int M_cal, float damp, void* d_prepared,
+                                      size_t prepared_bytes, void* stream);
+
 /* An extra low-rank branch merged into the 16-bit branch of a prepared
  * layer, without touching the quantized residual (walkthrough, Fig. 9 and
  * Fig. 16 section: a LoRA runs as part of the low-rank branch, so a new

@@ -323,14 +323,63 @@ def quantize_weights(R, fmt: str):
     return np.ascontiguousarray(q.T), np.ascontiguousarray(s.T)
 
 
+def gptq_weights(R, xhat_cal, fmt: str, damp: float = 0.01):
+    """GPTQ on the residual instead of rounding each group on its own.
+
+    [walkthrough] Table 3 row: quantizing the residual with GPTQ gives a
+    further gain in most settings.  Steps (GPTQ, restated): H = x_hat^T x_hat
+    of the calibration activations plus damp * mean(diag H) on the diagonal
+    (a channel never active gets 1); U the upper Cholesky factor of H^-1
+    (H^-1 = U^T U).  The residual's rows (input channels k) are quantized in
+    increasing k; a group's scales (per output column) are taken from the
+    current, already updated rows when k reaches the group's first row; the
+    rounding error of row k, divided by U[k, k], is subtracted from the rows
+    not yet quantized with weights U[k, k+1:].  Returns (codes K x N, scales
+    (K/g) x N) like ``quantize_weights``.
+    """
+    R = np.array(R, dtype=np.float64)
+    K, N = R.shape
+    g = GROUP[fmt]
+    x = np.asarray(xhat_cal, dtype=np.float64)
+    H = x.T @ x
+    d = np.diag(H).copy()
+    dead = d == 0
+    H[dead, dead] = 1.0
+    H += damp * np.mean(np.diag(H)) * np.eye(K)
+    Hinv = np.linalg.inv(H)
+    U = np.linalg.cholesky(Hinv).T                              # upper, H^-1 = U^T U
+    codes = np.zeros((K, N), dtype=np.int64)
+    scales = np.zeros((K // g, N), dtype=np.float64 if fmt == INT4 else np.int64)
+    for k in range(K):
+        if k % g == 0:
+            A = np.max(np.abs(R[k:k + g]), axis=0)
+            scales[k // g] = to_fp16(A / 7.0) if fmt == INT4 else e8m0_exponent(A)
+        s = scales[k // g]
+        if fmt == INT4:
+            safe = np.where(s > 0, s, 1.0)
+            q = np.where(s > 0, np.clip(rne_quotient(R[k], safe), -7, 7), 0.0)
+            deq = q * s
+        else:
+            q = e2m1_code(R[k] * np.exp2(-s.astype(np.float64)))
+            deq = e2m1_value(q) * np.exp2(s.astype(np.float64))
+        codes[k] = q
+        err = (R[k] - deq) / U[k, k]
+        R[k + 1:] -= U[k, k + 1:, None] * err[None, :]
+    if fmt == INT4:
+        return codes.astype(np.int8), scales
+    return codes.astype(np.uint8), scales.astype(np.int32)
+
+
 def prepare(W_bits, a, *, alpha: float, rank: int, fmt: str, bias_bits=None,
-            no_smoothing: bool = False, factors=None) -> dict:
+            no_smoothing: bool = False, factors=None, gptq=None) -> dict:
     """Offline preparation of one layer.
 
     W_bits: bf16 bits, K x N.  a: fp32 per-channel activation maxima (K,).
     factors: optional (L1b, L2b) fp64 arrays of bf16 values that replace the
     SVD (a caller-supplied split, e.g. factors read back from another
-    implementation); the residual is then taken against them.
+    implementation); the residual is then taken against them.  gptq:
+    optional (calibration X bf16 bits, damping) to quantize the residual with
+    ``gptq_weights`` instead of rounding.
     """
     W = bf16_bits_to_f64(W_bits)
     lam32, inv32 = smoothing_factors(a, W, alpha, no_smoothing)
@@ -341,7 +390,11 @@ def prepare(W_bits, a, *, alpha: float, rank: int, fmt: str, bias_bits=None,
     else:
         L1b, L2b = (np.asarray(f, dtype=np.float64) for f in factors)
     R = residual(W_hat, L1b, L2b)
-    w_codes, w_scales = quantize_weights(R, fmt)
+    if gptq is None:
+        w_codes, w_scales = quantize_weights(R, fmt)
+    else:
+        # gptq = (calibration X bf16 bits, damping): the quantizer sees x_hat
+        w_codes, w_scales = gptq_weights(R, smooth_act(gptq[0], inv32), fmt, gptq[1])
     bias = None if bias_bits is None else bf16_bits_to_f64(bias_bits)
     return dict(fmt=fmt, K=W.shape[0], N=W.shape[1], rank=rank, lam32=lam32,
                 inv32=inv32, W_hat=W_hat, L1b=L1b, L2b=L2b, R=R,

@@ -94,6 +94,13 @@ def test_runtime_validation_before_device():
     assert lib.svdq_prepare_weights(ctypes.byref(db), good, good, None, None, None, good, pb, None) == 1
     dg = _desc(flags=S.F_FACTORS_GIVEN)
     assert lib.svdq_prepare_weights(ctypes.byref(dg), good, good, None, None, None, good, pb, None) == 1
+    # prepare_weights_gptq: calibration activations required, damp >= 0 and finite, M_cal >= 1
+    pg = lib.svdq_prepare_weights_gptq
+    assert pg(ctypes.byref(d), good, good, None, None, None, None, 512, 0.01, good, pb, None) == 1
+    assert pg(ctypes.byref(d), good, good, None, None, None, good, 512, -1.0, good, pb, None) == 1
+    assert pg(ctypes.byref(d), good, good, None, None, None, good, 512, float("nan"), good, pb, None) == 1
+    assert pg(ctypes.byref(d), good, good, None, None, None, good, 0, 0.01, good, pb, None) == 2
+    assert pg(ctypes.byref(d), good, good, None, None, None, good, 512, 0.01, good, pb - 1, None) == 4
     # merge_lowrank: r_extra a positive multiple of 16 with rank + r_extra <= 128;
     # pointers, alignment, the output size and no overlap with the input
     out = 1 << 30
@@ -239,3 +246,40 @@ def test_host_jacobi_eigensolver(tmp_path):
         assert np.allclose(w, ref, atol=1e-10 * max(1.0, abs(ref).max()))
         assert np.allclose(V.T @ V, np.eye(n), atol=1e-10)
         assert np.allclose(A @ V, V * w, atol=1e-9 * max(1.0, abs(ref).max()))
+
+
+CHOL_MAIN = r"""
+#include <cstdio>
+#include <vector>
+namespace svdq { bool cholesky_upper_of_inverse(int n, std::vector<double> A, std::vector<double>& U); }
+int main() {
+  int n; if (scanf("%d", &n) != 1) return 1;
+  std::vector<double> A(n * n), U;
+  for (auto& x : A) if (scanf("%lf", &x) != 1) return 1;
+  if (!svdq::cholesky_upper_of_inverse(n, A, U)) { printf("notpd\n"); return 0; }
+  for (double u : U) printf("%.17g\n", u);
+  return 0;
+}
+"""
+
+
+def test_host_cholesky_of_inverse(tmp_path):
+    """The host factorization GPTQ uses: U upper triangular with U^T U = A^-1
+    (against numpy's inverse), and a rejection of a matrix that is not
+    positive definite."""
+    src = tmp_path / "main.cpp"
+    src.write_text(CHOL_MAIN)
+    exe = tmp_path / "chol"
+    lin = os.path.join(ROOT, "w4a4_quantized_gemm_amd", "csrc", "svdq_linalg.cpp")
+    subprocess.run(["g++", "-O2", "-std=c++17", str(src), lin, "-o", str(exe)], check=True)
+    rng = np.random.default_rng(1)
+    for n in (1, 5, 40):
+        B = rng.standard_normal((n, n))
+        A = B @ B.T + 0.5 * np.eye(n)
+        inp = f"{n}\n" + "\n".join(repr(float(x)) for x in A.ravel())
+        out = subprocess.run([str(exe)], input=inp, capture_output=True, text=True, check=True).stdout.split()
+        U = np.array([float(x) for x in out]).reshape(n, n)
+        assert np.all(np.tril(U, -1) == 0.0)
+        assert np.allclose(U.T @ U, np.linalg.inv(A), atol=1e-10 * np.abs(np.linalg.inv(A)).max())
+    bad = "2\n1 2\n2 1"
+    assert subprocess.run([str(exe)], input=bad, capture_output=True, text=True, check=True).stdout.strip() == "notpd"

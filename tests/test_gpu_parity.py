@@ -305,6 +305,57 @@ def test_w4a16(torch_dev, fmt, M, K, N):
         assert e <= (1e-5 if oname == "f32" else TOL), (oname, e)
 
 
+@pytest.mark.parametrize("fmt", [O.INT4, O.FP4])
+def test_prepare_gptq(torch_dev, fmt):
+    """GPTQ on the residual.  Uncorrelated calibration channels (a diagonal
+    H) reproduce the round-to-nearest blob byte for byte; correlated ones
+    lower the calibration error well below rounding's, match the oracle's
+    GPTQ on the blob's own residual (codes almost all equal; the error
+    within 2%: GPTQ passes every rounding difference on), and the layer
+    computed from the GPTQ blob matches the oracle given its codes."""
+    import w4a4_quantized_gemm_amd as S
+    torch, dev = torch_dev
+    _say(f"case: gptq fmt={fmt}")
+    M, K, N, r = 200, 384, 320, 16
+    cfg = WL.C2.with_(name="gptq", M=M, K=K, N=N, rank=r, fmt=fmt, w_std=1 / np.sqrt(K),
+                      n_outlier_channels=8, bias_std=0.02, seed=55)
+    X_bits, W_bits, b_bits = WL.make_layer(cfg)
+    layer, X, a = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
+    W = np_bits_to_bf16_tensor(W_bits, dev)
+    bias = np_bits_to_bf16_tensor(b_bits, dev)
+    rtn = blob_sections(layer)
+    # (1) diagonal H: calibration rows e_k * c_k
+    xd = np.zeros((K, K))
+    xd[np.arange(K), np.arange(K)] = np.linspace(0.5, 2.0, K)
+    Xd = np_bits_to_bf16_tensor(O.bf16_bits_of(O.to_bf16(xd).astype(np.float32)), dev)
+    g1 = S.SVDQLinear.prepare(W, a, r, fmt, cfg.alpha, bias=bias, gptq=(Xd, 0.01))
+    torch.cuda.synchronize()
+    assert torch.equal(g1.blob, layer.blob), "diagonal H must give the round-to-nearest blob"
+    # (2) correlated calibration activations
+    rng = np.random.default_rng(56)
+    xc = rng.standard_normal((512, 16)) @ rng.standard_normal((16, K)) + 0.3 * rng.standard_normal((512, K))
+    Xc_bits = O.bf16_bits_of(O.to_bf16(xc).astype(np.float32))
+    g2 = S.SVDQLinear.prepare(W, a, r, fmt, cfg.alpha, bias=bias, gptq=(np_bits_to_bf16_tensor(Xc_bits, dev), 0.01))
+    torch.cuda.synchronize()
+    sec = blob_sections(g2)
+    for k in ("lam32", "inv32", "L1b", "L2b", "bias"):
+        assert np.array_equal(sec[k], rtn[k]), k
+    ref = oracle_prep_from_blob(sec, W_bits, fmt, b_bits)
+    xh = O.smooth_act(Xc_bits, ref["inv32"])
+    q_or, s_or = O.gptq_weights(ref["R"], xh, fmt, 0.01)
+    agree = float(np.mean(sec["w_codes"] == q_or))
+    assert agree > 0.98, agree
+
+    def calib_err(codes, scales):
+        return np.linalg.norm(xh @ (ref["R"] - O.dequant_groups(codes.T, scales.T, fmt).T))
+
+    e_gpu, e_or, e_rtn = calib_err(sec["w_codes"], sec["w_scales"]), calib_err(q_or, s_or), calib_err(ref["w_codes"], ref["w_scales"])
+    _say(f"  codes agreeing {agree:.4f}; calibration error gpu {e_gpu:.4g} oracle {e_or:.4g} rounding {e_rtn:.4g}")
+    assert e_gpu < 0.8 * e_rtn and abs(e_gpu - e_or) <= 0.02 * e_or, (e_gpu, e_or, e_rtn)
+    ref_g = dict(ref, w_codes=sec["w_codes"], w_scales=sec["w_scales"])
+    _check_linear(torch_dev, g2, X, X_bits, ref_g, modes=[(S.OUT_BF16, False), (S.OUT_F32, False)])
+
+
 E2M1_MIDPOINTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
 
 

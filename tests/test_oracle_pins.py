@@ -546,3 +546,47 @@ def test_w4a16_exact_when_weights_are_on_the_grid(fmt):
     y = O.linear_w4a16(prep, Xb, out="f32")["Y64"]
     assert np.allclose(y, X @ W, rtol=1e-13, atol=1e-12)
     assert not np.allclose(O.linear(prep, Xb, out="f32")["Y64"], X @ W, rtol=1e-6, atol=1e-6)
+
+
+def _gptq_case(seed, K=256, N=24, M=512, correlated=True):
+    rng = np.random.default_rng(seed)
+    R = rng.standard_normal((K, N)) * 0.05
+    if correlated:
+        # calibration activations with strongly correlated channels
+        B = rng.standard_normal((K, 16))
+        x = rng.standard_normal((M, 16)) @ B.T + 0.3 * rng.standard_normal((M, K))
+    else:
+        x = rng.standard_normal((M, K))
+    return R, x
+
+
+@pytest.mark.parametrize("fmt", [O.INT4, O.FP4])
+def test_gptq_reduces_to_rounding_for_a_diagonal_hessian(fmt):
+    """With uncorrelated calibration channels (x_hat = diag(d), so H is
+    diagonal) the Cholesky factor of H^-1 is diagonal, no error is passed on,
+    and GPTQ gives exactly the round-to-nearest codes and scales."""
+    R, _ = _gptq_case(25, correlated=False)
+    K = R.shape[0]
+    x = np.diag(np.linspace(0.5, 2.0, K))
+    q, s = O.gptq_weights(R, x, fmt, damp=0.01)
+    q0, s0 = O.quantize_weights(R, fmt)
+    assert np.array_equal(q, q0) and np.array_equal(s, s0)
+
+
+@pytest.mark.parametrize("fmt", [O.INT4, O.FP4])
+def test_gptq_lowers_the_calibration_error(fmt):
+    """GPTQ's purpose: ||x_hat (R - Q(R))||_F on the calibration data is
+    clearly below round-to-nearest's (walkthrough, Table 3 row on GPTQ), while
+    every code stays on the grid with its group's scale."""
+    R, x = _gptq_case(26)
+    q, s = O.gptq_weights(R, x, fmt, damp=0.01)
+    q0, s0 = O.quantize_weights(R, fmt)
+    dq = O.dequant_groups(q.T, s.T, fmt).T
+    dq0 = O.dequant_groups(q0.T, s0.T, fmt).T
+    e_gptq = np.linalg.norm(x @ (R - dq))
+    e_rtn = np.linalg.norm(x @ (R - dq0))
+    assert e_gptq < 0.8 * e_rtn, (e_gptq, e_rtn)
+    if fmt == O.INT4:
+        assert np.all(np.abs(q) <= 7)
+    else:
+        assert np.all(q < 16)

@@ -34,7 +34,8 @@ STATUS_NAMES = {
 # every symbol include/svdq.h declares
 EXPORTED = (
     "svdq_status_string", "svdq_version", "svdq_prepared_bytes", "svdq_workspace_bytes",
-    "svdq_act_sizes", "svdq_act_absmax", "svdq_prepare_weights", "svdq_merge_lowrank", "svdq_check_blob",
+    "svdq_act_sizes", "svdq_act_absmax", "svdq_prepare_weights", "svdq_prepare_weights_gptq", "svdq_merge_lowrank",
+    "svdq_check_blob",
     "svdq_quantize_act", "svdq_quantize_act_ln", "svdq_gemm", "svdq_linear", "svdq_linear_ln", "svdq_linear_w4a16",
     "svdq_linear_unfused", "svdq_blob_layout_of",
 )
@@ -81,6 +82,7 @@ def _lib() -> ctypes.CDLL:
             "svdq_act_sizes": ([D, I, ctypes.POINTER(Z), ctypes.POINTER(Z), ctypes.POINTER(Z)], S),
             "svdq_act_absmax": ([P, I, I, P, I, P], S),
             "svdq_prepare_weights": ([D, P, P, P, P, P, P, Z, P], S),
+            "svdq_prepare_weights_gptq": ([D, P, P, P, P, P, P, I, F, P, Z, P], S),
             "svdq_merge_lowrank": ([D, P, P, P, I, P, Z, P], S),
             "svdq_check_blob": ([D, P, P], S),
             "svdq_quantize_act": ([D, P, P, I, P, P, P, P, Z, P], S),
@@ -165,6 +167,15 @@ def svdq_prepare_weights(desc: LayerDesc, W, act_absmax, prepared, bias=None, L1
     _check(_lib().svdq_prepare_weights(ctypes.byref(desc), _ptr(W), _ptr(act_absmax), _ptr(bias),
                                        _ptr(L1), _ptr(L2), _ptr(prepared), prepared.numel(),
                                        _stream(stream)), "svdq_prepare_weights")
+
+
+def svdq_prepare_weights_gptq(desc: LayerDesc, W, act_absmax, prepared, Xcal, damp: float = 0.01, bias=None, L1=None,
+                              L2=None, stream=None):
+    """Offline preparation with the residual quantized by GPTQ on the
+    calibration activations ``Xcal`` (bf16, M_cal x K); synchronous."""
+    _check(_lib().svdq_prepare_weights_gptq(ctypes.byref(desc), _ptr(W), _ptr(act_absmax), _ptr(bias), _ptr(L1),
+                                            _ptr(L2), _ptr(Xcal), Xcal.shape[0], float(damp), _ptr(prepared),
+                                            prepared.numel(), _stream(stream)), "svdq_prepare_weights_gptq")
 
 
 def svdq_merge_lowrank(desc: LayerDesc, prepared, A, B, out, stream=None):
@@ -270,7 +281,8 @@ class SVDQLinear:
 
     @classmethod
     def prepare(cls, W, act_absmax, rank: int, fmt="int4", alpha: float = 0.5, bias=None,
-                L1=None, L2=None, no_smoothing: bool = False, stream=None) -> "SVDQLinear":
+                L1=None, L2=None, no_smoothing: bool = False, stream=None, gptq=None) -> "SVDQLinear":
+        """``gptq`` = (calibration X, damping) quantizes the residual with GPTQ."""
         import torch
         K, N = W.shape
         flags = (F_HAS_BIAS if bias is not None else 0) | (F_NO_SMOOTHING if no_smoothing else 0) | \
@@ -280,7 +292,11 @@ class SVDQLinear:
         if nbytes == 0:
             raise SvdqError(2, "svdq_prepared_bytes")
         blob = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
-        svdq_prepare_weights(desc, W, act_absmax, blob, bias=bias, L1=L1, L2=L2, stream=stream)
+        if gptq is not None:
+            svdq_prepare_weights_gptq(desc, W, act_absmax, blob, gptq[0], gptq[1], bias=bias, L1=L1, L2=L2,
+                                      stream=stream)
+        else:
+            svdq_prepare_weights(desc, W, act_absmax, blob, bias=bias, L1=L1, L2=L2, stream=stream)
         return cls(desc, blob)
 
     def merge_lowrank(self, A, B, stream=None) -> "SVDQLinear":

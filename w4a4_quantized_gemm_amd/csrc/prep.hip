@@ -298,6 +298,104 @@ __global__ void merge_l2_kernel(const uint16_t* __restrict__ old_l2t, const uint
   l2t[bf16_block_index(n, t, R)] = v;
 }
 
+// GPTQ on the residual (the walkthrough's Table 3 row on GPTQ): the rows
+// (input channels) of R are quantized in order; the rounding error of row k,
+// divided by U[k][k], is taken off the later rows with weights U[k][k+1:],
+// U the upper Cholesky factor of H^-1, H = x_hat^T x_hat of calibration
+// activations (damped).  A group's scales come from the current rows when k
+// reaches its first row.  The quantization of one value is the round-to-
+// nearest path's (wquant_kernel), so a diagonal H reproduces it exactly.
+
+// x_hat of the calibration activations in fp64: fp32(x * inv_lambda), as the
+// runtime computes it.
+__global__ void xhat64_kernel(const uint16_t* __restrict__ X, const float* __restrict__ inv, long MK, int K,
+                              double* __restrict__ out) {
+  const long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= MK) return;
+  const float x = __uint_as_float(static_cast<uint32_t>(X[idx]) << 16);
+  out[idx] = static_cast<double>(x * inv[idx % K]);
+}
+
+// Scales of the group starting at row k, one thread per column: fp16 bits
+// (INT4) or the E8M0 byte (FP4).
+template <int FMT>
+__global__ void gptq_scale_kernel(const double* __restrict__ R, int k, int N, uint32_t* __restrict__ sc) {
+  constexpr int G = FMT == SVDQ_INT4_G64_FP16 ? 64 : 32;
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  double a = 0.0;
+  for (int j = 0; j < G; j++) a = fmax(a, fabs(R[static_cast<long>(k + j) * N + n]));
+  sc[static_cast<long>(k / G) * N + n] =
+      FMT == SVDQ_INT4_G64_FP16 ? f64_round_bits(a / 7.0, 10, 5) : static_cast<uint32_t>(e8m0_exponent_f64(a) + 127);
+}
+
+// Row k: codes and the error (value - dequantized code) / U[k][k].
+template <int FMT>
+__global__ void gptq_row_kernel(const double* __restrict__ R, int k, int N, const uint32_t* __restrict__ sc, double ukk,
+                                uint8_t* __restrict__ codes, double* __restrict__ err) {
+  constexpr int G = FMT == SVDQ_INT4_G64_FP16 ? 64 : 32;
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  const double w = R[static_cast<long>(k) * N + n];
+  const uint32_t sb = sc[static_cast<long>(k / G) * N + n];
+  double deq;
+  if constexpr (FMT == SVDQ_INT4_G64_FP16) {
+    const double s = half_bits_to_f64(sb);
+    double q = 0.0;
+    if (s > 0.0) q = fmin(fmax(rne_quotient_f64(w, s), -7.0), 7.0);
+    deq = q * s;
+    codes[static_cast<long>(k) * N + n] = static_cast<uint8_t>(static_cast<int>(q) & 0xFF);
+  } else {
+    const int e = static_cast<int>(sb) - 127;
+    const uint32_t c = e2m1_code_f64(ldexp(w, -e));
+    const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    deq = ldexp((c & 8u) ? -grid[c & 7u] : grid[c & 7u], e);
+    codes[static_cast<long>(k) * N + n] = static_cast<uint8_t>(c);
+  }
+  err[n] = (w - deq) / ukk;
+}
+
+// R[i][n] -= U[k][i] err[n] for the rows i > k.
+__global__ void gptq_update_kernel(double* __restrict__ R, int k, int K, int N, const double* __restrict__ urow,
+                                   const double* __restrict__ err) {
+  const long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<long>(K - k - 1) * N) return;
+  const long i = k + 1 + idx / N;
+  const int n = static_cast<int>(idx % N);
+  R[i * N + n] -= urow[i] * err[n];
+}
+
+// Packs the GPTQ codes and scales into the blob layout (the layout
+// wquant_kernel writes); one thread per (output column n, K group g).
+template <int FMT>
+__global__ void gptq_pack_kernel(const uint8_t* __restrict__ codes, const uint32_t* __restrict__ sc, int K, int N,
+                                 uint8_t* __restrict__ wcodes, void* __restrict__ wscales) {
+  constexpr int G = FMT == SVDQ_INT4_G64_FP16 ? 64 : 32;
+  const long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const long groups = K / G;
+  if (idx >= groups * N) return;
+  const long g = idx / N, n = idx % N;
+  uint32_t words[G / 8];
+#pragma unroll
+  for (int w = 0; w < G / 8; w++) words[w] = 0u;
+  for (int k = 0; k < G; k++) {
+    const uint8_t c = codes[(g * G + k) * N + n];
+    if constexpr (FMT == SVDQ_INT4_G64_FP16)
+      words[k >> 3] |= int4_code_bits(static_cast<int8_t>(c), k & 7);
+    else
+      words[k >> 3] |= static_cast<uint32_t>(c & 0xF) << (4 * (k & 7));
+  }
+  const uint32_t sb = sc[g * N + n];
+  if constexpr (FMT == SVDQ_INT4_G64_FP16)
+    reinterpret_cast<uint16_t*>(wscales)[n * groups + g] = static_cast<uint16_t>(sb);
+  else
+    reinterpret_cast<uint8_t*>(wscales)[fp4_scale_offset(n, static_cast<int>(g * G), K)] = static_cast<uint8_t>(sb);
+#pragma unroll
+  for (int w = 0; w < G / 32; w++)
+    *reinterpret_cast<u32x4*>(wcodes + code_chunk_offset(n, static_cast<int>(g * G + 32 * w), K)) =
+        u32x4{words[4 * w], words[4 * w + 1], words[4 * w + 2], words[4 * w + 3]};
+}
+
 __global__ void bias_kernel(const uint16_t* __restrict__ b, int N, float* __restrict__ out) {
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
   if (n < N) out[n] = __uint_as_float(static_cast<uint32_t>(b[n]) << 16);
@@ -358,9 +456,64 @@ svdq_status orthonormalize(double* Y, double* tmp, double* G, int n, int b, hipS
 
 }  // namespace
 
+template <int FMT>
+svdq_status gptq_impl(const svdq_layer_desc& d, double* R, const float* inv, const GptqArgs& gq, uint8_t* wcodes,
+                      void* wscales, hipStream_t st) {
+  constexpr int G = FMT == SVDQ_INT4_G64_FP16 ? 64 : 32;
+  const int K = d.K, N = d.N, Mc = gq.M;
+  DevBuf xh, H;
+  SVDQ_TRY(xh.alloc(sizeof(double) * static_cast<size_t>(Mc) * K));
+  SVDQ_TRY(H.alloc(sizeof(double) * static_cast<size_t>(K) * K));
+  const long MK = static_cast<long>(Mc) * K;
+  hipLaunchKernelGGL(xhat64_kernel, dim3(blocks_for(MK)), dim3(256), 0, st, gq.X, inv, MK, K, xh.d());
+  SVDQ_TRY(hipGetLastError());
+  SVDQ_TRY(dgemm(true, K, K, Mc, xh.d(), K, xh.d(), K, H.d(), K, st));
+  std::vector<double> Hh(static_cast<size_t>(K) * K), U;
+  SVDQ_TRY(hipMemcpyAsync(Hh.data(), H.p, Hh.size() * sizeof(double), hipMemcpyDeviceToHost, st));
+  SVDQ_TRY(hipStreamSynchronize(st));
+  // a channel the calibration never activates gets 1 on the diagonal; then
+  // damp * mean(diag) on every diagonal entry
+  double mean = 0.0;
+  for (int k = 0; k < K; k++) {
+    double& h = Hh[static_cast<size_t>(k) * K + k];
+    if (h == 0.0) h = 1.0;
+    mean += h;
+  }
+  mean /= K;
+  for (int k = 0; k < K; k++) Hh[static_cast<size_t>(k) * K + k] += gq.damp * mean;
+  if (!cholesky_upper_of_inverse(K, Hh, U)) return SVDQ_ERR_INVALID_ARGUMENT;
+  DevBuf dU, codes, sc, err;
+  SVDQ_TRY(dU.alloc(sizeof(double) * static_cast<size_t>(K) * K));
+  SVDQ_TRY(codes.alloc(static_cast<size_t>(K) * N));
+  SVDQ_TRY(sc.alloc(sizeof(uint32_t) * static_cast<size_t>(K / G) * N));
+  SVDQ_TRY(err.alloc(sizeof(double) * N));
+  SVDQ_TRY(hipMemcpyAsync(dU.p, U.data(), U.size() * sizeof(double), hipMemcpyHostToDevice, st));
+  uint8_t* cd = static_cast<uint8_t*>(codes.p);
+  uint32_t* scd = static_cast<uint32_t*>(sc.p);
+  for (int k = 0; k < K; k++) {
+    if (k % G == 0) {
+      hipLaunchKernelGGL(gptq_scale_kernel<FMT>, dim3(blocks_for(N)), dim3(256), 0, st, R, k, N, scd);
+      SVDQ_TRY(hipGetLastError());
+    }
+    hipLaunchKernelGGL(gptq_row_kernel<FMT>, dim3(blocks_for(N)), dim3(256), 0, st, R, k, N, scd,
+                       U[static_cast<size_t>(k) * K + k], cd, err.d());
+    SVDQ_TRY(hipGetLastError());
+    if (k + 1 < K) {
+      hipLaunchKernelGGL(gptq_update_kernel, dim3(blocks_for(static_cast<long>(K - k - 1) * N)), dim3(256), 0, st, R, k,
+                         K, N, dU.d() + static_cast<size_t>(k) * K, err.d());
+      SVDQ_TRY(hipGetLastError());
+    }
+  }
+  hipLaunchKernelGGL(gptq_pack_kernel<FMT>, dim3(blocks_for(static_cast<long>(K / G) * N)), dim3(256), 0, st, cd, scd,
+                     K, N, wcodes, wscales);
+  SVDQ_TRY(hipGetLastError());
+  SVDQ_TRY(hipStreamSynchronize(st));
+  return SVDQ_OK;
+}
+
 svdq_status prepare_impl(const svdq_layer_desc& d, const uint16_t* W, const float* act_absmax,
                          const uint16_t* bias, const uint16_t* L1, const uint16_t* L2, uint8_t* blob,
-                         hipStream_t st, const PrepOptions& opt) {
+                         hipStream_t st, const PrepOptions& opt, const GptqArgs* gptq) {
   const int K = d.K, N = d.N, r = d.rank;
   const svdq_blob_layout L = layout_of(d);
   float* lam = reinterpret_cast<float*>(blob + L.lambda);
@@ -459,7 +612,11 @@ svdq_status prepare_impl(const svdq_layer_desc& d, const uint16_t* W, const floa
   uint8_t* wcodes = blob + L.wcodes;
   void* wscales = blob + L.wscales;
   const long groups = static_cast<long>(K / group_of(d.fmt)) * N;
-  if (d.fmt == SVDQ_INT4_G64_FP16)
+  if (gptq) {
+    const svdq_status gs = d.fmt == SVDQ_INT4_G64_FP16 ? gptq_impl<SVDQ_INT4_G64_FP16>(d, what.d(), inv, *gptq, wcodes, wscales, st)
+                                                      : gptq_impl<SVDQ_FP4_E2M1_G32_E8M0>(d, what.d(), inv, *gptq, wcodes, wscales, st);
+    if (gs != SVDQ_OK) return gs;
+  } else if (d.fmt == SVDQ_INT4_G64_FP16)
     hipLaunchKernelGGL(wquant_kernel<SVDQ_INT4_G64_FP16>, dim3(blocks_for(groups)), dim3(256), 0, st, what.d(), K, N,
                        wcodes, wscales);
   else

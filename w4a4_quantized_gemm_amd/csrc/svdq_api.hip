@@ -182,6 +182,31 @@ svdq_status svdq_prepare_weights(const svdq_layer_desc* desc, const void* d_W, c
                       static_cast<uint8_t*>(d_prepared), as_stream(stream), opt);
 }
 
+svdq_status svdq_prepare_weights_gptq(const svdq_layer_desc* desc, const void* d_W, const float* d_act_absmax,
+                                      const void* d_bias, const void* d_L1, const void* d_L2, const void* d_Xcal,
+                                      int M_cal, float damp, void* d_prepared, size_t prepared_bytes, void* stream) {
+  svdq_status st = validate_desc(desc);
+  if (st != SVDQ_OK) return st;
+  if (!d_W || !d_prepared || !d_Xcal) return SVDQ_ERR_INVALID_ARGUMENT;
+  if (!(damp >= 0.f && damp < 3.0e38f)) return SVDQ_ERR_INVALID_ARGUMENT;
+  if ((st = validate_m(M_cal)) != SVDQ_OK) return st;
+  if (!(desc->flags & SVDQ_F_NO_SMOOTHING) && !d_act_absmax) return SVDQ_ERR_INVALID_ARGUMENT;
+  if ((desc->flags & SVDQ_F_HAS_BIAS) && !d_bias) return SVDQ_ERR_INVALID_ARGUMENT;
+  if ((desc->flags & SVDQ_F_FACTORS_GIVEN) && desc->rank > 0 && (!d_L1 || !d_L2)) return SVDQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(d_prepared) || !aligned16(d_W)) return SVDQ_ERR_MISALIGNED;
+  if (prepared_bytes < layout_of(*desc).total) return SVDQ_ERR_BUFFER_TOO_SMALL;
+  if ((st = check_device()) != SVDQ_OK) return st;
+  PrepOptions opt;
+  if (const char* e = std::getenv("SVDQ_PREP_ITERS")) opt.iterations = std::atoi(e);
+  GptqArgs gq;
+  gq.X = static_cast<const uint16_t*>(d_Xcal);
+  gq.M = M_cal;
+  gq.damp = damp;
+  return prepare_impl(*desc, static_cast<const uint16_t*>(d_W), d_act_absmax, static_cast<const uint16_t*>(d_bias),
+                      static_cast<const uint16_t*>(d_L1), static_cast<const uint16_t*>(d_L2),
+                      static_cast<uint8_t*>(d_prepared), as_stream(stream), opt, &gq);
+}
+
 svdq_status svdq_merge_lowrank(const svdq_layer_desc* desc, const void* d_prepared, const void* d_A, const void* d_B,
                                int r_extra, void* d_out, size_t out_bytes, void* stream) {
   svdq_status st = validate_desc(desc);

@@ -60,4 +60,59 @@ void jacobi_eigh(int n, std::vector<double>& A, std::vector<double>& V, std::vec
   V.swap(Vs);
 }
 
+// Upper Cholesky factor U of A^-1 (A^-1 = U^T U) for a symmetric positive
+// definite n x n row-major A, as GPTQ needs it: A = L L^T (lower Cholesky),
+// L^-1 by forward substitution, A^-1 = L^-T L^-1, then A^-1 = G G^T and
+// U = G^T.  Returns false if A is not numerically positive definite.  U is
+// n x n row-major (zeros below the diagonal).
+static bool cholesky_lower(int n, std::vector<double>& A) {
+  for (int j = 0; j < n; j++) {
+    double* aj = &A[static_cast<size_t>(j) * n];
+    double d = aj[j];
+    for (int k = 0; k < j; k++) d -= aj[k] * aj[k];
+    if (!(d > 0.0)) return false;
+    d = std::sqrt(d);
+    aj[j] = d;
+    for (int i = j + 1; i < n; i++) {
+      double* ai = &A[static_cast<size_t>(i) * n];
+      double v = ai[j];
+      for (int k = 0; k < j; k++) v -= ai[k] * aj[k];
+      ai[j] = v / d;
+    }
+  }
+  for (int i = 0; i < n; i++)
+    for (int j = i + 1; j < n; j++) A[static_cast<size_t>(i) * n + j] = 0.0;
+  return true;
+}
+
+bool cholesky_upper_of_inverse(int n, std::vector<double> A, std::vector<double>& U) {
+  if (!cholesky_lower(n, A)) return false;
+  // Li = L^-1 (lower), column by column: L Li[:, c] = e_c
+  std::vector<double> Li(static_cast<size_t>(n) * n, 0.0);
+  for (int c = 0; c < n; c++) {
+    for (int i = c; i < n; i++) {
+      const double* li = &A[static_cast<size_t>(i) * n];
+      double v = i == c ? 1.0 : 0.0;
+      for (int k = c; k < i; k++) v -= li[k] * Li[static_cast<size_t>(k) * n + c];
+      Li[static_cast<size_t>(i) * n + c] = v / li[i];
+    }
+  }
+  // Ainv = Li^T Li: Ainv[i][j] = sum_{k >= max(i, j)} Li[k][i] Li[k][j]
+  std::vector<double> Ai(static_cast<size_t>(n) * n, 0.0);
+  for (int k = 0; k < n; k++) {
+    const double* lk = &Li[static_cast<size_t>(k) * n];
+    for (int i = 0; i <= k; i++) {
+      const double v = lk[i];
+      if (v == 0.0) continue;
+      double* ai = &Ai[static_cast<size_t>(i) * n];
+      for (int j = 0; j <= k; j++) ai[j] += v * lk[j];
+    }
+  }
+  if (!cholesky_lower(n, Ai)) return false;
+  U.assign(static_cast<size_t>(n) * n, 0.0);
+  for (int i = 0; i < n; i++)
+    for (int j = i; j < n; j++) U[static_cast<size_t>(i) * n + j] = Ai[static_cast<size_t>(j) * n + i];
+  return true;
+}
+
 }  // namespace svdq

@@ -83,7 +83,9 @@ __device__ __forceinline__ float load_out(const void* Y, I idx) {
 
 // Tile: 4 waves in a 2 x 2 grid, each owning 64 x 64 (2 x 2 MFMA tiles).
 // The per-group dequantization updates the accumulators with VALU fma, so
-// they are VGPRs; 128 x 128 per workgroup, two workgroups per CU.
+// they are VGPRs; 128 x 128 per workgroup.  About 300 registers per lane:
+// one wave per SIMD, one workgroup per CU (a bound to two waves per SIMD
+// fits in 256 without spilling but measured no faster).
 constexpr int RB = 2, CB = 2;                      // 32-row (-column) blocks per wave
 constexpr int BM = 2 * RB * 32, BN = 2 * CB * 32;
 constexpr int NTHREADS = 256;

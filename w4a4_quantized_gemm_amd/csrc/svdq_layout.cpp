@@ -95,7 +95,8 @@ int w4a16_rows(int M) {
 
 // The smallest number of parts (a divisor of K / 64) such that a part's fp32
 // activations (rows x K / parts) fit 64 KB of LDS and either there are at
-// least 512 workgroups of 128 columns or a part is at most 8 blocks of 64.
+// least 1024 workgroups of 128 columns (about four per CU, enough loads in
+// flight to cover HBM latency) or a part is at most 8 blocks of 64.
 int w4a16_ksplit(int M, int K, int N) {
   const int rows = w4a16_rows(M), kb = K / 64, nb = (N / 32 + 3) / 4;   // workgroups of 4 x 32 columns
   int ks = 1;
@@ -103,7 +104,7 @@ int w4a16_ksplit(int M, int K, int N) {
     if (kb % d) continue;
     ks = d;
     const bool fits = static_cast<long>(kb / d) * 64 * rows * 4 <= 65536;
-    if (fits && (static_cast<long>(nb) * d >= 512 || kb / d <= 8)) break;
+    if (fits && (static_cast<long>(nb) * d >= 1024 || kb / d <= 8)) break;
   }
   return ks;
 }

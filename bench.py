@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the SVDQuant W4A4 linear layer (fused low-rank branch) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--sweep]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--sweep] [--peaks]
 
 One step = one forward pass of the layer over one batch: the fused
 activation pass (smoothing + group quantization + rank-r down-projection)
@@ -12,11 +12,21 @@ step works on the next of several copies of (X, blob, workspace, Y) whose
 total exceeds the 256 MB Infinity Cache, so no step is served from a warm
 last-level cache.
 
+Protocol: every workload is first warmed up for at least a second of
+launches (and at least --warmup steps), so that the clock has settled;
+then exactly --steps fused steps are timed between two synchronizations
+(the headline value and ms_per_step); then --steps rounds run the fused
+layer, the unfused layer and the two kernels of the fused layer one after
+the other, each call timed with HIP events on its stream, and the medians,
+10th and 90th percentiles of those per-call times give the kernel times,
+the rooflines and the fused-versus-unfused speedup (interleaving keeps the
+variants on the same clock and cache state).
+
 Printed: one JSON line with the effective TOPS of the layer (2 M K N per
-layer time), the kernel roofline of the dominant kernel (the 4-bit GEMM,
-timed with HIP events on the stream it is launched on), the activation
-kernel's HBM roofline, the fused-versus-unfused speedup, and the CPU oracle's
-throughput on a bounded row sample of the same workload.
+layer time), the kernel roofline of the dominant kernel (the 4-bit GEMM),
+the activation kernel's HBM roofline, the fused-versus-unfused speedup, the
+low-rank slab's overhead t(r) / t(r = 0), further workloads, and the CPU
+oracle's throughput on a bounded row sample of the same workload.
 """
 from __future__ import annotations
 
@@ -36,14 +46,18 @@ PEAK_TFLOPS = {"int4": 5000.0, "fp4": 10100.0}   # 8-bit MFMA (INT4 runs on the 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 INFINITY_CACHE = 256 << 20
+HEADLINE = "c3_fc1_4608x3072x12288_fp4"
+EXTRAS = ("c3_fc1_4608x3072x12288_int4,c2_qkv_4608x3072x9216_int4,c4_fc2_4608x12288x3072_int4,"
+          "c4_fc2_4608x12288x3072_fp4,c5_M16384_K3072_N12288_r64")
+WARM_SECONDS = 1.0
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2_qkv_4608x3072x9216_int4")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle row sample (0: automatic)")
     ap.add_argument("--sweep", action="store_true", help="also time the shape sweep (one line each, to stderr)")
@@ -64,8 +78,12 @@ def parse():
                     help="skip timing the LayerNorm-fused layer against a separate norm pass")
     ap.add_argument("--lora", type=int, default=16,
                     help="also time the main workload with an extra rank-LORA branch merged in (0: skip)")
-    ap.add_argument("--extra", default="c3_fc1_4608x3072x12288_fp4",
+    ap.add_argument("--extra", default=EXTRAS,
                     help="comma-separated further workloads reported in the same line ('' for none)")
+    ap.add_argument("--rank0", default="c3_fc1_4608x3072x12288_fp4,c2_qkv_4608x3072x9216_int4",
+                    help="workloads whose rank-0 layer is timed too (slab overhead t(r) / t(0))")
+    ap.add_argument("--peaks", action="store_true",
+                    help="also run the MFMA and HBM peak microbenchmarks and report them")
     return ap.parse_args()
 
 
@@ -138,31 +156,102 @@ class Rig:
         torch.cuda.synchronize()
 
 
-def time_fused(torch, S, rig, steps, warmup, unfused=False):
-    d = rig.layer.desc
-    fn = S.svdq_linear_unfused if unfused else S.svdq_linear
-    n = rig.nsets
-    for k in range(warmup):
-        s = rig.sets[k % n]
-        fn(d, s["blob"], s["X"], s["Y"], s["ws"], S.OUT_BF16)
+def pct(xs):
+    """Median, 10th and 90th percentile (linear interpolation) of a list."""
+    xs = sorted(xs)
+    n = len(xs)
+
+    def q(p):
+        i = (n - 1) * p
+        lo = int(i)
+        hi = min(lo + 1, n - 1)
+        return xs[lo] + (xs[hi] - xs[lo]) * (i - lo)
+    return {"median": q(0.5), "p10": q(0.1), "p90": q(0.9)}
+
+
+def us(d):
+    return {k: v * 1e3 for k, v in d.items()}
+
+
+def warm(torch, fns, min_iters, min_seconds=WARM_SECONDS):
+    """Round-robin over fns (each called with the round index) until each
+    ran min_iters times and min_seconds of wall time passed."""
+    t0 = time.perf_counter()
+    k = 0
+    while True:
+        for f in fns:
+            f(k)
+        k += 1
+        if k % 8 == 0:
+            torch.cuda.synchronize()
+        if k >= min_iters and time.perf_counter() - t0 >= min_seconds:
+            break
+    torch.cuda.synchronize()
+
+
+def bracket(torch, fn, steps):
+    """Exactly `steps` calls between two synchronizations: ms per call from
+    events at both ends (the stream's own clock) and the wall time."""
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
     for k in range(steps):
-        s = rig.sets[k % n]
-        fn(d, s["blob"], s["X"], s["Y"], s["ws"], S.OUT_BF16)
+        fn(k)
     e1.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return e0.elapsed_time(e1) / steps, wall
+    return e0.elapsed_time(e1) / steps, time.perf_counter() - t0
+
+
+def interleaved(torch, variants, rounds):
+    """`rounds` rounds, each calling every variant once in order, each call
+    bracketed by events on the current stream; returns the per-call times
+    (ms) of every variant."""
+    evs = {name: [] for name, _ in variants}
+    for k in range(rounds):
+        for name, fn in variants:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn(k)
+            e1.record()
+            evs[name].append((e0, e1))
+    torch.cuda.synchronize()
+    return {name: [a.elapsed_time(b) for a, b in lst] for name, lst in evs.items()}
+
+
+def layer_fns(S, rig):
+    """The timed calls on a rig (each takes the round index, which picks the
+    buffer set): fused layer, unfused layer, and the fused layer's two
+    launches on their own (activation pass, GEMM), which read and write the
+    same buffers as one svdq_linear call."""
+    d = rig.layer.desc
+    n = rig.nsets
+    M = rig.cfg.M
+
+    def fused(k):
+        s = rig.sets[k % n]
+        S.svdq_linear(d, s["blob"], s["X"], s["Y"], s["ws"], S.OUT_BF16)
+
+    def unfused(k):
+        s = rig.sets[k % n]
+        S.svdq_linear_unfused(d, s["blob"], s["X"], s["Y"], s["ws"], S.OUT_BF16)
+
+    def quant(k):
+        s = rig.sets[k % n]
+        S.svdq_quantize_act(d, s["blob"], s["X"], s["codes"], s["scales"], s["T"] if d.rank else None, s["ws"])
+
+    def gemm(k):
+        s = rig.sets[k % n]
+        S.svdq_gemm(d, s["blob"], s["codes"], s["scales"], s["T"] if d.rank else None, M, s["Y"], S.OUT_BF16)
+
+    return fused, unfused, quant, gemm
 
 
 def time_norm(torch, S, rig, steps, warmup, eps=1e-6):
     """The layer on a LayerNorm's input: the norm fused into the activation
     pass (svdq_linear_ln) against the norm as its own pass (torch's
     layer_norm writing the bf16 normalized activations) followed by
-    svdq_linear.  Returns (fused ms, separate ms) per step."""
+    svdq_linear, interleaved.  Returns (fused, separate) median ms."""
     d = rig.layer.desc
     n = rig.nsets
     g = torch.Generator(device="cpu").manual_seed(rig.cfg.seed + 2)
@@ -170,26 +259,18 @@ def time_norm(torch, S, rig, steps, warmup, eps=1e-6):
     beta = (0.1 * torch.randn(d.K, generator=g)).to(torch.bfloat16).to("cuda:0")
     F = torch.nn.functional
 
-    def fused(s):
+    def fused(k):
+        s = rig.sets[k % n]
         S.svdq_linear_ln(d, s["blob"], s["X"], gamma, beta, eps, s["Y"], s["ws"], S.OUT_BF16)
 
-    def separate(s):
+    def separate(k):
+        s = rig.sets[k % n]
         xn = F.layer_norm(s["X"], (d.K,), gamma, beta, eps)
         S.svdq_linear(d, s["blob"], xn, s["Y"], s["ws"], S.OUT_BF16)
 
-    out = []
-    for fn in (fused, separate):
-        for k in range(warmup):
-            fn(rig.sets[k % n])
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for k in range(steps):
-            fn(rig.sets[k % n])
-        e1.record()
-        torch.cuda.synchronize()
-        out.append(e0.elapsed_time(e1) / steps)
-    return out[0], out[1]
+    warm(torch, [fused, separate], warmup, 0.3)
+    t = interleaved(torch, [("fused", fused), ("separate", separate)], steps)
+    return statistics.median(t["fused"]), statistics.median(t["separate"])
 
 
 W4A16_SHAPES = ((1, 3072, 18432), (16, 3072, 18432))   # AdaLN modulation projection: one sample / a batch of 16
@@ -198,8 +279,8 @@ W4A16_SHAPES = ((1, 3072, 18432), (16, 3072, 18432))   # AdaLN modulation projec
 def time_w4a16(torch, S, WL, to_tensor, steps, warmup, fmt="int4"):
     """The weight-only 4-bit layer on the modulation projection's shape
     (3072 -> 6 x 3072), against torch's bf16 matmul of the same weights and
-    the W4A4 layer (rank 0) at the same M.  Enough blob copies rotate to
-    defeat the Infinity Cache.  Returns one dict per M."""
+    the W4A4 layer (rank 0) at the same M, interleaved.  Enough blob copies
+    rotate to defeat the Infinity Cache.  Returns one dict per M."""
     res = []
     for M, K, N in W4A16_SHAPES:
         cfg = WL.C2.with_(name="w4a16", M=64, K=K, N=N, rank=0, fmt=fmt, w_std=1 / K ** 0.5, bias_std=0.02, seed=5)
@@ -214,62 +295,23 @@ def time_w4a16(torch, S, WL, to_tensor, steps, warmup, fmt="int4"):
         blobs = [layer.blob] + [layer.blob.clone() for _ in range(ncopy - 1)]
         nw = max(2, -(-2 * INFINITY_CACHE // (W.numel() * 2)))
         Ws = [W] + [W.clone() for _ in range(nw - 1)]
-        ws = torch.empty(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev)
+        ws = layer.workspace(M)
+        ws4 = layer.workspace(M)
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-
-        def run(fn, n):
-            for k in range(warmup):
-                fn(k % n)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for k in range(steps):
-                fn(k % n)
-            e1.record()
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / steps * 1e3
-
-        us = run(lambda i: S.svdq_linear_w4a16(layer.desc, blobs[i], X, Y, ws, S.OUT_BF16), len(blobs))
-        ws4 = torch.empty(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev)
-        us_w4a4 = run(lambda i: S.svdq_linear(layer.desc, blobs[i], X, Y, ws4, S.OUT_BF16), len(blobs))
-        us_bf16 = run(lambda i: torch.matmul(X, Ws[i]), len(Ws))
+        fns = [("w4a16", lambda k: S.svdq_linear_w4a16(layer.desc, blobs[k % ncopy], X, Y, ws, S.OUT_BF16)),
+               ("w4a4", lambda k: S.svdq_linear(layer.desc, blobs[k % ncopy], X, Y, ws4, S.OUT_BF16)),
+               ("bf16", lambda k: torch.matmul(X, Ws[k % nw]))]
+        warm(torch, [f for _, f in fns], warmup, 0.3)
+        t = interleaved(torch, fns, steps)
+        med = {k: statistics.median(v) * 1e3 for k, v in t.items()}
         wbytes = K * N // 2 + (K // (64 if fmt == "int4" else 32)) * N * (2 if fmt == "int4" else 1)
-        res.append({"M": M, "K": K, "N": N, "format": fmt, "us": us, "weight_gbs": wbytes / (us * 1e-6) / 1e9,
-                    "frac_hbm": wbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, "us_bf16_matmul": us_bf16,
-                    "us_w4a4_rank0": us_w4a4})
+        res.append({"M": M, "K": K, "N": N, "format": fmt, "us": med["w4a16"],
+                    "weight_gbs": wbytes / (med["w4a16"] * 1e-6) / 1e9,
+                    "frac_hbm": wbytes / (med["w4a16"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                    "us_bf16_matmul": med["bf16"], "us_w4a4_rank0": med["w4a4"]})
         del blobs, Ws, layer, W, Xf
         torch.cuda.empty_cache()
     return res
-
-
-def time_kernels(torch, S, rig, steps, warmup):
-    """Per-kernel durations with events on the launch stream: the activation
-    pass (svdq_quantize_act) and the GEMM (svdq_gemm), which together are the
-    same two launches as svdq_linear."""
-    d = rig.layer.desc
-    n = rig.nsets
-    M = rig.cfg.M
-
-    def one(s, evs=None):
-        if evs:
-            evs[0].record()
-        S.svdq_quantize_act(d, s["blob"], s["X"], s["codes"], s["scales"], s["T"] if d.rank else None, s["ws"])
-        if evs:
-            evs[1].record()
-        S.svdq_gemm(d, s["blob"], s["codes"], s["scales"], s["T"] if d.rank else None, M, s["Y"], S.OUT_BF16)
-        if evs:
-            evs[2].record()
-
-    for k in range(warmup):
-        one(rig.sets[k % n])
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for k in range(steps):
-        one(rig.sets[k % n], evs[k])
-    torch.cuda.synchronize()
-    tq = [e[0].elapsed_time(e[1]) for e in evs]
-    tg = [e[1].elapsed_time(e[2]) for e in evs]
-    return tq, tg
 
 
 def cpu_baseline(rig, rows_req):
@@ -497,19 +539,49 @@ def summarize_util(dirs, cfg, src_hash):
                       for k in kernels if k in out}))
 
 
-def run_config(args, cfg, torch, S, WL, to_tensor, with_cpu, lora=0, norm=False):
+def measure(args, cfg, torch, S, WL, to_tensor, with_cpu=False, lora=0, norm=False, rank0=False, contract=False):
+    """All timings of one workload (see the module docstring)."""
     rig = Rig(cfg, torch, S, WL, to_tensor, lora)
-    ms_fused, wall = time_fused(torch, S, rig, args.steps, args.warmup)
-    tq, tg = time_kernels(torch, S, rig, args.steps, args.warmup)
-    ms_unfused, _ = time_fused(torch, S, rig, args.steps, args.warmup, unfused=True)
-    ms_norm = time_norm(torch, S, rig, args.steps, args.warmup) if norm else None
-    A = algorithmic(cfg)
-    tq_ms, tg_ms = statistics.mean(tq), statistics.mean(tg)
-    out = dict(rig=rig, ms_fused=ms_fused, wall=wall, ms_unfused=ms_unfused, tq=tq, tg=tg, A=A,
-               tq_ms=tq_ms, tg_ms=tg_ms, ms_norm=ms_norm)
+    fused, unfused, quant, gemm = layer_fns(S, rig)
+    warm(torch, [fused, unfused, quant, gemm], args.warmup)
+    out = dict(rig=rig, A=algorithmic(cfg))
+    if contract:
+        out["ms_bracket"], out["wall"] = bracket(torch, fused, args.steps)
+    variants = [("fused", fused), ("unfused", unfused), ("quant", quant), ("gemm", gemm)]
+    rig0 = None
+    if rank0 and cfg.rank > 0:
+        rig0 = Rig(cfg.with_(rank=0), torch, S, WL, to_tensor)
+        fused0 = layer_fns(S, rig0)[0]
+        warm(torch, [fused0], args.warmup, 0.3)
+        variants.append(("fused_rank0", fused0))
+    t = interleaved(torch, variants, args.steps)
+    out["t"] = {k: pct(v) for k, v in t.items()}
+    if rig0 is not None:
+        out["prep_s_rank0"] = rig0.prep_s
+        del rig0
+    out["ms_norm"] = time_norm(torch, S, rig, args.steps, args.warmup) if norm else None
     if with_cpu:
         out["cpu"] = cpu_baseline(rig, args.cpu_rows)
     return out
+
+
+def summary(r, cfg):
+    """The per-workload record (times in microseconds)."""
+    A, t = r["A"], r["t"]
+    f, u, q, g = t["fused"]["median"], t["unfused"]["median"], t["quant"]["median"], t["gemm"]["median"]
+    gt = A["gemm_ops"] / (g / 1e3) / 1e12
+    rec = {"us_per_layer": us(t["fused"]), "us_per_layer_unfused": us(t["unfused"]),
+           "fused_vs_unfused_speedup": u / f, "effective_tops": A["gemm_ops"] / (f / 1e3) / 1e12,
+           "gemm_us": us(t["gemm"]), "gemm_tops": gt, "gemm_frac_peak": gt / PEAK_TFLOPS[cfg.fmt],
+           "peak_tops": PEAK_TFLOPS[cfg.fmt], "quant_us": us(t["quant"]),
+           "quant_frac_hbm": A["q_bytes"] / (q / 1e3) / 1e9 / PEAK_HBM_GBS}
+    if "fused_rank0" in t:
+        rec["us_per_layer_rank0"] = us(t["fused_rank0"])
+        rec["slab_overhead"] = f / t["fused_rank0"]["median"]
+    if r.get("ms_norm"):
+        rec["us_per_layer_norm_fused"] = r["ms_norm"][0] * 1e3
+        rec["us_per_layer_norm_separate"] = r["ms_norm"][1] * 1e3
+    return rec
 
 
 def main():
@@ -544,20 +616,24 @@ def main():
         if args.calibrate_copy:
             calibration_copy(torch)
         rig = Rig(cfg, torch, S, WL, to_tensor)
-        ms, _ = time_fused(torch, S, rig, args.steps, args.warmup)
-        time_fused(torch, S, rig, args.steps, args.warmup, unfused=True)
-        tq, tg = time_kernels(torch, S, rig, args.steps, args.warmup)
-        print(json.dumps({"workload": cfg.name, "ms_per_step": ms, "quant_ms": statistics.mean(tq),
-                          "gemm_ms": statistics.mean(tg)}), flush=True)
+        fused, unfused, quant, gemm = layer_fns(S, rig)
+        warm(torch, [fused, unfused, quant, gemm], args.warmup, 0.0)
+        t = interleaved(torch, [("fused", fused), ("unfused", unfused), ("quant", quant), ("gemm", gemm)],
+                        args.steps)
+        print(json.dumps({"workload": cfg.name, **{k: statistics.median(v) for k, v in t.items()}}), flush=True)
         return
 
-    r = run_config(args, cfg, torch, S, WL, to_tensor, with_cpu=not args.no_cpu_baseline, norm=args.norm)
+    rank0 = set(n for n in args.rank0.split(",") if n)
+    r = measure(args, cfg, torch, S, WL, to_tensor, with_cpu=not args.no_cpu_baseline, norm=args.norm,
+                rank0=cfg.name in rank0, contract=True)
     A, rig = r["A"], r["rig"]
     fmt = cfg.fmt
-    t_layer_s = r["ms_fused"] / 1e3
+    rec = summary(r, cfg)
+    t_layer_s = r["ms_bracket"] / 1e3
     tops = A["gemm_ops"] / t_layer_s / 1e12
-    gemm_tops = A["gemm_ops"] / (r["tg_ms"] / 1e3) / 1e12
-    q_gbs = A["q_bytes"] / (r["tq_ms"] / 1e3) / 1e9
+    g_ms, q_ms = r["t"]["gemm"]["median"], r["t"]["quant"]["median"]
+    gemm_tops = A["gemm_ops"] / (g_ms / 1e3) / 1e12
+    q_gbs = A["q_bytes"] / (q_ms / 1e3) / 1e9
     src_hash = kernel_source_hash()
     traffic, act_traffic = load_traffic(cfg.name, src_hash)
     line = {
@@ -567,7 +643,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": r["ms_fused"],
+        "ms_per_step": r["ms_bracket"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -579,16 +655,13 @@ def main():
         "roofline": {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_TFLOPS[fmt], "unit": "TFLOP/s",
                      "frac": gemm_tops / PEAK_TFLOPS[fmt], "traffic": traffic,
                      "kernel": ("gemm_fp4_kernel (FP4 block-scaled MFMA GEMM" if fmt == "fp4" else
-                                "gemm_kernel (INT4 codes on the E4M3 block-scaled MFMA") + f" + rank-{cfg.rank} bf16 slab + bias)",
-                     "avg_us": r["tg_ms"] * 1e3},
+                                "gemm_kernel (INT4 codes on the block-scaled MFMA") + f" + rank-{cfg.rank} bf16 slab + bias)",
+                     "avg_us": g_ms * 1e3, "timing": "median of per-launch HIP events"},
         "roofline_quant": {"bound": "hbm", "achieved": q_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": q_gbs / PEAK_HBM_GBS, "traffic": act_traffic,
-                           "kernel": "act_kernel (smooth + quantize + down-proj) + t_reduce_kernel",
-                           "avg_us": r["tq_ms"] * 1e3, "bytes": A["q_bytes"]},
-        "us_per_layer": r["ms_fused"] * 1e3,
-        "us_per_layer_unfused": r["ms_unfused"] * 1e3,
-        "fused_vs_unfused_speedup": r["ms_unfused"] / r["ms_fused"],
-        "gemm_effective_tops": gemm_tops,
+                           "kernel": "activation pass (smooth + quantize + down-projection)",
+                           "avg_us": q_ms * 1e3, "bytes": A["q_bytes"]},
+        **rec,
         "slab_share_of_ops": A["slab_flops"] / A["gemm_ops"],
         "prep_seconds": rig.prep_s,
         "working_set_mb": rig.working_set / 2 ** 20,
@@ -599,54 +672,35 @@ def main():
     }
     if "cpu" in r:
         line["cpu_baseline"] = r["cpu"]
-    if r.get("ms_norm"):
-        nf, ns = r["ms_norm"]
-        line["layernorm_fused"] = {"us_per_layer_norm_fused": nf * 1e3, "us_per_layer_norm_separate": ns * 1e3,
-                                   "speedup": ns / nf,
-                                   "note": "svdq_linear_ln on the norm's input against torch layer_norm (bf16 "
-                                           "out) followed by svdq_linear"}
+    del r, rig
+    torch.cuda.empty_cache()
     extra = {}
     for name in [n for n in args.extra.split(",") if n and n != cfg.name]:
         c = cfgs[name]
-        rr = run_config(args, c, torch, S, WL, to_tensor, with_cpu=False, norm=args.norm)
-        Ax = rr["A"]
-        gt = Ax["gemm_ops"] / (rr["tg_ms"] / 1e3) / 1e12
-        extra[name] = {"us_per_layer": rr["ms_fused"] * 1e3, "us_per_layer_unfused": rr["ms_unfused"] * 1e3,
-                       "fused_vs_unfused_speedup": rr["ms_unfused"] / rr["ms_fused"],
-                       "effective_tops": Ax["gemm_ops"] / (rr["ms_fused"] / 1e3) / 1e12,
-                       "gemm_us": rr["tg_ms"] * 1e3, "gemm_tops": gt, "gemm_frac_peak": gt / PEAK_TFLOPS[c.fmt],
-                       "peak_tops": PEAK_TFLOPS[c.fmt], "quant_us": rr["tq_ms"] * 1e3,
-                       "quant_frac_hbm": Ax["q_bytes"] / (rr["tq_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS}
-        if rr.get("ms_norm"):
-            extra[name]["us_per_layer_norm_fused"] = rr["ms_norm"][0] * 1e3
-            extra[name]["us_per_layer_norm_separate"] = rr["ms_norm"][1] * 1e3
+        rr = measure(args, c, torch, S, WL, to_tensor, norm=False, rank0=name in rank0)
+        extra[name] = summary(rr, c)
         del rr
         torch.cuda.empty_cache()
-    if args.w4a16:
-        line["w4a16_modulation"] = time_w4a16(torch, S, WL, to_tensor, min(args.steps, 200), args.warmup)
     if args.lora:
-        rr = run_config(args, cfg, torch, S, WL, to_tensor, with_cpu=False, lora=args.lora)
-        extra[f"{cfg.name}+lora{args.lora}"] = {
-            "rank": cfg.rank + args.lora, "us_per_layer": rr["ms_fused"] * 1e3,
-            "us_per_layer_unfused": rr["ms_unfused"] * 1e3,
-            "fused_vs_unfused_speedup": rr["ms_unfused"] / rr["ms_fused"],
-            "overhead_vs_base": rr["ms_fused"] / r["ms_fused"] - 1.0, "gemm_us": rr["tg_ms"] * 1e3,
-            "quant_us": rr["tq_ms"] * 1e3}
+        rr = measure(args, cfg, torch, S, WL, to_tensor, lora=args.lora)
+        rec_l = summary(rr, cfg)
+        rec_l["rank"] = cfg.rank + args.lora
+        rec_l["overhead_vs_base"] = rec_l["us_per_layer"]["median"] / line["us_per_layer"]["median"] - 1.0
+        extra[f"{cfg.name}+lora{args.lora}"] = rec_l
         del rr
         torch.cuda.empty_cache()
     if extra:
         line["extra_workloads"] = extra
+    if args.w4a16:
+        line["w4a16_modulation"] = time_w4a16(torch, S, WL, to_tensor, min(args.steps, 200), args.warmup)
+    if args.peaks:
+        line["measured_peaks"] = S.measure_peaks()
     print(json.dumps(line), flush=True)
 
     if args.sweep:
         for c in WL.sweep_configs():
-            rr = run_config(args, c, torch, S, WL, to_tensor, with_cpu=False)
-            A = rr["A"]
-            rec = {"workload": c.name, "us_per_layer": rr["ms_fused"] * 1e3,
-                   "us_unfused": rr["ms_unfused"] * 1e3, "speedup": rr["ms_unfused"] / rr["ms_fused"],
-                   "effective_tops": A["gemm_ops"] / (rr["ms_fused"] / 1e3) / 1e12,
-                   "gemm_frac_int8_peak": A["gemm_ops"] / (rr["tg_ms"] / 1e3) / 1e12 / PEAK_TFLOPS["int4"],
-                   "quant_gbs": A["q_bytes"] / (rr["tq_ms"] / 1e3) / 1e9}
+            rr = measure(args, c, torch, S, WL, to_tensor)
+            rec = {"workload": c.name, **summary(rr, c)}
             print(json.dumps(rec), file=sys.stderr, flush=True)
             del rr
             torch.cuda.empty_cache()

@@ -13,8 +13,8 @@ Sources (the pages are cited by title and section / equation):
       error identity, eq. (7)/(8), (10)-(14) residual bound, Fig. 6 fusion,
       Table 4 latency.
   [handbook] ai-infra handbook, quantization chapter ("扩散模型和 LLM 不一样的
-      地方"): fake-quant snippet (symmetric absmax, round-half-even, clamp),
-      SmoothQuant section (lambda_j = max|X_j|^a / max|W_j|^(1-a)), SVDQuant
+      地方"): printed toy tables (per-tensor / per-channel error, SmoothQuant
+      and rank tables), SmoothQuant section (lambda_j = max|X_j|^a / max|W_j|^(1-a)), SVDQuant
       section (L1 = U_r S_r, L2 = V_r^T, R = W_hat - L1 L2; per-64-element
       group scales), timestep section (dynamic activation scales).
 
@@ -24,14 +24,16 @@ notes of the repository):
     (the handbook uses torch.round, which is half-to-even).
   * INT4 groups: 64 consecutive elements along K (per token row for X, per
     output column for the residual R); scale s = fp16(max|v| / 7) (round to
-    nearest even); s == 0 gives all-zero codes; codes clamp to [-7, 7].
+    nearest even), saturating at 65504; s == 0 gives all-zero codes; codes
+    clamp to [-7, 7].
   * FP4 groups: 32 along K; E2M1 codes (grid 0, .5, 1, 1.5, 2, 3, 4, 6) with
     round-to-nearest, ties to the even code; a power-of-two (E8M0) scale
     2^e with e the smallest integer such that max|v| <= 6 * 2^e, clamped to
     [-127, 127]; an all-zero group has e = -127.
   * Negative values that round to zero are encoded as +0 (code 0).
-  * Smoothing factors are stored as fp32 lambda and fp32 1/lambda; the runtime
-    activation is x_hat = fp32(x * inv_lambda); W_hat = lambda32 * W (exact).
+  * Smoothing factors are stored as fp32 lambda (the real lambda rounded once)
+    and fp32 1/lambda; the runtime activation is x_hat = fp32(x * inv_lambda);
+    W_hat = lambda32 * W (exact).
   * Low-rank factors are stored in bf16; the residual is computed from the
     stored bf16 factors: R = W_hat - sum_t L1b[:, t] L2b[t, :] (fp64, t
     increasing) so that W_hat = L1b L2b + R holds to fp64 rounding.
@@ -42,6 +44,8 @@ notes of the repository):
     to the output type first, then adds Tb L2b and rounds again.
 """
 from __future__ import annotations
+
+from decimal import Decimal, localcontext
 
 import numpy as np
 
@@ -118,7 +122,8 @@ def rne_quotient(num, den) -> np.ndarray:
 
     Valid when den has at most 24 significant bits and |num/den| < 2^20, so
     that the half-way points (q +- 0.5) * den are exact in fp64 and the
-    comparisons below are exact.  The fp64 quotient picks a candidate q;
+    comparisons below are exact (larger quotients only occur with a
+    saturated scale, where the caller clamps the result to +-7 anyway).  The fp64 quotient picks a candidate q;
     the exact comparisons move q by one where the candidate is on the wrong
     side of (or exactly on) a half-way point.
     """
@@ -140,6 +145,13 @@ def _groups(v: np.ndarray, group: int) -> np.ndarray:
     return v.reshape(v.shape[:-1] + (K // group, group))
 
 
+def int4_scale(A) -> np.ndarray:
+    """INT4 group scale from the group absmax A: s = fp16(A / 7), saturating
+    at the largest finite fp16 value (65504) instead of overflowing to
+    infinity for A / 7 >= 65520; the codes then clamp to +-7."""
+    return np.minimum(to_fp16(np.asarray(A, dtype=np.float64) / 7.0), FP16_MAX)
+
+
 def quantize_int4_groups(v) -> tuple[np.ndarray, np.ndarray]:
     """Eq. (1) per group of 64 along the last axis, q_max = 7, fp16 scale.
 
@@ -150,7 +162,7 @@ def quantize_int4_groups(v) -> tuple[np.ndarray, np.ndarray]:
     """
     g = _groups(np.asarray(v, dtype=np.float64), 64)
     A = np.max(np.abs(g), axis=-1)
-    s = to_fp16(A / 7.0)
+    s = int4_scale(A)
     safe = np.where(s > 0, s, 1.0)[..., None]
     q = np.clip(rne_quotient(g, safe), -7, 7)
     q = np.where((s > 0)[..., None], q, 0.0)
@@ -263,22 +275,37 @@ def act_absmax(X_bits) -> np.ndarray:
     return np.max(np.abs(bf16_bits_to_f64(X_bits)), axis=0).astype(np.float32)
 
 
+def real_to_fp32(v: Decimal) -> float:
+    """The fp32 number nearest to the positive real v (a Decimal), ties to
+    the even significand: the neighbours of a first guess are compared with
+    v exactly (Decimal(float) is exact)."""
+    f = np.float32(float(v))
+    cands = [np.nextafter(f, np.float32(0)), f, np.nextafter(f, np.float32(np.inf))]
+    best = min(cands, key=lambda c: (abs(Decimal(float(c)) - v), int(np.float32(c).view(np.uint32)) & 1))
+    return float(best)
+
+
 def smoothing_factors(a, W, alpha: float, no_smoothing: bool = False):
     """[handbook] SmoothQuant section: lambda_j = max|X_j|^alpha / max|W_j|^(1-alpha),
     where W_j is row j of the K x N weight; [walkthrough] eq. (5): X W =
-    (X diag(lambda)^-1)(diag(lambda) W).  Computed in fp64; stored as
-    lambda32 = fp32(lambda) and inv32 = fp32(1 / lambda32).  A channel with a
+    (X diag(lambda)^-1)(diag(lambda) W).
+
+    lambda32 is the real lambda_j rounded once to fp32 (evaluated as
+    exp(alpha ln a - (1 - alpha) ln w) with 60 significant digits, far more
+    than the rounding needs); inv32 = fp32(1 / lambda32).  A channel with a
     zero activation or weight maximum keeps lambda = 1.
     """
     a = np.asarray(a, dtype=np.float64)
     w = np.max(np.abs(np.asarray(W, dtype=np.float64)), axis=1)
-    if no_smoothing:
-        lam = np.ones_like(a)
-    else:
-        ok = (a > 0) & (w > 0)
-        with np.errstate(divide="ignore", invalid="ignore"):
-            lam = np.where(ok, a ** alpha / w ** (1.0 - alpha), 1.0)
-    lam32 = to_fp32(lam)
+    lam32 = np.ones_like(a)
+    if not no_smoothing:
+        with localcontext() as ctx:
+            ctx.prec = 60
+            al = Decimal(float(alpha))
+            for j in range(a.size):
+                if a[j] > 0 and w[j] > 0:
+                    v = (al * Decimal(float(a[j])).ln() - (1 - al) * Decimal(float(w[j])).ln()).exp()
+                    lam32[j] = real_to_fp32(v)
     inv32 = to_fp32(1.0 / lam32)
     return lam32, inv32
 
@@ -353,7 +380,7 @@ def gptq_weights(R, xhat_cal, fmt: str, damp: float = 0.01):
     for k in range(K):
         if k % g == 0:
             A = np.max(np.abs(R[k:k + g]), axis=0)
-            scales[k // g] = to_fp16(A / 7.0) if fmt == INT4 else e8m0_exponent(A)
+            scales[k // g] = int4_scale(A) if fmt == INT4 else e8m0_exponent(A)
         s = scales[k // g]
         if fmt == INT4:
             safe = np.where(s > 0, s, 1.0)
@@ -539,15 +566,29 @@ def linear_rows(prep: dict, X_bits_rows, out: str = "bf16") -> dict:
 # ============================================================ error analysis
 
 
-def fake_quant(x, bits: int, axis=None):
-    """Symmetric absmax fake-quantization of eq. (1) at one scale per tensor
-    (axis None) or per slice along ``axis``; amax floored at 1e-8 as in the
-    [handbook] fake-quant snippet.  Returns s * clamp(round(x / s))."""
+def q_eq1(x, bits: int, axis=None) -> np.ndarray:
+    """Q(x) of [walkthrough] eq. (1) as real values, for the pages' toy
+    tables: s * round(x / s) with s = max|x| / q_max and q_max = 2^(bits-1) - 1,
+    one scale for the whole tensor (axis None) or one per slice along
+    ``axis``; round is half-to-even of the fp64 quotient (the toy tables
+    are printed to 4 decimals).  A slice with max|x| = 0 quantizes to 0 (the
+    group reading of ``quantize_int4_groups``).  |x / s| <= q_max holds by
+    the choice of s, so no clamp is needed."""
     x = np.asarray(x, dtype=np.float64)
-    qmax = 2 ** (bits - 1) - 1
-    amax = np.abs(x).max() if axis is None else np.abs(x).max(axis=axis, keepdims=True)
-    s = np.maximum(amax, 1e-8) / qmax
-    return np.clip(np.rint(x / s), -qmax, qmax) * s
+    q_max = float(2 ** (bits - 1) - 1)
+    s = np.broadcast_to(np.max(np.abs(x), axis=axis, keepdims=axis is not None) / q_max, x.shape)
+    codes = np.rint(np.divide(x, s, out=np.zeros_like(x), where=s > 0))
+    return codes * s
+
+
+def eq5_toy(x_hat, W_hat, rank: int, bits: int) -> np.ndarray:
+    """[walkthrough] eq. (5) with the toy tables' per-tensor quantizer:
+    X_hat L1 L2 + Q(X_hat) Q(R), R = W_hat - L1 L2, L1 L2 the rank-r SVD
+    factors (no bf16 rounding: the toy tables keep the branch in high
+    precision)."""
+    L1, L2 = lowrank_factors(W_hat, rank)
+    R = residual(W_hat, L1, L2)
+    return q_eq1(x_hat, bits) @ q_eq1(R, bits) + (x_hat @ L1) @ L2
 
 
 def quant_error(X, W, QX, QW) -> float:

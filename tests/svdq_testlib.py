@@ -152,12 +152,13 @@ def blob_sections(layer):
                 bias=bias, raw_wcodes=raw_codes, raw_wscales=raw_scales, l1t=l1t, l2t=l2t)
 
 
-def oracle_prep_from_blob(sections, W_bits, fmt: str, bias_bits=None, cols=None) -> dict:
-    """The oracle's prepared layer built on the blob's stored lambda32, L1b,
-    L2b (the SVD factors are not unique, so parity is checked given them).
+def oracle_prep_from_blob(sections, W_bits, fmt: str, bias_bits=None, cols=None, lam32=None) -> dict:
+    """The oracle's prepared layer built on the blob's stored L1b, L2b (the
+    SVD factors are not unique, so parity is checked given them) and on
+    ``lam32`` (the oracle's own smoothing factors; the blob's when None).
     ``cols`` restricts the residual to a subset of output columns."""
     W = O.bf16_bits_to_f64(W_bits)
-    lam32 = sections["lam32"]
+    lam32 = sections["lam32"] if lam32 is None else np.asarray(lam32, dtype=np.float64)
     inv32 = O.to_fp32(1.0 / lam32)
     L2b = sections["L2b"]
     if cols is not None:

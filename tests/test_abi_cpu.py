@@ -226,7 +226,7 @@ def test_host_jacobi_eigensolver(tmp_path):
     src.write_text(JACOBI_MAIN)
     exe = tmp_path / "jac"
     lin = os.path.join(ROOT, "w4a4_quantized_gemm_amd", "csrc", "svdq_linalg.cpp")
-    subprocess.run(["g++", "-O2", "-std=c++17", str(src), lin, "-o", str(exe)], check=True)
+    subprocess.run(["g++", "-O2", "-std=c++17", str(src), lin, "-o", str(exe), "-lquadmath"], check=True)
     rng = np.random.default_rng(0)
     for n, kind in ((1, "rand"), (7, "rand"), (48, "rand"), (96, "lowrank"), (64, "zero")):
         if kind == "zero":
@@ -271,7 +271,7 @@ def test_host_cholesky_of_inverse(tmp_path):
     src.write_text(CHOL_MAIN)
     exe = tmp_path / "chol"
     lin = os.path.join(ROOT, "w4a4_quantized_gemm_amd", "csrc", "svdq_linalg.cpp")
-    subprocess.run(["g++", "-O2", "-std=c++17", str(src), lin, "-o", str(exe)], check=True)
+    subprocess.run(["g++", "-O2", "-std=c++17", str(src), lin, "-o", str(exe), "-lquadmath"], check=True)
     rng = np.random.default_rng(1)
     for n in (1, 5, 40):
         B = rng.standard_normal((n, n))
@@ -283,3 +283,46 @@ def test_host_cholesky_of_inverse(tmp_path):
         assert np.allclose(U.T @ U, np.linalg.inv(A), atol=1e-10 * np.abs(np.linalg.inv(A)).max())
     bad = "2\n1 2\n2 1"
     assert subprocess.run([str(exe)], input=bad, capture_output=True, text=True, check=True).stdout.strip() == "notpd"
+
+
+LAMBDA_MAIN = r"""
+#include <cstdio>
+#include <vector>
+namespace svdq { void smoothing_lambda(const float*, const float*, int, float, bool, float*, float*); }
+int main() {
+  int n; float alpha; int nosm;
+  if (scanf("%d %f %d", &n, &alpha, &nosm) != 3) return 1;
+  std::vector<float> a(n), w(n), l(n), i(n);
+  for (int j = 0; j < n; j++) if (scanf("%a %a", &a[j], &w[j]) != 2) return 1;
+  svdq::smoothing_lambda(a.data(), w.data(), n, alpha, nosm != 0, l.data(), i.data());
+  for (int j = 0; j < n; j++) printf("%a %a\n", l[j], i[j]);
+  return 0;
+}
+"""
+
+
+def test_host_smoothing_factors_match_oracle(tmp_path):
+    """The library computes lambda32 on the host (the real a^alpha /
+    w^(1 - alpha) rounded once to fp32): bit-equal to the oracle's at several
+    strengths, on random maxima over many binades, zero channels and the
+    no-smoothing flag."""
+    import oracle as O
+    src = tmp_path / "main.cpp"
+    src.write_text(LAMBDA_MAIN)
+    exe = tmp_path / "lam"
+    lin = os.path.join(ROOT, "w4a4_quantized_gemm_amd", "csrc", "svdq_linalg.cpp")
+    subprocess.run(["g++", "-O2", "-std=c++17", str(src), lin, "-o", str(exe), "-lquadmath"], check=True)
+    rng = np.random.default_rng(3)
+    n = 3000
+    a = (rng.random(n) * np.exp2(rng.integers(-40, 40, n))).astype(np.float32)
+    w = (rng.random(n) * np.exp2(rng.integers(-40, 40, n))).astype(np.float32)
+    a[:5] = 0.0
+    w[5:10] = 0.0
+    for alpha, nosm in ((0.5, 0), (0.25, 0), (0.75, 0), (0.3, 0), (0.5, 1)):
+        inp = f"{n} {float(np.float32(alpha)).hex()} {nosm}\n" + "\n".join(
+            f"{float(x).hex()} {float(y).hex()}" for x, y in zip(a, w))
+        out = subprocess.run([str(exe)], input=inp, capture_output=True, text=True, check=True).stdout.split()
+        got = np.array([float.fromhex(x) for x in out]).reshape(n, 2)
+        lam32, inv32 = O.smoothing_factors(a, w.astype(np.float64)[:, None], float(np.float32(alpha)), nosm == 1)
+        assert np.array_equal(got[:, 0], lam32), (alpha, int(np.sum(got[:, 0] != lam32)))
+        assert np.array_equal(got[:, 1], inv32)

@@ -61,9 +61,16 @@ def _prepare(torch_dev, cfg, X_bits, W_bits, b_bits, **kw):
     return layer, X, a
 
 
-def _check_weights(layer, W_bits, fmt, b_bits=None, cols=None):
+def _check_weights(layer, W_bits, fmt, b_bits=None, cols=None, X_bits=None, alpha=0.5, no_smoothing=False):
+    """Weight codes, scales and bias of the blob against the oracle's
+    quantization of the residual taken against the blob's L1b, L2b.  With the
+    calibration activations (or no smoothing) the blob's lambda32 must equal
+    the oracle's bit for bit, and the reference uses the oracle's own."""
     sec = blob_sections(layer)
-    ref = oracle_prep_from_blob(sec, W_bits, fmt, b_bits, cols)
+    lam_ref = None
+    if X_bits is not None or no_smoothing:
+        lam_ref = _check_lambda(sec, X_bits, W_bits, alpha, no_smoothing)
+    ref = oracle_prep_from_blob(sec, W_bits, fmt, b_bits, cols, lam32=lam_ref)
     codes, scales = sec["w_codes"], sec["w_scales"]
     if cols is not None:
         codes, scales = codes[:, cols], scales[:, cols]
@@ -79,12 +86,12 @@ def _check_weights(layer, W_bits, fmt, b_bits=None, cols=None):
 
 
 def _check_lambda(sec, X_bits, W_bits, alpha, no_smoothing=False):
-    lam32, _ = O.smoothing_factors(O.act_absmax(X_bits), O.bf16_bits_to_f64(W_bits), alpha, no_smoothing)
-    got = sec["lam32"].astype(np.float32)
-    ref = lam32.astype(np.float32)
-    ulps = np.abs(got.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
-    assert ulps.max() <= 1, ulps.max()
-    return int((ulps > 0).sum())
+    """lambda32 bit-equal to the oracle's (the real lambda rounded once to
+    fp32, on both sides); returns the oracle's."""
+    a = np.zeros(sec["lam32"].size, np.float32) if X_bits is None else O.act_absmax(X_bits)
+    lam32, _ = O.smoothing_factors(a, O.bf16_bits_to_f64(W_bits), alpha, no_smoothing)
+    assert np.array_equal(sec["lam32"], lam32), int(np.sum(sec["lam32"] != lam32))
+    return lam32
 
 
 def _run_act(torch_dev, layer, X, M, with_ws):
@@ -148,6 +155,7 @@ def _check_linear(torch_dev, layer, X, X_bits, ref_prep, rows=None, cols=None, m
             Y = Y[rows]
         if cols is not None:
             Y = Y[:, cols]
+        assert np.all(np.isfinite(Y)), "non-finite output"
         e = O.rel_fro(Y, ref)
         errs[(oname, unfused)] = e
         assert e <= TOL, (oname, unfused, e)
@@ -178,8 +186,7 @@ def test_tiny_config_end_to_end(torch_dev, fmt):
     layer, X, _ = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
     import w4a4_quantized_gemm_amd as S
     S.svdq_check_blob(layer.desc, layer.blob)
-    sec, ref = _check_weights(layer, W_bits, fmt)
-    _check_lambda(sec, X_bits, W_bits, cfg.alpha)
+    sec, ref = _check_weights(layer, W_bits, fmt, X_bits=X_bits, alpha=cfg.alpha)
     # the GPU SVD reaches the Eckart-Young optimum (walkthrough: SVD gives the
     # minimal ||W_hat - L1 L2||_F over rank-r approximations)
     sig = np.linalg.svd(ref["W_hat"], compute_uv=False)
@@ -211,9 +218,49 @@ def test_small_shapes(torch_dev, M, K, N, rank, bias, fmt):
                       n_outlier_channels=min(8, K // 16), bias_std=0.02 if bias else 0.0, seed=M + K + N)
     X_bits, W_bits, b_bits = WL.make_layer(cfg)
     layer, X, _ = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
-    sec, ref = _check_weights(layer, W_bits, fmt, b_bits)
+    sec, ref = _check_weights(layer, W_bits, fmt, b_bits, X_bits=X_bits, alpha=cfg.alpha)
     _check_act(torch_dev, layer, X, X_bits, ref)
     _check_linear(torch_dev, layer, X, X_bits, ref)
+
+
+@pytest.mark.parametrize("alpha,fmt", [(0.25, O.INT4), (0.75, O.INT4), (0.25, O.FP4), (0.75, O.FP4)])
+def test_smoothing_strengths(torch_dev, alpha, fmt):
+    """Smoothing strengths other than 0.5 (the handbook's SmoothQuant
+    section: alpha is a tuning knob, commonly 0.5): lambda32 bit-equal to
+    the oracle's, then the usual weight, activation and layer parity."""
+    _say(f"case: alpha={alpha} fmt={fmt}")
+    cfg = WL.C2.with_(name="alpha", M=300, K=384, N=320, rank=16, fmt=fmt, alpha=alpha, w_std=1 / np.sqrt(384),
+                      bias_std=0.02, seed=41)
+    X_bits, W_bits, b_bits = WL.make_layer(cfg)
+    layer, X, _ = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
+    sec, ref = _check_weights(layer, W_bits, fmt, b_bits, X_bits=X_bits, alpha=alpha)
+    assert np.ptp(np.log2(sec["lam32"])) > 1.0                 # smoothing is active
+    _check_act(torch_dev, layer, X, X_bits, ref)
+    _check_linear(torch_dev, layer, X, X_bits, ref)
+
+
+def test_blob_round_trip(torch_dev, tmp_path):
+    """A prepared blob is position independent: written to a file, read back
+    into a new device buffer, it passes the header check and gives the same
+    output bit for bit."""
+    import w4a4_quantized_gemm_amd as S
+    torch, dev = torch_dev
+    _say("case: blob save / reload")
+    cfg = WL.C1.with_(fmt=O.FP4, bias_std=0.02)
+    X_bits, W_bits, b_bits = WL.make_layer(cfg)
+    layer, X, _ = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
+    path = tmp_path / "layer.npy"
+    np.save(path, to_np(layer.blob))
+    pad = torch.empty(4096, dtype=torch.uint8, device=dev)       # a different device address
+    blob2 = torch.from_numpy(np.load(path)).to(dev)
+    layer2 = S.SVDQLinear(layer.desc, blob2)
+    S.svdq_check_blob(layer2.desc, layer2.blob)
+    assert layer2.blob.data_ptr() != layer.blob.data_ptr()
+    y1 = layer(X, out_dtype=S.OUT_F32)
+    y2 = layer2(X, out_dtype=S.OUT_F32)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    del pad
 
 
 def test_factors_given_and_no_smoothing(torch_dev):
@@ -234,14 +281,13 @@ def test_factors_given_and_no_smoothing(torch_dev):
     layer = S.SVDQLinear.prepare(W, ad, 32, "int4", 0.5, L1=L1, L2=L2)
     sec = blob_sections(layer)
     assert np.array_equal(sec["L1b"], ref["L1b"]) and np.array_equal(sec["L2b"], ref["L2b"])
-    _check_lambda(sec, X_bits, W_bits, 0.5)
-    sec, ref2 = _check_weights(layer, W_bits, O.INT4)
+    sec, ref2 = _check_weights(layer, W_bits, O.INT4, X_bits=X_bits, alpha=0.5)
     _check_linear(torch_dev, layer, X, X_bits, ref2)
     # no smoothing: lambda = 1 exactly
     layer = S.SVDQLinear.prepare(W, None, 32, "fp4", 0.5, no_smoothing=True)
     sec = blob_sections(layer)
     assert np.all(sec["lam32"] == 1.0) and np.all(sec["inv32"] == 1.0)
-    sec, ref3 = _check_weights(layer, W_bits, O.FP4)
+    sec, ref3 = _check_weights(layer, W_bits, O.FP4, no_smoothing=True)
     _check_act(torch_dev, layer, X, X_bits, ref3)
     _check_linear(torch_dev, layer, X, X_bits, ref3)
 
@@ -260,7 +306,7 @@ def test_merge_lowrank(torch_dev, fmt, re):
                       n_outlier_channels=8, bias_std=0.02, seed=77)
     X_bits, W_bits, b_bits = WL.make_layer(cfg)
     layer, X, _ = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
-    sec, ref = _check_weights(layer, W_bits, fmt, b_bits)
+    sec, ref = _check_weights(layer, W_bits, fmt, b_bits, X_bits=X_bits, alpha=cfg.alpha)
     rng = np.random.default_rng(78)
     A_bits = O.bf16_bits_of(O.to_bf16(rng.standard_normal((K, re)) * 0.05).astype(np.float32))
     B_bits = O.bf16_bits_of(O.to_bf16(rng.standard_normal((re, N)) * 0.05).astype(np.float32))
@@ -293,7 +339,7 @@ def test_w4a16(torch_dev, fmt, M, K, N):
                       n_outlier_channels=8, bias_std=0.02, seed=M + K)
     X_bits, W_bits, b_bits = WL.make_layer(cfg)
     layer, Xfull, _ = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
-    sec, ref = _check_weights(layer, W_bits, fmt, b_bits)
+    sec, ref = _check_weights(layer, W_bits, fmt, b_bits, X_bits=X_bits, alpha=cfg.alpha)
     X = Xfull[:M].contiguous()
     ws = torch.empty(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev)
     for out, oname in ((S.OUT_F32, "f32"), (S.OUT_BF16, "bf16")):
@@ -382,7 +428,7 @@ def test_norm_fused_pass(torch_dev, fmt):
     g_bits = O.bf16_bits_of(O.to_bf16(rng.uniform(0.5, 1.5, K)).astype(np.float32))
     be_bits = O.bf16_bits_of(O.to_bf16(rng.standard_normal(K) * 0.1).astype(np.float32))
     layer, X, _ = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
-    sec, ref = _check_weights(layer, W_bits, fmt, b_bits)
+    sec, ref = _check_weights(layer, W_bits, fmt, b_bits, X_bits=X_bits, alpha=cfg.alpha)
     gamma, beta = np_bits_to_bf16_tensor(g_bits, dev), np_bits_to_bf16_tensor(be_bits, dev)
     for beta_t, beta_b in ((beta, be_bits), (None, None)):
         norm = (g_bits, beta_b, eps)
@@ -454,13 +500,16 @@ def test_quantizer_edge_values(torch_dev):
     x[7] = rng.standard_normal(K) * 2.0 ** -125           # E8M0 exponents near -127 (exact FP4 path)
     x[8] = rng.standard_normal(K) * 2.0 ** -118           # around the -120 switch of the FP4 conversion
     x[9] = (np.arange(K) % 7 - 3.0) * 2.0 ** -131         # bf16 subnormals
+    x[10] = rng.standard_normal(K) * 1.0e6                # INT4 scales saturate at 65504 (A / 7 > 65520)
+    x[11, :64] = 7.0 * 65504.0                             # exactly at the largest finite scale
+    x[11, 64:128] = np.linspace(-1.0e7, 1.0e7, 64)
     X_bits = O.bf16_bits_of(O.to_bf16(x).astype(np.float32))
     W_bits = O.bf16_bits_of(O.to_bf16(rng.standard_normal((K, N)) * 0.05).astype(np.float32))
     X = np_bits_to_bf16_tensor(X_bits, dev)
     W = np_bits_to_bf16_tensor(W_bits, dev)
     for fmt in ("int4", "fp4"):
         layer = S.SVDQLinear.prepare(W, None, 16, fmt, 0.5, no_smoothing=True)
-        sec, ref = _check_weights(layer, W_bits, fmt)
+        sec, ref = _check_weights(layer, W_bits, fmt, no_smoothing=True)
         _check_act(torch_dev, layer, X, X_bits, ref)
         _check_linear(torch_dev, layer, X, X_bits, ref, modes=[(S.OUT_F32, False), (S.OUT_F32, True)])
 
@@ -499,9 +548,44 @@ def test_full_size_workloads(torch_dev, cfg):
     rng = np.random.default_rng(11)
     rows = np.unique(np.concatenate([rng.choice(cfg.M, 192, replace=False), [0, cfg.M - 1]]))
     cols = np.unique(np.concatenate([rng.choice(cfg.N, 384, replace=False), [0, cfg.N - 1]]))
-    sec, ref = _check_weights(layer, W_bits, cfg.fmt, b_bits, cols=cols)
-    nlam = _check_lambda(sec, X_bits, W_bits, cfg.alpha)
-    _say(f"  lambda32 differing by one ulp: {nlam}")
+    sec, ref = _check_weights(layer, W_bits, cfg.fmt, b_bits, cols=cols, X_bits=X_bits, alpha=cfg.alpha)
+    if cfg is not WL.C4_FP4:            # the same weight (and split) as the INT4 variant
+        # the GPU's randomized SVD reaches the Eckart-Young optimum at full
+        # size too: ||R||_F within (1 + 1e-4) of sqrt(sum_{i > r} sigma_i^2)
+        W_hat = sec["lam32"][:, None] * O.bf16_bits_to_f64(W_bits)
+        R_norm = np.linalg.norm(O.residual(W_hat, sec["L1b"], sec["L2b"]))
+        sig = np.linalg.svd(W_hat, compute_uv=False)
+        opt = np.sqrt(np.sum(sig[cfg.rank:] ** 2))
+        _say(f"  ||R||_F / optimum - 1 = {R_norm / opt - 1:.3e}")
+        assert opt * (1 - 1e-12) <= R_norm <= opt * (1 + 1e-4)
+        del W_hat
+    _check_act(torch_dev, layer, X, X_bits, ref, rows=rows)
+    errs = _check_linear(torch_dev, layer, X, X_bits, ref, rows=rows, cols=cols)
+    _say(f"  rel errors {errs}")
+
+
+# ---------------------------------------------- further large shapes, sampled
+SAMPLED = [
+    # the FP4 GEMM's general path (rank above 96, or fewer stages than the
+    # straight-line schedule needs) with more tiles than compute units
+    WL.C3.with_(name="c3_fc1_rank128_fp4", rank=128),
+    WL.C3.with_(name="fp4_4608x256x4096_r16", K=256, N=4096, rank=16, w_std=1 / 16.0, seed=7),
+    # two points of the shape sweep: few rows over a long K (the activation
+    # pass splits K eight ways), and the largest M
+    [c for c in WL.sweep_configs() if c.name == "c5_M256_K12288_N3072_r64"][0],
+    [c for c in WL.sweep_configs() if c.name == "c5_M16384_K3072_N12288_r32"][0],
+]
+
+
+@pytest.mark.parametrize("cfg", SAMPLED, ids=[c.name for c in SAMPLED])
+def test_sampled_shapes(torch_dev, cfg):
+    _say(f"case: sampled {cfg.name} ({cfg.M}x{cfg.K}x{cfg.N}, r={cfg.rank}, {cfg.fmt})")
+    X_bits, W_bits, b_bits = WL.make_layer(cfg)
+    layer, X, _ = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
+    rng = np.random.default_rng(12)
+    rows = np.unique(np.concatenate([rng.choice(cfg.M, min(cfg.M, 160), replace=False), [0, cfg.M - 1]]))
+    cols = np.unique(np.concatenate([rng.choice(cfg.N, 320, replace=False), [0, cfg.N - 1]]))
+    sec, ref = _check_weights(layer, W_bits, cfg.fmt, b_bits, cols=cols, X_bits=X_bits, alpha=cfg.alpha)
     _check_act(torch_dev, layer, X, X_bits, ref, rows=rows)
     errs = _check_linear(torch_dev, layer, X, X_bits, ref, rows=rows, cols=cols)
     _say(f"  rel errors {errs}")

@@ -351,7 +351,7 @@ def test_eq8_gaussian_residual_bound_monte_carlo():
     errs, norms = [], []
     for _ in range(30):
         R = rng.standard_normal((n_side, n_side)) * 0.3
-        errs.append(np.linalg.norm(R - O.fake_quant(R, 4)))
+        errs.append(np.linalg.norm(R - O.q_eq1(R, 4)))
         norms.append(np.linalg.norm(R))
     size = n_side * n_side
     c = O.gaussian_c(size)
@@ -372,48 +372,52 @@ def test_unfused_rounding_model_differs_only_by_double_rounding():
 
 
 # ---------------------------------------------------- the handbook's tables
-def _handbook_inputs():
+def _toy_inputs():
+    """The toy tensors of the handbook's quantization chapter, regenerated:
+    torch's generator seeded with 0, a 1024 x 512 standard normal activation
+    and a 512 x 512 weight of standard deviation 0.02, drawn in that order
+    (the chapter's shapes and seed; the printed tables depend on them)."""
     torch = pytest.importorskip("torch")
     torch.manual_seed(0)
-    base = torch.randn(1024, 512).double().numpy()
+    x = torch.randn(1024, 512).double().numpy()
     W = (torch.randn(512, 512) * 0.02).double().numpy()
-    return base, W
+    return x, W
 
 
-def _smooth_plain(x, W, alpha=0.5):
-    """The handbook's per-channel smoothing, through the oracle's factors."""
-    lam32, inv32 = O.smoothing_factors(np.abs(x).max(axis=0), W, alpha)
-    return x * inv32[None, :], W * lam32[:, None]
+def _with_outliers(x, factor):
+    """Channels 0-3 scaled by ``factor`` (the chapter's outlier channels)."""
+    y = x.copy()
+    y[:, :4] *= factor
+    return y
 
 
 def test_handbook_printed_tables():
+    """The oracle's eq. (1) quantizer, smoothing factors and eq. (5) split
+    reproduce the three toy tables of the handbook's quantization chapter
+    (outlier table; SmoothQuant table; SVDQuant rank table) to their four
+    printed decimals."""
     gold = json.load(open(os.path.join(HERE, "golden", "handbook_toy_tables.json")))
-    base, W = _handbook_inputs()
+    x0, W = _toy_inputs()
     tol = 6e-5   # printed to 4 decimals; the page computed in fp32
     for factor, row in gold["outlier_table"]["rows"].items():
-        x = base.copy()
-        x[:, :4] *= float(factor)
-        got = [O.rel_fro(O.fake_quant(x, 8)[:, 4:], x[:, 4:]),
-               O.rel_fro(O.fake_quant(x, 8, axis=0)[:, 4:], x[:, 4:]),
-               O.rel_fro(O.fake_quant(x, 4)[:, 4:], x[:, 4:]),
-               O.rel_fro(O.fake_quant(x, 4, axis=0)[:, 4:], x[:, 4:])]
+        x = _with_outliers(x0, float(factor))
+        normal = slice(4, None)            # the error is reported on the normal channels
+        got = [O.rel_fro(O.q_eq1(x, bits, axis)[:, normal], x[:, normal])
+               for bits, axis in ((8, None), (8, 0), (4, None), (4, 0))]
         assert np.allclose(got, row, atol=tol), (factor, got, row)
-    x = base.copy()
-    x[:, :4] *= 50
+    x = _with_outliers(x0, 50.0)
     y = x @ W
+    lam32, inv32 = O.smoothing_factors(np.abs(x).max(axis=0), W, 0.5)
+    x_hat, W_hat = x * inv32[None, :], W * lam32[:, None]
     sq = gold["smoothquant_table"]
-    xs, Ws = _smooth_plain(x, W)
-    assert abs(O.rel_fro(O.fake_quant(x, 8) @ O.fake_quant(W, 8), y) - sq["w8a8_direct"]) < tol
-    assert abs(O.rel_fro(O.fake_quant(xs, 8) @ O.fake_quant(Ws, 8), y) - sq["w8a8_smooth"]) < tol
-    assert abs(O.rel_fro(O.fake_quant(x, 4) @ O.fake_quant(W, 4), y) - sq["w4a4_direct"]) < tol
-    assert abs(O.rel_fro(O.fake_quant(xs, 4) @ O.fake_quant(Ws, 4), y) - sq["w4a4_smooth"]) < tol
+    for key, a, b, bits in (("w8a8_direct", x, W, 8), ("w8a8_smooth", x_hat, W_hat, 8),
+                            ("w4a4_direct", x, W, 4), ("w4a4_smooth", x_hat, W_hat, 4)):
+        got = O.rel_fro(O.q_eq1(a, bits) @ O.q_eq1(b, bits), y)
+        assert abs(got - sq[key]) < tol, (key, got, sq[key])
     for r, want in gold["svdquant_table"]["rank"].items():
-        r = int(r)
-        L1, L2 = O.lowrank_factors(Ws, r)
-        R = O.residual(Ws, L1, L2)
-        yq = O.fake_quant(xs, 4) @ O.fake_quant(R, 4) + xs @ L1 @ L2
-        assert abs(O.rel_fro(yq, y) - want) < tol, (r, O.rel_fro(yq, y), want)
-    floor = O.rel_fro(O.fake_quant(base, 4) @ O.fake_quant(W, 4), base @ W)
+        got = O.rel_fro(O.eq5_toy(x_hat, W_hat, int(r), 4), y)
+        assert abs(got - want) < tol, (r, got, want)
+    floor = O.rel_fro(O.q_eq1(x0, 4) @ O.q_eq1(W, 4), x0 @ W)
     assert abs(floor - gold["svdquant_table"]["no_outlier_w4a4_floor"]) < tol
 
 
@@ -590,3 +594,94 @@ def test_gptq_lowers_the_calibration_error(fmt):
         assert np.all(np.abs(q) <= 7)
     else:
         assert np.all(q < 16)
+
+
+# ---------------------------------------------------------- exact hand cases
+def test_smoothing_exponents_hand_cases():
+    """lambda = a^alpha / w^(1 - alpha) (handbook SmoothQuant section) at
+    alpha != 0.5, on values whose powers are exact: swapping the two
+    exponents, or the roles of a and w, changes every one of these."""
+    a = np.array([16.0, 1.0, 81.0, 16.0, 625.0], np.float32)
+    W = np.array([[1.0], [16.0], [1.0], [81.0], [1.0]])
+    lam32, inv32 = O.smoothing_factors(a, W, 0.25)
+    # 16^.25 = 2; 1 / 16^.75 = 1/8; 81^.25 = 3; 16^.25 / 81^.75 = 2/27; 625^.25 = 5
+    assert lam32.tolist() == [2.0, 0.125, 3.0, float(np.float32(2.0 / 27.0)), 5.0]
+    assert inv32.tolist() == [0.5, 8.0, float(np.float32(1.0 / np.float32(3.0))), float(np.float32(27.0 / 2.0)), float(np.float32(1.0 / np.float32(5.0)))]
+    lam32, _ = O.smoothing_factors(a, W, 0.75)
+    # 16^.75 = 8; 1 / 16^.25 = 1/2; 81^.75 = 27; 16^.75 / 81^.25 = 8/3; 625^.75 = 125
+    assert lam32.tolist() == [8.0, 0.5, 27.0, float(np.float32(8.0 / 3.0)), 125.0]
+
+
+def test_smoothing_lambda_is_correctly_rounded():
+    """At alpha = 0.5 and w a power of two, lambda = sqrt(a / w) with a / w
+    exact in fp32, and IEEE's fp32 square root is correctly rounded: the
+    stored lambda32 must be exactly that value (a value computed in fp64
+    and then rounded to fp32 is not, for some inputs)."""
+    rng = np.random.default_rng(31)
+    a = (rng.random(4000) * np.exp2(rng.integers(-20, 20, 4000))).astype(np.float32)
+    w = np.exp2(rng.integers(-10, 10, 4000)).astype(np.float64)
+    lam32, _ = O.smoothing_factors(a, w[:, None], 0.5)
+    ref = np.sqrt((a.astype(np.float64) / w).astype(np.float32)).astype(np.float64)
+    assert np.array_equal(lam32, ref)
+
+
+def test_int4_scale_saturates_at_fp16_max():
+    """A group absmax beyond 7 * 65504 keeps the largest finite fp16 scale
+    (no infinity), and its codes clamp to +-7."""
+    q, s = _int4_one_group([1.0e6, -3.0e5, 65504.0 * 7.0, 1.0, 0.0])
+    assert s == 65504.0
+    assert q.tolist() == [7, -5, 7, 0, 0]
+    assert O.int4_scale(np.array([7 * 65504.0, 7 * 65519.0, 7 * 65520.0, 1e30])).tolist() == [65504.0] * 4
+
+
+def test_unfused_rounding_hand_case():
+    """The unfused model rounds twice (walkthrough, Nunchaku section: the
+    separate branch writes the 4-bit product and adds the low-rank part in a
+    second pass).  A hand-built layer with main + b exactly on a bf16 tie:
+    main = 7 * 1 - 6 * 1 = 1, Tb = (7 - 6) 2^-12, low = Tb * (+-8) = +-2^-9.
+      column 0: b = 2^-8    fused bf16(1 + 3 2^-9) = 1 + 2^-7;
+                            unfused bf16(bf16(1 + 2^-8) + 2^-9) = bf16(1 + 2^-9) = 1
+      column 1: b = 3 2^-9  fused bf16(1 + 2^-8) = 1 (tie to even);
+                            unfused bf16(bf16(1 + 3 2^-9) - 2^-9) = bf16(1 + 3 2^-9) = 1 + 2^-7"""
+    K, N = 64, 2
+    x = np.zeros((1, K))
+    x[0, 0], x[0, 1] = 7.0, -6.0
+    w_codes = np.zeros((K, N), np.int8)
+    w_codes[0], w_codes[1] = 1, 1
+    L1b = np.zeros((K, 1))
+    L1b[0, 0] = L1b[1, 0] = 2.0 ** -12
+    prep = dict(fmt=O.INT4, K=K, N=N, rank=1, inv32=np.ones(K), L1b=L1b, L2b=np.array([[8.0, -8.0]]),
+                w_codes=w_codes, w_scales=np.ones((1, N)), bias=np.array([2.0 ** -8, 3 * 2.0 ** -9]))
+    X_bits = O.bf16_bits_of(x.astype(np.float32))
+    fused = O.linear(prep, X_bits, "bf16")
+    unfused = O.linear_unfused(prep, X_bits, "bf16")
+    assert fused["act"]["scales"].tolist() == [[1.0]] and fused["Tb"].tolist() == [[2.0 ** -12]]
+    assert fused["Y"].tolist() == [[1.0 + 2.0 ** -7, 1.0]]
+    assert unfused["Y"].tolist() == [[1.0, 1.0 + 2.0 ** -7]]
+
+
+def test_prop41_bound_is_attained():
+    """Proposition 4.1 (walkthrough eq. (4) / (9)) is attained when every
+    factor is rank one and aligned: X = 2 u a^T, W = 3 a c^T, Q(X) = 3 u a^T,
+    Q(W) = 4 a c^T (unit u, a, c) give E = ||6 u c^T - 12 u c^T|| = 6 and the
+    bound 2 * 1 + 1 * (3 + 1) = 6."""
+    rng = np.random.default_rng(32)
+    u, a, c = (v / np.linalg.norm(v) for v in (rng.standard_normal(5), rng.standard_normal(7), rng.standard_normal(3)))
+    X, W = 2 * np.outer(u, a), 3 * np.outer(a, c)
+    QX, QW = 3 * np.outer(u, a), 4 * np.outer(a, c)
+    assert abs(O.quant_error(X, W, QX, QW) - 6.0) < 1e-12
+    assert abs(O.prop41_bound(X, W, QX, QW) - 6.0) < 1e-12
+
+
+def test_gaussian_c_against_monte_carlo():
+    """eq. (10)-(14): for Gaussian R, E max|R| <= c E||R||_F with c the ratio
+    of the eq. (12) upper bound to the eq. (13) lower bound; both bounds are
+    within ~10-25% of the true expectations, so c sits between the measured
+    ratio and 1.5 times it, at several sizes (a base-2 logarithm in place of
+    the natural one gives about 1.6 times)."""
+    rng = np.random.default_rng(33)
+    for n in (256, 4096, 65536):
+        R = rng.standard_normal((64, n))
+        ratio = np.abs(R).max(axis=1).mean() / np.linalg.norm(R, axis=1).mean()
+        c = O.gaussian_c(n)
+        assert ratio <= c <= 1.5 * ratio, (n, ratio, c)

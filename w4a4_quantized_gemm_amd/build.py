@@ -35,7 +35,7 @@ HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", 
              "-fno-gpu-rdc", "-ffp-contract=off", "-mllvm", "-disable-promote-alloca-to-lds"]
 
 
-# per-file device flags: the INT4 GEMM dequantizes the i8 MFMA's int32 results
+# per-file device flags: the INT4 GEMM dequantizes each group's MFMA result
 # with VALU code, so its MFMAs write VGPRs directly (otherwise every result
 # would be read out of the accumulation registers first)
 FILE_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
@@ -67,7 +67,7 @@ def build(verbose: bool = True, jobs: int = 8) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-lquadmath"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

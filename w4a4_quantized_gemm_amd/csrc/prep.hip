@@ -53,6 +53,14 @@ __device__ uint32_t f64_round_bits(double d, int mbits, int ebits) {
   return sign_bit | bits;
 }
 
+// fp16 bits of the INT4 group scale A / 7, rounded to nearest even and
+// saturated at the largest finite fp16 value (65504, bits 0x7BFF) instead of
+// overflowing to infinity; codes then clamp to +-7.
+__device__ __forceinline__ uint32_t int4_scale_bits(double a) {
+  const uint32_t b = f64_round_bits(a / 7.0, 10, 5);
+  return b > 0x7BFFu ? 0x7BFFu : b;
+}
+
 __device__ __forceinline__ double half_bits_to_f64(uint32_t h) {
   return static_cast<double>(__half2float(__ushort_as_half(static_cast<unsigned short>(h))));
 }
@@ -102,20 +110,6 @@ __global__ void row_absmax_kernel(const uint16_t* __restrict__ W, int N, float* 
     __syncthreads();
   }
   if (threadIdx.x == 0) wmax[j] = __uint_as_float(red[0] << 16);
-}
-
-__global__ void lambda_kernel(const float* __restrict__ amax, const float* __restrict__ wmax, int K, float alpha,
-                              int no_smoothing, float* __restrict__ lam, float* __restrict__ inv) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= K) return;
-  double l = 1.0;
-  if (!no_smoothing) {
-    const double a = amax[j], w = wmax[j];
-    if (a > 0.0 && w > 0.0) l = pow(a, static_cast<double>(alpha)) / pow(w, 1.0 - static_cast<double>(alpha));
-  }
-  const float l32 = static_cast<float>(l);
-  lam[j] = l32;
-  inv[j] = static_cast<float>(1.0 / static_cast<double>(l32));
 }
 
 __global__ void what_kernel(const uint16_t* __restrict__ W, const float* __restrict__ lam, int K, int N,
@@ -241,7 +235,7 @@ __global__ void wquant_kernel(const double* __restrict__ R, int K, int N, uint8_
 #pragma unroll
   for (int w = 0; w < G / 8; w++) words[w] = 0u;
   if constexpr (FMT == SVDQ_INT4_G64_FP16) {
-    const uint32_t sbits = f64_round_bits(a / 7.0, 10, 5);
+    const uint32_t sbits = int4_scale_bits(a);
     const double s = half_bits_to_f64(sbits);
     if (s > 0.0) {
       for (int k = 0; k < G; k++) {
@@ -326,7 +320,7 @@ __global__ void gptq_scale_kernel(const double* __restrict__ R, int k, int N, ui
   double a = 0.0;
   for (int j = 0; j < G; j++) a = fmax(a, fabs(R[static_cast<long>(k + j) * N + n]));
   sc[static_cast<long>(k / G) * N + n] =
-      FMT == SVDQ_INT4_G64_FP16 ? f64_round_bits(a / 7.0, 10, 5) : static_cast<uint32_t>(e8m0_exponent_f64(a) + 127);
+      FMT == SVDQ_INT4_G64_FP16 ? int4_scale_bits(a) : static_cast<uint32_t>(e8m0_exponent_f64(a) + 127);
 }
 
 // Row k: codes and the error (value - dequantized code) / U[k][k].
@@ -527,9 +521,19 @@ svdq_status prepare_impl(const svdq_layer_desc& d, const uint16_t* W, const floa
   SVDQ_TRY(wmax.alloc(sizeof(float) * K));
   hipLaunchKernelGGL(row_absmax_kernel, dim3(K), dim3(256), 0, st, W, N, static_cast<float*>(wmax.p));
   SVDQ_TRY(hipGetLastError());
-  hipLaunchKernelGGL(lambda_kernel, dim3(blocks_for(K)), dim3(256), 0, st, act_absmax, static_cast<float*>(wmax.p), K,
-                     d.alpha, nosmooth ? 1 : 0, lam, inv);
   SVDQ_TRY(hipGetLastError());
+  {
+    // the factors themselves on the host (K values; the preparation is
+    // synchronous anyway)
+    std::vector<float> ha(K, 0.0f), hw(K), hl(K), hi(K);
+    if (!nosmooth) SVDQ_TRY(hipMemcpyAsync(ha.data(), act_absmax, sizeof(float) * K, hipMemcpyDeviceToHost, st));
+    SVDQ_TRY(hipMemcpyAsync(hw.data(), wmax.p, sizeof(float) * K, hipMemcpyDeviceToHost, st));
+    SVDQ_TRY(hipStreamSynchronize(st));
+    smoothing_lambda(ha.data(), hw.data(), K, d.alpha, nosmooth, hl.data(), hi.data());
+    SVDQ_TRY(hipMemcpyAsync(lam, hl.data(), sizeof(float) * K, hipMemcpyHostToDevice, st));
+    SVDQ_TRY(hipMemcpyAsync(inv, hi.data(), sizeof(float) * K, hipMemcpyHostToDevice, st));
+    SVDQ_TRY(hipStreamSynchronize(st));
+  }
 
   // W_hat in fp64
   const long KN = static_cast<long>(K) * N;

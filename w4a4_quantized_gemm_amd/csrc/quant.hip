@@ -238,7 +238,8 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
       uint32_t packed[4] = {0u, 0u, 0u, 0u};
       if constexpr (FMT == SVDQ_INT4_G64_FP16) {
         amax = fmaxf(amax, __shfl_xor(amax, 16));
-        const __half sh = __float2half_rn(amax / 7.0f);
+        // s = fp16(A / 7), saturated at the largest finite fp16 value
+        const __half sh = __float2half_rn(fminf(amax / 7.0f, 65504.0f));
         const float s = __half2float(sh);
         const float r = s > 0.f ? 1.0f / s : 0.f;
         // t = x / s with one rounding (the product with the rounded

@@ -1,10 +1,33 @@
-// Small dense symmetric eigensolver for the offline SVD (host, no HIP).
+// Host-side numerics of the offline preparation (no HIP): the smoothing
+// factors, a small dense symmetric eigensolver for the SVD, and the Cholesky
+// factor GPTQ uses.
+#include <quadmath.h>
+
 #include <algorithm>
 #include <cmath>
 #include <numeric>
 #include <vector>
 
 namespace svdq {
+
+// lambda_j = a_j^alpha / w_j^(1 - alpha) (the handbook's SmoothQuant
+// section) rounded once to fp32: evaluated as exp(alpha ln a - (1 - alpha)
+// ln w) in binary128 (relative error near 2^-110), whose single rounding to
+// fp32 is the correctly rounded value unless the real lambda lies within
+// about 2^-100 of an fp32 rounding midpoint.  1 / lambda32 is rounded to
+// fp64 and then fp32, which equals its correctly rounded fp32 value (53 >=
+// 2 * 24 + 2).  Channels with a zero maximum keep lambda = 1.
+void smoothing_lambda(const float* a, const float* w, int K, float alpha, bool no_smoothing, float* lam, float* inv) {
+  const __float128 al = alpha;
+  for (int j = 0; j < K; j++) {
+    float l = 1.0f;
+    if (!no_smoothing && a[j] > 0.0f && w[j] > 0.0f)
+      l = static_cast<float>(expq(al * logq(static_cast<__float128>(a[j])) -
+                                  (1 - al) * logq(static_cast<__float128>(w[j]))));
+    lam[j] = l;
+    inv[j] = static_cast<float>(1.0 / static_cast<double>(l));
+  }
+}
 
 void jacobi_eigh(int n, std::vector<double>& A, std::vector<double>& V, std::vector<double>& w) {
   V.assign(static_cast<size_t>(n) * n, 0.0);

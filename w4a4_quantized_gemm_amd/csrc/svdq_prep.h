@@ -14,6 +14,12 @@ struct PrepOptions {
   uint64_t seed = 0x5344;  // seed of the Gaussian start block
 };
 
+// Smoothing factors lambda32 (the real a^alpha / w^(1 - alpha) rounded once
+// to fp32; 1 where a channel's maximum is 0 or with no_smoothing) and
+// inv32 = fp32(1 / lambda32), from host copies of the activation and weight
+// channel maxima.
+void smoothing_lambda(const float* a, const float* w, int K, float alpha, bool no_smoothing, float* lam, float* inv);
+
 // Symmetric eigendecomposition by cyclic Jacobi rotations.  A is n x n
 // row-major and is overwritten.  On return w holds the eigenvalues in
 // descending order and V (n x n row-major) the matching eigenvectors as

@@ -83,7 +83,10 @@ C4_INT4 = LayerConfig(name="c4_fc2_4608x12288x3072_int4", M=4608, K=12288, N=307
                       planted_rank=8, planted_scale=10.0)
 C4_FP4 = C4_INT4.with_(name="c4_fc2_4608x12288x3072_fp4", fmt=FP4)
 
-CONFIGS = {c.name: c for c in (C1, C2, C3, C4_INT4, C4_FP4)}
+# the fc1 shape in the INT4 format (the same inputs as C3)
+C3_INT4 = C3.with_(name="c3_fc1_4608x3072x12288_int4", fmt=INT4)
+
+CONFIGS = {c.name: c for c in (C1, C2, C3, C3_INT4, C4_INT4, C4_FP4)}
 
 
 def sweep_configs():

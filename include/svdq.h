@@ -335,6 +335,26 @@ svdq_status svdq_linear_unfused(const svdq_layer_desc* desc, const void* d_prepa
                                 const void* d_X, int M, void* d_Y, int out_dtype,
                                 void* d_workspace, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the fused
+ * layer of svdq_linear without a workspace argument.  The activation codes,
+ * scales, Tb and the partial down-projections go to a scratch array inside
+ * the library, SVDQ_NOALLOC_SCRATCH_BYTES on each device it runs on, held
+ * until the process ends.  The call allocates nothing: its first call on a
+ * device looks up the array's device address once.
+ *  - M is limited by the array: svdq_workspace_bytes(desc, M, 0) must not
+ *    exceed SVDQ_NOALLOC_SCRATCH_BYTES, else SVDQ_ERR_BUFFER_TOO_SMALL and
+ *    nothing is launched (64 MiB holds e.g. M = 16384 at K = 3072, M = 4608
+ *    at K = 12288).
+ *  - Every call on a device uses that device's one array, which keeps the
+ *    last call's contents: calls that overlap on one device (different
+ *    streams, or different threads without ordering) race on it and give
+ *    wrong results.  Calls ordered on one stream are safe.
+ * Other arguments, output and errors as svdq_linear.  Asynchronous. */
+#define SVDQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+svdq_status svdq_linear_noalloc(const svdq_layer_desc* desc, const void* d_prepared, const void* d_X, int M,
+                                void* d_Y, int out_dtype, void* stream);
+
 /* Byte offsets of the blob's sections (for inspection, serialization and
  * tests).  All offsets are multiples of 256.
  *   lambda      fp32[K]

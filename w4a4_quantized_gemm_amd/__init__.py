@@ -37,8 +37,11 @@ EXPORTED = (
     "svdq_act_sizes", "svdq_act_absmax", "svdq_prepare_weights", "svdq_prepare_weights_gptq", "svdq_merge_lowrank",
     "svdq_check_blob",
     "svdq_quantize_act", "svdq_quantize_act_ln", "svdq_gemm", "svdq_linear", "svdq_linear_ln", "svdq_linear_w4a16",
-    "svdq_linear_unfused", "svdq_blob_layout_of",
+    "svdq_linear_unfused", "svdq_blob_layout_of", "svdq_linear_noalloc",
 )
+
+# bytes of the library's scratch array behind svdq_linear_noalloc (per device)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class SvdqError(RuntimeError):
@@ -92,6 +95,7 @@ def _lib() -> ctypes.CDLL:
             "svdq_linear_w4a16": ([D, P, P, I, P, I, P, Z, P], S),
             "svdq_linear": ([D, P, P, I, P, I, P, Z, P], S),
             "svdq_linear_unfused": ([D, P, P, I, P, I, P, Z, P], S),
+            "svdq_linear_noalloc": ([D, P, P, I, P, I, P], S),
             "svdq_blob_layout_of": ([D, ctypes.POINTER(BlobLayout)], S),
         }
         for name, (args, res) in sig.items():
@@ -244,6 +248,16 @@ def svdq_linear_unfused(desc: LayerDesc, prepared, X, Y, workspace, out_dtype: i
     _check(_lib().svdq_linear_unfused(ctypes.byref(desc), _ptr(prepared), _ptr(X), M, _ptr(Y), out_dtype,
                                       _ptr(workspace), workspace.numel(), _stream(stream)),
            "svdq_linear_unfused")
+
+
+def svdq_linear_noalloc(desc: LayerDesc, prepared, X, Y, out_dtype: int = OUT_BF16, stream=None):
+    """svdq_linear with the library's own scratch array instead of a
+    workspace (for callers that cannot allocate); calls that overlap on one
+    device race on that array."""
+    M = X.shape[0]
+    _check(_lib().svdq_linear_noalloc(ctypes.byref(desc), _ptr(prepared), _ptr(X), M, _ptr(Y), out_dtype,
+                                      _stream(stream)),
+           "svdq_linear_noalloc")
 
 
 # ----------------------------------------------------------------- convenience

@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "svdq_internal.h"
 #include "svdq_kernels.h"
@@ -148,6 +149,36 @@ svdq_status run_layer(const svdq_layer_desc* desc, const void* prepared, const v
   if (desc->rank > 0 && (st = from_hip(launch_act(desc->fmt, false, true, a, s))) != SVDQ_OK) return st;
   if ((st = from_hip(launch_gemm(desc->fmt, false, out_dtype, g, s))) != SVDQ_OK) return st;
   return from_hip(launch_up(out_dtype, a.Tb, bp.l2t, Y, M, desc->N, desc->rank, s));
+}
+
+// Scratch of svdq_linear_noalloc: the fused layer's workspace (activation
+// codes, scales, Tb, partial down-projections) for callers that cannot
+// allocate.  One copy per device (the code object's global), zero at load.
+// Host code never passes this name to a kernel: it stands for a host-side
+// shadow, not the device address; scratch_ptr() returns the device address.
+static __device__ __align__(256) uint8_t scratch[SVDQ_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; null on failure.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -375,6 +406,17 @@ svdq_status svdq_linear(const svdq_layer_desc* desc, const void* d_prepared, con
 svdq_status svdq_linear_unfused(const svdq_layer_desc* desc, const void* d_prepared, const void* d_X, int M,
                                 void* d_Y, int out_dtype, void* d_workspace, size_t ws_bytes, void* stream) {
   return run_layer(desc, d_prepared, d_X, M, d_Y, out_dtype, d_workspace, ws_bytes, stream, true);
+}
+
+svdq_status svdq_linear_noalloc(const svdq_layer_desc* desc, const void* d_prepared, const void* d_X, int M,
+                                void* d_Y, int out_dtype, void* stream) {
+  svdq_status st = validate_runtime(desc, d_prepared, d_X, M);
+  if (st != SVDQ_OK) return st;
+  if (act_layout(*desc, M).total > SVDQ_NOALLOC_SCRATCH_BYTES) return SVDQ_ERR_BUFFER_TOO_SMALL;
+  if ((st = check_device()) != SVDQ_OK) return st;
+  void* ws = scratch_ptr();
+  if (!ws) return SVDQ_ERR_HIP;
+  return run_layer(desc, d_prepared, d_X, M, d_Y, out_dtype, ws, SVDQ_NOALLOC_SCRATCH_BYTES, stream, false);
 }
 
 }  // extern "C"

@@ -82,8 +82,8 @@ def parse():
                     help="comma-separated further workloads reported in the same line ('' for none)")
     ap.add_argument("--rank0", default="c3_fc1_4608x3072x12288_fp4,c2_qkv_4608x3072x9216_int4",
                     help="workloads whose rank-0 layer is timed too (slab overhead t(r) / t(0))")
-    ap.add_argument("--peaks", action="store_true",
-                    help="also run the MFMA and HBM peak microbenchmarks and report them")
+    ap.add_argument("--no-peaks", dest="peaks", action="store_false",
+                    help="skip the MFMA and HBM peak microbenchmarks (libsvdq_peaks)")
     return ap.parse_args()
 
 
@@ -146,7 +146,7 @@ class Rig:
         for i in range(self.nsets):
             Xi = X if i == 0 else X.clone()
             bi = layer.blob if i == 0 else layer.blob.clone()
-            ws = torch.empty(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev)
+            ws = torch.zeros(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev)
             Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             codes = torch.empty(c_b, dtype=torch.uint8, device=dev)
             scales = torch.empty(s_b, dtype=torch.uint8, device=dev)
@@ -539,6 +539,56 @@ def summarize_util(dirs, cfg, src_hash):
                       for k in kernels if k in out}))
 
 
+PEAK_KINDS = (("fp4", 0, PEAK_TFLOPS["fp4"]), ("fp6", 1, 10100.0), ("fp8", 2, 5000.0), ("int8", 3, 5000.0),
+              ("bf16", 4, PEAK_BF16_TFLOPS), ("f16", 5, 2500.0))
+
+
+def measure_peaks(torch):
+    """The matrix-core and HBM ceilings measured on this device with
+    libsvdq_peaks (simple unobstructed loops; include/svdq_peaks.h), next to
+    the datasheet figures the rooflines use."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "w4a4_quantized_gemm_amd", "libsvdq_peaks.so"))
+    lib.svdq_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    lib.svdq_peak_hbm.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    st = torch.cuda.current_stream().cuda_stream
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(256 * cus, dtype=torch.float32, device="cuda:0")
+    tops, ms = ctypes.c_double(), ctypes.c_double()
+    out = {"note": "one wave per SIMD, 8 independent MFMAs per wave (32x32 shapes); 'random' operands are "
+                   "pseudo-random valid codes, 'const' one repeated code; HBM: 1 GiB buffers, read-only and copy",
+           "mfma": {}}
+    for name, kind, datasheet in PEAK_KINDS:
+        rec = {"datasheet_tops": datasheet}
+        for rnd in (0, 1):
+            lib.svdq_peak_mfma(kind, 2000, 0, rnd, sink.data_ptr(), ctypes.byref(tops), ctypes.byref(ms), st)
+            iters = max(2000, int(2000 * 40.0 / max(ms.value, 1e-3)))       # about 40 ms
+            rc = lib.svdq_peak_mfma(kind, iters, 0, rnd, sink.data_ptr(), ctypes.byref(tops), ctypes.byref(ms), st)
+            if rc:
+                raise RuntimeError(f"svdq_peak_mfma({name}) failed: {rc}")
+            rec["random_tops" if rnd else "const_tops"] = tops.value
+        rec["random_frac_of_datasheet"] = rec["random_tops"] / datasheet
+        out["mfma"][name] = rec
+    nbytes = 1 << 30
+    a = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    gbs = ctypes.c_double()
+    for mode, key in ((0, "hbm_read_gbs"), (1, "hbm_copy_gbs")):
+        lib.svdq_peak_hbm(mode, a.data_ptr(), b.data_ptr(), nbytes, ctypes.byref(gbs), ctypes.byref(ms), st)
+        best = 0.0
+        for _ in range(3):
+            if lib.svdq_peak_hbm(mode, a.data_ptr(), b.data_ptr(), nbytes, ctypes.byref(gbs), ctypes.byref(ms), st):
+                raise RuntimeError("svdq_peak_hbm failed")
+            best = max(best, gbs.value)
+        out[key] = best
+    out["hbm_datasheet_gbs"] = PEAK_HBM_GBS
+    del a, b, sink
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure(args, cfg, torch, S, WL, to_tensor, with_cpu=False, lora=0, norm=False, rank0=False, contract=False):
     """All timings of one workload (see the module docstring)."""
     rig = Rig(cfg, torch, S, WL, to_tensor, lora)
@@ -694,7 +744,7 @@ def main():
     if args.w4a16:
         line["w4a16_modulation"] = time_w4a16(torch, S, WL, to_tensor, min(args.steps, 200), args.warmup)
     if args.peaks:
-        line["measured_peaks"] = S.measure_peaks()
+        line["measured_peaks"] = measure_peaks(torch)
     print(json.dumps(line), flush=True)
 
     if args.sweep:

@@ -155,7 +155,8 @@ size_t svdq_prepared_bytes(const svdq_layer_desc* desc);
  * the packed activation codes (ceil(M/32)*32 x K/2 bytes), the scales, the
  * bf16 down-projection (ceil(M/32)*32 x rank) and, for M <= 16384, room for
  * the fp32 partial down-projections of a K-split activation pass
- * (8 x M x rank x 4 bytes); 0 if arguments are invalid. */
+ * (8 x M x rank x 4 bytes); 0 if arguments are invalid.  Every section is
+ * written before it is read, so one workspace serves any layer and M. */
 size_t svdq_workspace_bytes(const svdq_layer_desc* desc, int M, int unfused);
 
 /* Byte sizes of svdq_quantize_act's three outputs for M tokens (codes,

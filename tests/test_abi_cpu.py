@@ -34,6 +34,30 @@ def test_library_exports_every_declared_symbol():
         assert name in syms, name
 
 
+def test_peaks_library_exports_its_header():
+    """The peak-measurement probes (libsvdq_peaks.so) export what
+    include/svdq_peaks.h declares, and refuse invalid arguments before any
+    device call."""
+    hdr = os.path.join(ROOT, "include", "svdq_peaks.h")
+    text = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(svdq_[a-z_0-9]+)\s*\(", text)))
+    path = os.path.join(ROOT, "w4a4_quantized_gemm_amd", "libsvdq_peaks.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    assert declared == ["svdq_peak_hbm", "svdq_peak_mfma"]
+    assert all(n in syms for n in declared)
+    lib = ctypes.CDLL(path)
+    d = ctypes.c_double()
+    lib.svdq_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    lib.svdq_peak_hbm.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    assert lib.svdq_peak_mfma(9, 10, 0, 0, 1 << 20, ctypes.byref(d), ctypes.byref(d), None) == 1
+    assert lib.svdq_peak_mfma(0, 0, 0, 0, 1 << 20, ctypes.byref(d), ctypes.byref(d), None) == 1
+    assert lib.svdq_peak_hbm(2, 1 << 20, 1 << 21, 1 << 20, ctypes.byref(d), ctypes.byref(d), None) == 1
+    assert lib.svdq_peak_hbm(0, 1 << 20, 1 << 21, 17, ctypes.byref(d), ctypes.byref(d), None) == 1
+
+
 def test_status_strings_and_version():
     lib = S.load()
     for code, name in S.STATUS_NAMES.items():

@@ -102,7 +102,7 @@ def _run_act(torch_dev, layer, X, M, with_ws):
     codes = torch.empty(cb, dtype=torch.uint8, device=dev)
     scales = torch.empty(sb, dtype=torch.uint8, device=dev)
     T = torch.empty(max(tb // 2, 1), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev) if with_ws else None
+    ws = torch.zeros(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev) if with_ws else None
     S.svdq_quantize_act(layer.desc, layer.blob, X, codes, scales, T if layer.desc.rank else None, ws)
     torch.cuda.synchronize()
     return codes, scales, T
@@ -341,7 +341,7 @@ def test_w4a16(torch_dev, fmt, M, K, N):
     layer, Xfull, _ = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
     sec, ref = _check_weights(layer, W_bits, fmt, b_bits, X_bits=X_bits, alpha=cfg.alpha)
     X = Xfull[:M].contiguous()
-    ws = torch.empty(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev)
     for out, oname in ((S.OUT_F32, "f32"), (S.OUT_BF16, "bf16")):
         Y = torch.empty((M, N), dtype=torch.float32 if out == S.OUT_F32 else torch.bfloat16, device=dev)
         S.svdq_linear_w4a16(layer.desc, layer.blob, X, Y, ws, out)
@@ -436,7 +436,7 @@ def test_norm_fused_pass(torch_dev, fmt):
         codes = torch.empty(cb, dtype=torch.uint8, device=dev)
         scales = torch.empty(sb, dtype=torch.uint8, device=dev)
         T = torch.empty(tb // 2, dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev)
         S.svdq_quantize_act_ln(layer.desc, layer.blob, X, gamma, beta_t, eps, codes, scales, T, ws)
         torch.cuda.synchronize()
         q, s, _, _ = decode_act(codes, scales, layer.desc.fmt, M, K)
@@ -512,6 +512,40 @@ def test_quantizer_edge_values(torch_dev):
         sec, ref = _check_weights(layer, W_bits, fmt, no_smoothing=True)
         _check_act(torch_dev, layer, X, X_bits, ref)
         _check_linear(torch_dev, layer, X, X_bits, ref, modes=[(S.OUT_F32, False), (S.OUT_F32, True)])
+
+
+@pytest.mark.parametrize("fmt", [O.INT4, O.FP4])
+def test_workspace_reuse_across_shapes(torch_dev, fmt):
+    """One zero-filled workspace serves calls of different M (different K
+    splits of the activation pass, whose arrival counters must be back at
+    zero after every call): T, codes and scales equal those of a fresh
+    workspace each time, and T equals the oracle's."""
+    import w4a4_quantized_gemm_amd as S
+    torch, dev = torch_dev
+    _say(f"case: workspace reuse fmt={fmt}")
+    cfg = WL.C2.with_(name="reuse", M=4608, K=1536, N=256, rank=32, fmt=fmt, w_std=1 / np.sqrt(1536),
+                      bias_std=0.0, seed=71)
+    X_bits, W_bits, b_bits = WL.make_layer(cfg)
+    layer, X, _ = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
+    sec, ref = _check_weights(layer, W_bits, fmt, b_bits, X_bits=X_bits, alpha=cfg.alpha)
+    ws = torch.zeros(S.svdq_workspace_bytes(layer.desc, cfg.M), dtype=torch.uint8, device=dev)
+    for M in (4608, 200, 4608, 1000, 33):
+        cb, sb, tb = S.svdq_act_sizes(layer.desc, M)
+        outs = []
+        for w in (ws, torch.zeros(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev)):
+            # zero-filled: rows past M in the padded 32-row blocks are never written
+            codes = torch.zeros(cb, dtype=torch.uint8, device=dev)
+            scales = torch.zeros(sb, dtype=torch.uint8, device=dev)
+            T = torch.zeros(tb // 2, dtype=torch.bfloat16, device=dev)
+            S.svdq_quantize_act(layer.desc, layer.blob, X[:M].contiguous(), codes, scales, T, w)
+            outs.append((codes, scales, T))
+        torch.cuda.synchronize()
+        for a, b in zip(*outs):
+            assert torch.equal(a, b), f"M={M}: reused workspace differs"
+        Tg = O.bf16_bits_to_f64(untile_bf16(u16_tensor_to_np(outs[0][2]), M, cfg.rank))
+        _, Tref = O.down_proj(O.quantize_act(X_bits[:M], ref["inv32"], fmt)["xhat"], ref["L1b"])
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(Tref), 1e-30))) - 7)
+        assert np.all(np.abs(Tg - Tref) <= ulp * 1.0001), M
 
 
 def test_determinism_and_bad_blob(torch_dev):

@@ -42,7 +42,7 @@ def test_noalloc_matches_linear(fmt):
         dt = torch.float32 if out == S.OUT_F32 else torch.bfloat16
         Y0 = torch.empty((M, cfg.N), dtype=dt, device=dev)
         Y1 = torch.full((M, cfg.N), float("nan"), dtype=dt, device=dev)
-        ws = torch.empty(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(S.svdq_workspace_bytes(layer.desc, M), dtype=torch.uint8, device=dev)
         S.svdq_linear(layer.desc, layer.blob, Xm, Y0, ws, out)
         S.svdq_linear_noalloc(layer.desc, layer.blob, Xm, Y1, out)
         torch.cuda.synchronize()

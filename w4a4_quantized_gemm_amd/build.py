@@ -5,7 +5,8 @@
 HIP sources (*.hip) are compiled by hipcc for gfx950 only; the HIP-free host
 sources (*.cpp: validation, blob layout, the small eigensolver) by g++.
 Objects go to w4a4_quantized_gemm_amd/_build/, the shared library to
-w4a4_quantized_gemm_amd/libsvdq.so.
+w4a4_quantized_gemm_amd/libsvdq.so; the peak-measurement probes
+(csrc_peaks/, include/svdq_peaks.h) to libsvdq_peaks.so.
 """
 from __future__ import annotations
 
@@ -22,6 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsvdq.so")
+PEAKS_LIB = os.path.join(PKG, "libsvdq_peaks.so")
 
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
@@ -72,8 +74,16 @@ def build(verbose: bool = True, jobs: int = 8) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     shutil.move(tmp, LIB)
+    # the peak-measurement probes (a measurement aid, a library of its own)
+    pobj = _compile(os.path.join(PKG, "csrc_peaks", "peaks.hip"))
+    ptmp = PEAKS_LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", ptmp, pobj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    shutil.move(ptmp, PEAKS_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAKS_LIB}")
     return LIB
 
 

@@ -61,24 +61,6 @@ __device__ __forceinline__ u32x4 e4m3_hi(const u32x4& c) {
                __builtin_amdgcn_alignbit(c.z, c.z, 4) & MSK, __builtin_amdgcn_alignbit(c.w, c.w, 4) & MSK};
 }
 
-template <int OUT, typename I>
-__device__ __forceinline__ void store_out(void* Y, I idx, float v) {
-  if constexpr (OUT == SVDQ_OUT_F32) {
-    reinterpret_cast<float*>(Y)[idx] = v;
-  } else {
-    reinterpret_cast<uint16_t*>(Y)[idx] = static_cast<uint16_t>(f32_to_bf16_bits(v));
-  }
-}
-
-template <int OUT, typename I>
-__device__ __forceinline__ float load_out(const void* Y, I idx) {
-  if constexpr (OUT == SVDQ_OUT_F32) {
-    return reinterpret_cast<const float*>(Y)[idx];
-  } else {
-    return __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(Y)[idx]) << 16);
-  }
-}
-
 }  // namespace
 
 // Tile: 4 waves in a 2 x 2 grid, each owning 64 x 64 (2 x 2 MFMA tiles).
@@ -101,17 +83,16 @@ __device__ __forceinline__ int lds_block(int rowblk, int j) { return (rowblk * 2
 
 template <bool SLAB, int OUT>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
-  constexpr int STAGE_A = (BM / 32) * 2 * 2048, STAGE_B = (BN / 32) * 2 * 2048;
-  // LDS: two stage buffers of A and B operands plus the scales as f16 MFMA
-  // operand words ([stage][group][row]: fp16 bits in the low half); the
-  // epilogue reuses the operand buffers to stage the output tile.
-  constexpr int LDS_A = 2 * STAGE_A, LDS_B = 2 * STAGE_B;
-  constexpr int LDS_SA = 2 * 2 * BM * 4, LDS_SB = 2 * 2 * BN * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_A + LDS_B + LDS_SA + LDS_SB];
-  auto sA = reinterpret_cast<uint8_t(*)[STAGE_A]>(smem);
-  auto sB = reinterpret_cast<uint8_t(*)[STAGE_B]>(smem + LDS_A);
-  auto sSA = reinterpret_cast<uint32_t(*)[2][BM]>(smem + LDS_A + LDS_B);
-  auto sSB = reinterpret_cast<uint32_t(*)[2][BN]>(smem + LDS_A + LDS_B + LDS_SA);
+  // LDS: a ring of NBUF stages, each the raw codes of the tile's rows and
+  // columns for 128 K (A then B: per 32-row block the two 1 KB operand
+  // blocks of the stage, as they lie in HBM) and their scales (A: the 128-byte
+  // scale blocks of the four 32-row blocks; B: one 4-byte word per column);
+  // the epilogue reuses the ring to stage the output tile.
+  constexpr int RING_A = 0, RING_B = (BM / 32) * 2048, RING_SA = RING_B + (BN / 32) * 2048;
+  constexpr int RING_SB = RING_SA + (BM / 32) * 128, RING_STAGE = RING_SB + BN * 4;
+  constexpr int NBUF = 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF * RING_STAGE];
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)smem));
 
   // kernel arguments in registers (a lambda capturing g would read them
   // from the argument segment with vector loads)
@@ -122,7 +103,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   void* __restrict__ Yout = g.Y;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  tile_of(blockIdx.x, tiles_m, tiles_n, g.xcd_map, tm, tn);
   const long m0 = static_cast<long>(tm) * BM;
   const long n0 = static_cast<long>(tn) * BN;
 
@@ -165,172 +146,158 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     }
   }
 
-  // ---- global -> registers -> LDS, through buffer resources over the
-  // workgroup's own row blocks (32-bit offsets; the stage is the scalar
-  // offset).  A stage of the A (B) tile is BM / 16 (BN / 16) operand blocks
-  // of 1 KB; thread t copies 16-byte pieces q = t + 256 i: block q / 64, lane
-  // slot q % 64 (64 threads cover one block contiguously).  Row blocks past
-  // the matrix are clamped to its last one (their outputs are never
-  // stored).  Waves 0-1 load the scale words of the 128 A rows, waves 2-3
-  // those of the 128 B columns.
-  struct Regs {
-    u32x4 a[A_CH], b[B_CH];
-    uint32_t sc;
-  };
+  // ---- global -> LDS copies (global_load_lds, 16 or 4 bytes per lane) of
+  // the raw codes and scales, NBUF - 1 stages ahead of the MFMAs.  Per stage
+  // wave w copies: the two 1 KB blocks of A row block w, those of B column
+  // block w, and a quarter of the scales (waves 0-1: A scale blocks 2w,
+  // 2w + 1; waves 2-3: B scale words of 64 columns each).  Row (column)
+  // blocks past the matrix repeat its last one (never stored); stages past
+  // the last repeat the last one (never consumed), so every stage issues the
+  // same 5 copies per wave and the explicit waits count exactly.
   const long KBLK = K / 64;                       // 1 KB blocks per 32-row block
-  const int a_blks = static_cast<int>(min(static_cast<long>(BM / 32), (M + 31) / 32 - m0 / 32));
-  const int b_blks = static_cast<int>(min(static_cast<long>(BN / 32), N / 32 - n0 / 32));
-  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(g.acodes + (m0 / 32) * KBLK * 1024), 0, static_cast<int>(a_blks * KBLK * 1024), 0x00020000);
-  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(g.wcodes + (n0 / 32) * KBLK * 1024), 0, static_cast<int>(b_blks * KBLK * 1024), 0x00020000);
-  uint32_t aoff[A_CH], boff[B_CH];
-#pragma unroll
-  for (int i = 0; i < A_CH; i++) {
-    const int q = t + i * NTHREADS, blk = q >> 6;
-    aoff[i] = static_cast<uint32_t>(((min(blk >> 1, a_blks - 1) * KBLK + (blk & 1)) << 10) + (q & 63) * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < B_CH; i++) {
-    const int q = t + i * NTHREADS, blk = q >> 6;
-    boff[i] = static_cast<uint32_t>(((min(blk >> 1, b_blks - 1) * KBLK + (blk & 1)) << 10) + (q & 63) * 16);
-  }
-  // scale words: activation scales in 32-row blocks (word (row, st) at
-  // ((row / 32) * SW + st) * 32 + row % 32), weight scales row-major
-  const bool sc_is_a = wave < 2;
-  __amdgpu_buffer_rsrc_t sr;
-  uint32_t soff;
-  int sstep;
-  if (sc_is_a) {
-    const long rows = min(static_cast<long>(BM), static_cast<long>(M) - m0);
-    const long r = min(static_cast<long>(t), rows - 1);
-    sr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(static_cast<const void*>(static_cast<const uint32_t*>(g.ascales) + (m0 >> 5) * SW * 32)), 0,
-        static_cast<int>(((rows + 31) >> 5) * SW * 128), 0x00020000);
-    soff = static_cast<uint32_t>(((r >> 5) * SW * 32 + (r & 31)) * 4);
-    sstep = 128;
-  } else {
-    const long cols = min(static_cast<long>(BN), static_cast<long>(N) - n0);
-    const long c = min(static_cast<long>(t - BM), cols - 1);
-    sr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(static_cast<const void*>(static_cast<const uint32_t*>(g.wscales) + n0 * SW)), 0,
-        static_cast<int>(cols * SW * 4), 0x00020000);
-    soff = static_cast<uint32_t>(c * SW * 4);
-    sstep = 4;
-  }
-  auto load_stage = [&](Regs& r, int st) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < A_CH; i++) r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff[i], st * 2048, 0);
-#pragma unroll
-    for (int i = 0; i < B_CH; i++) r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(br, boff[i], st * 2048, 0);
-    r.sc = __builtin_amdgcn_raw_buffer_load_b32(sr, soff, st * sstep, 0);
-  };
-  auto store_stage = [&](const Regs& r, int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < A_CH; i++) {
-      const int q = t + i * NTHREADS, off = ((q >> 6) << 11) + (q & 63) * 16;
-      *reinterpret_cast<u32x4*>(&sA[buf][off]) = e4m3_lo(r.a[i]);
-      *reinterpret_cast<u32x4*>(&sA[buf][off + 1024]) = e4m3_hi(r.a[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < B_CH; i++) {
-      const int q = t + i * NTHREADS, off = ((q >> 6) << 11) + (q & 63) * 16;
-      *reinterpret_cast<u32x4*>(&sB[buf][off]) = e4m3_lo(r.b[i]);
-      *reinterpret_cast<u32x4*>(&sB[buf][off + 1024]) = e4m3_hi(r.b[i]);
-    }
-    // fp16 bits of the two groups' scales, as the f16 MFMA operands take them
-    uint32_t(*ss)[BM] = sc_is_a ? sSA[buf] : sSB[buf];
-    const int idx = sc_is_a ? t : t - BM;
-    ss[0][idx] = r.sc & 0xFFFFu;
-    ss[1][idx] = r.sc >> 16;
-  };
-
-  // Stage k's codes are loaded into register set R[k % 2].  Schedule of
-  // stage s: (1) store register set R[(s + 1) % 2] (stage s + 1, loaded two
-  // stages earlier) to the other LDS buffer, (2) reuse that set for the
-  // global loads of stage s + 3, (3) run the MFMAs of stage s, (4) barrier.
-  // Loads past the last stage re-read the last stage (their data is never
-  // used), so that every stage issues the same loads and the compiler's
-  // wait counts stay exact across the loop.
-  // The prologue issues its loads stage by stage (no interleaving), in the
-  // same order as the loop, so that the compiler's load counters agree at
-  // the loop head and each wait covers exactly the stage it needs.
-  Regs R0, R1;
+  const int last_ablk = (M + 31) / 32 - 1, last_bblk = N / 32 - 1;
   const int last = stages - 1;
-  load_stage(R0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  load_stage(R1, min(1, last));
-  __builtin_amdgcn_sched_barrier(0);
-  store_stage(R0, 0);
-  load_stage(R0, min(2, last));
-  __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();
-
-  auto stage_body = [&](int s, Regs& Rn, auto BUF) __attribute__((always_inline)) {
-    constexpr int buf = decltype(BUF)::value;
-    store_stage(Rn, buf ^ 1);
-    load_stage(Rn, min(s + 3, last));
-    __builtin_amdgcn_sched_barrier(0);
-
-#pragma unroll
-    for (int j = 0; j < 2; j++) {          // two 64-wide MFMA steps per stage
-      // E4M3 operands (codes 0-3 of the lane's words, then codes 4-7) and
-      // the scale operands of the f16 MFMA that forms the tile's scale
-      // products: every lane holds its row's (column's) fp16 scale in its
-      // first element, so K slots 0 and 4 both carry s_x[i] s_w[j] and the
-      // MFMA gives 2 s_x[i] s_w[j] (exact); the E4M3 MFMA's block scales
-      // (2^9, 2^8) give P_g / 2 to match.
-      i32x8 a8[RB], b8[CB];
-      f16x4 fa[RB], fb[CB];
-#pragma unroll
-      for (int rb = 0; rb < RB; rb++) {
-        const int o = lds_block(wrow0 / 32 + rb, j) + lane * 16;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(&sA[buf][o]);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(&sA[buf][o + 1024]);
-        a8[rb] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        fa[rb] = __builtin_bit_cast(f16x4, u32x2{sSA[buf][j][wrow0 + rb * 32 + l32], 0u});
-      }
-#pragma unroll
-      for (int cb = 0; cb < CB; cb++) {
-        const int o = lds_block(wcol0 / 32 + cb, j) + lane * 16;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(&sB[buf][o]);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(&sB[buf][o + 1024]);
-        b8[cb] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        fb[cb] = __builtin_bit_cast(f16x4, u32x2{sSB[buf][j][wcol0 + cb * 32 + l32], 0u});
-      }
-      // software pipeline over the wave's output tiles: the MFMAs of tile
-      // u + 1 (P_g / 2 = sum q_x q_w / 2, exact in fp32: codes are q 2^-9;
-      // and 2 s_x s_w) are in flight while tile u is dequantized with one fma
-      // per accumulator (the product of the two is P_g s_x s_w exactly)
-      constexpr int NT = RB * CB;
-      f32x16 p[2], sp[2];
-      auto mma = [&](int u, f32x16& dst, f32x16& sdst) __attribute__((always_inline)) {
-        const int rb = u / CB, cb = u % CB;
-        f32x16 zf;
-#pragma unroll
-        for (int v = 0; v < 16; v++) zf[v] = 0.f;
-        dst = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8[rb], b8[cb], zf, 0, 0, 0, 127 + 9, 0, 127 + 8);
-        sdst = __builtin_amdgcn_mfma_f32_32x32x8f16(fa[rb], fb[cb], zf, 0, 0, 0);
-      };
-      mma(0, p[0], sp[0]);
-#pragma unroll
-      for (int u = 0; u < NT; u++) {
-        const int rb = u / CB, cb = u % CB;
-        if (u + 1 < NT) mma(u + 1, p[(u + 1) & 1], sp[(u + 1) & 1]);
-        const f32x16& pp = p[u & 1];
-        const f32x16& ss = sp[u & 1];
-#pragma unroll
-        for (int v = 0; v < 16; v++) acc[rb][cb][v] = __builtin_fmaf(pp[v], ss[v], acc[rb][cb][v]);
-      }
-    }
-    __syncthreads();
-  };
-  int s = 0;
-  for (; s + 1 < stages; s += 2) {
-    stage_body(s, R1, std::integral_constant<int, 0>{});
-    stage_body(s + 1, R0, std::integral_constant<int, 1>{});
+  const uint8_t* cpa = g.acodes + ((static_cast<long>(min(static_cast<int>(m0 / 32) + wave, last_ablk)) * KBLK) << 10);
+  const uint8_t* cpb = g.wcodes + ((static_cast<long>(min(static_cast<int>(n0 / 32) + wave, last_bblk)) * KBLK) << 10);
+  const uint8_t* cps;
+  uint32_t svoff, sstride;
+  if (wave < 2) {
+    // A scale blocks: per 32-row block and stage 128 bytes at ((row block) *
+    // SW + st) * 128; lanes 0-31 block 2w, lanes 32-63 block 2w + 1
+    const int rb = min(static_cast<int>(m0 / 32) + 2 * wave + (lane >> 5), last_ablk);
+    cps = static_cast<const uint8_t*>(g.ascales);
+    svoff = static_cast<uint32_t>(rb * SW * 128 + (lane & 31) * 4);
+    sstride = 128;
+  } else {
+    // B scale words: column n's two fp16 scales of stage st at (n * SW + st) * 4
+    const long c = min(n0 + (wave - 2) * 64 + lane, static_cast<long>(N - 1));
+    cps = static_cast<const uint8_t*>(g.wscales);
+    svoff = static_cast<uint32_t>(c * SW * 4);
+    sstride = 4;
   }
-  if (s < stages) stage_body(s, R1, std::integral_constant<int, 0>{});
+  const uint32_t lane16 = lane * 16u;
+  const uint32_t sdst = wave < 2 ? RING_SA + wave * 256 : RING_SB + (wave - 2) * 256;
+  // copy item i (0..4) of stage st into ring slot st % NBUF
+  auto copy_item = [&](int st, int i) __attribute__((always_inline)) {
+    const int cs = min(st, last);
+    const uint32_t slot = lds0 + static_cast<uint32_t>(st % NBUF) * RING_STAGE;
+    switch (i) {
+      case 0: set_m0_nop(slot + RING_A + wave * 2048); dma16<0>(cpa + cs * 2048, lane16); break;
+      case 1: dma16<1024>(cpa + cs * 2048, lane16); break;
+      case 2: set_m0_nop(slot + RING_B + wave * 2048); dma16<0>(cpb + cs * 2048, lane16); break;
+      case 3: dma16<1024>(cpb + cs * 2048, lane16); break;
+      default: set_m0_nop(slot + sdst); dma4<0>(cps, svoff + static_cast<uint32_t>(cs) * sstride); break;
+    }
+  };
+
+  // Operands of one 64-wide MFMA step, read from the ring and widened: the
+  // E4M3 operand words of the wave's row blocks (A) and column blocks (B) --
+  // codes 0-3 of the lane's words, then codes 4-7 -- and the operands of the
+  // f16 MFMA that forms the tile's scale products: every lane holds its row's
+  // (column's) fp16 scale in its first element, so K slots 0 and 4 both
+  // carry s_x[i] s_w[j] and the MFMA gives 2 s_x[i] s_w[j] (exact); the E4M3
+  // MFMA's block scales (2^9, 2^8) give P_g / 2 to match.
+  struct Ops {
+    i32x8 a[RB], b[CB];
+    f16x4 fa[RB], fb[CB];
+  };
+  // part p of the operands of step j of stage st: p < RB row block p, else
+  // column block p - RB
+  auto read_part = [&](Ops& o, int st, int j, int p) __attribute__((always_inline)) {
+    const uint8_t* ring = smem + (st % NBUF) * RING_STAGE;
+    if (p < RB) {
+      const int rb = wrow0 / 32 + p;
+      const u32x4 c = *reinterpret_cast<const u32x4*>(ring + RING_A + (rb * 2 + j) * 1024 + lane16);
+      const u32x4 lo = e4m3_lo(c), hi = e4m3_hi(c);
+      o.a[p] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const uint32_t sb = *reinterpret_cast<const uint16_t*>(ring + RING_SA + rb * 128 + l32 * 4 + j * 2);
+      o.fa[p] = __builtin_bit_cast(f16x4, u32x2{sb, 0u});
+    } else {
+      const int cb = wcol0 / 32 + p - RB;
+      const u32x4 c = *reinterpret_cast<const u32x4*>(ring + RING_B + (cb * 2 + j) * 1024 + lane16);
+      const u32x4 lo = e4m3_lo(c), hi = e4m3_hi(c);
+      o.b[p - RB] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const uint32_t sb = *reinterpret_cast<const uint16_t*>(ring + RING_SB + (cb * 32 + l32) * 4 + j * 2);
+      o.fb[p - RB] = __builtin_bit_cast(f16x4, u32x2{sb, 0u});
+    }
+  };
+
+  // The MFMAs of output tile u of a step (P_g / 2 = sum q_x q_w / 2, exact
+  // in fp32: codes are q 2^-9; and 2 s_x s_w) go to result slot u % 2; the
+  // tile is retired (dequantized into its accumulators, one fma per value:
+  // the product of the two is P_g s_x s_w exactly) after the next tile's
+  // MFMAs are issued, across step and stage boundaries, so the matrix core
+  // and the VALU overlap continuously.  Slot 1 starts at zero: the first
+  // retirement (of a "previous" tile 3) adds 0 * 0 to its accumulators.
+  constexpr int NT = RB * CB;
+  static_assert(NT == 4, "the schedule below retires tile NT - 1 of the previous step first");
+  f32x16 P[2], Sc[2];
+#pragma unroll
+  for (int v = 0; v < 16; v++) P[1][v] = Sc[1][v] = 0.f;
+  auto issue = [&](const Ops& o, int u, int slot) __attribute__((always_inline)) {
+    const int rb = u / CB, cb = u % CB;
+    f32x16 zf;
+#pragma unroll
+    for (int v = 0; v < 16; v++) zf[v] = 0.f;
+    P[slot] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.a[rb], o.b[cb], zf, 0, 0, 0, 127 + 9, 0, 127 + 8);
+    Sc[slot] = __builtin_amdgcn_mfma_f32_32x32x8f16(o.fa[rb], o.fb[cb], zf, 0, 0, 0);
+  };
+  auto retire = [&](int u, int slot) __attribute__((always_inline)) {
+    const int rb = u / CB, cb = u % CB;
+#pragma unroll
+    for (int v = 0; v < 16; v++) acc[rb][cb][v] = __builtin_fmaf(P[slot][v], Sc[slot][v], acc[rb][cb][v]);
+  };
+
+  // Schedule of stage s (its codes in ring slot s % NBUF; its step-0
+  // operands already in registers):
+  //   step 0: per output tile its MFMAs, the fmas of the previous tile, the
+  //           reads of a quarter of step 1's operands, one copy item of stage
+  //           s + 3 (into the slot stage s - 1 released);
+  //   wait + barrier: this wave's copies of stage s + 1 are complete once at
+  //           most those of stages s + 2 and s + 3 (10) are outstanding, the
+  //           barrier publishes stage s + 1 and every wave is done reading
+  //           stage s - 1 ... s;
+  //   step 1: the same with step 0's operands of stage s + 1.
+  constexpr int NCOPY = 5;
+  static_assert(NCOPY == NT + 1, "one copy per tile slot of step 0, the fifth with the last");
+#pragma unroll 1
+  for (int p = 0; p < NBUF - 1; p++)
+#pragma unroll
+    for (int i = 0; i < NCOPY; i++) copy_item(p, i);
+  SVDQ_VM_BARRIER(10);
+  Ops OA, OB;
+#pragma unroll
+  for (int p = 0; p < RB + CB; p++) read_part(OA, 0, 0, p);
+#pragma unroll 1
+  for (int s = 0; s < stages; s++) {
+#pragma unroll
+    for (int u = 0; u < NT; u++) {
+      // the fences keep the order MFMAs, fmas of the previous tile, then the
+      // reads and copies: the fmas run under the MFMAs
+      issue(OA, u, u & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      retire(u == 0 ? NT - 1 : u - 1, (u + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      read_part(OB, s, 1, u);
+      copy_item(s + NBUF - 1, u);
+      if (u == NT - 1) copy_item(s + NBUF - 1, NT);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    SVDQ_VM_BARRIER(10);
+#pragma unroll
+    for (int u = 0; u < NT; u++) {
+      issue(OB, u, u & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      retire(u == 0 ? NT - 1 : u - 1, (u + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      read_part(OA, s + 1, 0, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  retire(NT - 1, 1);
+  // no copy may still be writing the ring, and every wave is done reading
+  // it, before the epilogue stages its output there
+  SVDQ_VM_BARRIER(0);
 
   // ---- epilogue: bias, rounding, store.  Each wave stages one 32-row
   // slice of its tile at a time in its own LDS region (row-major, output
@@ -339,7 +306,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     constexpr int OB = OUT == SVDQ_OUT_F32 ? 4 : 2;     // output bytes per element
     constexpr int ROWB = CB * 32 * OB;                  // bytes of one slice row
     constexpr int SLICE = 32 * ROWB;
-    static_assert(4 * SLICE <= LDS_A + LDS_B, "epilogue staging must fit the stage buffers");
+    static_assert(4 * SLICE <= NBUF * RING_STAGE, "epilogue staging must fit the ring");
     uint8_t* stage = smem + wave * SLICE;
     float bv[CB];
 #pragma unroll
@@ -377,57 +344,118 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   }
 }
 
-// Unfused up-projection: Y = round(Y + Tb L2b), 64 x 64 tile per workgroup.
+// Unfused up-projection: Y = round(Y + Tb L2b) in place, the separate second
+// pass of the naive pipeline (re-reads and re-writes the 16-bit output).  It
+// is HBM-bound (Y is read and written once; Tb and L2b are small), so a
+// workgroup owns 64 rows x 128 columns: the Y loads (16 bytes per lane, whole
+// rows) are issued first, the low-rank tile is computed meanwhile on the
+// bf16 MFMA (wave w: column block w, both 32-row blocks) and staged in LDS
+// as fp32, then every lane adds it to its Y pieces, rounds and stores them
+// (16 bytes per lane).  Rows past M and columns past N are neither read nor
+// written (buffer offsets past the resource).
 template <int OUT>
 __global__ __launch_bounds__(256) void up_kernel(const uint16_t* __restrict__ Tb, const uint16_t* __restrict__ l2t,
                                                  void* __restrict__ Y, int M, int N, int rank) {
-  const int tiles_n = (N + 63) / 64;
+  constexpr int OB = OUT == SVDQ_OUT_F32 ? 4 : 2;       // output bytes per element
+  constexpr int ROWB = 128 * OB;                        // bytes of one tile row
+  constexpr int PIECES = 64 * ROWB / 16 / 256;          // 16-byte pieces per thread
+  __shared__ __attribute__((aligned(16))) float low[64][128 + 4];
+  const int tiles_n = (N + 127) / 128;
   const long m0 = static_cast<long>(blockIdx.x / tiles_n) * 64;
-  const long n0 = static_cast<long>(blockIdx.x % tiles_n) * 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long n0 = static_cast<long>(blockIdx.x % tiles_n) * 128;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l32 = lane & 31, lh = lane >> 5;
-  const long r = m0 + (wave >> 1) * 32 + l32;
-  const long c = n0 + (wave & 1) * 32 + l32;
-  f32x16 acc;
+  const int rows = static_cast<int>(min(static_cast<long>(M) - m0, 64L));
+  const int cols = static_cast<int>(min(static_cast<long>(N) - n0, 128L));
+  const uint32_t gro = static_cast<uint32_t>(N) * OB;   // global row bytes
+  const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<uint8_t*>(Y) + (m0 * N + n0) * OB, 0, static_cast<int>(static_cast<uint32_t>(rows - 1) * gro + cols * OB),
+      0x00020000);
+  // piece q = t + 256 i: tile row q / (ROWB / 16), 16-byte column piece q % (ROWB / 16)
+  uint32_t off[PIECES];
+  u32x4 y[PIECES];
 #pragma unroll
-  for (int v = 0; v < 16; v++) acc[v] = 0.f;
-  bf16x8 z;
-#pragma unroll
-  for (int e = 0; e < 8; e++) z[e] = static_cast<__bf16>(0.f);
-  for (int tb = 0; tb < rank / 16; tb++) {
-    const bf16x8 a = r < M ? *reinterpret_cast<const bf16x8*>(Tb + bf16_block_index(r, tb * 16 + lh * 8, rank)) : z;
-    const bf16x8 b = c < N ? *reinterpret_cast<const bf16x8*>(l2t + bf16_block_index(c, tb * 16 + lh * 8, rank)) : z;
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+  for (int i = 0; i < PIECES; i++) {
+    const int q = t + 256 * i, r = q / (ROWB / 16), c = q % (ROWB / 16);
+    const bool ok = r < rows && c * 16 < cols * OB;
+    off[i] = ok ? static_cast<uint32_t>(r) * gro + c * 16 : 0x80000000u;
+    y[i] = __builtin_amdgcn_raw_buffer_load_b128(yr, off[i], 0, 0);
   }
-  if (c >= N) return;
+  // low-rank tile: column block `wave`, row blocks 0 and 1 (rows and
+  // columns past the matrix clamp to its last one; never stored)
+  f32x16 acc[2];
 #pragma unroll
-  for (int v = 0; v < 16; v++) {
-    const long rr = m0 + (wave >> 1) * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-    if (rr < M) {
-      const long idx = rr * N + c;
-      store_out<OUT>(Y, idx, load_out<OUT>(Y, idx) + acc[v]);
+  for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+    for (int v = 0; v < 16; v++) acc[rb][v] = 0.f;
+  const long c = min(n0 + wave * 32 + l32, static_cast<long>(N - 1));
+  for (int tb = 0; tb < rank / 16; tb++) {
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(l2t + bf16_block_index(c, tb * 16 + lh * 8, rank));
+#pragma unroll
+    for (int rb = 0; rb < 2; rb++) {
+      const long r = min(m0 + rb * 32 + l32, static_cast<long>(M - 1));
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Tb + bf16_block_index(r, tb * 16 + lh * 8, rank));
+      acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[rb], 0, 0, 0);
     }
+  }
+#pragma unroll
+  for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+    for (int v = 0; v < 16; v++) low[rb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3)][wave * 32 + l32] = acc[rb][v];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < PIECES; i++) {
+    const int q = t + 256 * i, r = q / (ROWB / 16), c0 = (q % (ROWB / 16)) * (16 / OB);
+    u32x4 o;
+    if constexpr (OUT == SVDQ_OUT_F32) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&low[r][c0]);
+      o = u32x4{__float_as_uint(__uint_as_float(y[i].x) + l4.x), __float_as_uint(__uint_as_float(y[i].y) + l4.y),
+                __float_as_uint(__uint_as_float(y[i].z) + l4.z), __float_as_uint(__uint_as_float(y[i].w) + l4.w)};
+    } else {
+      const f32x4 la = *reinterpret_cast<const f32x4*>(&low[r][c0]);
+      const f32x4 lb = *reinterpret_cast<const f32x4*>(&low[r][c0 + 4]);
+      const uint32_t w[4] = {y[i].x, y[i].y, y[i].z, y[i].w};
+      const float l8[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+      uint32_t out[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++)
+        out[e] = f32_to_bf16_bits(bf16_lo(w[e]) + l8[2 * e]) | (f32_to_bf16_bits(bf16_hi(w[e]) + l8[2 * e + 1]) << 16);
+      o = u32x4{out[0], out[1], out[2], out[3]};
+    }
+    __builtin_amdgcn_raw_buffer_store_b128(o, yr, off[i], 0, 0);
   }
 }
 
-hipError_t launch_gemm(int fmt, bool slab, int out_dtype, const GemmArgs& g, hipStream_t st) {
+int gemm_xcd_map(int M, int N, int K, int tiles_m, int tiles_n) {
+  constexpr double L2_SLICE = 3.0 * (1 << 20);   // of the 4 MB L2 of an XCD
+  const double a = static_cast<double>(M) * K / 2 / 8, b = static_cast<double>(N) * K / 2 / 8;
+  const bool cols = tiles_n % 8 == 0 && b <= L2_SLICE;
+  const bool rows = tiles_m % 8 == 0 && a <= L2_SLICE;
+  if (cols && (!rows || b <= a)) return 1;
+  if (rows) return 2;
+  return 0;
+}
+
+hipError_t launch_gemm(int fmt, bool slab, int out_dtype, const GemmArgs& ga, hipStream_t st) {
   const bool f32 = out_dtype == SVDQ_OUT_F32;
   if (fmt == SVDQ_INT4_G64_FP16) {
-    const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-    dim3 grid(tiles), block(256);
+    const int tiles_m = (ga.M + BM - 1) / BM, tiles_n = (ga.N + BN - 1) / BN;
+    GemmArgs g = ga;
+    g.xcd_map = gemm_xcd_map(g.M, g.N, g.K, tiles_m, tiles_n);
+    dim3 grid(tiles_m * tiles_n), block(256);
 #define SVDQ_G(S, O) hipLaunchKernelGGL((gemm_kernel<S, O>), grid, block, 0, st, g)
     if (slab) { if (f32) SVDQ_G(true, SVDQ_OUT_F32); else SVDQ_G(true, SVDQ_OUT_BF16); }
     else      { if (f32) SVDQ_G(false, SVDQ_OUT_F32); else SVDQ_G(false, SVDQ_OUT_BF16); }
 #undef SVDQ_G
     return hipGetLastError();
   }
-  return launch_gemm_fp4(slab, out_dtype, g, st);
+  return launch_gemm_fp4(slab, out_dtype, ga, st);
 }
 
 hipError_t launch_up(int out_dtype, const uint16_t* Tb, const uint16_t* l2t, void* Y, int M, int N, int rank,
                      hipStream_t st) {
   if (rank == 0) return hipSuccess;
-  const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  const int tiles = ((M + 63) / 64) * ((N + 127) / 128);
   if (out_dtype == SVDQ_OUT_F32)
     hipLaunchKernelGGL(up_kernel<SVDQ_OUT_F32>, dim3(tiles), dim3(256), 0, st, Tb, l2t, Y, M, N, rank);
   else

@@ -65,37 +65,6 @@ constexpr int F_BIAS = F_EPI + 4 * 4096;
 constexpr int F_LDS = F_BIAS + F_NBIAS * 1024;    // 157696 bytes
 constexpr int F_NCOPY = 11;                       // copies per wave per stage
 
-// The global -> LDS copies are written as inline asm, so the compiler's own
-// wait insertion neither sees them nor adds conservative waits before LDS
-// reads; every wait on them is explicit below (s_waitcnt vmcnt counts them in
-// issue order, together with the epilogue's stores).  A copy reads
-// sbase + voff + OFF (64-bit scalar base, 32-bit per-lane offset, immediate
-// OFF) and writes LDS at m0 + OFF + 16 l (4 l) for lane l: the immediate
-// offset moves both addresses.  An LDS copy needs one wait state after a
-// scalar write of m0: the stage bodies keep an MFMA between set_m0 and the
-// first copy that reads it (scheduling fences fix that order), and the
-// prologue waits explicitly (set_m0_nop).  Nothing else in these
-// kernels uses m0 (the compiler warns that a reserved register in a clobber
-// list may not be preserved, which these copies do not rely on: m0 is always
-// written right before the copies that read it).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void set_m0(uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0" ::"s"(lds) : "memory", "m0");
-}
-__device__ __forceinline__ void set_m0_nop(uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0" ::"s"(lds) : "memory", "m0");
-}
-template <int OFF>
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff) {
-  asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2" ::"v"(voff), "s"(sbase), "i"(OFF) : "memory");
-}
-template <int OFF>
-__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff) {
-  asm volatile("global_load_lds_dword %0, %1 offset:%2" ::"v"(voff), "s"(sbase), "i"(OFF) : "memory");
-}
-#pragma clang diagnostic pop
-
 // Four accumulator values (held in AGPRs) read out where the epilogue uses
 // them: the volatile asm keeps the reads in program order, so the compiler
 // cannot move all 256 reads to the start of the epilogue (whose register
@@ -109,16 +78,6 @@ __device__ __forceinline__ f32x4 acc_read4(float a, float b, float c, float d) {
       : "a"(a), "a"(b), "a"(c), "a"(d));
   return r;
 }
-
-// s_waitcnt lgkmcnt(0) (as a builtin, so the compiler knows this wave's LDS
-// reads are complete), s_waitcnt vmcnt(n), then s_barrier; also a compiler
-// memory barrier
-constexpr int LGKM0 = 0xC07F;     // s_waitcnt encoding: lgkmcnt(0), vmcnt and expcnt unconstrained
-#define SVDQ_VM_BARRIER(n)                  \
-  do {                                      \
-    __builtin_amdgcn_s_waitcnt(LGKM0);      \
-    asm volatile("s_waitcnt vmcnt(" #n ")\n\ts_barrier" ::: "memory"); \
-  } while (0)
 
 }  // namespace
 
@@ -150,6 +109,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
 
   const int tiles_m = (M + F_TILE - 1) / F_TILE, tiles_n = (N + F_TILE - 1) / F_TILE;
   const int ntiles = tiles_m * tiles_n;
+  const int xmap = g.xcd_map;
   const int grid = static_cast<int>(gridDim.x), wg = static_cast<int>(blockIdx.x);
   const int my_tiles = (ntiles - wg + grid - 1) / grid;   // >= 1: the grid never exceeds the tile count
   const int last_ablk = (M + 31) / 32 - 1, last_bblk = N / 32 - 1;
@@ -161,7 +121,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
 
   auto tile_blocks = [&](int seq, int& mb0, int& nb0) __attribute__((always_inline)) {
     int tm, tn;
-    tile_of(wg + seq * grid, tiles_m, tiles_n, tm, tn);
+    tile_of(wg + seq * grid, tiles_m, tiles_n, xmap, tm, tn);
     // uniform by construction; made scalar so that addresses and buffer
     // resources built from them stay in SGPRs
     mb0 = wave_uniform(tm * (F_TILE / 32));
@@ -593,8 +553,13 @@ int device_cu_count() {
   return n;
 }
 
-hipError_t launch_gemm_fp4(bool slab, int out_dtype, const GemmArgs& g, hipStream_t st) {
-  const int tiles = ((g.M + F_TILE - 1) / F_TILE) * ((g.N + F_TILE - 1) / F_TILE);
+hipError_t launch_gemm_fp4(bool slab, int out_dtype, const GemmArgs& ga, hipStream_t st) {
+  const int tiles_m = (ga.M + F_TILE - 1) / F_TILE, tiles_n = (ga.N + F_TILE - 1) / F_TILE;
+  const int tiles = tiles_m * tiles_n;
+  GemmArgs g = ga;
+  // the strip maps need the grid's workgroups spread evenly over the XCDs
+  // (a grid that is a multiple of 8 walking all tiles)
+  g.xcd_map = gemm_xcd_map(g.M, g.N, g.K, tiles_m, tiles_n);
   // a workgroup walks several tiles only when a tile has at least 3 stages,
   // so that the copies (3 stages ahead) never run more than one tile ahead
   const int stages = (slab ? (g.rank / 16 + 1) / 2 : 0) + g.K / 128;

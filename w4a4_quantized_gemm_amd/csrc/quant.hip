@@ -9,14 +9,14 @@
 // Work split: a workgroup owns 16 token rows and one of `kparts` equal
 // parts of the 128-wide K chunks (the launch splits K so that there are
 // about four workgroups per CU: with one workgroup per 16-row block the M
-// of a layer would leave most of the chip idle); its 4 waves take
+// of a layer would leave most of the chip idle); its NW (4 or 8) waves take
 // interleaved chunks of the part.  In a chunk, lane l holds row l % 16 and
 // the 32 consecutive K elements 32 * (l / 16) .. + 31, loaded as four
 // 16-byte vectors.  An INT4 group (64) is the lane pair (l, l ^ 16); an FP4
 // group (32) is one lane.  The 32 values are also the A operands of four
 // 16x16x32 bf16 MFMAs (8 consecutive K per MFMA), whose B operands come from
 // L1 stored transposed (L1t[t][k]), so the k index sets of A and B match.
-// The per-wave partial T tiles are summed across the 4 waves in LDS in a
+// The per-wave partial T tiles are summed across the NW waves in LDS in a
 // fixed order; with several K parts each part writes its fp32 partial and
 // t_reduce_kernel adds the parts in order and rounds once, so T is
 // deterministic.
@@ -74,8 +74,8 @@ __device__ __forceinline__ void x_hat8(const uint8_t* xs, const float* ils, int 
 // row's mean mu and 1/sqrt(var + eps) rho from `rowstat` (two floats per row)
 // and inv_lam pointing at gamma' = gamma * inv_lambda (K floats) followed by
 // beta' = beta * inv_lambda (K floats).
-template <int FMT, bool QUANT, bool DOWN, int RB, bool NORM>
-__global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X, int M, int K,
+template <int FMT, bool QUANT, bool DOWN, int RB, bool NORM, int NW>
+__global__ __launch_bounds__(NW * 64) void act_kernel(const uint16_t* __restrict__ X, int M, int K,
                                                   const float* __restrict__ inv_lam,
                                                   const float* __restrict__ rowstat,
                                                   const uint16_t* __restrict__ l1op,
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
   // smoothing factors (512 B; NORM: 128 gamma' then 128 beta'); after the
   // loop the same memory holds the cross-wave T reduction
   constexpr int WSTAGE = 4096 + (NORM ? 1024 : 512);
-  constexpr int LDS_BYTES = (LR && 256 * R > 4 * WSTAGE) ? 256 * R : 4 * WSTAGE;
+  constexpr int LDS_BYTES = (LR && NW * 64 * R > NW * WSTAGE) ? NW * 64 * R : NW * WSTAGE;
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
     rho = rowstat[2 * sr_row + 1];
   }
   // Two chunks of each wave are in flight while it processes a third: chunk
-  // it + 8 is requested into the registers chunk it arrived in.
+  // it + 2 NW is requested into the registers chunk it arrived in.
   const int it0 = part * cpp + wave;
   const u32x4 z4 = u32x4{0u, 0u, 0u, 0u};
   u32x4 xa[4] = {z4, z4, z4, z4}, xb[4] = {z4, z4, z4, z4};
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
     iv = __builtin_amdgcn_raw_buffer_load_b128(ir, ioff, ok ? c0 * 512 : i_oob, 0);
   };
   fetch(it0, xa, ia);
-  fetch(it0 + 4, xb, ib);
+  fetch(it0 + NW, xb, ib);
   auto body = [&](int it, u32x4 (&x)[4], u32x4& iv) __attribute__((always_inline)) {
     const int kb = it * 128 + kq * 32;
     // stage the chunk: piece p of row r goes to slot p ^ r of the row, so
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
     // The X prefetch is issued after the L1 loads: vector memory counters
     // complete in issue order, so waiting for the L1 operands does not wait
     // for the prefetch.
-    fetch(it + 8, x, iv);
+    fetch(it + 2 * NW, x, iv);
     // lane (row, kq): elements kq * 32 .. + 31 of its row = pieces 4 kq .. 4 kq + 3
     float xh[32];
 #pragma unroll
@@ -329,9 +329,9 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
     if constexpr (!MFMA_FIRST) down();
   };
   int it = it0;
-  for (; it + 4 < c_end; it += 8) {
+  for (; it + NW < c_end; it += 2 * NW) {
     body(it, xa, ia);
-    body(it + 4, xb, ib);
+    body(it + NW, xb, ib);
   }
   if (it < c_end) body(it, xa, ia);
 
@@ -345,10 +345,11 @@ __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ X
 #pragma unroll
       for (int v = 0; v < 4; v++) red[(wave * 16 + 4 * kq + v) * R + nb * 16 + row] = acc[nb][v];
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * R; idx += 256) {
+    for (int idx = threadIdx.x; idx < 16 * R; idx += NW * 64) {
       const int rr = idx / R, t = idx % R;
-      const float s = ((red[(0 * 16 + rr) * R + t] + red[(1 * 16 + rr) * R + t]) + red[(2 * 16 + rr) * R + t]) +
-                      red[(3 * 16 + rr) * R + t];
+      float s = red[rr * R + t];
+#pragma unroll
+      for (int w = 1; w < NW; w++) s += red[(w * 16 + rr) * R + t];
       const long gr = static_cast<long>(rblk) * 16 + rr;
       if (gr < M) {
         if (kparts == 1) Tb[bf16_block_index(gr, t, R)] = static_cast<uint16_t>(f32_to_bf16_bits(s));
@@ -420,12 +421,23 @@ static int choose_kparts(int M, int K, bool down, bool have_tpart, bool fp4) {
 
 template <int FMT, bool QUANT, bool DOWN, bool NORM>
 static hipError_t launch_act_rb(int rb, const ActArgs& a, hipStream_t st) {
-  const int kparts = choose_kparts(a.M, a.K, DOWN && rb > 0, a.tpart != nullptr, FMT == SVDQ_FP4_E2M1_G32_E8M0);
-  dim3 grid(((a.M + 15) / 16) * kparts), block(256);
-#define SVDQ_ACT_CASE(RBV)                                                                                  \
-  case RBV:                                                                                               \
-    hipLaunchKernelGGL((act_kernel<FMT, QUANT, DOWN, RBV, NORM>), grid, block, 0, st, a.X, a.M, a.K, a.inv_lam, \
-                       a.rowstat, a.l1t, a.codes, a.scales, a.Tb, kparts, a.tpart);                      \
+  int kparts = choose_kparts(a.M, a.K, DOWN && rb > 0, a.tpart != nullptr, FMT == SVDQ_FP4_E2M1_G32_E8M0);
+  // One or two row blocks per CU over a short K: eight waves per workgroup
+  // share a row block's chunks instead of splitting its K over workgroups,
+  // so the down-projection needs no second (reduction) launch and each CU
+  // still has enough loads in flight.
+  const long nrb = (a.M + 15) / 16, cus = device_cu_count();
+  const bool wide = DOWN && rb > 0 && nrb >= cus && nrb <= 2 * cus && (a.K >> 7) <= 32;
+  if (wide) kparts = 1;
+  dim3 grid(static_cast<unsigned>(nrb * kparts)), block(wide ? 512 : 256);
+#define SVDQ_ACT_CASE(RBV)                                                                                        \
+  case RBV:                                                                                                     \
+    if (wide)                                                                                                   \
+      hipLaunchKernelGGL((act_kernel<FMT, QUANT, DOWN, RBV, NORM, 8>), grid, block, 0, st, a.X, a.M, a.K, a.inv_lam, \
+                         a.rowstat, a.l1t, a.codes, a.scales, a.Tb, kparts, a.tpart);                           \
+    else                                                                                                        \
+      hipLaunchKernelGGL((act_kernel<FMT, QUANT, DOWN, RBV, NORM, 4>), grid, block, 0, st, a.X, a.M, a.K, a.inv_lam, \
+                         a.rowstat, a.l1t, a.codes, a.scales, a.Tb, kparts, a.tpart);                           \
     break;
   switch (rb) {
     SVDQ_ACT_CASE(0) SVDQ_ACT_CASE(1) SVDQ_ACT_CASE(2) SVDQ_ACT_CASE(3) SVDQ_ACT_CASE(4)

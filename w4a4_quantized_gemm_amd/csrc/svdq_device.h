@@ -110,15 +110,75 @@ __host__ __device__ __forceinline__ long l1_operand_index(int t, long k, int R) 
          (k & 7);
 }
 
+// Direct global -> LDS copies (global_load_lds), written as inline asm so
+// that the compiler's own wait insertion neither sees them nor adds
+// conservative waits before LDS reads; every wait on them is explicit
+// (s_waitcnt vmcnt counts them in issue order, together with any other
+// vector memory operation of the wave).  A copy reads sbase + voff + OFF
+// (64-bit scalar base, 32-bit per-lane offset, immediate OFF) and writes LDS
+// at m0 + OFF + 16 l (4 l) for lane l: the immediate offset moves both
+// addresses.  A copy needs one wait state after a scalar write of m0
+// (set_m0_nop provides it; set_m0 leaves it to the caller).  Nothing else in
+// these kernels uses m0 (the compiler warns that a reserved register in a
+// clobber list may not be preserved, which these copies do not rely on: m0
+// is always written right before the copies that read it).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void set_m0(uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0" ::"s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void set_m0_nop(uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0" ::"s"(lds) : "memory", "m0");
+}
+template <int OFF>
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff) {
+  asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2" ::"v"(voff), "s"(sbase), "i"(OFF) : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff) {
+  asm volatile("global_load_lds_dword %0, %1 offset:%2" ::"v"(voff), "s"(sbase), "i"(OFF) : "memory");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt lgkmcnt(0) (as a builtin, so the compiler knows this wave's LDS
+// reads are complete), s_waitcnt vmcnt(n), then s_barrier; also a compiler
+// memory barrier
+constexpr int LGKM0 = 0xC07F;     // s_waitcnt encoding: lgkmcnt(0), vmcnt and expcnt unconstrained
+#define SVDQ_VM_BARRIER(n)                  \
+  do {                                      \
+    __builtin_amdgcn_s_waitcnt(svdq::LGKM0); \
+    asm volatile("s_waitcnt vmcnt(" #n ")\n\ts_barrier" ::: "memory"); \
+  } while (0)
+
 // Workgroup (or persistent turn) id b -> output tile (tm, tn).  The hardware
-// deals workgroups round-robin to the 8 XCDs, so b % 8 is the XCD; each XCD
-// gets a contiguous range of tiles, walked 4 tile rows at a time so that the
-// workgroups resident on one XCD share rows of A and columns of B in its L2.
-__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+// deals workgroups round-robin to the 8 XCDs, so b % 8 is the XCD and b / 8
+// its j-th workgroup; each XCD works through its own set of tiles, so that
+// its L2 serves the operand data its resident workgroups share.
+//  map 1 (column strips; tiles_n % 8 == 0): XCD x owns tile columns
+//    [x w, (x + 1) w), w = tiles_n / 8, and walks them row by row: its slice
+//    of the weight codes stays in its L2 while the activation rows stream;
+//  map 2 (row strips; tiles_m % 8 == 0): the same with rows and columns
+//    exchanged;
+//  map 0: XCD x takes a contiguous range of the tiles in 4-row groups
+//    walked column by column.
+// The launch picks the map whose resident slice is smaller (and fits an L2).
+__device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int map, int& tm, int& tn) {
   constexpr int NXCD = 8, GROUP_TM = 4;
+  const int x = b % NXCD, j = b / NXCD;
+  if (map == 1) {
+    const int w = tiles_n / NXCD;
+    tm = j / w;
+    tn = x * w + j % w;
+    return;
+  }
+  if (map == 2) {
+    const int h = tiles_m / NXCD;
+    tn = j / h;
+    tm = x * h + j % h;
+    return;
+  }
   const int T = tiles_m * tiles_n;
   const int q = T / NXCD, rem = T % NXCD;
-  const int x = b % NXCD, j = b / NXCD;
   const int t = x * q + (x < rem ? x : rem) + j;
   const int per_group = GROUP_TM * tiles_n;
   const int grp = t / per_group;

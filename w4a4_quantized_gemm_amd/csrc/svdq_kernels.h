@@ -43,7 +43,14 @@ struct GemmArgs {
   const float* bias;      // N or null
   void* Y;                // M x N, bf16 bits or fp32
   int M, K, N, rank;
+  int xcd_map;            // tile -> XCD assignment (tile_of), set by the launch
 };
+
+// The tile -> XCD map for a GEMM of tiles_m x tiles_n tiles over M x K
+// activations and N x K weights (4-bit codes): column strips when the weight
+// slice per XCD is the smaller one and fits in an L2, row strips in the
+// opposite case, else contiguous 4-row groups.
+int gemm_xcd_map(int M, int N, int K, int tiles_m, int tiles_n);
 
 // slab: append the rank-r bf16 K-slab Tb L2b before the epilogue.
 hipError_t launch_gemm(int fmt, bool slab, int out_dtype, const GemmArgs& g, hipStream_t st);

@@ -87,13 +87,21 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
+# the sources each profiled kernel is built from: a counter summary stays
+# valid while these are unchanged
+KERNEL_SOURCES = {
+    "fp4": ("gemm_fp4.hip", "svdq_device.h", "svdq_kernels.h"),
+    "int4": ("gemm.hip", "svdq_device.h", "svdq_kernels.h"),
+    "act": ("quant.hip", "svdq_device.h", "svdq_kernels.h"),
+}
+
+
+def kernel_source_hash(kind: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "w4a4_quantized_gemm_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + f.read())
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
@@ -273,42 +281,45 @@ def time_norm(torch, S, rig, steps, warmup, eps=1e-6):
     return statistics.median(t["fused"]), statistics.median(t["separate"])
 
 
-W4A16_SHAPES = ((1, 3072, 18432), (16, 3072, 18432))   # AdaLN modulation projection: one sample / a batch of 16
+W4A16_SHAPE = (3072, 18432)        # AdaLN modulation projection: 3072 -> 6 x 3072
+W4A16_ROWS = (1, 16)                # one sample / a batch of 16
 
 
-def time_w4a16(torch, S, WL, to_tensor, steps, warmup, fmt="int4"):
-    """The weight-only 4-bit layer on the modulation projection's shape
-    (3072 -> 6 x 3072), against torch's bf16 matmul of the same weights and
-    the W4A4 layer (rank 0) at the same M, interleaved.  Enough blob copies
-    rotate to defeat the Infinity Cache.  Returns one dict per M."""
+def time_w4a16(torch, S, WL, to_tensor, steps, warmup, fmts=("int4", "fp4")):
+    """The weight-only 4-bit layer on the modulation projection's shape,
+    against torch's bf16 matmul of the same weights and the W4A4 layer
+    (rank 0) at the same M, interleaved.  Enough blob copies rotate to
+    defeat the Infinity Cache.  Returns one dict per (format, M)."""
     res = []
-    for M, K, N in W4A16_SHAPES:
+    K, N = W4A16_SHAPE
+    dev = "cuda:0"
+    for fmt in fmts:
         cfg = WL.C2.with_(name="w4a16", M=64, K=K, N=N, rank=0, fmt=fmt, w_std=1 / K ** 0.5, bias_std=0.02, seed=5)
         X_bits, W_bits, b_bits = WL.make_layer(cfg)
-        dev = "cuda:0"
         Xf, W, b = to_tensor(X_bits, dev), to_tensor(W_bits, dev), to_tensor(b_bits, dev)
         a = torch.empty(K, dtype=torch.float32, device=dev)
         S.svdq_act_absmax(Xf, a)
         layer = S.SVDQLinear.prepare(W, a, 0, fmt, cfg.alpha, bias=b)
-        X = Xf[:M].contiguous()
         ncopy = max(2, -(-2 * INFINITY_CACHE // layer.blob.numel()))
         blobs = [layer.blob] + [layer.blob.clone() for _ in range(ncopy - 1)]
         nw = max(2, -(-2 * INFINITY_CACHE // (W.numel() * 2)))
         Ws = [W] + [W.clone() for _ in range(nw - 1)]
-        ws = layer.workspace(M)
-        ws4 = layer.workspace(M)
-        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        fns = [("w4a16", lambda k: S.svdq_linear_w4a16(layer.desc, blobs[k % ncopy], X, Y, ws, S.OUT_BF16)),
-               ("w4a4", lambda k: S.svdq_linear(layer.desc, blobs[k % ncopy], X, Y, ws4, S.OUT_BF16)),
-               ("bf16", lambda k: torch.matmul(X, Ws[k % nw]))]
-        warm(torch, [f for _, f in fns], warmup, 0.3)
-        t = interleaved(torch, fns, steps)
-        med = {k: statistics.median(v) * 1e3 for k, v in t.items()}
         wbytes = K * N // 2 + (K // (64 if fmt == "int4" else 32)) * N * (2 if fmt == "int4" else 1)
-        res.append({"M": M, "K": K, "N": N, "format": fmt, "us": med["w4a16"],
-                    "weight_gbs": wbytes / (med["w4a16"] * 1e-6) / 1e9,
-                    "frac_hbm": wbytes / (med["w4a16"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                    "us_bf16_matmul": med["bf16"], "us_w4a4_rank0": med["w4a4"]})
+        for M in W4A16_ROWS:
+            X = Xf[:M].contiguous()
+            ws = layer.workspace(M)
+            ws4 = layer.workspace(M)
+            Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            fns = [("w4a16", lambda k: S.svdq_linear_w4a16(layer.desc, blobs[k % ncopy], X, Y, ws, S.OUT_BF16)),
+                   ("w4a4", lambda k: S.svdq_linear(layer.desc, blobs[k % ncopy], X, Y, ws4, S.OUT_BF16)),
+                   ("bf16", lambda k: torch.matmul(X, Ws[k % nw]))]
+            warm(torch, [f for _, f in fns], warmup, 0.3)
+            t = interleaved(torch, fns, steps)
+            med = {k: statistics.median(v) * 1e3 for k, v in t.items()}
+            res.append({"M": M, "K": K, "N": N, "format": fmt, "us": med["w4a16"],
+                        "weight_gbs": wbytes / (med["w4a16"] * 1e-6) / 1e9,
+                        "frac_hbm": wbytes / (med["w4a16"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                        "us_bf16_matmul": med["bf16"], "us_w4a4_rank0": med["w4a4"]})
         del blobs, Ws, layer, W, Xf
         torch.cuda.empty_cache()
     return res
@@ -364,10 +375,11 @@ def _cpu_model():
     return "unknown"
 
 
-def load_traffic(workload, src_hash):
+def load_traffic(workload, fmt):
     """HBM traffic per launch of the GEMM kernel and of the activation pass
-    from the committed rocprofv3 counter summary, if it was taken on the
-    current kernel sources: (gemm_bytes, act_bytes), None where unknown."""
+    from the committed rocprofv3 counter summary, each only if it was taken
+    on that kernel's current sources: (gemm_bytes, act_bytes), None where
+    unknown."""
     path = os.path.join(ROOT, "profiles", f"gemm_{workload}_hbm_counters.json")
     if not os.path.exists(path):
         return None, None
@@ -375,9 +387,9 @@ def load_traffic(workload, src_hash):
         d = json.load(open(path))
     except (OSError, ValueError):
         return None, None
-    if d.get("kernel_source_hash") != src_hash:
-        return None, None
-    return d.get("traffic_bytes_per_launch"), d.get("act_traffic_bytes_per_launch")
+    g = d.get("traffic_bytes_per_launch") if d.get("kernel_source_hash") == kernel_source_hash(fmt) else None
+    a = d.get("act_traffic_bytes_per_launch") if d.get("act_source_hash") == kernel_source_hash("act") else None
+    return g, a
 
 
 COPY_BYTES = 1 << 30          # the calibration copy moves this many bytes each way
@@ -396,7 +408,7 @@ def calibration_copy(torch):
     torch.cuda.empty_cache()
 
 
-def summarize_counters(fetch_dir, write_dir, cfg, src_hash):
+def summarize_counters(fetch_dir, write_dir, cfg):
     """Per-dispatch HBM traffic of the GEMM kernel from two rocprofv3 --pmc
     runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), each scaled by the ratio
     of the calibration copy's known bytes to what the same counter read for
@@ -421,7 +433,8 @@ def summarize_counters(fetch_dir, write_dir, cfg, src_hash):
         (lambda k: k.startswith("void svdq::gemm_kernel<"))
     # torch's copy kernel of the calibration: the largest elementwise-copy dispatch
     is_copy = lambda k: "copy" in k.lower() and not k.startswith("void svdq::")
-    out = {"workload": cfg.name, "kernel_source_hash": src_hash, "copy_bytes": COPY_BYTES,
+    out = {"workload": cfg.name, "kernel_source_hash": kernel_source_hash(cfg.fmt),
+           "act_source_hash": kernel_source_hash("act"), "copy_bytes": COPY_BYTES,
            "commands": [f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{c}_{cfg.name} -o run -- "
                         f"python3 bench.py --profile-only --calibrate-copy --steps 4 --warmup 1 --workload {cfg.name}"
                         for c in ("FETCH_SIZE", "WRITE_SIZE")] +
@@ -475,7 +488,7 @@ UTIL_PASSES = (
 N_XCD, N_SIMD = 8, 1024      # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
 
 
-def summarize_util(dirs, cfg, src_hash):
+def summarize_util(dirs, cfg):
     """MFMA / VALU / wait counters of the GEMM kernel and the activation pass
     from rocprofv3 --pmc passes of --profile-only (per-dispatch means), with
     the derived figures: the shader clock (GRBM_GUI_ACTIVE is summed over the
@@ -502,7 +515,8 @@ def summarize_util(dirs, cfg, src_hash):
                     if key not in seen:
                         seen.add(key)
                         durs[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
-    out = {"workload": cfg.name, "kernel_source_hash": src_hash,
+    out = {"workload": cfg.name, "kernel_source_hash": kernel_source_hash(cfg.fmt),
+           "act_source_hash": kernel_source_hash("act"),
            "commands": [f"rocprofv3 --pmc {p} --output-format csv -d gpurun_out/pmc_{cfg.name}_{i + 1} -o run -- "
                         f"python3 bench.py --profile-only --steps 4 --warmup 1 --workload {cfg.name}"
                         for i, p in enumerate(UTIL_PASSES)] +
@@ -655,11 +669,11 @@ def main():
     cfg = cfgs[args.workload]
 
     if args.summarize_util:
-        summarize_util(args.summarize_util, cfg, kernel_source_hash())
+        summarize_util(args.summarize_util, cfg)
         return
 
     if args.summarize_counters:
-        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], cfg, kernel_source_hash())
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], cfg)
         return
 
     if args.profile_only:
@@ -684,8 +698,8 @@ def main():
     g_ms, q_ms = r["t"]["gemm"]["median"], r["t"]["quant"]["median"]
     gemm_tops = A["gemm_ops"] / (g_ms / 1e3) / 1e12
     q_gbs = A["q_bytes"] / (q_ms / 1e3) / 1e9
-    src_hash = kernel_source_hash()
-    traffic, act_traffic = load_traffic(cfg.name, src_hash)
+    src_hash = kernel_source_hash(fmt)
+    traffic, act_traffic = load_traffic(cfg.name, fmt)
     line = {
         "metric": "W4A4+low-rank linear effective TOPS & % MFMA peak; fused vs unfused speedup",
         "value": tops,

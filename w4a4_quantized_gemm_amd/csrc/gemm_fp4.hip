@@ -197,8 +197,9 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
     o.vsx = lane4 + upper * static_cast<uint32_t>((xb - xa) * KS * 128) + static_cast<uint32_t>(ks) * 128u;
     o.vsw = lane4 + upper * static_cast<uint32_t>((wb - wa) * KS * 128) + static_cast<uint32_t>(ks) * 128u;
   };
-  // copy items of a stage into ring buffer rc, one group per MFMA slot t of
-  // the stage's first step: each m0 write sits one slot before the copies
+  // copy items of a stage into ring buffer rc, one group per MFMA slot t
+  // (items 0..4 in slots 0..4 of the first step, items 5..11 in slots
+  // 8..14 of the second): each m0 write sits one slot before the copies
   // that read it (the MFMA between them is the wait state the copy needs)
   auto copy_slot = [&](const CopyDesc& d, const CopyOff& o, uint32_t rc, int t) __attribute__((always_inline)) {
     // one copy per slot: bursts of copies stall the issuing wave
@@ -279,17 +280,20 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
 
   // One stage G (ring buffer rb = G % 4), a single basic block.
   //  step 0: 16 MFMAs on R0 (stage G, step 0), with the reads of step 1 into
-  //          R1 and the 15 copy items of stage G + 3 into ring buffer
+  //          R1 and the 4 activation copies of stage G + 3 into ring buffer
   //          (G + 3) % 4 -- stage G - 1's, released by the previous barrier;
   //  wait + barrier: this wave's copies of stage G + 1 are complete once at
-  //          most the F_NCOPY copies of each of stages G + 2 and G + 3 are
-  //          outstanding (in the first stages of a tile the previous tile's
-  //          epilogue stores come after those copies, so the same count also
-  //          waits for the older stores); lgkmcnt(0) completes this wave's
-  //          reads of stage G; the barrier then publishes stage G + 1 and
-  //          releases stage G's buffer;
+  //          most the F_NCOPY copies of stage G + 2 and the 4 of stage G + 3
+  //          are outstanding (in the first stages of a tile the previous
+  //          tile's epilogue stores come after those copies, so the same
+  //          count also waits for the older stores); lgkmcnt(0) completes
+  //          this wave's reads of stage G; the barrier then publishes stage
+  //          G + 1 and releases stage G's buffer;
   //  step 1: 16 MFMAs on R1 with the reads of stage G + 1 step 0 into R0 and
-  //          of its scales.
+  //          of its scales, and the other 7 copies of stage G + 3 (weights,
+  //          scales, bias) in its second half, after the reads.  Spreading
+  //          the copies over both steps keeps fewer of them in flight behind
+  //          the MFMAs at once.
   static_assert(F_NCOPY == 11, "the wait counts below assume 11 copies per wave per stage");
   // (sx, sw): this stage's scales; (nsx, nsw): where the next stage's go
   auto stage = [&](Ops& R0, const uint32_t (&sx)[4], const uint32_t (&sw)[4], uint32_t (&nsx)[4],
@@ -305,10 +309,10 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
       mfma(R0, sx, sw, t, std::integral_constant<int, 0>{}, LR, wmask);
       __builtin_amdgcn_sched_barrier(0);
       if (t < 8) read_piece(R1, ax, aw, 1, t);
-      copy_slot(d, o, rc, t);
+      if (t <= 4) copy_slot(d, o, rc, t);
       __builtin_amdgcn_sched_barrier(0);
     }
-    SVDQ_VM_BARRIER(22);
+    SVDQ_VM_BARRIER(15);
     __builtin_amdgcn_sched_barrier(0);
     const uint32_t nx = rx + rn * F_STAGE, nw = rw + rn * F_STAGE;
     const uint32_t nsxa = rsx + rn * 2048, nswa = rsw + rn * 2048;
@@ -317,6 +321,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
       mfma(R1, sx, sw, t, std::integral_constant<int, 1>{}, LR, wmask);
       if (t < 8) read_piece(R0, nx, nw, 0, t);
       if (t < 8) read_scale(nsx, nsw, nsxa, nswa, t);
+      if (t >= 8) copy_slot(d, o, rc, t - 3);
       __builtin_amdgcn_sched_barrier(0);
     }
     o.v += d.inc;

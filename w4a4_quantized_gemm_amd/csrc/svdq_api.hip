@@ -394,7 +394,7 @@ svdq_status svdq_linear_w4a16(const svdq_layer_desc* desc, const void* d_prepare
   a.bias = bp.bias;
   a.Y = d_Y;
   a.out_f32 = out_dtype == SVDQ_OUT_F32;
-  a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(d_workspace) + A.w4a16);
+  a.pieces = static_cast<uint8_t*>(d_workspace) + A.w4a16;
   return from_hip(launch_w4a16(desc->fmt, a, as_stream(stream)));
 }
 

@@ -54,13 +54,10 @@ struct ActLayout {
 };
 ActLayout act_layout(const svdq_layer_desc& d, int M);
 
-// Weight-only (W4A16) layer for small M: rows are padded to kW4A16Rows[b]
-// (1, 2, 4, 8 or 16), K is split into w4a16_ksplit parts (a divisor of
-// K / 64) so that a part's fp32 activations fit the kernel's LDS and there
-// are enough workgroups; with more than one part the fp32 partial outputs
-// (parts x M x N) sit in the workspace.
+// Weight-only (W4A16) layer for small M (at most 16 rows): the bf16 pieces
+// of x_hat in MFMA A-operand order sit in the workspace, one operand plane
+// (up to 8 rows) or two (up to 16 rows) of K * 64 bytes each.
 constexpr int kW4A16MaxM = 16;
-int w4a16_rows(int M);
-int w4a16_ksplit(int M, int K, int N);
+inline int w4a16_planes(int M) { return M <= 8 ? 1 : 2; }
 
 }  // namespace svdq

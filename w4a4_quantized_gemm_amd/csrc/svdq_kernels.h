@@ -66,7 +66,7 @@ struct W4A16Args {
   const float* bias;      // N or null
   void* Y;                // M x N
   int out_f32;
-  float* part;            // fp32 partial outputs of the K parts (workspace), when w4a16_ksplit > 1
+  void* pieces;           // workspace: the bf16 pieces of x_hat in MFMA A-operand order (K * 64 * w4a16_planes(M) bytes)
 };
 // The weight-only 4-bit layer (rank 0 blob), small M.
 hipError_t launch_w4a16(int fmt, const W4A16Args& a, hipStream_t st);

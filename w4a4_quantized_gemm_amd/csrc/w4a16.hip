@@ -6,236 +6,302 @@
 //   Y     = round(x_hat dequant(Q(R)) + b)  (R = W_hat: a prepared layer of rank 0)
 //
 // Memory-bound: the 4-bit weights (K N / 2 bytes) are read once, the
-// activations are a few KB.  A workgroup owns 4 x 32 output columns and one
-// of `parts` equal K ranges: it stages the range's x_hat (rows x range fp32,
-// at most 64 KB, sized at launch) in LDS, then each wave walks every fourth
-// 64-wide K block of the range with two to four blocks in flight; in a block lane l
-// holds column l % 32 of each of the 4 column blocks and the 32 codes of K
-// half l / 32 (one 16-byte load each: the weight codes' operand-block order
-// is exactly this), dequantizes them four K at a time exactly in fp32 (INT4:
-// the E4M3 code times s 2^9; FP4: the E2M1 value times 2^e) and multiplies
-// them with every row's four activations (one LDS broadcast read feeding 16
-// fma).  The two K halves, the four waves and
-// (through the workspace) the K parts are added in a fixed order, so the
-// result is deterministic.
+// activations are a few KB.  The product runs on the bf16 matrix cores with
+// exact products and fp32 accumulation:
+//
+//  * every x_hat value is cut into three bf16 pieces, x_hat = hi + mid + lo
+//    exactly (each piece the leading 8 significant bits of what the previous
+//    ones leave: truncation leaves at most 16, then at most 8 bits), and
+//    every 4-bit weight is exact in bf16 (INT4: the E4M3 code byte m 2^-9,
+//    its fp16 scale applied in fp32 per 64-group; FP4: the E2M1 value times
+//    its power-of-two scale), so each MFMA product is exact;
+//  * a 32 x 32 x 16 MFMA takes 32 A rows: the pieces of up to 8 token rows
+//    fill rows 0-7 (hi), 8-15 (mid), 16-23 (lo) of one operand; up to 16
+//    rows take two operands ([hi | mid], [lo | 0]); the output row of a
+//    token is the sum of its pieces' rows, added once at the end.
+//
+// Two launches: w4a16_split_kernel writes the pieces once, already in the
+// MFMA A-operand order (1 KB per K step of 16 and operand, 64 lanes x 16
+// bytes: K order inside a 64-block is permuted so that lane half h of K step
+// s holds K = 32 h + 8 s + 0..7, the order of the weight codes' 16-byte lane
+// slots), into the workspace; w4a16_kernel then streams the weights.  A
+// workgroup of 8 waves owns CBW 32-column blocks and all of K: wave w takes
+// the 64-blocks kb = w, w + 8, .. and all CBW column blocks of each (the
+// A operands loaded once serve CBW MFMA chains), two blocks ahead in
+// registers; the eight waves' partial sums are added in wave order through
+// LDS, so the result is deterministic.
 #include <algorithm>
 
 #include "svdq_device.h"
+#include "svdq_internal.h"
 #include "svdq_kernels.h"
 
 namespace svdq {
 
 namespace {
-typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+constexpr int XW = 8;        // waves per workgroup of the weight-streaming kernel
+constexpr int XPF = 2;       // 64-blocks in flight per wave
+
+// bf16 bits of piece p (0 hi, 1 mid, 2 lo) of x: x = hi + mid + lo exactly
+// for finite x (fp32 subnormal remainders aside); a non-finite x is carried
+// by hi alone (a NaN keeps a set mantissa bit).
+__device__ __forceinline__ uint32_t piece_bits(float x, int p) {
+  const uint32_t xb = __float_as_uint(x);
+  if ((xb & 0x7F800000u) == 0x7F800000u) return p == 0 ? ((xb >> 16) | ((xb & 0x7FFFFFu) ? 0x40u : 0u)) : 0u;
+  const uint32_t hi = xb & 0xFFFF0000u;
+  if (p == 0) return hi >> 16;
+  const float r1 = x - __uint_as_float(hi);                 // exact: x's low 16 significand bits
+  const uint32_t mid = __float_as_uint(r1) & 0xFFFF0000u;
+  if (p == 1) return mid >> 16;
+  return __float_as_uint(r1 - __uint_as_float(mid)) >> 16;  // exact and at most 8 significant bits
+}
 }  // namespace
 
-constexpr int W_CB = 4;        // 32-column blocks per workgroup (each lane holds one column of each)
-
-template <int FMT, int MB>
-__global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t* __restrict__ X, int M, int K, int N,
-                                                    const float* __restrict__ inv_lam,
-                                                    const uint8_t* __restrict__ wcodes, const void* __restrict__ wscales,
-                                                    const float* __restrict__ bias, void* __restrict__ Y, int out_f32,
-                                                    int parts, float* __restrict__ part_out) {
-  // MB x range fp32 activations; after the K loop the same memory holds the
-  // cross-wave reduction (launch-sized to the larger of the two)
-  extern __shared__ __attribute__((aligned(16))) float xs[];
-  const int part = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = wave_uniform(threadIdx.x >> 6);
-  const int kblocks = K / 64, kbp = kblocks / parts, kb0 = part * kbp;
-  const int range = kbp * 64;                     // K values of this part
-  const int k0 = kb0 * 64;
-  const int ncb = N / 32;                         // 32-column blocks
-
-  // stage x_hat of rows < MB (rows past M are zero) for the part's K range
-  for (int i = threadIdx.x; i < MB * range / 2; i += 256) {
-    const int m = (2 * i) / range, kk = (2 * i) % range;
-    float a = 0.f, b = 0.f;
-    if (m < M) {
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(X + static_cast<long>(m) * K + k0 + kk);
-      a = bf16_lo(v) * inv_lam[k0 + kk];
-      b = bf16_hi(v) * inv_lam[k0 + kk + 1];
+// A-operand slot of (64-block kb, K step s, operand o, lane): 16 bytes, the
+// bf16 pieces of a token row's x_hat at K = 64 kb + 32 (lane / 32) + 8 s + 0..7.
+// Row r = lane % 32 of operand o holds: nop == 1: piece r / 8 of token row
+// r % 8 (r >= 24: zero); nop == 2: o == 0: hi (r < 16) or mid (r >= 16) of
+// token row r % 16, o == 1: lo of token row r (r < 16), zero above.  Token
+// rows >= M are zero.
+__global__ __launch_bounds__(256) void w4a16_split_kernel(const uint16_t* __restrict__ X, int M, int K,
+                                                          const float* __restrict__ inv_lam, int nop,
+                                                          u32x4* __restrict__ A) {
+  const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  const long total = static_cast<long>(K / 64) * 4 * nop * 64;
+  if (idx >= total) return;
+  const int lane = static_cast<int>(idx & 63);
+  const long q = idx >> 6;
+  const int o = static_cast<int>(q % nop), s = static_cast<int>((q / nop) & 3);
+  const long kb = q / (nop * 4);
+  const int r = lane & 31, h = lane >> 5;
+  int p, m;
+  if (nop == 1) {
+    p = r >> 3;
+    m = r & 7;
+  } else {
+    m = r & 15;
+    p = o == 0 ? (r >> 4) : (r < 16 ? 2 : 3);
+  }
+  u32x4 out = u32x4{0u, 0u, 0u, 0u};
+  if (p < 3 && m < M) {
+    const long k0 = kb * 64 + 32 * h + 8 * s;
+    const u32x4 xv = *reinterpret_cast<const u32x4*>(X + static_cast<long>(m) * K + k0);
+    const f32x4 l0 = *reinterpret_cast<const f32x4*>(inv_lam + k0);
+    const f32x4 l1 = *reinterpret_cast<const f32x4*>(inv_lam + k0 + 4);
+    const float lam[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    uint32_t pk[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const float a = bf16_lo(xw[j]) * lam[2 * j];         // x_hat = fp32(x * inv_lambda)
+      const float b = bf16_hi(xw[j]) * lam[2 * j + 1];
+      pk[j] = piece_bits(a, p) | (piece_bits(b, p) << 16);
     }
-    xs[m * range + kk] = a;
-    xs[m * range + kk + 1] = b;
+    out = u32x4{pk[0], pk[1], pk[2], pk[3]};
   }
-  __syncthreads();
+  A[idx] = out;
+}
 
-  const int h = lane >> 5;
-  const long KB = kblocks;
-  // the lane's W_CB columns (blocks past the matrix are clamped to its last
-  // one and not stored)
-  int cbk[W_CB], col[W_CB];
+template <int FMT, int NOP, int CBW>
+__global__ __launch_bounds__(XW * 64) void w4a16_kernel(const u32x4* __restrict__ A, int M, int K, int N,
+                                                        const uint8_t* __restrict__ wcodes,
+                                                        const void* __restrict__ wscales,
+                                                        const float* __restrict__ bias, void* __restrict__ Y,
+                                                        int out_f32) {
+  // the waves' partial sums, [wave][column block][value][lane]
+  constexpr int NV = NOP == 2 ? 8 : 4;       // output values per lane and column block
+  extern __shared__ __attribute__((aligned(16))) float red[];
+  const int lane = threadIdx.x & 63, wave = wave_uniform(threadIdx.x >> 6);
+  const int h = lane >> 5, r = lane & 31;
+  const int KB = K / 64, ncb = N / 32;
+  const int cb0 = static_cast<int>(blockIdx.x) * CBW;
+  // the lane's column of each block (blocks past the matrix are clamped to
+  // its last one and not stored)
+  int cbk[CBW], col[CBW];
 #pragma unroll
-  for (int b = 0; b < W_CB; b++) {
-    cbk[b] = min(static_cast<int>(blockIdx.x) * W_CB + b, ncb - 1);
-    col[b] = cbk[b] * 32 + (lane & 31);
+  for (int c = 0; c < CBW; c++) {
+    cbk[c] = min(cb0 + c, ncb - 1);
+    col[c] = cbk[c] * 32 + r;
   }
-  float acc[MB][W_CB];
+  // which A slots hold anything for this lane (the others read as zero
+  // through an offset past the buffer)
+  bool act[NOP];
 #pragma unroll
-  for (int m = 0; m < MB; m++)
-#pragma unroll
-    for (int b = 0; b < W_CB; b++) acc[m][b] = 0.f;
-  // The wave's blocks kb = kb0 + wave + 4 t, t < nt, per column block one
-  // 16-byte code load and one scale load per lane, requested PF blocks ahead
-  // through buffer resources (offsets past a part's last block lie past the
-  // resource's end and read nothing).
-  constexpr int PF = MB <= 2 ? 4 : 2;       // fewer blocks in flight where the accumulators take the registers
-  const int nt = (kbp - wave + 3) / 4;
+  for (int o = 0; o < NOP; o++) {
+    if constexpr (NOP == 1) act[o] = (r >> 3) < 3 && (r & 7) < M;
+    else act[o] = (r & 15) < M && (o == 0 || r < 16);
+  }
+  const int nt = wave < KB ? (KB - wave + XW - 1) / XW : 0;
+  const uint32_t a_bytes = static_cast<uint32_t>(KB) * 4u * NOP * 1024u;
+  const __amdgpu_buffer_rsrc_t ar =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4*>(A), 0, static_cast<int>(a_bytes), 0x00020000);
+  const uint32_t c_bytes = static_cast<uint32_t>(ncb) * static_cast<uint32_t>(KB) * 1024u;
   const __amdgpu_buffer_rsrc_t cr =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wcodes), 0, static_cast<int>(ncb * KB * 1024), 0x00020000);
-  const uint32_t c_oob = static_cast<uint32_t>(ncb * KB * 1024);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wcodes), 0, static_cast<int>(c_bytes), 0x00020000);
   // scales: INT4 one fp16 per 64-group, FP4 one byte per 32-group: 2 N K / 64 bytes either way
-  const int sbytes = N * static_cast<int>(KB) * 2;
-  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(wscales), 0, sbytes, 0x00020000);
-  u32x4 cq[PF][W_CB];
-  uint32_t sq[PF][W_CB];
+  const uint32_t s_bytes = static_cast<uint32_t>(N) * static_cast<uint32_t>(KB) * 2u;
+  const __amdgpu_buffer_rsrc_t sr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(wscales), 0, static_cast<int>(s_bytes), 0x00020000);
+
+  u32x4 aq[XPF][4 * NOP], wq[XPF][CBW];
+  uint32_t sq[XPF][CBW];
   auto fetch = [&](int t, int slot) __attribute__((always_inline)) {
-    const int kb = kb0 + wave + 4 * t;
+    const int kb = wave + XW * t;
     const bool ok = t < nt;
 #pragma unroll
-    for (int b = 0; b < W_CB; b++) {
-      cq[slot][b] = __builtin_amdgcn_raw_buffer_load_b128(
-          cr, ok ? static_cast<uint32_t>((cbk[b] * KB + kb) * 1024 + lane * 16) : c_oob, 0, 0);
+    for (int c = 0; c < CBW; c++) {
+      wq[slot][c] = __builtin_amdgcn_raw_buffer_load_b128(
+          cr, ok ? (static_cast<uint32_t>(cbk[c]) * KB + kb) * 1024u + lane * 16u : c_bytes, 0, 0);
       if constexpr (FMT == SVDQ_INT4_G64_FP16)
-        sq[slot][b] = __builtin_amdgcn_raw_buffer_load_b16(
-            sr, ok ? static_cast<uint32_t>((static_cast<long>(col[b]) * KB + kb) * 2) : static_cast<uint32_t>(sbytes), 0, 0);
+        sq[slot][c] = __builtin_amdgcn_raw_buffer_load_b16(
+            sr, ok ? (static_cast<uint32_t>(col[c]) * KB + kb) * 2u : s_bytes, 0, 0);
       else
-        sq[slot][b] = __builtin_amdgcn_raw_buffer_load_b8(
-            sr, ok ? static_cast<uint32_t>(fp4_scale_offset(col[b], kb * 64 + 32 * h, K)) : static_cast<uint32_t>(sbytes),
-            0, 0);
+        sq[slot][c] = __builtin_amdgcn_raw_buffer_load_b8(
+            sr, ok ? static_cast<uint32_t>(fp4_scale_offset(col[c], kb * 64 + 32 * h, K)) : s_bytes, 0, 0);
     }
+#pragma unroll
+    for (int so = 0; so < 4 * NOP; so++)
+      aq[slot][so] = __builtin_amdgcn_raw_buffer_load_b128(
+          ar, ok && act[so % NOP] ? (static_cast<uint32_t>(kb) * 4u * NOP + so) * 1024u + lane * 16u : a_bytes, 0, 0);
   };
+
+  f32x16 acc[CBW];
 #pragma unroll
-  for (int d = 0; d < PF; d++) fetch(d, d);
-  for (int t0 = 0; t0 < nt; t0 += PF) {
+  for (int c = 0; c < CBW; c++)
 #pragma unroll
-    for (int d = 0; d < PF; d++) {
+    for (int v = 0; v < 16; v++) acc[c][v] = 0.f;
+
+#pragma unroll
+  for (int d = 0; d < XPF; d++) fetch(d, d);
+  for (int t0 = 0; t0 < nt; t0 += XPF) {
+#pragma unroll
+    for (int d = 0; d < XPF; d++) {
       const int t = t0 + d;
-      u32x4 c[W_CB];
-      float sc[W_CB];
+      u32x4 a[4 * NOP], w[CBW];
+      float sc[CBW];
 #pragma unroll
-      for (int b = 0; b < W_CB; b++) {
-        c[b] = cq[d][b];
+      for (int so = 0; so < 4 * NOP; so++) a[so] = aq[d][so];
+#pragma unroll
+      for (int c = 0; c < CBW; c++) {
+        w[c] = wq[d][c];
         if constexpr (FMT == SVDQ_INT4_G64_FP16)
-          sc[b] = __half2float(__ushort_as_half(static_cast<uint16_t>(sq[d][b]))) * 512.0f;   // s 2^9
+          sc[c] = __half2float(__ushort_as_half(static_cast<uint16_t>(sq[d][c]))) * 512.0f;   // s 2^9
         else
-          sc[b] = __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(sq[d][b] & 0xFFu) - 127);   // 2^e
+          sc[c] = __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(sq[d][c] & 0xFFu) - 127);   // 2^e
       }
-      fetch(t + PF, d);
+      fetch(t + XPF, d);
       if (t < nt) {
-        const int kb = kb0 + wave + 4 * t;
-        const float* xr = xs + (kb - kb0) * 64 + 32 * h;
-        // four K values at a time: the exact fp32 weights of the W_CB
-        // columns, then every row's four activations (one LDS broadcast
-        // read) times them
-#pragma unroll 2
-        for (int j = 0; j < 8; j++) {
-          float w[W_CB][4];
+        // INT4: the 64-group's exact partial products first, then its scale
+        f32x16 P[CBW];
+        if constexpr (FMT == SVDQ_INT4_G64_FP16) {
 #pragma unroll
-          for (int b = 0; b < W_CB; b++) {
-            const uint32_t wd = j < 2 ? c[b].x : j < 4 ? c[b].y : j < 6 ? c[b].z : c[b].w;
+          for (int c = 0; c < CBW; c++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) P[c][v] = 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+#pragma unroll
+          for (int c = 0; c < CBW; c++) {
+            const uint32_t wd = s == 0 ? w[c].x : s == 1 ? w[c].y : s == 2 ? w[c].z : w[c].w;
+            bf16x2 e0, e1, e2, e3;
             if constexpr (FMT == SVDQ_INT4_G64_FP16) {
-              // E4M3 code bytes: word & 0x87878787 (codes 0-3), rotr(word, 4) & 0x87878787 (codes 4-7)
-              const uint32_t q = ((j & 1) ? __builtin_amdgcn_alignbit(wd, wd, 4) : wd) & 0x87878787u;
-              w[b][0] = __builtin_amdgcn_cvt_f32_fp8(q, 0) * sc[b];
-              w[b][1] = __builtin_amdgcn_cvt_f32_fp8(q, 1) * sc[b];
-              w[b][2] = __builtin_amdgcn_cvt_f32_fp8(q, 2) * sc[b];
-              w[b][3] = __builtin_amdgcn_cvt_f32_fp8(q, 3) * sc[b];
+              // E4M3 code bytes: K 8 s + 0..3 in word & 0x87878787, K 8 s + 4..7 in rotr(word, 4) & 0x87878787
+              const uint32_t lo = wd & 0x87878787u;
+              const uint32_t hi = __builtin_amdgcn_alignbit(wd, wd, 4) & 0x87878787u;
+              e0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+              e1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+              e2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+              e3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
             } else {
-              // E2M1 pairs, even K in the low nibble: bytes 2 (j % 2) and 2 (j % 2) + 1
-              const f32x2 p0 = (j & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, 1.0f, 2)
-                                       : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, 1.0f, 0);
-              const f32x2 p1 = (j & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, 1.0f, 3)
-                                       : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, 1.0f, 1);
-              w[b][0] = p0.x * sc[b];
-              w[b][1] = p0.y * sc[b];
-              w[b][2] = p1.x * sc[b];
-              w[b][3] = p1.y * sc[b];
+              // E2M1 pairs, even K in the low nibble: byte b holds K 8 s + 2 b, + 1;
+              // the power-of-two scale is exact in bf16
+              e0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc[c], 0);
+              e1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc[c], 1);
+              e2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc[c], 2);
+              e3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc[c], 3);
+            }
+            const bf16x8 b = bf16x8{e0.x, e0.y, e1.x, e1.y, e2.x, e2.y, e3.x, e3.y};
+#pragma unroll
+            for (int o = 0; o < NOP; o++) {
+              const bf16x8 av = __builtin_bit_cast(bf16x8, a[s * NOP + o]);
+              if constexpr (FMT == SVDQ_INT4_G64_FP16)
+                P[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b, P[c], 0, 0, 0);
+              else
+                acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b, acc[c], 0, 0, 0);
             }
           }
+        }
+        if constexpr (FMT == SVDQ_INT4_G64_FP16) {
 #pragma unroll
-          for (int m = 0; m < MB; m++) {
-            const f32x4 x4 = *reinterpret_cast<const f32x4*>(xr + m * range + 4 * j);
+          for (int c = 0; c < CBW; c++)
 #pragma unroll
-            for (int b = 0; b < W_CB; b++) {
-              acc[m][b] = __builtin_fmaf(x4.x, w[b][0], acc[m][b]);
-              acc[m][b] = __builtin_fmaf(x4.y, w[b][1], acc[m][b]);
-              acc[m][b] = __builtin_fmaf(x4.z, w[b][2], acc[m][b]);
-              acc[m][b] = __builtin_fmaf(x4.w, w[b][3], acc[m][b]);
-            }
-          }
+            for (int v = 0; v < 16; v++) acc[c][v] = __builtin_fmaf(P[c][v], sc[c], acc[c][v]);
         }
       }
     }
   }
-  // K halves (lane l and l + 32), then the waves in order, through LDS
-  __syncthreads();                               // every wave is done with xs
-  float* red = xs;                               // [4][MB][W_CB * 32]
+  // Lane l, value v of an accumulator is A row 8 (v / 4) + 4 (l / 32) + v % 4
+  // of output column l % 32.  Token row of value u: nop == 2: u < 8 is row
+  // 8 (u / 4) + 4 h + u % 4, the sum of values u (hi + lo) and u + 8 (mid);
+  // nop == 1: row 4 h + u, the sum of values u (hi), u + 4 (mid), u + 8 (lo).
 #pragma unroll
-  for (int m = 0; m < MB; m++)
+  for (int c = 0; c < CBW; c++)
 #pragma unroll
-    for (int b = 0; b < W_CB; b++) {
-      const float o = __shfl_xor(acc[m][b], 32);
-      if (h == 0) red[(wave * MB + m) * (W_CB * 32) + b * 32 + lane] = acc[m][b] + o;
+    for (int u = 0; u < NV; u++) {
+      const float y = NOP == 2 ? acc[c][u] + acc[c][u + 8] : (acc[c][u] + acc[c][u + 4]) + acc[c][u + 8];
+      red[((wave * CBW + c) * NV + u) * 64 + lane] = y;
     }
   __syncthreads();
-  for (int i = threadIdx.x; i < MB * W_CB * 32; i += 256) {
-    const int m = i / (W_CB * 32), cc = i % (W_CB * 32);
-    const int cb = static_cast<int>(blockIdx.x) * W_CB + cc / 32;
-    if (m >= M || cb >= ncb) continue;
-    const int st = MB * W_CB * 32;
-    const float v = ((red[m * W_CB * 32 + cc] + red[st + m * W_CB * 32 + cc]) + red[2 * st + m * W_CB * 32 + cc]) +
-                    red[3 * st + m * W_CB * 32 + cc];
-    const long n = static_cast<long>(cb) * 32 + cc % 32;
-    if (parts > 1) {
-      part_out[(static_cast<long>(part) * M + m) * N + n] = v;
-    } else {
-      const float y = v + (bias ? bias[n] : 0.f);
-      if (out_f32) static_cast<float*>(Y)[static_cast<long>(m) * N + n] = y;
-      else static_cast<uint16_t*>(Y)[static_cast<long>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16_bits(y));
-    }
+  for (int i = threadIdx.x; i < CBW * NV * 64; i += XW * 64) {
+    const int c = i / (NV * 64), u = (i / 64) % NV, l = i & 63;
+    const int row = NOP == 2 ? 8 * (u >> 2) + 4 * (l >> 5) + (u & 3) : 4 * (l >> 5) + u;
+    if (row >= M || cb0 + c >= ncb) continue;
+    float v = red[(c * NV + u) * 64 + l];
+#pragma unroll
+    for (int w = 1; w < XW; w++) v += red[((w * CBW + c) * NV + u) * 64 + l];
+    const long n = static_cast<long>(cb0 + c) * 32 + (l & 31);
+    const float y = v + (bias ? bias[n] : 0.f);
+    if (out_f32) static_cast<float*>(Y)[static_cast<long>(row) * N + n] = y;
+    else static_cast<uint16_t*>(Y)[static_cast<long>(row) * N + n] = static_cast<uint16_t>(f32_to_bf16_bits(y));
   }
 }
 
-// Y = round(sum over the parts, in part order, + b).
-__global__ void w4a16_reduce_kernel(const float* __restrict__ part_out, int parts, int M, int N,
-                                    const float* __restrict__ bias, void* __restrict__ Y, int out_f32) {
-  const long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= static_cast<long>(M) * N) return;
-  float v = part_out[i];
-  for (int p = 1; p < parts; p++) v += part_out[static_cast<long>(p) * M * N + i];
-  const float y = v + (bias ? bias[i % N] : 0.f);
-  if (out_f32) static_cast<float*>(Y)[i] = y;
-  else static_cast<uint16_t*>(Y)[i] = static_cast<uint16_t>(f32_to_bf16_bits(y));
-}
+int device_cu_count();
 
 hipError_t launch_w4a16(int fmt, const W4A16Args& a, hipStream_t st) {
-  const int rows = w4a16_rows(a.M), parts = w4a16_ksplit(a.M, a.K, a.N);
-  dim3 grid((a.N / 32 + W_CB - 1) / W_CB, parts), block(256);
-  // the part's activations (at most 64 KB by the choice of parts) or the cross-wave reduction
-  const size_t shmem = std::max(static_cast<size_t>(rows) * (a.K / parts) * 4, static_cast<size_t>(4 * rows * W_CB * 32 * 4));
-#define SVDQ_W(F, MBV)                                                                                                  \
-  hipLaunchKernelGGL((w4a16_kernel<F, MBV>), grid, block, shmem, st, a.X, a.M, a.K, a.N, a.inv_lam, a.wcodes, a.wscales, \
-                     a.bias, a.Y, a.out_f32, parts, a.part)
-#define SVDQ_WF(F)                       \
-  switch (rows) {                        \
-    case 1: SVDQ_W(F, 1); break;         \
-    case 2: SVDQ_W(F, 2); break;         \
-    case 4: SVDQ_W(F, 4); break;         \
-    case 8: SVDQ_W(F, 8); break;         \
-    case 16: SVDQ_W(F, 16); break;       \
-    default: return hipErrorInvalidValue; \
+  const int nop = w4a16_planes(a.M);
+  const long slots = static_cast<long>(a.K / 64) * 4 * nop * 64;
+  hipLaunchKernelGGL(w4a16_split_kernel, dim3(static_cast<unsigned>((slots + 255) / 256)), dim3(256), 0, st, a.X,
+                     a.M, a.K, a.inv_lam, nop, static_cast<u32x4*>(a.pieces));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // column blocks per workgroup: one workgroup per compute unit where the
+  // blocks allow (at most 3 per workgroup: the registers of INT4's per-group
+  // partial products)
+  const int ncb = a.N / 32, cus = device_cu_count();
+  const int cbw = std::min(3, std::max(1, (ncb + cus - 1) / cus));
+  const dim3 grid(static_cast<unsigned>((ncb + cbw - 1) / cbw)), block(XW * 64);
+  const size_t shmem = static_cast<size_t>(XW) * cbw * (nop == 2 ? 8 : 4) * 64 * 4;
+#define SVDQ_W(F, NP, CB)                                                                                             \
+  hipLaunchKernelGGL((w4a16_kernel<F, NP, CB>), grid, block, shmem, st, static_cast<const u32x4*>(a.pieces), a.M, a.K, a.N, a.wcodes, a.wscales, \
+                     a.bias, a.Y, a.out_f32)
+#define SVDQ_WC(F, NP)                  \
+  switch (cbw) {                        \
+    case 1: SVDQ_W(F, NP, 1); break;    \
+    case 2: SVDQ_W(F, NP, 2); break;    \
+    default: SVDQ_W(F, NP, 3); break;   \
   }
+#define SVDQ_WF(F)                      \
+  if (nop == 1) { SVDQ_WC(F, 1) }       \
+  else { SVDQ_WC(F, 2) }
   if (fmt == SVDQ_INT4_G64_FP16) { SVDQ_WF(SVDQ_INT4_G64_FP16) }
   else { SVDQ_WF(SVDQ_FP4_E2M1_G32_E8M0) }
 #undef SVDQ_WF
+#undef SVDQ_WC
 #undef SVDQ_W
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || parts == 1) return e;
-  const long n = static_cast<long>(a.M) * a.N;
-  hipLaunchKernelGGL(w4a16_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, a.part, parts,
-                     a.M, a.N, a.bias, a.Y, a.out_f32);
   return hipGetLastError();
 }
 

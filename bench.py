@@ -74,6 +74,8 @@ def parse():
                          "--profile-only (SQ / GRBM / TCC counters; one directory per pass)")
     ap.add_argument("--no-w4a16", dest="w4a16", action="store_false",
                     help="skip timing the weight-only layer on the modulation projection's shape")
+    ap.add_argument("--w4a16-only", action="store_true",
+                    help="time only the weight-only layer (one JSON line; for profilers)")
     ap.add_argument("--no-norm", dest="norm", action="store_false",
                     help="skip timing the LayerNorm-fused layer against a separate norm pass")
     ap.add_argument("--lora", type=int, default=16,
@@ -211,14 +213,25 @@ def bracket(torch, fn, steps):
     return e0.elapsed_time(e1) / steps, time.perf_counter() - t0
 
 
-def interleaved(torch, variants, rounds):
+GATE_CYCLES = 200_000     # a short busy kernel ahead of every timed call (see interleaved)
+
+
+def interleaved(torch, variants, rounds, gate=False):
     """`rounds` rounds, each calling every variant once in order, each call
     bracketed by events on the current stream; returns the per-call times
-    (ms) of every variant."""
+    (ms) of every variant.  Where a round's GPU work is long the host runs
+    ahead and the events time the launches on the GPU.  For calls of a few
+    microseconds (gate=True) a fixed-length busy kernel (torch.cuda._sleep)
+    runs ahead of each bracket, so the host has enqueued the call's launches
+    before the stream reaches them: the events then time the launches back
+    to back, not the host's launch overhead."""
     evs = {name: [] for name, _ in variants}
+    sleep = getattr(torch.cuda, "_sleep", None) if gate else None
     for k in range(rounds):
         for name, fn in variants:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if sleep is not None:
+                sleep(GATE_CYCLES)
             e0.record()
             fn(k)
             e1.record()
@@ -314,7 +327,7 @@ def time_w4a16(torch, S, WL, to_tensor, steps, warmup, fmts=("int4", "fp4")):
                    ("w4a4", lambda k: S.svdq_linear(layer.desc, blobs[k % ncopy], X, Y, ws4, S.OUT_BF16)),
                    ("bf16", lambda k: torch.matmul(X, Ws[k % nw]))]
             warm(torch, [f for _, f in fns], warmup, 0.3)
-            t = interleaved(torch, fns, steps)
+            t = interleaved(torch, fns, steps, gate=True)
             med = {k: statistics.median(v) * 1e3 for k, v in t.items()}
             res.append({"M": M, "K": K, "N": N, "format": fmt, "us": med["w4a16"],
                         "weight_gbs": wbytes / (med["w4a16"] * 1e-6) / 1e9,
@@ -674,6 +687,11 @@ def main():
 
     if args.summarize_counters:
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1], cfg)
+        return
+
+    if args.w4a16_only:
+        print(json.dumps({"w4a16_modulation": time_w4a16(torch, S, WL, to_tensor, args.steps, args.warmup)}),
+              flush=True)
         return
 
     if args.profile_only:

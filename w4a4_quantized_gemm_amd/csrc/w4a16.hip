@@ -20,16 +20,18 @@
 //    rows take two operands ([hi | mid], [lo | 0]); the output row of a
 //    token is the sum of its pieces' rows, added once at the end.
 //
-// Two launches: w4a16_split_kernel writes the pieces once, already in the
-// MFMA A-operand order (1 KB per K step of 16 and operand, 64 lanes x 16
-// bytes: K order inside a 64-block is permuted so that lane half h of K step
-// s holds K = 32 h + 8 s + 0..7, the order of the weight codes' 16-byte lane
-// slots), into the workspace; w4a16_kernel then streams the weights.  A
-// workgroup of 8 waves owns CBW 32-column blocks and all of K: wave w takes
-// the 64-blocks kb = w, w + 8, .. and all CBW column blocks of each (the
-// A operands loaded once serve CBW MFMA chains), two blocks ahead in
-// registers; the eight waves' partial sums are added in wave order through
-// LDS, so the result is deterministic.
+// Where the pieces of all of x_hat fit in LDS (3 M K bf16 within 144 KB: up
+// to 8 rows at K = 3072) a workgroup computes them itself before its loop:
+// one launch.  Otherwise w4a16_split_kernel writes them once into the
+// workspace, already in the MFMA A-operand order (1 KB per K step of 16 and
+// operand, 64 lanes x 16 bytes), and the workgroups load them from there.
+// Either way the K order inside a 64-block is permuted so that lane half h
+// of K step s holds K = 32 h + 8 s + 0..7, the order of the weight codes'
+// 16-byte lane slots.  A workgroup of 8 waves owns CBW 32-column blocks and
+// all of K: wave w takes the 64-blocks kb = w, w + 8, .. and all CBW column
+// blocks of each (one A operand serves CBW MFMA chains), with up to six
+// blocks of weights in flight; the eight waves' partial sums are added in
+// wave order through LDS, so the result is deterministic.
 #include <algorithm>
 
 #include "svdq_device.h"
@@ -42,7 +44,9 @@ namespace {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int XW = 8;        // waves per workgroup of the weight-streaming kernel
-constexpr int XPF = 2;       // 64-blocks in flight per wave
+constexpr int XPF = 2;       // 64-blocks in flight per wave (A operands from the workspace)
+constexpr int XDEPTH = 6;    // 64-blocks in flight per wave (A operands in LDS)
+constexpr int W_LDS = 147456;  // LDS of the in-LDS form: 3 M K bf16 pieces (M = 8, K = 3072 fit)
 
 // bf16 bits of piece p (0 hi, 1 mid, 2 lo) of x: x = hi + mid + lo exactly
 // for finite x (fp32 subnormal remainders aside); a non-finite x is carried
@@ -104,15 +108,29 @@ __global__ __launch_bounds__(256) void w4a16_split_kernel(const uint16_t* __rest
   A[idx] = out;
 }
 
-template <int FMT, int NOP, int CBW>
-__global__ __launch_bounds__(XW * 64) void w4a16_kernel(const u32x4* __restrict__ A, int M, int K, int N,
+// The weight-streaming kernel.  LDSA: the pieces of all of x_hat sit in
+// LDS (3 M K bf16, [piece][row][K]), computed by the workgroup itself from
+// X before its loop -- one launch, and the only vector-memory loads in the
+// loop are the weights, so DEPTH 64-blocks of them stay in flight per wave
+// (vector loads complete in issue order: A operands loaded next to the
+// weights would make every wait for them a wait for the whole prefetch).
+// Otherwise the A operands come from w4a16_split_kernel's workspace, two
+// blocks ahead together with the weights.
+template <int FMT, int NOP, int CBW, bool LDSA>
+__global__ __launch_bounds__(XW * 64) void w4a16_kernel(const u32x4* __restrict__ A, const uint16_t* __restrict__ X,
+                                                        const float* __restrict__ inv_lam, int M, int K, int N,
                                                         const uint8_t* __restrict__ wcodes,
                                                         const void* __restrict__ wscales,
                                                         const float* __restrict__ bias, void* __restrict__ Y,
                                                         int out_f32) {
-  // the waves' partial sums, [wave][column block][value][lane]
   constexpr int NV = NOP == 2 ? 8 : 4;       // output values per lane and column block
-  extern __shared__ __attribute__((aligned(16))) float red[];
+  constexpr int PF = LDSA ? XDEPTH : XPF;    // 64-blocks in flight per wave
+  constexpr int NA = LDSA ? 1 : 4 * NOP;     // A operands held per prefetch slot
+  // LDSA: the pieces, then (after the loop) the waves' partial sums
+  // [wave][column block][value][lane]; else only the partial sums
+  constexpr int LDS_BYTES = LDSA ? W_LDS : XW * CBW * NV * 64 * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+  float* const red = reinterpret_cast<float*>(lds);
   const int lane = threadIdx.x & 63, wave = wave_uniform(threadIdx.x >> 6);
   const int h = lane >> 5, r = lane & 31;
   const int KB = K / 64, ncb = N / 32;
@@ -125,13 +143,21 @@ __global__ __launch_bounds__(XW * 64) void w4a16_kernel(const u32x4* __restrict_
     cbk[c] = min(cb0 + c, ncb - 1);
     col[c] = cbk[c] * 32 + r;
   }
-  // which A slots hold anything for this lane (the others read as zero
-  // through an offset past the buffer)
+  // the A row of operand o of this lane: piece pc[o] of token row mr[o], or
+  // nothing (act[o] false: zero)
   bool act[NOP];
+  int pc[NOP], mr[NOP];
 #pragma unroll
   for (int o = 0; o < NOP; o++) {
-    if constexpr (NOP == 1) act[o] = (r >> 3) < 3 && (r & 7) < M;
-    else act[o] = (r & 15) < M && (o == 0 || r < 16);
+    if constexpr (NOP == 1) {
+      pc[o] = r >> 3;
+      mr[o] = r & 7;
+      act[o] = pc[o] < 3 && mr[o] < M;
+    } else {
+      pc[o] = o == 0 ? (r >> 4) : 2;
+      mr[o] = r & 15;
+      act[o] = mr[o] < M && (o == 0 || r < 16);
+    }
   }
   const int nt = wave < KB ? (KB - wave + XW - 1) / XW : 0;
   const uint32_t a_bytes = static_cast<uint32_t>(KB) * 4u * NOP * 1024u;
@@ -145,8 +171,8 @@ __global__ __launch_bounds__(XW * 64) void w4a16_kernel(const u32x4* __restrict_
   const __amdgpu_buffer_rsrc_t sr =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(wscales), 0, static_cast<int>(s_bytes), 0x00020000);
 
-  u32x4 aq[XPF][4 * NOP], wq[XPF][CBW];
-  uint32_t sq[XPF][CBW];
+  u32x4 aq[PF][NA], wq[PF][CBW];
+  uint32_t sq[PF][CBW];
   auto fetch = [&](int t, int slot) __attribute__((always_inline)) {
     const int kb = wave + XW * t;
     const bool ok = t < nt;
@@ -161,11 +187,59 @@ __global__ __launch_bounds__(XW * 64) void w4a16_kernel(const u32x4* __restrict_
         sq[slot][c] = __builtin_amdgcn_raw_buffer_load_b8(
             sr, ok ? static_cast<uint32_t>(fp4_scale_offset(col[c], kb * 64 + 32 * h, K)) : s_bytes, 0, 0);
     }
+    if constexpr (!LDSA) {
 #pragma unroll
-    for (int so = 0; so < 4 * NOP; so++)
-      aq[slot][so] = __builtin_amdgcn_raw_buffer_load_b128(
-          ar, ok && act[so % NOP] ? (static_cast<uint32_t>(kb) * 4u * NOP + so) * 1024u + lane * 16u : a_bytes, 0, 0);
+      for (int so = 0; so < 4 * NOP; so++)
+        aq[slot][so] = __builtin_amdgcn_raw_buffer_load_b128(
+            ar, ok && act[so % NOP] ? (static_cast<uint32_t>(kb) * 4u * NOP + so) * 1024u + lane * 16u : a_bytes, 0, 0);
+    }
   };
+
+  if constexpr (LDSA) {
+    // pieces of x_hat into LDS, 8 consecutive K of one row per item: the
+    // first item's loads go out before the weight prefetch (the pieces are
+    // computed while the weights stream in), later items' after it
+    const int kv = K / 8, nvec = M * kv;
+    auto load_item = [&](int v, u32x4& xv, f32x4& l0, f32x4& l1) __attribute__((always_inline)) {
+      const int m = v / kv, k = (v - m * kv) * 8;
+      xv = *reinterpret_cast<const u32x4*>(X + static_cast<long>(m) * K + k);
+      l0 = *reinterpret_cast<const f32x4*>(inv_lam + k);
+      l1 = *reinterpret_cast<const f32x4*>(inv_lam + k + 4);
+    };
+    auto store_item = [&](int v, const u32x4& xv, const f32x4& l0, const f32x4& l1) __attribute__((always_inline)) {
+      const int m = v / kv, k = (v - m * kv) * 8;
+      const float lam[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+      float xh[8];
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        xh[2 * j] = bf16_lo(xw[j]) * lam[2 * j];           // x_hat = fp32(x * inv_lambda)
+        xh[2 * j + 1] = bf16_hi(xw[j]) * lam[2 * j + 1];
+      }
+#pragma unroll
+      for (int p = 0; p < 3; p++) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) pk[j] = piece_bits(xh[2 * j], p) | (piece_bits(xh[2 * j + 1], p) << 16);
+        *reinterpret_cast<u32x4*>(lds + ((static_cast<long>(p) * M + m) * K + k) * 2) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+      }
+    };
+    const int v0 = threadIdx.x;
+    u32x4 xv;
+    f32x4 l0, l1;
+    if (v0 < nvec) load_item(v0, xv, l0, l1);
+#pragma unroll
+    for (int d = 0; d < PF; d++) fetch(d, d);
+    if (v0 < nvec) store_item(v0, xv, l0, l1);
+    for (int v = v0 + XW * 64; v < nvec; v += XW * 64) {
+      load_item(v, xv, l0, l1);
+      store_item(v, xv, l0, l1);
+    }
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int d = 0; d < PF; d++) fetch(d, d);
+  }
 
   f32x16 acc[CBW];
 #pragma unroll
@@ -173,16 +247,16 @@ __global__ __launch_bounds__(XW * 64) void w4a16_kernel(const u32x4* __restrict_
 #pragma unroll
     for (int v = 0; v < 16; v++) acc[c][v] = 0.f;
 
+  for (int t0 = 0; t0 < nt; t0 += PF) {
 #pragma unroll
-  for (int d = 0; d < XPF; d++) fetch(d, d);
-  for (int t0 = 0; t0 < nt; t0 += XPF) {
-#pragma unroll
-    for (int d = 0; d < XPF; d++) {
+    for (int d = 0; d < PF; d++) {
       const int t = t0 + d;
-      u32x4 a[4 * NOP], w[CBW];
+      u32x4 aslot[NA], w[CBW];
       float sc[CBW];
+      if constexpr (!LDSA) {
 #pragma unroll
-      for (int so = 0; so < 4 * NOP; so++) a[so] = aq[d][so];
+        for (int so = 0; so < NA; so++) aslot[so] = aq[d][so];
+      }
 #pragma unroll
       for (int c = 0; c < CBW; c++) {
         w[c] = wq[d][c];
@@ -191,8 +265,19 @@ __global__ __launch_bounds__(XW * 64) void w4a16_kernel(const u32x4* __restrict_
         else
           sc[c] = __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(sq[d][c] & 0xFFu) - 127);   // 2^e
       }
-      fetch(t + XPF, d);
+      fetch(t + PF, d);
       if (t < nt) {
+        const int kb = wave + XW * t;
+        // A operand o of K step s
+        auto a_op = [&](int s, int o) __attribute__((always_inline)) {
+          if constexpr (LDSA) {
+            const long off = ((static_cast<long>(pc[o]) * M + mr[o]) * K + kb * 64 + 32 * h + 8 * s) * 2;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(lds + (act[o] ? off : 0));
+            return act[o] ? v : u32x4{0u, 0u, 0u, 0u};
+          } else {
+            return aslot[s * NOP + o];
+          }
+        };
         // INT4: the 64-group's exact partial products first, then its scale
         f32x16 P[CBW];
         if constexpr (FMT == SVDQ_INT4_G64_FP16) {
@@ -203,6 +288,9 @@ __global__ __launch_bounds__(XW * 64) void w4a16_kernel(const u32x4* __restrict_
         }
 #pragma unroll
         for (int s = 0; s < 4; s++) {
+          bf16x8 av[NOP];
+#pragma unroll
+          for (int o = 0; o < NOP; o++) av[o] = __builtin_bit_cast(bf16x8, a_op(s, o));
 #pragma unroll
           for (int c = 0; c < CBW; c++) {
             const uint32_t wd = s == 0 ? w[c].x : s == 1 ? w[c].y : s == 2 ? w[c].z : w[c].w;
@@ -226,11 +314,10 @@ __global__ __launch_bounds__(XW * 64) void w4a16_kernel(const u32x4* __restrict_
             const bf16x8 b = bf16x8{e0.x, e0.y, e1.x, e1.y, e2.x, e2.y, e3.x, e3.y};
 #pragma unroll
             for (int o = 0; o < NOP; o++) {
-              const bf16x8 av = __builtin_bit_cast(bf16x8, a[s * NOP + o]);
               if constexpr (FMT == SVDQ_INT4_G64_FP16)
-                P[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b, P[c], 0, 0, 0);
+                P[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[o], b, P[c], 0, 0, 0);
               else
-                acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b, acc[c], 0, 0, 0);
+                acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[o], b, acc[c], 0, 0, 0);
             }
           }
         }
@@ -247,6 +334,7 @@ __global__ __launch_bounds__(XW * 64) void w4a16_kernel(const u32x4* __restrict_
   // of output column l % 32.  Token row of value u: nop == 2: u < 8 is row
   // 8 (u / 4) + 4 h + u % 4, the sum of values u (hi + lo) and u + 8 (mid);
   // nop == 1: row 4 h + u, the sum of values u (hi), u + 4 (mid), u + 8 (lo).
+  if constexpr (LDSA) __syncthreads();          // every wave is done with the pieces
 #pragma unroll
   for (int c = 0; c < CBW; c++)
 #pragma unroll
@@ -271,32 +359,41 @@ __global__ __launch_bounds__(XW * 64) void w4a16_kernel(const u32x4* __restrict_
 
 int device_cu_count();
 
+bool w4a16_pieces_in_lds(int M, int K) { return 6L * M * K <= W_LDS; }
+
 hipError_t launch_w4a16(int fmt, const W4A16Args& a, hipStream_t st) {
   const int nop = w4a16_planes(a.M);
-  const long slots = static_cast<long>(a.K / 64) * 4 * nop * 64;
-  hipLaunchKernelGGL(w4a16_split_kernel, dim3(static_cast<unsigned>((slots + 255) / 256)), dim3(256), 0, st, a.X,
-                     a.M, a.K, a.inv_lam, nop, static_cast<u32x4*>(a.pieces));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const bool ldsa = w4a16_pieces_in_lds(a.M, a.K);
+  if (!ldsa) {
+    const long slots = static_cast<long>(a.K / 64) * 4 * nop * 64;
+    hipLaunchKernelGGL(w4a16_split_kernel, dim3(static_cast<unsigned>((slots + 255) / 256)), dim3(256), 0, st, a.X,
+                       a.M, a.K, a.inv_lam, nop, static_cast<u32x4*>(a.pieces));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   // column blocks per workgroup: one workgroup per compute unit where the
   // blocks allow (at most 3 per workgroup: the registers of INT4's per-group
   // partial products)
   const int ncb = a.N / 32, cus = device_cu_count();
   const int cbw = std::min(3, std::max(1, (ncb + cus - 1) / cus));
   const dim3 grid(static_cast<unsigned>((ncb + cbw - 1) / cbw)), block(XW * 64);
-  const size_t shmem = static_cast<size_t>(XW) * cbw * (nop == 2 ? 8 : 4) * 64 * 4;
-#define SVDQ_W(F, NP, CB)                                                                                             \
-  hipLaunchKernelGGL((w4a16_kernel<F, NP, CB>), grid, block, shmem, st, static_cast<const u32x4*>(a.pieces), a.M, a.K, a.N, a.wcodes, a.wscales, \
-                     a.bias, a.Y, a.out_f32)
-#define SVDQ_WC(F, NP)                  \
-  switch (cbw) {                        \
-    case 1: SVDQ_W(F, NP, 1); break;    \
-    case 2: SVDQ_W(F, NP, 2); break;    \
-    default: SVDQ_W(F, NP, 3); break;   \
+#define SVDQ_W(F, NP, CB, L)                                                                                    \
+  hipLaunchKernelGGL((w4a16_kernel<F, NP, CB, L>), grid, block, 0, st, static_cast<const u32x4*>(a.pieces), a.X, \
+                     a.inv_lam, a.M, a.K, a.N, a.wcodes, a.wscales, a.bias, a.Y, a.out_f32)
+#define SVDQ_WC(F, NP, L)                  \
+  switch (cbw) {                           \
+    case 1: SVDQ_W(F, NP, 1, L); break;    \
+    case 2: SVDQ_W(F, NP, 2, L); break;    \
+    default: SVDQ_W(F, NP, 3, L); break;   \
   }
-#define SVDQ_WF(F)                      \
-  if (nop == 1) { SVDQ_WC(F, 1) }       \
-  else { SVDQ_WC(F, 2) }
+#define SVDQ_WF(F)                                \
+  if (nop == 1) {                                 \
+    if (ldsa) { SVDQ_WC(F, 1, true) }             \
+    else { SVDQ_WC(F, 1, false) }                 \
+  } else {                                        \
+    if (ldsa) { SVDQ_WC(F, 2, true) }             \
+    else { SVDQ_WC(F, 2, false) }                 \
+  }
   if (fmt == SVDQ_INT4_G64_FP16) { SVDQ_WF(SVDQ_INT4_G64_FP16) }
   else { SVDQ_WF(SVDQ_FP4_E2M1_G32_E8M0) }
 #undef SVDQ_WF

@@ -74,6 +74,9 @@ def parse():
                          "--profile-only (SQ / GRBM / TCC counters; one directory per pass)")
     ap.add_argument("--no-w4a16", dest="w4a16", action="store_false",
                     help="skip timing the weight-only layer on the modulation projection's shape")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="write profiles/<kind>_<workload>_kernel_trace.txt from a rocprofv3 --kernel-trace "
+                         "--stats run of --profile-only (or of --w4a16-only with --workload w4a16)")
     ap.add_argument("--w4a16-only", action="store_true",
                     help="time only the weight-only layer (one JSON line; for profilers)")
     ap.add_argument("--no-norm", dest="norm", action="store_false",
@@ -491,6 +494,47 @@ def summarize_counters(fetch_dir, write_dir, cfg):
     print(json.dumps(out))
 
 
+def summarize_trace(trace_dir, name):
+    """Per-kernel call count and average / min / max duration from a
+    rocprofv3 --kernel-trace --stats run (its kernel_stats CSV), written as
+    text next to the command that produced it."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    rows = list(csv.DictReader(open(files[0])))
+    w4 = name == "w4a16"
+    run = ("python3 bench.py --w4a16-only --steps 50 --warmup 10" if w4 else
+           f"python3 bench.py --profile-only --steps 50 --warmup 10 --workload {name}")
+    lines = [f"rocprofv3 kernel-trace summary, workload {name}", "",
+             "command (from the repository root, on one MI355X):",
+             f"  rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/kt_{name} -o run -- \\",
+             f"      {run}",
+             f"  python3 bench.py --summarize-trace gpurun_out/kt_{name} --workload {name}", ""]
+    if w4:
+        lines += ["The run prepares a 3072 x 18432 rank-0 layer per format (INT4, FP4) and times the",
+                  "weight-only layer at 1 and 16 rows against torch's bf16 matmul (the Cijk_* kernels) and",
+                  "the W4A4 layer at the same rows (act_kernel + gemm kernels), interleaved; warm-up runs",
+                  "for at least 0.3 s, so the call counts are large.  spin_kernel is the fixed busy kernel",
+                  "ahead of each timed call.  Durations in microseconds."]
+    else:
+        lines += ["The run prepares the layer once (dgemm/residual/wquant/...: offline weight preparation),",
+                  "then times fused layer calls (act_kernel with quantization and down-projection, then the",
+                  "GEMM with the slab), unfused calls (quantize-only and down-only activation passes, the",
+                  "GEMM without the slab, up_kernel) and split calls (quantize_act + gemm), interleaved, so",
+                  "the fused path's kernels appear twice as often.  Durations in microseconds."]
+    lines += ["", f"{'kernel':92s} {'calls':>6} {'avg':>9} {'min':>9} {'max':>9}"]
+    for r in rows:
+        lines.append(f"{r['Name'][:92]:92s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.1f} "
+                     f"{float(r['MinNs']) / 1e3:9.1f} {float(r['MaxNs']) / 1e3:9.1f}")
+    kind = "w4a16" if w4 else "layer"
+    path = os.path.join(ROOT, "profiles", f"{kind}_{name}_kernel_trace.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+
+
 UTIL_PASSES = (
     "GRBM_GUI_ACTIVE SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_INSTS_VALU "
     "SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT",
@@ -669,6 +713,9 @@ def main():
                                    "sharding is a design note, not built (use --gpus 1)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.workload)
+        return
     import torch
     import w4a4_quantized_gemm_amd as S
     import workloads as WL

@@ -77,6 +77,10 @@ def parse():
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="write profiles/<kind>_<workload>_kernel_trace.txt from a rocprofv3 --kernel-trace "
                          "--stats run of --profile-only (or of --w4a16-only with --workload w4a16)")
+    ap.add_argument("--norm-only", action="store_true",
+                    help="time only the LayerNorm-fused layer against the separate norm (one JSON line; for profilers)")
+    ap.add_argument("--trace-kind", default="layer", choices=("layer", "w4a16", "norm"),
+                    help="with --summarize-trace: which run the trace is of")
     ap.add_argument("--w4a16-only", action="store_true",
                     help="time only the weight-only layer (one JSON line; for profilers)")
     ap.add_argument("--no-norm", dest="norm", action="store_false",
@@ -494,7 +498,7 @@ def summarize_counters(fetch_dir, write_dir, cfg):
     print(json.dumps(out))
 
 
-def summarize_trace(trace_dir, name):
+def summarize_trace(trace_dir, name, kind):
     """Per-kernel call count and average / min / max duration from a
     rocprofv3 --kernel-trace --stats run (its kernel_stats CSV), written as
     text next to the command that produced it."""
@@ -504,15 +508,23 @@ def summarize_trace(trace_dir, name):
     if not files:
         raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
     rows = list(csv.DictReader(open(files[0])))
-    w4 = name == "w4a16"
-    run = ("python3 bench.py --w4a16-only --steps 50 --warmup 10" if w4 else
-           f"python3 bench.py --profile-only --steps 50 --warmup 10 --workload {name}")
+    w4 = kind == "w4a16"
+    run = {"w4a16": "python3 bench.py --w4a16-only --steps 50 --warmup 10",
+           "norm": f"python3 bench.py --norm-only --steps 50 --warmup 10 --workload {name}",
+           "layer": f"python3 bench.py --profile-only --steps 50 --warmup 10 --workload {name}"}[kind]
+    tag = "w4a16" if w4 else name
     lines = [f"rocprofv3 kernel-trace summary, workload {name}", "",
              "command (from the repository root, on one MI355X):",
-             f"  rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/kt_{name} -o run -- \\",
+             f"  rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/kt_{kind}_{tag} -o run -- \\",
              f"      {run}",
-             f"  python3 bench.py --summarize-trace gpurun_out/kt_{name} --workload {name}", ""]
-    if w4:
+             f"  python3 bench.py --summarize-trace gpurun_out/kt_{kind}_{tag} --trace-kind {kind} --workload {name}", ""]
+    if kind == "norm":
+        lines += ["The run prepares the layer and times the layer on a LayerNorm's input, interleaved:",
+                  "svdq_linear_ln (norm_stats_kernel, then act_kernel with the norm folded in, then the GEMM)",
+                  "against torch's layer_norm writing the normalized bf16 activations followed by",
+                  "svdq_linear (act_kernel + GEMM); warm-up runs for at least 0.3 s.  Durations in",
+                  "microseconds."]
+    elif w4:
         lines += ["The run prepares a 3072 x 18432 rank-0 layer per format (INT4, FP4) and times the",
                   "weight-only layer at 1 and 16 rows against torch's bf16 matmul (the Cijk_* kernels) and",
                   "the W4A4 layer at the same rows (act_kernel + gemm kernels), interleaved; warm-up runs",
@@ -528,8 +540,7 @@ def summarize_trace(trace_dir, name):
     for r in rows:
         lines.append(f"{r['Name'][:92]:92s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.1f} "
                      f"{float(r['MinNs']) / 1e3:9.1f} {float(r['MaxNs']) / 1e3:9.1f}")
-    kind = "w4a16" if w4 else "layer"
-    path = os.path.join(ROOT, "profiles", f"{kind}_{name}_kernel_trace.txt")
+    path = os.path.join(ROOT, "profiles", f"{kind}_{tag}_kernel_trace.txt")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(path)
@@ -714,7 +725,7 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.workload)
+        summarize_trace(args.summarize_trace, args.workload, args.trace_kind)
         return
     import torch
     import w4a4_quantized_gemm_amd as S
@@ -734,6 +745,13 @@ def main():
 
     if args.summarize_counters:
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1], cfg)
+        return
+
+    if args.norm_only:
+        rig = Rig(cfg, torch, S, WL, to_tensor)
+        f_ms, s_ms = time_norm(torch, S, rig, args.steps, args.warmup)
+        print(json.dumps({"workload": cfg.name, "us_norm_fused": f_ms * 1e3, "us_norm_separate": s_ms * 1e3}),
+              flush=True)
         return
 
     if args.w4a16_only:

@@ -9,8 +9,7 @@
 //                                              (eq. (2) per group)
 //   Y[i, n]    = round(acc[i, n] + b[n])
 //
-// Group 64, fp16 scales: the packed codes of each K stage are moved to LDS
-// as they are stored.  An INT4 code is kept as the E4M3 bits of q * 2^-9
+// Group 64, fp16 scales.  An INT4 code is kept as the E4M3 bits of q * 2^-9
 // (sign-magnitude: |q| <= 7 is a subnormal), two per byte, so that on the
 // way from LDS to the registers one AND (codes 0-3 of a word) or one rotate
 // and AND (codes 4-7) per 4 codes yields the 8-bit float operands.  One
@@ -25,15 +24,16 @@
 // overlap.
 //
 // Tiling: 4 waves per workgroup in a 2 x 2 grid, 128 x 128 per workgroup,
-// 32 x 32 MFMA tiles.  A K stage is 128 wide (two 64-wide MFMA steps); the
-// LDS holds two stages, the global loads of a stage are issued three stages
-// before its MFMAs (two register sets), and each stage has one barrier.  In
-// every MFMA, lane l owns row (column) l % 32 and the 16-byte half l / 32 of
-// the 64-wide K step, for A and B alike, so both operands enumerate K in the
-// same order.  Workgroups are mapped to tiles so that the workgroups
-// resident on one XCD (the hardware deals them round-robin to the 8 XCDs)
-// cover a compact block of tiles that shares rows of A and columns of B in
-// that XCD's L2.
+// 32 x 32 MFMA tiles.  A K stage is 128 wide (two 64-wide MFMA steps): its
+// raw codes (the 1 KB operand blocks as they lie in HBM) and scales are
+// copied global -> LDS directly (global_load_lds, 16 bytes per lane) into a
+// ring of 4 stage buffers, 3 stages ahead of the MFMAs, and widened as each
+// wave reads its operands; each stage has one barrier.  In every MFMA, lane
+// l owns row (column) l % 32 and the 16-byte half l / 32 of the 64-wide K
+// step, for A and B alike, so both operands enumerate K in the same order.
+// Workgroups are mapped to tiles so that the workgroups resident on one XCD
+// (the hardware deals them round-robin to the 8 XCDs) share rows of A or
+// columns of B in that XCD's L2.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>

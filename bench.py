@@ -79,6 +79,8 @@ def parse():
                          "--stats run of --profile-only (or of --w4a16-only with --workload w4a16)")
     ap.add_argument("--norm-only", action="store_true",
                     help="time only the LayerNorm-fused layer against the separate norm (one JSON line; for profilers)")
+    ap.add_argument("--summarize-sweep", metavar="SWEEP_STDERR",
+                    help="write profiles/sweep_c5_int4.txt from the stderr of a --sweep run")
     ap.add_argument("--trace-kind", default="layer", choices=("layer", "w4a16", "norm"),
                     help="with --summarize-trace: which run the trace is of")
     ap.add_argument("--w4a16-only", action="store_true",
@@ -546,6 +548,30 @@ def summarize_trace(trace_dir, name, kind):
     print(path)
 
 
+SWEEP_CMD = ('python3 bench.py --steps 50 --warmup 5 --sweep --no-w4a16 --no-norm --no-peaks --extra "" '
+             '--lora 0 --no-cpu-baseline --rank0 "" > gpurun_out/bench_sweep.json 2> gpurun_out/bench_sweep.err')
+
+
+def summarize_sweep(path):
+    """The shape sweep's per-point records (one JSON line each on stderr) as
+    a table."""
+    rows = [json.loads(l) for l in open(path) if l.strip().startswith("{")]
+    lines = ["INT4 shape sweep: M x K -> N at ranks 16/32/64 (c2 generators), fused layer against the",
+             "unfused one, times in microseconds (median of per-call HIP events, interleaved rounds).", "",
+             "command (from the repository root, on one MI355X):", f"  {SWEEP_CMD}",
+             "  python3 bench.py --summarize-sweep gpurun_out/bench_sweep.err", "",
+             f"{'workload':30s} {'fused':>8} {'unfused':>8} {'speedup':>8} {'eff TOPS':>9} {'G us':>8} "
+             f"{'G frac':>7} {'Q us':>7}"]
+    for d in rows:
+        lines.append(f"{d['workload']:30s} {d['us_per_layer']['median']:8.1f} {d['us_per_layer_unfused']['median']:8.1f} "
+                     f"{d['fused_vs_unfused_speedup']:8.3f} {d['effective_tops']:9.0f} {d['gemm_us']['median']:8.1f} "
+                     f"{d['gemm_frac_peak']:7.3f} {d['quant_us']['median']:7.1f}")
+    out = os.path.join(ROOT, "profiles", "sweep_c5_int4.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
 UTIL_PASSES = (
     "GRBM_GUI_ACTIVE SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_INSTS_VALU "
     "SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT",
@@ -726,6 +752,9 @@ def main():
         sys.exit(2)
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.workload, args.trace_kind)
+        return
+    if args.summarize_sweep:
+        summarize_sweep(args.summarize_sweep)
         return
     import torch
     import w4a4_quantized_gemm_amd as S

@@ -62,8 +62,9 @@ constexpr int F_SC = F_NBUF * F_STAGE;            // scale ring: per stage 1 KB 
 constexpr int F_EPI = F_SC + F_NBUF * 2048;       // epilogue staging: 4 KB per wave
 constexpr int F_NBIAS = 2;                        // tile bias buffers (1 KB each, by turn parity)
 constexpr int F_BIAS = F_EPI + 4 * 4096;
-constexpr int F_LDS = F_BIAS + F_NBIAS * 1024;    // 157696 bytes
-constexpr int F_NCOPY = 11;                       // copies per wave per stage
+constexpr int F_DUMMY = F_BIAS + F_NBIAS * 1024;  // 1 KB landing place of wave 3's balancing copy
+constexpr int F_LDS = F_DUMMY + 1024;             // 158720 bytes
+constexpr int F_NCOPY = 9;                        // copies per wave per stage
 
 // Four accumulator values (held in AGPRs) read out where the epilogue uses
 // them: the volatile asm keeps the reads in program order, so the compiler
@@ -135,12 +136,14 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
   // when S >= 3, so the copies never run more than one tile ahead); past the
   // last tile the last stage is repeated (never consumed).  For a stage,
   // wave w copies the two 1 KB blocks (both MFMA steps) of activation row
-  // blocks 2w, 2w + 1 and of weight row blocks 2w, 2w + 1 (8 copies), the
-  // scales of the same row blocks (2 copies of 4 bytes per lane: lanes 0-31
-  // row block 2w, lanes 32-63 row block 2w + 1) and a quarter of the tile's
-  // bias (1 copy; every stage copies the same bytes into the tile's bias
-  // buffer).  Row blocks past the matrix repeat its last block (their
-  // outputs are never stored).
+  // blocks 2w, 2w + 1 and of weight row blocks 2w, 2w + 1 (8 copies) and one
+  // more kilobyte, 16 bytes per lane: wave 0 the stage's activation scales
+  // (lane l: 16 bytes of the 128-byte block of row block l / 8), wave 1 the
+  // weight scales the same way, wave 2 the tile's bias (every stage copies
+  // the same bytes into the tile's bias buffer) and wave 3 the bias again
+  // into a dummy area, so that every wave issues the same 9 copies and the
+  // waits below count alike.  Row blocks past the matrix repeat its last
+  // block (their outputs are never stored).
   //
   // A run of consecutive stages whose copies come from one tile and one kind
   // (low-rank or FP4) shares a descriptor of scalar bases; the per-lane
@@ -153,15 +156,13 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
   // the compute side zeroes).
   struct CopyDesc {
     const uint8_t *x[4], *w[4];         // bases of block copies q = 0..3
-    const uint8_t *sx, *sw;             // scale bases (sw minus 1024: its copy has OFF 1024)
-    const uint8_t* b;                   // this wave's quarter of the tile's bias
-    uint32_t bias_lds;                  // its LDS destination
-    uint32_t inc, sinc;                 // per-stage growth of voff / the scale offsets
+    const uint8_t* e;                   // base of the wave's ninth copy (scales or bias)
+    uint32_t e_lds;                     // its LDS destination (waves 2, 3; the scales go to the ring)
+    uint32_t inc, einc;                 // per-stage growth of voff / of the ninth copy's offset
   };
   struct CopyOff {
-    uint32_t v, vsx, vsw;               // per-lane offsets: blocks, activation / weight scales
+    uint32_t v, ve;                     // per-lane offsets: blocks, the ninth copy
   };
-  const uint32_t lane4 = (lane & 31) * 4, upper = lane >> 5;
   // descriptor of a run starting at stage cst of the tile (mb0, nb0) of turn
   // `turn`; rep: the run repeats that stage
   auto make_desc = [&](int mb0, int nb0, int turn, int cst, bool rep, CopyDesc& d, CopyOff& o)
@@ -187,20 +188,36 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
     d.w[2] = wb0 - 2048;
     d.w[3] = wb0 + dk - 3072;
     const int ks = lr ? 0 : cst - RS;             // FP4 stage (low-rank stages copy unused scales of stage 0)
-    d.sx = ascales + static_cast<long>(xa) * KS * 128;
-    d.sw = wscales + static_cast<long>(wa) * KS * 128 - 1024;
-    d.b = biasb + (has_bias ? (min(nb0 * 32 + wave * 64, N - 64) * 4) : 0);
-    d.bias_lds = lds0 + F_BIAS + (turn & 1) * 1024 + wave * 256;
     d.inc = rep ? 0u : 2048u;
-    d.sinc = (rep || lr) ? 0u : 128u;
     o.v = lane16 + static_cast<uint32_t>(lr ? cst : ks) * 2048u;
-    o.vsx = lane4 + upper * static_cast<uint32_t>((xb - xa) * KS * 128) + static_cast<uint32_t>(ks) * 128u;
-    o.vsw = lane4 + upper * static_cast<uint32_t>((wb - wa) * KS * 128) + static_cast<uint32_t>(ks) * 128u;
+    if (wave < 2) {
+      // scales: lane l takes 16 bytes (l % 8) of row block (l / 8) of the
+      // tile, relative to the tile's first (clamped) row block
+      const int first = wave == 0 ? min(mb0, last_ablk) : min(nb0, last_bblk);
+      const int blk = wave == 0 ? min(mb0 + (lane >> 3), last_ablk) : min(nb0 + (lane >> 3), last_bblk);
+      d.e = (wave == 0 ? ascales : wscales) + static_cast<long>(first) * KS * 128;
+      d.e_lds = 0u;
+      d.einc = (rep || lr) ? 0u : 128u;
+      o.ve = static_cast<uint32_t>((blk - first) * KS * 128 + ks * 128 + (lane & 7) * 16);
+    } else {
+      // bias: lane l takes columns 4 l .. 4 l + 3 of the tile (clamped to the
+      // matrix); without a bias 1 KB of the activation codes (never used)
+      d.e = biasb;
+      d.e_lds = lds0 + (wave == 2 ? F_BIAS + (turn & 1) * 1024 : F_DUMMY);
+      d.einc = 0u;
+      o.ve = has_bias ? static_cast<uint32_t>(min(nb0 * 32 + 4 * lane, N - 4) * 4) : lane16;
+    }
   };
   // copy items of a stage into ring buffer rc, one group per MFMA slot t
-  // (items 0..4 in slots 0..4 of the first step, items 5..11 in slots
-  // 8..14 of the second): each m0 write sits one slot before the copies
-  // that read it (the MFMA between them is the wait state the copy needs)
+  // (items 0..4 in slots 0..4 of the first step, items 5..9 in slots 8..12
+  // of the second): each m0 write sits one slot before the copies that read
+  // it (the MFMA between them is the wait state the copy needs)
+  // LDS destination of the ninth copy: the ring's scale area (waves 0, 1) or
+  // the descriptor's (waves 2, 3); uniform, so it stays scalar
+  auto ninth_lds = [&](const CopyDesc& d, uint32_t rc) __attribute__((always_inline)) {
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_readfirstlane(wave < 2 ? lds0 + F_SC + rc * 2048 + wave * 1024 : d.e_lds));
+  };
   auto copy_slot = [&](const CopyDesc& d, const CopyOff& o, uint32_t rc, int t) __attribute__((always_inline)) {
     // one copy per slot: bursts of copies stall the issuing wave
     switch (t) {
@@ -212,10 +229,8 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
       case 5: dma16<0>(d.w[0], o.v); break;
       case 6: dma16<1024>(d.w[1], o.v); break;
       case 7: dma16<2048>(d.w[2], o.v); break;
-      case 8: dma16<3072>(d.w[3], o.v); set_m0(lds0 + F_SC + rc * 2048 + wave * 256); break;
-      case 9: dma4<0>(d.sx, o.vsx); break;
-      case 10: dma4<1024>(d.sw, o.vsw); set_m0(d.bias_lds); break;
-      case 11: dma4<0>(d.b, lane * 4u); break;
+      case 8: dma16<3072>(d.w[3], o.v); set_m0(ninth_lds(d, rc)); break;
+      case 9: dma16<0>(d.e, o.ve); break;
       default: break;
     }
   };
@@ -225,10 +240,8 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
     dma16<0>(d.x[0], o.v); dma16<1024>(d.x[1], o.v); dma16<2048>(d.x[2], o.v); dma16<3072>(d.x[3], o.v);
     set_m0_nop(lds0 + rc * F_STAGE + F_WB + wave * 4096);
     dma16<0>(d.w[0], o.v); dma16<1024>(d.w[1], o.v); dma16<2048>(d.w[2], o.v); dma16<3072>(d.w[3], o.v);
-    set_m0_nop(lds0 + F_SC + rc * 2048 + wave * 256);
-    dma4<0>(d.sx, o.vsx); dma4<1024>(d.sw, o.vsw);
-    set_m0_nop(d.bias_lds);
-    dma4<0>(d.b, lane * 4u);
+    set_m0_nop(ninth_lds(d, rc));
+    dma16<0>(d.e, o.ve);
   };
 
   // ---- compute side.  Operands of one MFMA step: weight blocks i = 0..3
@@ -283,18 +296,18 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
   //          R1 and the 4 activation copies of stage G + 3 into ring buffer
   //          (G + 3) % 4 -- stage G - 1's, released by the previous barrier;
   //  wait + barrier: this wave's copies of stage G + 1 are complete once at
-  //          most the F_NCOPY copies of stage G + 2 and the 4 of stage G + 3
-  //          are outstanding (in the first stages of a tile the previous
+  //          most the F_NCOPY (9) copies of stage G + 2 and the 4 of stage
+  //          G + 3 are outstanding (in the first stages of a tile the previous
   //          tile's epilogue stores come after those copies, so the same
   //          count also waits for the older stores); lgkmcnt(0) completes
   //          this wave's reads of stage G; the barrier then publishes stage
   //          G + 1 and releases stage G's buffer;
   //  step 1: 16 MFMAs on R1 with the reads of stage G + 1 step 0 into R0 and
-  //          of its scales, and the other 7 copies of stage G + 3 (weights,
-  //          scales, bias) in its second half, after the reads.  Spreading
+  //          of its scales, and the other 5 copies of stage G + 3 (weights
+  //          and the ninth copy) in its second half, after the reads.  Spreading
   //          the copies over both steps keeps fewer of them in flight behind
   //          the MFMAs at once.
-  static_assert(F_NCOPY == 11, "the wait counts below assume 11 copies per wave per stage");
+  static_assert(F_NCOPY == 9, "the wait counts below assume 9 copies per wave per stage");
   // (sx, sw): this stage's scales; (nsx, nsw): where the next stage's go
   auto stage = [&](Ops& R0, const uint32_t (&sx)[4], const uint32_t (&sw)[4], uint32_t (&nsx)[4],
                    uint32_t (&nsw)[4], long G, const CopyDesc& d, CopyOff& o, uint32_t wmask, auto LR)
@@ -312,7 +325,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
       if (t <= 4) copy_slot(d, o, rc, t);
       __builtin_amdgcn_sched_barrier(0);
     }
-    SVDQ_VM_BARRIER(15);
+    SVDQ_VM_BARRIER(13);
     __builtin_amdgcn_sched_barrier(0);
     const uint32_t nx = rx + rn * F_STAGE, nw = rw + rn * F_STAGE;
     const uint32_t nsxa = rsx + rn * 2048, nswa = rsw + rn * 2048;
@@ -325,8 +338,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
       __builtin_amdgcn_sched_barrier(0);
     }
     o.v += d.inc;
-    o.vsx += d.sinc;
-    o.vsw += d.sinc;
+    o.ve += d.einc;
   };
   // n consecutive stages of one kind and descriptor (the next stage's scales
   // are read into (nsx, nsw) and moved into place after each stage)
@@ -483,7 +495,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
     copy_all(d, o, p);
   }
   // stage 0 complete: the copies of stages 1 and 2 may stay in flight
-  SVDQ_VM_BARRIER(22);
+  SVDQ_VM_BARRIER(18);
   Ops oa;
   uint32_t sx[4], sw[4];
 #pragma unroll

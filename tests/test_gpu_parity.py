@@ -214,6 +214,10 @@ SMALL = [
     (64, 1024, 128, 32, True, O.INT4),
     (257, 640, 576, 64, False, O.FP4),
     (16400, 256, 64, 16, False, O.FP4),    # M above the K-split limit: one part per row block
+    # 17 x 16 = 272 FP4 output tiles on 256 compute units: the last 16 tiles
+    # run as 32 column-half items (straight-line and general schedules)
+    (4352, 384, 4096, 16, True, O.FP4),
+    (4352, 256, 4096, 16, False, O.FP4),
 ]
 
 

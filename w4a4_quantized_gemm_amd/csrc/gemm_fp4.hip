@@ -18,6 +18,9 @@
 // Shape and data movement (chosen by measurement on MI355X):
 //  - persistent: one workgroup of 4 waves per CU (the LDS ring takes the CU)
 //    walks its 256 x 256 output tiles in sequence, XCD-aware tile order;
+//    a last round of tiles that would fill at most half of the CUs runs as
+//    twice as many column-half items instead (same copies, half the MFMAs
+//    and half the epilogue per item);
 //  - one wave per SIMD, 2 x 2 waves, each owning 128 x 128 outputs (4 x 4
 //    MFMA tiles, 256 fp32 accumulators): every operand kilobyte a wave reads
 //    from LDS feeds 4 MFMAs, which keeps the LDS read traffic at 2 KB per
@@ -112,7 +115,25 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
   const int ntiles = tiles_m * tiles_n;
   const int xmap = g.xcd_map;
   const int grid = static_cast<int>(gridDim.x), wg = static_cast<int>(blockIdx.x);
-  const int my_tiles = (ntiles - wg + grid - 1) / grid;   // >= 1: the grid never exceeds the tile count
+  // Tail split: when the last round of tiles (ntiles mod grid of them) fills
+  // at most half of the grid, each of its tiles becomes two column-half
+  // items, taken by two workgroups of the XCD whose L2 holds the tile's
+  // operands (tile_of puts tile b on XCD b % 8, the XCD of workgroup b), so
+  // that the last round takes about half a tile's time instead of a whole
+  // one.  A workgroup's items: full tiles wg + seq * grid for seq < nfull,
+  // then possibly one half item, whose waves compute weight blocks 2 h and
+  // 2 h + 1 of their four (columns 64 h .. 64 h + 63 of each 128-column
+  // half); its copies are the whole tile's, as for any tile.
+  const int rounds = ntiles / grid, rtail = ntiles - rounds * grid;
+  const bool split = (grid & 7) == 0 && rtail > 0 && 2 * rtail <= grid && S >= F_AHEAD;
+  const int xcd = wg & 7, kx = wg >> 3;
+  const int tails_x = xcd < rtail ? (rtail - 1 - xcd) / 8 + 1 : 0;   // tail tiles on this XCD
+  const bool half_item = split && kx < 2 * tails_x;
+  const int nfull = split ? rounds : (ntiles - wg + grid - 1) / grid;  // >= 1: the grid never exceeds the tile count
+  const int my_tiles = nfull + (half_item ? 1 : 0);                      // items
+  const int hsel = kx & 1;                                               // the half item's column half
+  const uint32_t half_woff = static_cast<uint32_t>(hsel) * 4096u;       // its weight blocks in the stage
+  const uint32_t half_soff = static_cast<uint32_t>(hsel) * 256u;        // and their scales
   const int last_ablk = (M + 31) / 32 - 1, last_bblk = N / 32 - 1;
 
   const int lane = threadIdx.x & 63;
@@ -122,7 +143,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
 
   auto tile_blocks = [&](int seq, int& mb0, int& nb0) __attribute__((always_inline)) {
     int tm, tn;
-    tile_of(wg + seq * grid, tiles_m, tiles_n, xmap, tm, tn);
+    tile_of(seq < nfull ? wg + seq * grid : rounds * grid + xcd + 8 * (kx >> 1), tiles_m, tiles_n, xmap, tm, tn);
     // uniform by construction; made scalar so that addresses and buffer
     // resources built from them stay in SGPRs
     mb0 = wave_uniform(tm * (F_TILE / 32));
@@ -309,32 +330,37 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
   //          the MFMAs at once.
   static_assert(F_NCOPY == 9, "the wait counts below assume 9 copies per wave per stage");
   // (sx, sw): this stage's scales; (nsx, nsw): where the next stage's go
+  // HALF (a half item): 8 MFMAs per step on weight blocks 0, 1 (read from
+  // blocks 2 h, 2 h + 1), 6 operand pieces, the same copies and waits.
   auto stage = [&](Ops& R0, const uint32_t (&sx)[4], const uint32_t (&sw)[4], uint32_t (&nsx)[4],
-                   uint32_t (&nsw)[4], long G, const CopyDesc& d, CopyOff& o, uint32_t wmask, auto LR)
+                   uint32_t (&nsw)[4], long G, const CopyDesc& d, CopyOff& o, uint32_t wmask, auto LR, auto HALF)
       __attribute__((always_inline)) {
+    constexpr bool H = decltype(HALF)::value;
+    constexpr int NT = H ? 8 : 16, NP = H ? 6 : 8;   // MFMAs, operand pieces per step
+    const uint32_t hw = H ? half_woff : 0u, hs = H ? half_soff : 0u;
     const uint32_t rb = static_cast<uint32_t>(G & (F_NBUF - 1));
     const uint32_t rn = static_cast<uint32_t>((G + 1) & (F_NBUF - 1));
     const uint32_t rc = static_cast<uint32_t>((G + F_AHEAD) & (F_NBUF - 1));
-    const uint32_t ax = rx + rb * F_STAGE, aw = rw + rb * F_STAGE;
+    const uint32_t ax = rx + rb * F_STAGE, aw = rw + rb * F_STAGE + hw;
     Ops R1;
 #pragma unroll
-    for (int t = 0; t < 16; t++) {
+    for (int t = 0; t < NT; t++) {
       mfma(R0, sx, sw, t, std::integral_constant<int, 0>{}, LR, wmask);
       __builtin_amdgcn_sched_barrier(0);
-      if (t < 8) read_piece(R1, ax, aw, 1, t);
+      if (t < NP) read_piece(R1, ax, aw, 1, t);
       if (t <= 4) copy_slot(d, o, rc, t);
       __builtin_amdgcn_sched_barrier(0);
     }
     SVDQ_VM_BARRIER(13);
     __builtin_amdgcn_sched_barrier(0);
-    const uint32_t nx = rx + rn * F_STAGE, nw = rw + rn * F_STAGE;
-    const uint32_t nsxa = rsx + rn * 2048, nswa = rsw + rn * 2048;
+    const uint32_t nx = rx + rn * F_STAGE, nw = rw + rn * F_STAGE + hw;
+    const uint32_t nsxa = rsx + rn * 2048, nswa = rsw + rn * 2048 + hs;
 #pragma unroll
-    for (int t = 0; t < 16; t++) {
+    for (int t = 0; t < NT; t++) {
       mfma(R1, sx, sw, t, std::integral_constant<int, 1>{}, LR, wmask);
-      if (t < 8) read_piece(R0, nx, nw, 0, t);
-      if (t < 8) read_scale(nsx, nsw, nsxa, nswa, t);
-      if (t >= 8) copy_slot(d, o, rc, t - 3);
+      if (t < NP) read_piece(R0, nx, nw, 0, t);
+      if (t < NP) read_scale(nsx, nsw, nsxa, nswa, t);
+      if (H ? t >= 3 : t >= 8) copy_slot(d, o, rc, H ? t + 2 : t - 3);
       __builtin_amdgcn_sched_barrier(0);
     }
     o.v += d.inc;
@@ -343,15 +369,15 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
   // n consecutive stages of one kind and descriptor (the next stage's scales
   // are read into (nsx, nsw) and moved into place after each stage)
   auto run = [&](Ops& R0, uint32_t (&sx)[4], uint32_t (&sw)[4], long& G, int n, const CopyDesc& d, CopyOff& o,
-                 uint32_t wmask_last, auto LR) __attribute__((always_inline)) {
+                 uint32_t wmask_last, auto LR, auto HALF) __attribute__((always_inline)) {
 #pragma unroll 1
     for (; n > 0; n--, G++) {
       uint32_t nsx[4], nsw[4];
-      stage(R0, sx, sw, nsx, nsw, G, d, o, n == 1 ? wmask_last : ~0u, LR);
+      stage(R0, sx, sw, nsx, nsw, G, d, o, n == 1 ? wmask_last : ~0u, LR, HALF);
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         sx[q] = nsx[q];
-        sw[q] = nsw[q];
+        if (!decltype(HALF)::value || q < 2) sw[q] = nsw[q];
       }
     }
   };
@@ -360,11 +386,13 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
   // bias buffer seq % 2 with the copies of the tile's stages, the first of
   // which completed at the barrier before the tile's first stage), so the
   // epilogue only rounds: acc[i][j][v] = b[128 wn + 32 i + 8 (v / 4) + 4 lh + v % 4].
-  auto init_acc = [&](int seq) __attribute__((always_inline)) {
+  auto init_acc = [&](int seq, auto HALF) __attribute__((always_inline)) {
+    constexpr int NI = decltype(HALF)::value ? 2 : 4;   // weight blocks computed
     if (has_bias) {
-      const float* bl = reinterpret_cast<const float*>(smem + F_BIAS + (seq & 1) * 1024) + wn * 128 + 4 * (lane >> 5);
+      const float* bl = reinterpret_cast<const float*>(smem + F_BIAS + (seq & 1) * 1024) + wn * 128 + 4 * (lane >> 5) +
+                        (decltype(HALF)::value ? 64 * hsel : 0);
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
+      for (int i = 0; i < NI; i++) {
         f32x4 b4[4];
 #pragma unroll
         for (int gq = 0; gq < 4; gq++) b4[gq] = *reinterpret_cast<const f32x4*>(bl + 32 * i + 8 * gq);
@@ -375,7 +403,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; i++)
+      for (int i = 0; i < NI; i++)
 #pragma unroll
         for (int j = 0; j < 4; j++)
 #pragma unroll
@@ -394,7 +422,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
   // every wave's read-back ahead of those copies).  Rows past M and columns
   // past N get an offset past the buffer resource and are dropped, so every
   // store instruction issues (the waits count them).
-  auto epilogue = [&](int mb0, int nb0, long G) __attribute__((always_inline)) {
+  auto epilogue = [&](int mb0, int nb0, long G, auto HALF) __attribute__((always_inline)) {
     // lane indices recomputed through an opaque move, so that the compiler
     // does not hoist the epilogue's per-lane addresses out of the tile loop
     int lane_e;
@@ -404,7 +432,8 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
     uint8_t* const slot[2] = {smem + F_EPI + wave * 4096,
                               smem + static_cast<uint32_t>(G & (F_NBUF - 1)) * F_STAGE + wave * 4096};
     const long m0 = static_cast<long>(mb0) * 32;
-    const long colw = static_cast<long>(nb0) * 32 + wn * 128;     // the wave's first column
+    // the wave's first column (of a half item: of its column half)
+    const long colw = static_cast<long>(nb0) * 32 + wn * 128 + (decltype(HALF)::value ? 64 * hsel : 0);
     const uint32_t rowb = static_cast<uint32_t>(N * OB);            // output row bytes
     const int valid_rows = static_cast<int>(min(static_cast<long>(M) - m0, static_cast<long>(F_TILE)));
     const uint32_t nrec = static_cast<uint32_t>(valid_rows) * rowb;
@@ -415,7 +444,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
     constexpr int NSL = OUT == SVDQ_OUT_F32 ? 4 : 2;        // column slices of the wave's 128 columns
     constexpr int SLW = 128 / NSL;                          // slice width in columns
     constexpr int NII = SLW / 32;
-    constexpr int NQ = NSL * 4;                             // slices: (column slice, 32-row block)
+    constexpr int NQ = NSL * 4 / (decltype(HALF)::value ? 2 : 1);   // slices: (column slice, 32-row block)
     auto write_slice = [&](int q) __attribute__((always_inline)) {
       const int sl = q >> 2, j = q & 3;
       uint8_t* stg = slot[q & 1];
@@ -505,38 +534,48 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
 
   long G = 0;
   const uint32_t last_mask = (RK & 1) ? 0u : ~0u;    // zero weight operand in the odd half of the last low-rank stage
-#pragma unroll 1
-  for (int seq = 0; seq < my_tiles; seq++) {
+  // one item: a full tile, or (HALF) a half item
+  auto item = [&](int seq, auto HALF) __attribute__((always_inline)) {
     if (seq > 0) {
       mb0 = nmb0;
       nb0 = nnb0;
       tile_blocks(min(seq + 1, my_tiles - 1), nmb0, nnb0);
     }
-    init_acc(seq);
+    if constexpr (decltype(HALF)::value) {
+      // the previous stage read this stage's weight operands and scales of
+      // blocks 0, 1; a half item's are blocks 2 h, 2 h + 1 (stage G, published
+      // and not yet overwritten)
+      const uint32_t rb = static_cast<uint32_t>(G & (F_NBUF - 1));
+      read_piece(oa, rx + rb * F_STAGE, rw + rb * F_STAGE + half_woff, 0, 0);
+      read_piece(oa, rx + rb * F_STAGE, rw + rb * F_STAGE + half_woff, 0, 5);
+      read_scale(sx, sw, rsx + rb * 2048, rsw + rb * 2048 + half_soff, 4);
+      read_scale(sx, sw, rsx + rb * 2048, rsw + rb * 2048 + half_soff, 5);
+    }
+    init_acc(seq, HALF);
     const bool has = seq + 1 < my_tiles;         // else the copies repeat the last stage
     if constexpr (!GENERAL) {
       // A, B: stages [0, S - 3), copies of this tile's FP4 stages from stage 3
       make_desc(mb0, nb0, seq, F_AHEAD, false, d, o);
-      if constexpr (SLAB) run(oa, sx, sw, G, RS, d, o, last_mask, std::true_type{});
-      run(oa, sx, sw, G, S - F_AHEAD - RS, d, o, ~0u, std::false_type{});
+      if constexpr (SLAB) run(oa, sx, sw, G, RS, d, o, last_mask, std::true_type{}, HALF);
+      run(oa, sx, sw, G, S - F_AHEAD - RS, d, o, ~0u, std::false_type{}, HALF);
       // C: copies of the next tile's low-rank stages (the odd tail stage,
       // with its own second-step bases, separately)
       if constexpr (SLAB) {
         if (RS > 1) {
           if (has) make_desc(nmb0, nnb0, seq + 1, 0, false, d, o);
           else make_desc(mb0, nb0, seq, S - 1, true, d, o);
-          run(oa, sx, sw, G, RS - 1, d, o, ~0u, std::false_type{});
+          run(oa, sx, sw, G, RS - 1, d, o, ~0u, std::false_type{}, HALF);
         }
         if (RS > 0) {
           if (has) make_desc(nmb0, nnb0, seq + 1, RS - 1, false, d, o);
           else make_desc(mb0, nb0, seq, S - 1, true, d, o);
-          run(oa, sx, sw, G, 1, d, o, ~0u, std::false_type{});
+          run(oa, sx, sw, G, 1, d, o, ~0u, std::false_type{}, HALF);
         }
       }
       // D: copies of the next tile's FP4 stages
       if (has) make_desc(nmb0, nnb0, seq + 1, RS, false, d, o);
       else make_desc(mb0, nb0, seq, S - 1, true, d, o);
-      run(oa, sx, sw, G, F_AHEAD - RS, d, o, ~0u, std::false_type{});
+      run(oa, sx, sw, G, F_AHEAD - RS, d, o, ~0u, std::false_type{}, HALF);
     } else {
       // any shape: a descriptor per stage
 #pragma unroll 1
@@ -546,12 +585,15 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
         const bool hs = !c_next || has;
         const int cst = !hs ? S - 1 : (c_next ? cg - S : cg);
         make_desc(c_next && hs ? nmb0 : mb0, c_next && hs ? nnb0 : nb0, c_next && hs ? seq + 1 : seq, cst, !hs, d, o);
-        if (SLAB && st < RS) run(oa, sx, sw, G, 1, d, o, st == RS - 1 ? last_mask : ~0u, std::true_type{});
-        else run(oa, sx, sw, G, 1, d, o, ~0u, std::false_type{});
+        if (SLAB && st < RS) run(oa, sx, sw, G, 1, d, o, st == RS - 1 ? last_mask : ~0u, std::true_type{}, HALF);
+        else run(oa, sx, sw, G, 1, d, o, ~0u, std::false_type{}, HALF);
       }
     }
-    epilogue(mb0, nb0, G - 1);
-  }
+    epilogue(mb0, nb0, G - 1, HALF);
+  };
+#pragma unroll 1
+  for (int seq = 0; seq < nfull; seq++) item(seq, std::false_type{});
+  if (half_item) item(nfull, std::true_type{});
   // no copy may still be writing this workgroup's LDS when it exits
   SVDQ_VM_BARRIER(0);
 }

@@ -19,9 +19,10 @@
 // s_w[j] (exact in fp32, in the accumulator layout), and the group is
 // dequantized with one fma per accumulator.  That fma (16 per 32 x 32 tile
 // and group) is VALU work, which bounds this variant below the 8-bit MFMA
-// peak.  The MFMAs of the next output tile are issued before the
-// dequantization of the current one, so the matrix core and the VALU
-// overlap.
+// peak.  The E4M3 MFMA of the next output tile is issued before the
+// dequantization of the current one and its f16 MFMA after it, so each
+// MFMA executes under VALU work (a wave issues in order, and a second MFMA
+// would wait for the matrix core with the VALU work behind it).
 //
 // Tiling: 4 waves per workgroup in a 2 x 2 grid, 128 x 128 per workgroup,
 // 32 x 32 MFMA tiles.  A K stage is 128 wide (two 64-wide MFMA steps): its
@@ -234,12 +235,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   f32x16 P[2], Sc[2];
 #pragma unroll
   for (int v = 0; v < 16; v++) P[1][v] = Sc[1][v] = 0.f;
-  auto issue = [&](const Ops& o, int u, int slot) __attribute__((always_inline)) {
+  auto issue_p = [&](const Ops& o, int u, int slot) __attribute__((always_inline)) {
     const int rb = u / CB, cb = u % CB;
     f32x16 zf;
 #pragma unroll
     for (int v = 0; v < 16; v++) zf[v] = 0.f;
     P[slot] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.a[rb], o.b[cb], zf, 0, 0, 0, 127 + 9, 0, 127 + 8);
+  };
+  auto issue_s = [&](const Ops& o, int u, int slot) __attribute__((always_inline)) {
+    const int rb = u / CB, cb = u % CB;
+    f32x16 zf;
+#pragma unroll
+    for (int v = 0; v < 16; v++) zf[v] = 0.f;
     Sc[slot] = __builtin_amdgcn_mfma_f32_32x32x8f16(o.fa[rb], o.fb[cb], zf, 0, 0, 0);
   };
   auto retire = [&](int u, int slot) __attribute__((always_inline)) {
@@ -272,11 +279,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   for (int s = 0; s < stages; s++) {
 #pragma unroll
     for (int u = 0; u < NT; u++) {
-      // the fences keep the order MFMAs, fmas of the previous tile, then the
-      // reads and copies: the fmas run under the MFMAs
-      issue(OA, u, u & 1);
+      // the fences keep the order: the E4M3 MFMA, the fmas of the previous
+      // tile (they run while it executes), the f16 MFMA, then the reads,
+      // widening and copies (they run while that one executes).  A wave
+      // issues in order and a second MFMA waits for the matrix core, so two
+      // MFMAs back to back would hold the VALU work behind them.
+      issue_p(OA, u, u & 1);
       __builtin_amdgcn_sched_barrier(0);
       retire(u == 0 ? NT - 1 : u - 1, (u + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_s(OA, u, u & 1);
       __builtin_amdgcn_sched_barrier(0);
       read_part(OB, s, 1, u);
       copy_item(s + NBUF - 1, u);
@@ -286,9 +298,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     SVDQ_VM_BARRIER(10);
 #pragma unroll
     for (int u = 0; u < NT; u++) {
-      issue(OB, u, u & 1);
+      issue_p(OB, u, u & 1);
       __builtin_amdgcn_sched_barrier(0);
       retire(u == 0 ? NT - 1 : u - 1, (u + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_s(OB, u, u & 1);
       __builtin_amdgcn_sched_barrier(0);
       read_part(OA, s + 1, 0, u);
       __builtin_amdgcn_sched_barrier(0);

@@ -697,6 +697,37 @@ def measure_peaks(torch):
     return out
 
 
+def vendor_fp4_gemm_fn(torch, cfg):
+    """The vendor library's FP4 GEMM on the layer's GEMM shape, for context:
+    torch._scaled_mm on MX-FP4 operands (random E2M1 codes, E8M0 scales per
+    32 K, bf16 out; two operand sets alternate).  It has neither the low-rank
+    slab nor the bias.  None where this torch build does not offer it."""
+    if not (hasattr(torch, "float4_e2m1fn_x2") and hasattr(torch, "float8_e8m0fnu") and hasattr(torch, "_scaled_mm")):
+        return None
+    M, K, N = cfg.M, cfg.K, cfg.N
+    try:
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(5)
+        sets = []
+        for _ in range(2):
+            a = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device="cuda", generator=gen)
+            b = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device="cuda", generator=gen)
+            sa = torch.full((M, K // 32), 127, dtype=torch.uint8, device="cuda")
+            sb = torch.full((N, K // 32), 127, dtype=torch.uint8, device="cuda")
+            sets.append((a.view(torch.float4_e2m1fn_x2), b.view(torch.float4_e2m1fn_x2),
+                         sa.view(torch.float8_e8m0fnu), sb.view(torch.float8_e8m0fnu)))
+
+        def fn(k):
+            a, b, sa, sb = sets[k % 2]
+            return torch._scaled_mm(a, b.t(), sa, sb, out_dtype=torch.bfloat16)
+        fn(0)
+        torch.cuda.synchronize()
+        return fn
+    except Exception as ex:                      # not supported by this build or device
+        print(f"vendor FP4 GEMM unavailable: {ex!r}"[:300], file=sys.stderr)
+        return None
+
+
 def measure(args, cfg, torch, S, WL, to_tensor, with_cpu=False, lora=0, norm=False, rank0=False, contract=False):
     """All timings of one workload (see the module docstring)."""
     rig = Rig(cfg, torch, S, WL, to_tensor, lora)
@@ -706,6 +737,10 @@ def measure(args, cfg, torch, S, WL, to_tensor, with_cpu=False, lora=0, norm=Fal
     if contract:
         out["ms_bracket"], out["wall"] = bracket(torch, fused, args.steps)
     variants = [("fused", fused), ("unfused", unfused), ("quant", quant), ("gemm", gemm)]
+    vendor = vendor_fp4_gemm_fn(torch, cfg) if cfg.fmt == "fp4" and lora == 0 else None
+    if vendor is not None:
+        warm(torch, [vendor], args.warmup, 0.3)
+        variants.append(("vendor_fp4_gemm", vendor))
     rig0 = None
     if rank0 and cfg.rank > 0:
         rig0 = Rig(cfg.with_(rank=0), torch, S, WL, to_tensor)
@@ -733,6 +768,10 @@ def summary(r, cfg):
            "gemm_us": us(t["gemm"]), "gemm_tops": gt, "gemm_frac_peak": gt / PEAK_TFLOPS[cfg.fmt],
            "peak_tops": PEAK_TFLOPS[cfg.fmt], "quant_us": us(t["quant"]),
            "quant_frac_hbm": A["q_bytes"] / (q / 1e3) / 1e9 / PEAK_HBM_GBS}
+    if "vendor_fp4_gemm" in t:
+        # torch._scaled_mm MX-FP4 on the same M, K, N (no slab, no bias)
+        rec["vendor_fp4_gemm_us"] = us(t["vendor_fp4_gemm"])
+        rec["gemm_speedup_vs_vendor"] = t["vendor_fp4_gemm"]["median"] / g
     if "fused_rank0" in t:
         rec["us_per_layer_rank0"] = us(t["fused_rank0"])
         rec["slab_overhead"] = f / t["fused_rank0"]["median"]

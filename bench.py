@@ -747,6 +747,9 @@ def measure(args, cfg, torch, S, WL, to_tensor, with_cpu=False, lora=0, norm=Fal
         fused0 = layer_fns(S, rig0)[0]
         warm(torch, [fused0], args.warmup, 0.3)
         variants.append(("fused_rank0", fused0))
+        # the slab overhead from back-to-back calls at both ranks (per-call
+        # events carry a few microseconds of their own)
+        out["ms_bracket_pair"] = (bracket(torch, fused, args.steps)[0], bracket(torch, fused0, args.steps)[0])
     t = interleaved(torch, variants, args.steps)
     out["t"] = {k: pct(v) for k, v in t.items()}
     if rig0 is not None:
@@ -774,7 +777,10 @@ def summary(r, cfg):
         rec["gemm_speedup_vs_vendor"] = t["vendor_fp4_gemm"]["median"] / g
     if "fused_rank0" in t:
         rec["us_per_layer_rank0"] = us(t["fused_rank0"])
-        rec["slab_overhead"] = f / t["fused_rank0"]["median"]
+        rec["slab_overhead_per_call"] = f / t["fused_rank0"]["median"]
+        b_r, b_0 = r["ms_bracket_pair"]
+        rec["us_per_layer_back_to_back"] = {"rank": b_r * 1e3, "rank0": b_0 * 1e3}
+        rec["slab_overhead"] = b_r / b_0
     if r.get("ms_norm"):
         rec["us_per_layer_norm_fused"] = r["ms_norm"][0] * 1e3
         rec["us_per_layer_norm_separate"] = r["ms_norm"][1] * 1e3

@@ -342,6 +342,9 @@ def test_host_smoothing_factors_match_oracle(tmp_path):
     w = (rng.random(n) * np.exp2(rng.integers(-40, 40, n))).astype(np.float32)
     a[:5] = 0.0
     w[5:10] = 0.0
+    # sqrt(a / w) just past an fp32 rounding midpoint (a^0.5 / w^0.5 in fp64
+    # rounds the wrong way here)
+    a[10], w[10] = float.fromhex("0x1.19e7b4p+1"), float.fromhex("0x1.1ap+1")
     for alpha, nosm in ((0.5, 0), (0.25, 0), (0.75, 0), (0.3, 0), (0.5, 1)):
         inp = f"{n} {float(np.float32(alpha)).hex()} {nosm}\n" + "\n".join(
             f"{float(x).hex()} {float(y).hex()}" for x, y in zip(a, w))

@@ -625,6 +625,64 @@ def test_smoothing_lambda_is_correctly_rounded():
     assert np.array_equal(lam32, ref)
 
 
+def _fp32_rounding_of_sqrt(r: Fraction) -> float:
+    """The fp32 value nearest to sqrt(r) (ties to the even significand),
+    decided with exact rationals: c is the answer when sqrt(r) lies between
+    the midpoints to its neighbours, i.e. when their squares bracket r."""
+    c = np.float32(np.sqrt(float(r)))
+    for x in (np.nextafter(c, np.float32(0)), c, np.nextafter(c, np.float32(np.inf))):
+        lo = (Fraction(float(np.nextafter(x, np.float32(0)))) + Fraction(float(x))) / 2
+        hi = (Fraction(float(x)) + Fraction(float(np.nextafter(x, np.float32(np.inf))))) / 2
+        if lo * lo < r < hi * hi or ((lo * lo == r or hi * hi == r) and int(x.view(np.uint32)) % 2 == 0):
+            return float(x)
+    raise AssertionError("no candidate brackets sqrt(r)")
+
+
+def test_smoothing_lambda_hard_rounding_case():
+    """lambda = sqrt(a / w) at alpha = 0.5 (handbook, SmoothQuant section)
+    for an fp32 activation maximum a and a bf16 weight maximum w chosen
+    (by a search) so that sqrt(a / w) lies just past an fp32 rounding
+    midpoint: the value computed in fp64 as a^0.5 / w^0.5 and then rounded
+    to fp32 is one ulp low; the correctly rounded lambda32 is the exact
+    rational decision."""
+    a = np.float32(float.fromhex("0x1.19e7b4p+1"))
+    w = float.fromhex("0x1.1ap+1")                         # a bf16 value
+    want = _fp32_rounding_of_sqrt(Fraction(float(a)) / Fraction(w))
+    assert want == float.fromhex("0x1.ffe9f2p-1")
+    assert float(np.float32(float(a) ** 0.5 / w ** 0.5)) != want    # the fp64 route misses it
+    lam32, inv32 = O.smoothing_factors(np.array([a]), np.array([[w]]), 0.5)
+    assert lam32[0] == want
+    assert inv32[0] == float(np.float32(1.0 / want))
+
+
+def test_down_projection_rounds_xhat_to_bf16():
+    """The down-projection's operand is x_hat rounded to bf16 (the bf16
+    matrix-core input of the low-rank branch, walkthrough Fig. 6), not the
+    fp32 x_hat: with x_hat = (1 + 2^-9, 1) and L1 = (1, -1)^T, bf16(1 + 2^-9)
+    = 1 (2^-9 is below half a bf16 ulp at 1), so T = 0 exactly, while the
+    fp32 operand would give T = 2^-9."""
+    T, Tb = O.down_proj(np.array([[1.0 + 2.0 ** -9, 1.0]]), np.array([[1.0], [-1.0]]))
+    assert T.tolist() == [[0.0]] and Tb.tolist() == [[0.0]]
+
+
+def test_quantizer_decides_on_fp32_xhat():
+    """The quantizer sees x_hat = fp32(x * inv_lambda), one rounding of the
+    product (the smoothed activation is an fp32 tensor): x = 5.5 and inv =
+    fp32(12/11), which is above 12/11 by 3.3e-8, give x * inv = 6 + 1.8e-7,
+    within half an fp32 ulp of 6, so x_hat = 6 exactly; the FP4 group scale is
+    then 2^0 (6 <= 6 * 2^0) and the code is 6, where the unrounded product
+    would need 2^1 and code 3."""
+    inv = np.ones(32)
+    inv[0] = float(np.float32(12.0 / 11.0))
+    assert Fraction(11, 2) * Fraction(inv[0]) > 6
+    x = np.zeros((1, 32), np.float32)
+    x[0, 0] = 5.5
+    qa = O.quantize_act(O.bf16_bits_of(x), inv, O.FP4)
+    assert qa["xhat"][0, 0] == 6.0
+    assert qa["scales"].tolist() == [[0]] and qa["scale_bytes"].tolist() == [[127]]
+    assert int(qa["codes"][0, 0]) == 7                     # E2M1 code of +6 (index 7)
+
+
 def test_int4_scale_saturates_at_fp16_max():
     """A group absmax beyond 7 * 65504 keeps the largest finite fp16 scale
     (no infinity), and its codes clamp to +-7."""

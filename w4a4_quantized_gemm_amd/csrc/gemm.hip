@@ -204,22 +204,43 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   };
   // part p of the operands of step j of stage st: p < RB row block p, else
   // column block p - RB
-  auto read_part = [&](Ops& o, int st, int j, int p) __attribute__((always_inline)) {
-    const uint8_t* ring = smem + (st % NBUF) * RING_STAGE;
+  // Per-lane LDS addresses of a ring slot, made opaque so that the
+  // compiler keeps them in two registers per slot and puts every block's
+  // constant offset into the read instruction (it would otherwise add each
+  // one to the slot offset separately).
+  typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+  struct Bases {
+    uint32_t a, b, sa, sb;    // this wave's first A / B code block and scales in the slot
+  };
+  auto bases_of = [&](int st) __attribute__((always_inline)) {
+    Bases r;
+    const uint32_t slot = lds0 + static_cast<uint32_t>(st % NBUF) * RING_STAGE;
+    r.a = slot + RING_A + static_cast<uint32_t>(wrow0 / 32) * 2048u + lane16;
+    r.b = slot + RING_B + static_cast<uint32_t>(wcol0 / 32) * 2048u + lane16;
+    r.sa = slot + RING_SA + static_cast<uint32_t>(wrow0 / 32) * 128u + static_cast<uint32_t>(l32) * 4u;
+    r.sb = slot + RING_SB + static_cast<uint32_t>(wcol0 / 32) * 128u + static_cast<uint32_t>(l32) * 4u;
+    asm volatile("" : "+v"(r.a), "+v"(r.b), "+v"(r.sa), "+v"(r.sb));
+    return r;
+  };
+  auto lds_at = [](uint32_t addr) __attribute__((always_inline)) {
+    return reinterpret_cast<lds_u8*>(static_cast<uintptr_t>(addr));
+  };
+  auto read_part = [&](Ops& o, const Bases& bs, int j, int p) __attribute__((always_inline)) {
+    typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+    typedef __attribute__((address_space(3))) const uint16_t lds_u16;
     if (p < RB) {
-      const int rb = wrow0 / 32 + p;
-      const u32x4 c = *reinterpret_cast<const u32x4*>(ring + RING_A + (rb * 2 + j) * 1024 + lane16);
+      const u32x4 c = *reinterpret_cast<lds_u32x4*>(lds_at(bs.a) + (p * 2 + j) * 1024);
       const u32x4 lo = e4m3_lo(c), hi = e4m3_hi(c);
       o.a[p] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const uint32_t sb = *reinterpret_cast<const uint16_t*>(ring + RING_SA + rb * 128 + l32 * 4 + j * 2);
+      const uint32_t sb = *reinterpret_cast<lds_u16*>(lds_at(bs.sa) + p * 128 + j * 2);
       o.fa[p] = __builtin_bit_cast(f16x4, u32x2{sb, 0u});
     } else {
-      const int cb = wcol0 / 32 + p - RB;
-      const u32x4 c = *reinterpret_cast<const u32x4*>(ring + RING_B + (cb * 2 + j) * 1024 + lane16);
+      const int q = p - RB;
+      const u32x4 c = *reinterpret_cast<lds_u32x4*>(lds_at(bs.b) + (q * 2 + j) * 1024);
       const u32x4 lo = e4m3_lo(c), hi = e4m3_hi(c);
-      o.b[p - RB] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const uint32_t sb = *reinterpret_cast<const uint16_t*>(ring + RING_SB + (cb * 32 + l32) * 4 + j * 2);
-      o.fb[p - RB] = __builtin_bit_cast(f16x4, u32x2{sb, 0u});
+      o.b[q] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const uint32_t sb = *reinterpret_cast<lds_u16*>(lds_at(bs.sb) + q * 128 + j * 2);
+      o.fb[q] = __builtin_bit_cast(f16x4, u32x2{sb, 0u});
     }
   };
 
@@ -273,41 +294,61 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     for (int i = 0; i < NCOPY; i++) copy_item(p, i);
   SVDQ_VM_BARRIER(10);
   Ops OA, OB;
+  // bases of ring slot 0 (opaque); slot k is slot 0 + k * RING_STAGE, a
+  // constant offset where k is known at compile time
+  const Bases base0 = bases_of(0);
+  auto slot_bases = [&](int k) __attribute__((always_inline)) {
+    const uint32_t o = static_cast<uint32_t>(k) * RING_STAGE;
+    return Bases{base0.a + o, base0.b + o, base0.sa + o, base0.sb + o};
+  };
 #pragma unroll
-  for (int p = 0; p < RB + CB; p++) read_part(OA, 0, 0, p);
+  for (int p = 0; p < RB + CB; p++) read_part(OA, base0, 0, p);
+  // stage s with the bases of its slot (bs) and of the next stage's (bn)
+  auto stage_body = [&](int s, const Bases& bs, const Bases& bn) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < NT; u++) {
+        // the fences keep the order: the E4M3 MFMA, the fmas of the previous
+        // tile (they run while it executes), the f16 MFMA, then the reads,
+        // widening and copies (they run while that one executes).  A wave
+        // issues in order and a second MFMA waits for the matrix core, so two
+        // MFMAs back to back would hold the VALU work behind them.
+        issue_p(OA, u, u & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        retire(u == 0 ? NT - 1 : u - 1, (u + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_s(OA, u, u & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        read_part(OB, bs, 1, u);
+        copy_item(s + NBUF - 1, u);
+        if (u == NT - 1) copy_item(s + NBUF - 1, NT);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      SVDQ_VM_BARRIER(10);
+#pragma unroll
+      for (int u = 0; u < NT; u++) {
+        issue_p(OB, u, u & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        retire(u == 0 ? NT - 1 : u - 1, (u + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_s(OB, u, u & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        read_part(OA, bn, 0, u);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+  // unrolled by the ring depth so that every slot offset is a constant of
+  // the read instructions; the remaining stages with computed bases
+  int s = 0;
 #pragma unroll 1
-  for (int s = 0; s < stages; s++) {
-#pragma unroll
-    for (int u = 0; u < NT; u++) {
-      // the fences keep the order: the E4M3 MFMA, the fmas of the previous
-      // tile (they run while it executes), the f16 MFMA, then the reads,
-      // widening and copies (they run while that one executes).  A wave
-      // issues in order and a second MFMA waits for the matrix core, so two
-      // MFMAs back to back would hold the VALU work behind them.
-      issue_p(OA, u, u & 1);
-      __builtin_amdgcn_sched_barrier(0);
-      retire(u == 0 ? NT - 1 : u - 1, (u + 1) & 1);
-      __builtin_amdgcn_sched_barrier(0);
-      issue_s(OA, u, u & 1);
-      __builtin_amdgcn_sched_barrier(0);
-      read_part(OB, s, 1, u);
-      copy_item(s + NBUF - 1, u);
-      if (u == NT - 1) copy_item(s + NBUF - 1, NT);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    SVDQ_VM_BARRIER(10);
-#pragma unroll
-    for (int u = 0; u < NT; u++) {
-      issue_p(OB, u, u & 1);
-      __builtin_amdgcn_sched_barrier(0);
-      retire(u == 0 ? NT - 1 : u - 1, (u + 1) & 1);
-      __builtin_amdgcn_sched_barrier(0);
-      issue_s(OB, u, u & 1);
-      __builtin_amdgcn_sched_barrier(0);
-      read_part(OA, s + 1, 0, u);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  for (; s + NBUF <= stages; s += NBUF) {
+    static_assert(NBUF == 4, "the unrolled loop walks four ring slots");
+    stage_body(s, slot_bases(0), slot_bases(1));
+    stage_body(s + 1, slot_bases(1), slot_bases(2));
+    stage_body(s + 2, slot_bases(2), slot_bases(3));
+    stage_body(s + 3, slot_bases(3), slot_bases(0));
   }
+#pragma unroll 1
+  for (; s < stages; s++) stage_body(s, bases_of(s), bases_of(s + 1));
   retire(NT - 1, 1);
   // no copy may still be writing the ring, and every wave is done reading
   // it, before the epilogue stages its output there

@@ -22,7 +22,9 @@
 // peak.  The E4M3 MFMA of the next output tile is issued before the
 // dequantization of the current one and its f16 MFMA after it, so each
 // MFMA executes under VALU work (a wave issues in order, and a second MFMA
-// would wait for the matrix core with the VALU work behind it).
+// would wait for the matrix core with the VALU work behind it); operand
+// parts are read from LDS one MFMA slot before they are widened, so no
+// read's latency stalls the wave right after the read.
 //
 // Tiling: 4 waves per workgroup in a 2 x 2 grid, 128 x 128 per workgroup,
 // 32 x 32 MFMA tiles.  A K stage is 128 wide (two 64-wide MFMA steps): its
@@ -225,22 +227,34 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   auto lds_at = [](uint32_t addr) __attribute__((always_inline)) {
     return reinterpret_cast<lds_u8*>(static_cast<uintptr_t>(addr));
   };
-  auto read_part = [&](Ops& o, const Bases& bs, int j, int p) __attribute__((always_inline)) {
+  // An operand part is read raw (codes and scale) in one MFMA slot and
+  // widened in the next, so the read's latency passes under that slot's
+  // MFMAs and fmas instead of stalling the wave right after the read.
+  struct Raw {
+    u32x4 c;
+    uint32_t sc;
+  };
+  auto read_raw = [&](Raw& r, const Bases& bs, int j, int p) __attribute__((always_inline)) {
     typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
     typedef __attribute__((address_space(3))) const uint16_t lds_u16;
     if (p < RB) {
-      const u32x4 c = *reinterpret_cast<lds_u32x4*>(lds_at(bs.a) + (p * 2 + j) * 1024);
-      const u32x4 lo = e4m3_lo(c), hi = e4m3_hi(c);
-      o.a[p] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const uint32_t sb = *reinterpret_cast<lds_u16*>(lds_at(bs.sa) + p * 128 + j * 2);
-      o.fa[p] = __builtin_bit_cast(f16x4, u32x2{sb, 0u});
+      r.c = *reinterpret_cast<lds_u32x4*>(lds_at(bs.a) + (p * 2 + j) * 1024);
+      r.sc = *reinterpret_cast<lds_u16*>(lds_at(bs.sa) + p * 128 + j * 2);
     } else {
-      const int q = p - RB;
-      const u32x4 c = *reinterpret_cast<lds_u32x4*>(lds_at(bs.b) + (q * 2 + j) * 1024);
-      const u32x4 lo = e4m3_lo(c), hi = e4m3_hi(c);
-      o.b[q] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const uint32_t sb = *reinterpret_cast<lds_u16*>(lds_at(bs.sb) + q * 128 + j * 2);
-      o.fb[q] = __builtin_bit_cast(f16x4, u32x2{sb, 0u});
+      r.c = *reinterpret_cast<lds_u32x4*>(lds_at(bs.b) + ((p - RB) * 2 + j) * 1024);
+      r.sc = *reinterpret_cast<lds_u16*>(lds_at(bs.sb) + (p - RB) * 128 + j * 2);
+    }
+  };
+  auto widen = [&](Ops& o, const Raw& r, int p) __attribute__((always_inline)) {
+    const u32x4 lo = e4m3_lo(r.c), hi = e4m3_hi(r.c);
+    const i32x8 v = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    const f16x4 f = __builtin_bit_cast(f16x4, u32x2{r.sc, 0u});
+    if (p < RB) {
+      o.a[p] = v;
+      o.fa[p] = f;
+    } else {
+      o.b[p - RB] = v;
+      o.fb[p - RB] = f;
     }
   };
 
@@ -253,6 +267,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   // retirement (of a "previous" tile 3) adds 0 * 0 to its accumulators.
   constexpr int NT = RB * CB;
   static_assert(NT == 4, "the schedule below retires tile NT - 1 of the previous step first");
+  static_assert(RB + CB == NT, "one operand part is read per MFMA slot");
   f32x16 P[2], Sc[2];
 #pragma unroll
   for (int v = 0; v < 16; v++) P[1][v] = Sc[1][v] = 0.f;
@@ -301,8 +316,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     const uint32_t o = static_cast<uint32_t>(k) * RING_STAGE;
     return Bases{base0.a + o, base0.b + o, base0.sa + o, base0.sb + o};
   };
+  Raw raw[2];
 #pragma unroll
-  for (int p = 0; p < RB + CB; p++) read_part(OA, base0, 0, p);
+  for (int p = 0; p < RB + CB - 1; p++) {
+    read_raw(raw[0], base0, 0, p);
+    widen(OA, raw[0], p);
+  }
+  read_raw(raw[1], base0, 0, RB + CB - 1);     // widened in the first slot of the loop
   // stage s with the bases of its slot (bs) and of the next stage's (bn)
   auto stage_body = [&](int s, const Bases& bs, const Bases& bn) __attribute__((always_inline)) {
 #pragma unroll
@@ -318,7 +338,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
         issue_s(OA, u, u & 1);
         __builtin_amdgcn_sched_barrier(0);
-        read_part(OB, bs, 1, u);
+        // part u of OB is read; the part read in the previous slot is
+        // widened (in slot 0: OA's last part, read in the previous step)
+        read_raw(raw[u & 1], bs, 1, u);
+        if (u == 0) widen(OA, raw[1], NT - 1);
+        else widen(OB, raw[(u - 1) & 1], u - 1);
         copy_item(s + NBUF - 1, u);
         if (u == NT - 1) copy_item(s + NBUF - 1, NT);
         __builtin_amdgcn_sched_barrier(0);
@@ -332,7 +356,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
         issue_s(OB, u, u & 1);
         __builtin_amdgcn_sched_barrier(0);
-        read_part(OA, bn, 0, u);
+        read_raw(raw[u & 1], bn, 0, u);
+        if (u == 0) widen(OB, raw[1], NT - 1);
+        else widen(OA, raw[(u - 1) & 1], u - 1);
         __builtin_amdgcn_sched_barrier(0);
       }
   };

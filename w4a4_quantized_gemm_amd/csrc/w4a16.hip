@@ -31,7 +31,10 @@
 // all of K: wave w takes the 64-blocks kb = w, w + 8, .. and all CBW column
 // blocks of each (one A operand serves CBW MFMA chains), with up to six
 // blocks of weights in flight; the eight waves' partial sums are added in
-// wave order through LDS, so the result is deterministic.
+// wave order through LDS, so the result is deterministic.  The weight
+// scales of the workgroup's column blocks (one contiguous run of CBW K
+// bytes in both formats) are copied into LDS once, so the loop's only
+// gathers are gone (up to K = 4096 at three blocks).
 #include <algorithm>
 
 #include "svdq_device.h"
@@ -47,6 +50,7 @@ constexpr int XW = 8;        // waves per workgroup of the weight-streaming kern
 constexpr int XPF = 2;       // 64-blocks in flight per wave (A operands from the workspace)
 constexpr int XDEPTH = 6;    // 64-blocks in flight per wave (A operands in LDS)
 constexpr int W_LDS = 147456;  // LDS of the in-LDS form: 3 M K bf16 pieces (M = 8, K = 3072 fit)
+constexpr int S_LDS = 12288;   // the workgroup's weight scales (CBW K bytes) staged in LDS up to this size
 
 // bf16 bits of piece p (0 hi, 1 mid, 2 lo) of x: x = hi + mid + lo exactly
 // for finite x (fp32 subnormal remainders aside); a non-finite x is carried
@@ -116,7 +120,12 @@ __global__ __launch_bounds__(256) void w4a16_split_kernel(const uint16_t* __rest
 // weights would make every wait for them a wait for the whole prefetch).
 // Otherwise the A operands come from w4a16_split_kernel's workspace, two
 // blocks ahead together with the weights.
-template <int FMT, int NOP, int CBW, bool LDSA>
+// SCL: the scales of the workgroup's CBW column blocks (K bytes per block in
+// both formats, contiguous) are copied into LDS once with 16-byte loads and
+// read from there; otherwise every lane loads its column's scale per block,
+// a gather over 32 cache lines per instruction (most of the loop's cache
+// traffic by request count, next to 1 KB of weights per instruction).
+template <int FMT, int NOP, int CBW, bool LDSA, bool SCL>
 __global__ __launch_bounds__(XW * 64) void w4a16_kernel(const u32x4* __restrict__ A, const uint16_t* __restrict__ X,
                                                         const float* __restrict__ inv_lam, int M, int K, int N,
                                                         const uint8_t* __restrict__ wcodes,
@@ -128,8 +137,10 @@ __global__ __launch_bounds__(XW * 64) void w4a16_kernel(const u32x4* __restrict_
   constexpr int NA = LDSA ? 1 : 4 * NOP;     // A operands held per prefetch slot
   // LDSA: the pieces, then (after the loop) the waves' partial sums
   // [wave][column block][value][lane]; else only the partial sums
-  constexpr int LDS_BYTES = LDSA ? W_LDS : XW * CBW * NV * 64 * 4;
+  constexpr int LDS_MAIN = LDSA ? W_LDS : XW * CBW * NV * 64 * 4;
+  constexpr int LDS_BYTES = LDS_MAIN + (SCL ? S_LDS : 0);
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+  uint8_t* const sl = lds + LDS_MAIN;           // SCL: scales of column block c at c K
   float* const red = reinterpret_cast<float*>(lds);
   const int lane = threadIdx.x & 63, wave = wave_uniform(threadIdx.x >> 6);
   const int h = lane >> 5, r = lane & 31;
@@ -171,8 +182,40 @@ __global__ __launch_bounds__(XW * 64) void w4a16_kernel(const u32x4* __restrict_
   const __amdgpu_buffer_rsrc_t sr =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(wscales), 0, static_cast<int>(s_bytes), 0x00020000);
 
+  // SCL: the scale copy's loads go out first (16 bytes per lane, whole
+  // blocks; a block past the matrix repeats the last one)
+  constexpr int SC_IT = (S_LDS / 16 + XW * 64 - 1) / (XW * 64);
+  u32x4 sv[SCL ? SC_IT : 1];
+  const int n16 = CBW * K / 16, k16 = K / 16;
+  if constexpr (SCL) {
+#pragma unroll
+    for (int j = 0; j < SC_IT; j++) {
+      const int i = static_cast<int>(threadIdx.x) + j * XW * 64;
+      const int c = i / k16;
+      sv[j] = __builtin_amdgcn_raw_buffer_load_b128(
+          sr, i < n16 ? static_cast<uint32_t>(cbk[min(c, CBW - 1)]) * static_cast<uint32_t>(K) + (i - c * k16) * 16u
+                      : s_bytes, 0, 0);
+    }
+  }
+  auto store_scales = [&]() __attribute__((always_inline)) {
+    if constexpr (SCL) {
+#pragma unroll
+      for (int j = 0; j < SC_IT; j++) {
+        const int i = static_cast<int>(threadIdx.x) + j * XW * 64;
+        if (i < n16) *reinterpret_cast<u32x4*>(sl + i * 16) = sv[j];
+      }
+    }
+  };
+  // the scale of the lane's column of block c at 64-block kb
+  auto scale_lds = [&](int c, int kb) __attribute__((always_inline)) -> uint32_t {
+    if constexpr (FMT == SVDQ_INT4_G64_FP16)
+      return *reinterpret_cast<const uint16_t*>(sl + c * K + (r * KB + kb) * 2);
+    else
+      return sl[c * K + static_cast<int>(fp4_scale_offset(r, kb * 64 + 32 * h, K))];
+  };
+
   u32x4 aq[PF][NA], wq[PF][CBW];
-  uint32_t sq[PF][CBW];
+  uint32_t sq[PF][SCL ? 1 : CBW];
   auto fetch = [&](int t, int slot) __attribute__((always_inline)) {
     const int kb = wave + XW * t;
     const bool ok = t < nt;
@@ -180,12 +223,14 @@ __global__ __launch_bounds__(XW * 64) void w4a16_kernel(const u32x4* __restrict_
     for (int c = 0; c < CBW; c++) {
       wq[slot][c] = __builtin_amdgcn_raw_buffer_load_b128(
           cr, ok ? (static_cast<uint32_t>(cbk[c]) * KB + kb) * 1024u + lane * 16u : c_bytes, 0, 0);
-      if constexpr (FMT == SVDQ_INT4_G64_FP16)
+      if constexpr (SCL) {
+      } else if constexpr (FMT == SVDQ_INT4_G64_FP16) {
         sq[slot][c] = __builtin_amdgcn_raw_buffer_load_b16(
             sr, ok ? (static_cast<uint32_t>(col[c]) * KB + kb) * 2u : s_bytes, 0, 0);
-      else
+      } else {
         sq[slot][c] = __builtin_amdgcn_raw_buffer_load_b8(
             sr, ok ? static_cast<uint32_t>(fp4_scale_offset(col[c], kb * 64 + 32 * h, K)) : s_bytes, 0, 0);
+      }
     }
     if constexpr (!LDSA) {
 #pragma unroll
@@ -230,6 +275,7 @@ __global__ __launch_bounds__(XW * 64) void w4a16_kernel(const u32x4* __restrict_
     if (v0 < nvec) load_item(v0, xv, l0, l1);
 #pragma unroll
     for (int d = 0; d < PF; d++) fetch(d, d);
+    store_scales();
     if (v0 < nvec) store_item(v0, xv, l0, l1);
     for (int v = v0 + XW * 64; v < nvec; v += XW * 64) {
       load_item(v, xv, l0, l1);
@@ -239,6 +285,8 @@ __global__ __launch_bounds__(XW * 64) void w4a16_kernel(const u32x4* __restrict_
   } else {
 #pragma unroll
     for (int d = 0; d < PF; d++) fetch(d, d);
+    store_scales();
+    if constexpr (SCL) __syncthreads();
   }
 
   f32x16 acc[CBW];
@@ -260,10 +308,11 @@ __global__ __launch_bounds__(XW * 64) void w4a16_kernel(const u32x4* __restrict_
 #pragma unroll
       for (int c = 0; c < CBW; c++) {
         w[c] = wq[d][c];
+        const uint32_t sraw = SCL ? scale_lds(c, min(wave + XW * t, KB - 1)) : sq[d][SCL ? 0 : c];
         if constexpr (FMT == SVDQ_INT4_G64_FP16)
-          sc[c] = __half2float(__ushort_as_half(static_cast<uint16_t>(sq[d][c]))) * 512.0f;   // s 2^9
+          sc[c] = __half2float(__ushort_as_half(static_cast<uint16_t>(sraw))) * 512.0f;   // s 2^9
         else
-          sc[c] = __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(sq[d][c] & 0xFFu) - 127);   // 2^e
+          sc[c] = __builtin_amdgcn_ldexpf(1.0f, static_cast<int>(sraw & 0xFFu) - 127);   // 2^e
       }
       fetch(t + PF, d);
       if (t < nt) {
@@ -377,9 +426,18 @@ hipError_t launch_w4a16(int fmt, const W4A16Args& a, hipStream_t st) {
   const int ncb = a.N / 32, cus = device_cu_count();
   const int cbw = std::min(3, std::max(1, (ncb + cus - 1) / cus));
   const dim3 grid(static_cast<unsigned>((ncb + cbw - 1) / cbw)), block(XW * 64);
-#define SVDQ_W(F, NP, CB, L)                                                                                    \
-  hipLaunchKernelGGL((w4a16_kernel<F, NP, CB, L>), grid, block, 0, st, static_cast<const u32x4*>(a.pieces), a.X, \
-                     a.inv_lam, a.M, a.K, a.N, a.wcodes, a.wscales, a.bias, a.Y, a.out_f32)
+  // scales staged in LDS where the workgroup's (cbw K bytes) fit
+  const bool scl = static_cast<long>(cbw) * a.K <= S_LDS;
+#define SVDQ_W(F, NP, CB, L)                                                                                         \
+  do {                                                                                                              \
+    if (scl)                                                                                                        \
+      hipLaunchKernelGGL((w4a16_kernel<F, NP, CB, L, true>), grid, block, 0, st, static_cast<const u32x4*>(a.pieces), \
+                         a.X, a.inv_lam, a.M, a.K, a.N, a.wcodes, a.wscales, a.bias, a.Y, a.out_f32);               \
+    else                                                                                                            \
+      hipLaunchKernelGGL((w4a16_kernel<F, NP, CB, L, false>), grid, block, 0, st,                                    \
+                         static_cast<const u32x4*>(a.pieces), a.X, a.inv_lam, a.M, a.K, a.N, a.wcodes, a.wscales,   \
+                         a.bias, a.Y, a.out_f32);                                                                   \
+  } while (0)
 #define SVDQ_WC(F, NP, L)                  \
   switch (cbw) {                           \
     case 1: SVDQ_W(F, NP, 1, L); break;    \

@@ -23,9 +23,8 @@
 //    and half the epilogue per item);
 //  - one wave per SIMD, 2 x 2 waves, each owning 128 x 128 outputs (4 x 4
 //    MFMA tiles, 256 fp32 accumulators): every operand kilobyte a wave reads
-//    from LDS feeds 4 MFMAs, which keeps the LDS read traffic at 2 KB per
-//    MFMA-kilocycle -- the LDS, shared by the DMA writes and the operand
-//    reads, is the tightest resource after the matrix core;
+//    from LDS feeds 4 MFMAs (2 KB of reads per MFMA-kilocycle; halving them
+//    measured only 3% faster, so the LDS is not the bound);
 //  - the reduction of a tile is a stream of stages: rank/32 low-rank stages
 //    (32 ranks of Tb and L2b, two 32x32x16 bf16 MFMA steps) then K/128 FP4
 //    stages (two 32x32x64 steps).  A stage is 16 KB of activation blocks +

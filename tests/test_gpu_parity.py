@@ -338,13 +338,15 @@ def test_merge_lowrank(torch_dev, fmt, re):
 
 @pytest.mark.parametrize("fmt", [O.INT4, O.FP4])
 @pytest.mark.parametrize("M,K,N", [(1, 3072, 576), (3, 1024, 320), (5, 256, 64), (16, 4096, 192), (16, 1024, 9216),
-                                   (9, 3072, 18432)])
+                                   (9, 3072, 18432), (1, 16384, 64), (9, 16384, 128)])
 def test_w4a16(torch_dev, fmt, M, K, N):
     """The weight-only 4-bit layer on a rank-0 blob against the oracle's
     weight-only layer (x_hat unquantized, fp64 product): the products are
     exact on both sides and only the fp32 accumulation differs, so the f32
     output agrees to 1e-5.  Shapes: one and two operand planes (M <= 8,
-    M <= 16), 1-3 column blocks per workgroup, fewer 64-blocks than waves."""
+    M <= 16), 1-3 column blocks per workgroup, fewer 64-blocks than waves,
+    and K = 16384, where the workgroup's scales (K bytes per column block)
+    exceed the LDS staging area and every lane loads its own."""
     import w4a4_quantized_gemm_amd as S
     torch, dev = torch_dev
     _say(f"case: w4a16 fmt={fmt} M={M} K={K} N={N}")

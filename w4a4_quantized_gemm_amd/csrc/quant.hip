@@ -74,7 +74,9 @@ __device__ __forceinline__ void x_hat8(const uint8_t* xs, const float* ils, int 
 // row's mean mu and 1/sqrt(var + eps) rho from `rowstat` (two floats per row)
 // and inv_lam pointing at gamma' = gamma * inv_lambda (K floats) followed by
 // beta' = beta * inv_lambda (K floats).
-template <int FMT, bool QUANT, bool DOWN, int RB, bool NORM, int NW>
+// HV: 16-row halves per workgroup (1, or 2 for 32-row blocks whose halves
+// share every L1 operand load).
+template <int FMT, bool QUANT, bool DOWN, int RB, bool NORM, int NW, int HV = 1>
 __global__ __launch_bounds__(NW * 64) void act_kernel(const uint16_t* __restrict__ X, int M, int K,
                                                   const float* __restrict__ inv_lam,
                                                   const float* __restrict__ rowstat,
@@ -89,21 +91,20 @@ __global__ __launch_bounds__(NW * 64) void act_kernel(const uint16_t* __restrict
   // pieces are XOR-swizzled by the row index) and the chunk's 128 inverse
   // smoothing factors (512 B; NORM: 128 gamma' then 128 beta'); after the
   // loop the same memory holds the cross-wave T reduction
-  constexpr int WSTAGE = 4096 + (NORM ? 1024 : 512);
-  constexpr int LDS_BYTES = (LR && NW * 64 * R > NW * WSTAGE) ? NW * 64 * R : NW * WSTAGE;
+  constexpr int WSTAGE = 4096 * HV + (NORM ? 1024 : 512);
+  constexpr int LDS_BYTES = (LR && NW * 64 * R * HV > NW * WSTAGE) ? NW * 64 * R * HV : NW * WSTAGE;
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int row = lane & 15;
   const int kq = lane >> 4;
   const int rblk = static_cast<int>(blockIdx.x) / kparts, part = static_cast<int>(blockIdx.x) - rblk * kparts;
-  const long row0 = static_cast<long>(rblk) * 16;
-  const bool valid = row0 + row < M;
-  const int nrows = static_cast<int>(min(static_cast<long>(M) - row0, 16L));
+  const long row0 = static_cast<long>(rblk) * 16 * HV;
+  const int nrows = static_cast<int>(min(static_cast<long>(M) - row0, 16L * HV));
   const int cpp = (K >> 7) / kparts;              // chunks per part (kparts divides K / 128)
   const int c_end = (part + 1) * cpp;
-  uint8_t* xs = lds + wave * WSTAGE;             // this wave's X chunk
-  const float* ils = reinterpret_cast<const float*>(xs + 4096);
+  uint8_t* xs = lds + wave * WSTAGE;             // this wave's X chunk (per half 4 KB)
+  const float* ils = reinterpret_cast<const float*>(xs + 4096 * HV);
   const uint32_t rowb = static_cast<uint32_t>(K) * 2;
 
   // Buffer resources of the workgroup's rows: X (rows past M read as 0; their
@@ -114,20 +115,29 @@ __global__ __launch_bounds__(NW * 64) void act_kernel(const uint16_t* __restrict
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(inv_lam), 0, (NORM ? 2 : 1) * K * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(l1op), 0, static_cast<int>(static_cast<uint32_t>(K) * R * 2), 0x00020000);
-  // the 16 rows lie in one 32-row block of the code and FP4 scale layouts
+  // the workgroup's rows lie in one 32-row block of the code and FP4 scale layouts
   const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
       codes + (row0 >> 5) * (K >> 6) * 1024, 0, (K >> 6) * 1024, 0x00020000);
   // (both scale layouts give each 32-row block and 128-wide stage 128 bytes)
   const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
       static_cast<uint8_t*>(scales) + (row0 >> 5) * (K >> 7) * 128, 0, (K >> 7) * 128, 0x00020000);
-  const int r32 = static_cast<int>(row0 & 31) + row;   // the lane's row within its 32-row block
+  // the lane's row within its 32-row block, and whether it exists, per half
+  int r32[HV];
+  bool valid[HV];
+#pragma unroll
+  for (int h = 0; h < HV; h++) {
+    r32[h] = static_cast<int>(row0 & 31) + 16 * h + row;
+    valid[h] = row0 + 16 * h + row < M;
+  }
   // store offsets past the end of cr / sr: such stores write nothing
   const uint32_t c_oob = static_cast<uint32_t>(K >> 6) * 1024;
   const uint32_t s_oob = static_cast<uint32_t>(K >> 7) * 128;
 
-  f32x4 acc[LR ? RB : 1];
+  f32x4 acc[HV][LR ? RB : 1];
 #pragma unroll
-  for (int nb = 0; nb < (LR ? RB : 1); nb++) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int h = 0; h < HV; h++)
+#pragma unroll
+    for (int nb = 0; nb < (LR ? RB : 1); nb++) acc[h][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Loads are row-contiguous: load c of a lane takes the 16-byte piece l % 16
   // of row 4c + l / 16 (four whole 256-byte rows per instruction), and lane
@@ -137,43 +147,61 @@ __global__ __launch_bounds__(NW * 64) void act_kernel(const uint16_t* __restrict
   const uint32_t xoff = static_cast<uint32_t>(lrow) * rowb + piece * 16;
   const uint32_t ioff = static_cast<uint32_t>(lane & 31) * 16 + (NORM && lane >= 32 ? static_cast<uint32_t>(K) * 4 : 0u);
   // NORM: the row's mean and reciprocal standard deviation
-  float mu = 0.f, rho = 0.f;
-  if constexpr (NORM) {
-    const long sr_row = min(row0 + row, static_cast<long>(M - 1));
-    mu = rowstat[2 * sr_row];
-    rho = rowstat[2 * sr_row + 1];
+  float mu[HV], rho[HV];
+#pragma unroll
+  for (int h = 0; h < HV; h++) {
+    mu[h] = 0.f;
+    rho[h] = 0.f;
+    if constexpr (NORM) {
+      const long sr_row = min(row0 + 16 * h + row, static_cast<long>(M - 1));
+      mu[h] = rowstat[2 * sr_row];
+      rho[h] = rowstat[2 * sr_row + 1];
+    }
   }
-  // Two chunks of each wave are in flight while it processes a third: chunk
-  // it + 2 NW is requested into the registers chunk it arrived in.
+  // Two chunks of each wave are in flight while it processes a third (one
+  // with two halves): chunk it + PFD NW is requested into the registers
+  // chunk it arrived in, right after they are staged.
   const int it0 = part * cpp + wave;
   const u32x4 z4 = u32x4{0u, 0u, 0u, 0u};
-  u32x4 xa[4] = {z4, z4, z4, z4}, xb[4] = {z4, z4, z4, z4};
+  u32x4 xa[HV][4], xb[HV][4];
+#pragma unroll
+  for (int h = 0; h < HV; h++)
+#pragma unroll
+    for (int c = 0; c < 4; c++) xa[h][c] = xb[h][c] = z4;
   u32x4 ia = z4, ib = z4;
   // Every fetch is issued, also past the part's last chunk: there its offset
   // lies past the buffer's end, so it reads nothing and returns zeros.  The
   // compiler then counts the same number of loads in flight on every path and
   // its waits for the L1 operands never include a prefetch.
   const int x_oob = nrows * static_cast<int>(rowb), i_oob = (NORM ? 2 : 1) * K * 4;
-  auto fetch = [&](int c0, u32x4 (&x)[4], u32x4& iv) __attribute__((always_inline)) {
+  auto fetch = [&](int c0, u32x4 (&x)[HV][4], u32x4& iv) __attribute__((always_inline)) {
     const bool ok = c0 < c_end;
 #pragma unroll
-    for (int c = 0; c < 4; c++)
-      x[c] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, ok ? static_cast<int>(4 * c * rowb + c0 * 256) : x_oob, 0);
+    for (int h = 0; h < HV; h++)
+#pragma unroll
+      for (int c = 0; c < 4; c++)
+        x[h][c] = __builtin_amdgcn_raw_buffer_load_b128(
+            xr, xoff, ok ? static_cast<int>((16 * h + 4 * c) * rowb + c0 * 256) : x_oob, 0);
     iv = __builtin_amdgcn_raw_buffer_load_b128(ir, ioff, ok ? c0 * 512 : i_oob, 0);
   };
+  // chunks requested ahead: two (one half), or one (two halves: the same
+  // bytes in flight, half the prefetch registers)
+  constexpr int PFD = HV == 1 ? 2 : 1;
   fetch(it0, xa, ia);
-  fetch(it0 + NW, xb, ib);
-  auto body = [&](int it, u32x4 (&x)[4], u32x4& iv) __attribute__((always_inline)) {
+  if constexpr (PFD == 2) fetch(it0 + NW, xb, ib);
+  auto body = [&](int it, u32x4 (&x)[HV][4], u32x4& iv) __attribute__((always_inline)) {
     const int kb = it * 128 + kq * 32;
     // stage the chunk: piece p of row r goes to slot p ^ r of the row, so
     // that both these writes and the reads below touch 16 distinct 16-byte
     // bank groups per 16 lanes
 #pragma unroll
-    for (int c = 0; c < 4; c++) {
-      const int r = 4 * c + lrow;
-      *reinterpret_cast<u32x4*>(xs + r * 256 + ((piece ^ r) << 4)) = x[c];
-    }
-    if (NORM || lane < 32) *reinterpret_cast<u32x4*>(xs + 4096 + lane * 16) = iv;
+    for (int h = 0; h < HV; h++)
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const int r = 4 * c + lrow;
+        *reinterpret_cast<u32x4*>(xs + h * 4096 + r * 256 + ((piece ^ r) << 4)) = x[h][c];
+      }
+    if (NORM || lane < 32) *reinterpret_cast<u32x4*>(xs + 4096 * HV + lane * 16) = iv;
     // L1 operands of the chunk: one contiguous 1 KB block per (t block,
     // step), requested before the X prefetch (for up to 4 t blocks; wider
     // ranks load them next to their MFMAs).  The INT4 quantizer needs many
@@ -196,161 +224,172 @@ __global__ __launch_bounds__(NW * 64) void act_kernel(const uint16_t* __restrict
     // The X prefetch is issued after the L1 loads: vector memory counters
     // complete in issue order, so waiting for the L1 operands does not wait
     // for the prefetch.
-    fetch(it + 2 * NW, x, iv);
-    // lane (row, kq): elements kq * 32 .. + 31 of its row = pieces 4 kq .. 4 kq + 3
-    float xh[32];
+    fetch(it + PFD * NW, x, iv);
+    // each half of the workgroup's rows in turn (the L1 operands above serve both)
 #pragma unroll
-    for (int c = 0; c < 4; c++) x_hat8<NORM>(xs, ils, row, kq, c, mu, rho, xh + 8 * c);
+    for (int h = 0; h < HV; h++) {
+      // lane (row, kq): elements kq * 32 .. + 31 of its row = pieces 4 kq .. 4 kq + 3
+      float xh[32];
+#pragma unroll
+      for (int c = 0; c < 4; c++) x_hat8<NORM>(xs + h * 4096, ils, row, kq, c, mu[h], rho[h], xh + 8 * c);
 
-    // bf16 of x_hat, rounded to nearest even (v_cvt_pk_bf16_f32): the A
-    // operands of the down-projection, formed before the quantizer reuses xh
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    bf16x8 a[LR ? 4 : 1];
-    if constexpr (LR) {
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 p2 = __builtin_convertvector(f32x2{xh[8 * j + e], xh[8 * j + e + 1]}, bf16x2);
-          a[j][e] = p2[0];
-          a[j][e + 1] = p2[1];
-        }
-    }
-
-    auto down = [&]() __attribute__((always_inline)) {
+      // bf16 of x_hat, rounded to nearest even (v_cvt_pk_bf16_f32): the A
+      // operands of the down-projection, formed before the quantizer reuses xh
+      typedef float f32x2 __attribute__((ext_vector_type(2)));
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      bf16x8 a[LR ? 4 : 1];
       if constexpr (LR) {
 #pragma unroll
-        for (int nb = 0; nb < RB; nb++)
+        for (int j = 0; j < 4; j++)
 #pragma unroll
-          for (int j = 0; j < 4; j++) {
-            if constexpr (LT_EARLY) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], lt[nb][j], acc[nb], 0, 0, 0);
-            else acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], lt_load(nb, j), acc[nb], 0, 0, 0);
+          for (int e = 0; e < 8; e += 2) {
+            const bf16x2 p2 = __builtin_convertvector(f32x2{xh[8 * j + e], xh[8 * j + e + 1]}, bf16x2);
+            a[j][e] = p2[0];
+            a[j][e + 1] = p2[1];
           }
       }
-    };
-    if constexpr (MFMA_FIRST) down();
 
-    if constexpr (QUANT) {
-      float amax = 0.f;
+      auto down = [&]() __attribute__((always_inline)) {
+        if constexpr (LR) {
 #pragma unroll
-      for (int e = 0; e < 32; e++) amax = fmaxf(amax, __builtin_fabsf(xh[e]));
-      uint32_t packed[4] = {0u, 0u, 0u, 0u};
-      if constexpr (FMT == SVDQ_INT4_G64_FP16) {
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
-        // s = fp16(A / 7), saturated at the largest finite fp16 value
-        const __half sh = __float2half_rn(fminf(amax / 7.0f, 65504.0f));
-        const float s = __half2float(sh);
-        const float r = s > 0.f ? 1.0f / s : 0.f;
-        // t = x / s with one rounding (the product with the rounded
-        // reciprocal) is within 2^-20 of the exact quotient, so rint(t) is
-        // RNE(x / s) unless t lies within 2^-18 of a half-integer; a lane
-        // with such a value redoes its 32 quotients exactly.  (s = 0 gives
-        // r = 0 and all-zero codes.)
-        float dmax = 0.f;
+          for (int nb = 0; nb < RB; nb++)
 #pragma unroll
-        for (int e = 0; e < 32; e++) {
-          const float t = xh[e] * r;
-          const float q = __builtin_rintf(t);
-          dmax = fmaxf(dmax, __builtin_fabsf(t - q));
-          xh[e] = q;
+            for (int j = 0; j < 4; j++) {
+              if constexpr (LT_EARLY) acc[h][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], lt[nb][j], acc[h][nb], 0, 0, 0);
+              else acc[h][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], lt_load(nb, j), acc[h][nb], 0, 0, 0);
+            }
         }
-        if (dmax > 0.5f - 0x1p-18f) {
-          // xh holds rint(t) now: recompute x from the staged chunk
+      };
+      if constexpr (MFMA_FIRST) down();
+
+      if constexpr (QUANT) {
+        float amax = 0.f;
 #pragma unroll
-          for (int c = 0; c < 4; c++) {
-            float xv[8];
-            x_hat8<NORM>(xs, ils, row, kq, c, mu, rho, xv);
+        for (int e = 0; e < 32; e++) amax = fmaxf(amax, __builtin_fabsf(xh[e]));
+        uint32_t packed[4] = {0u, 0u, 0u, 0u};
+        if constexpr (FMT == SVDQ_INT4_G64_FP16) {
+          amax = fmaxf(amax, __shfl_xor(amax, 16));
+          // s = fp16(A / 7), saturated at the largest finite fp16 value
+          const __half sh = __float2half_rn(fminf(amax / 7.0f, 65504.0f));
+          const float s = __half2float(sh);
+          const float r = s > 0.f ? 1.0f / s : 0.f;
+          // t = x / s with one rounding (the product with the rounded
+          // reciprocal) is within 2^-20 of the exact quotient, so rint(t) is
+          // RNE(x / s) unless t lies within 2^-18 of a half-integer; a lane
+          // with such a value redoes its 32 quotients exactly.  (s = 0 gives
+          // r = 0 and all-zero codes.)
+          float dmax = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; e++) xh[8 * c + e] = rne_quotient(xv[e], s, r);
+          for (int e = 0; e < 32; e++) {
+            const float t = xh[e] * r;
+            const float q = __builtin_rintf(t);
+            dmax = fmaxf(dmax, __builtin_fabsf(t - q));
+            xh[e] = q;
           }
-        }
-        // codes (sign-magnitude, the E4M3 bits of q * 2^-9; the format's
-        // word layout): the hardware conversion of clamp(q, -7, 7) / 2^9
-        // (exact: |q| <= 7 are E4M3 subnormals), zeros made +0, then the
-        // bytes of codes 4-7 of each word rotated left by 4 bits over those
-        // of codes 0-3
+          if (dmax > 0.5f - 0x1p-18f) {
+            // xh holds rint(t) now: recompute x from the staged chunk
 #pragma unroll
-        for (int w = 0; w < 4; w++) {
-          uint32_t d[2];
+            for (int c = 0; c < 4; c++) {
+              float xv[8];
+              x_hat8<NORM>(xs + h * 4096, ils, row, kq, c, mu[h], rho[h], xv);
 #pragma unroll
-          for (int h = 0; h < 2; h++) {
-            const float* qv = xh + 8 * w + 4 * h;
-            fp8x2 v = {0, 0};
-            v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v, __builtin_amdgcn_fmed3f(qv[0], -7.0f, 7.0f),
-                                                         __builtin_amdgcn_fmed3f(qv[1], -7.0f, 7.0f), 512.0f, false);
-            v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v, __builtin_amdgcn_fmed3f(qv[2], -7.0f, 7.0f),
-                                                         __builtin_amdgcn_fmed3f(qv[3], -7.0f, 7.0f), 512.0f, true);
-            d[h] = e4m3_plus_zero(__builtin_bit_cast(uint32_t, v));
+              for (int e = 0; e < 8; e++) xh[8 * c + e] = rne_quotient(xv[e], s, r);
+            }
           }
-          packed[w] = d[0] | __builtin_amdgcn_alignbit(d[1], d[1], 28);
-        }
-        // INT4 scale block order within the 32-row block (the 4-byte word of
-        // row r32 holds the stage's two groups); rows past M and the odd lane
-        // of each pair store past the buffer's end: no write
-        __builtin_amdgcn_raw_buffer_store_b16(
-            __half_as_ushort(sh), sr,
-            valid && (kq & 1) == 0 ? static_cast<uint32_t>((kb >> 7) * 128 + r32 * 4 + ((kb >> 6) & 1) * 2) : s_oob, 0, 0);
-      } else {
-        // E2M1 of x / 2^ex, rounded to nearest even by the conversion
-        // instruction (|x / 2^ex| <= 6 by the choice of ex), two codes per
-        // instruction into byte e / 2 % 4 of word e / 8.  Groups whose scale
-        // is below 2^-120 (absmax under ~5e-36, all-zero groups included)
-        // take the exact bit-level rounding instead, so that no denormal
-        // scale or input reaches the conversion.
-        const int ex = e8m0_exponent(amax);
-        if (ex >= -120) {
-          const float sc = __builtin_amdgcn_ldexpf(1.0f, ex);
+          // codes (sign-magnitude, the E4M3 bits of q * 2^-9; the format's
+          // word layout): the hardware conversion of clamp(q, -7, 7) / 2^9
+          // (exact: |q| <= 7 are E4M3 subnormals), zeros made +0, then the
+          // bytes of codes 4-7 of each word rotated left by 4 bits over those
+          // of codes 0-3
 #pragma unroll
           for (int w = 0; w < 4; w++) {
-            uint32_t v = 0u;
-            v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, xh[8 * w + 0], xh[8 * w + 1], sc, 0);
-            v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, xh[8 * w + 2], xh[8 * w + 3], sc, 1);
-            v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, xh[8 * w + 4], xh[8 * w + 5], sc, 2);
-            v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, xh[8 * w + 6], xh[8 * w + 7], sc, 3);
-            packed[w] = e2m1_plus_zero(v);
-          }
-        } else {
+            uint32_t d[2];
 #pragma unroll
-          for (int e = 0; e < 32; e++)
-            packed[e >> 3] |= e2m1_code(__builtin_amdgcn_ldexpf(xh[e], -ex)) << (4 * (e & 7));
+            for (int h = 0; h < 2; h++) {
+              const float* qv = xh + 8 * w + 4 * h;
+              fp8x2 v = {0, 0};
+              v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v, __builtin_amdgcn_fmed3f(qv[0], -7.0f, 7.0f),
+                                                           __builtin_amdgcn_fmed3f(qv[1], -7.0f, 7.0f), 512.0f, false);
+              v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v, __builtin_amdgcn_fmed3f(qv[2], -7.0f, 7.0f),
+                                                           __builtin_amdgcn_fmed3f(qv[3], -7.0f, 7.0f), 512.0f, true);
+              d[h] = e4m3_plus_zero(__builtin_bit_cast(uint32_t, v));
+            }
+            packed[w] = d[0] | __builtin_amdgcn_alignbit(d[1], d[1], 28);
+          }
+          // INT4 scale block order within the 32-row block (the 4-byte word of
+          // row r32[h] holds the stage's two groups); rows past M and the odd lane
+          // of each pair store past the buffer's end: no write
+          __builtin_amdgcn_raw_buffer_store_b16(
+              __half_as_ushort(sh), sr,
+              valid[h] && (kq & 1) == 0 ? static_cast<uint32_t>((kb >> 7) * 128 + r32[h] * 4 + ((kb >> 6) & 1) * 2) : s_oob, 0, 0);
+        } else {
+          // E2M1 of x / 2^ex, rounded to nearest even by the conversion
+          // instruction (|x / 2^ex| <= 6 by the choice of ex), two codes per
+          // instruction into byte e / 2 % 4 of word e / 8.  Groups whose scale
+          // is below 2^-120 (absmax under ~5e-36, all-zero groups included)
+          // take the exact bit-level rounding instead, so that no denormal
+          // scale or input reaches the conversion.
+          const int ex = e8m0_exponent(amax);
+          if (ex >= -120) {
+            const float sc = __builtin_amdgcn_ldexpf(1.0f, ex);
+#pragma unroll
+            for (int w = 0; w < 4; w++) {
+              uint32_t v = 0u;
+              v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, xh[8 * w + 0], xh[8 * w + 1], sc, 0);
+              v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, xh[8 * w + 2], xh[8 * w + 3], sc, 1);
+              v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, xh[8 * w + 4], xh[8 * w + 5], sc, 2);
+              v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, xh[8 * w + 6], xh[8 * w + 7], sc, 3);
+              packed[w] = e2m1_plus_zero(v);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 32; e++)
+              packed[e >> 3] |= e2m1_code(__builtin_amdgcn_ldexpf(xh[e], -ex)) << (4 * (e & 7));
+          }
+          // FP4 scale block order within the 32-row block (fp4_scale_offset)
+          __builtin_amdgcn_raw_buffer_store_b8(
+              static_cast<uint8_t>(ex + 127), sr,
+              valid[h] ? static_cast<uint32_t>((kb >> 7) * 128 + (r32[h] + 32 * ((kb >> 5) & 1)) * 2 + ((kb >> 6) & 1)) : s_oob, 0, 0);
         }
-        // FP4 scale block order within the 32-row block (fp4_scale_offset)
-        __builtin_amdgcn_raw_buffer_store_b8(
-            static_cast<uint8_t>(ex + 127), sr,
-            valid ? static_cast<uint32_t>((kb >> 7) * 128 + (r32 + 32 * ((kb >> 5) & 1)) * 2 + ((kb >> 6) & 1)) : s_oob, 0, 0);
+        // code block order within the 32-row block (code_chunk_offset)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{packed[0], packed[1], packed[2], packed[3]}, cr,
+            valid[h] ? static_cast<uint32_t>((kb >> 6) * 1024 + (r32[h] + 32 * ((kb >> 5) & 1)) * 16) : c_oob, 0, 0);
       }
-      // code block order within the 32-row block (code_chunk_offset)
-      __builtin_amdgcn_raw_buffer_store_b128(
-          u32x4{packed[0], packed[1], packed[2], packed[3]}, cr,
-          valid ? static_cast<uint32_t>((kb >> 6) * 1024 + (r32 + 32 * ((kb >> 5) & 1)) * 16) : c_oob, 0, 0);
-    }
 
-    if constexpr (!MFMA_FIRST) down();
+      if constexpr (!MFMA_FIRST) down();
+    }
   };
   int it = it0;
-  for (; it + NW < c_end; it += 2 * NW) {
-    body(it, xa, ia);
-    body(it + NW, xb, ib);
+  if constexpr (PFD == 2) {
+    for (; it + NW < c_end; it += 2 * NW) {
+      body(it, xa, ia);
+      body(it + NW, xb, ib);
+    }
+    if (it < c_end) body(it, xa, ia);
+  } else {
+    for (; it < c_end; it += NW) body(it, xa, ia);
   }
-  if (it < c_end) body(it, xa, ia);
 
   if constexpr (LR) {
-    // acc[nb][v] is this wave's partial T[4 * kq + v][nb * 16 + (lane & 15)];
-    // the staging memory is reused once every wave has left the loop
+    // acc[h][nb][v] is this wave's partial T[16 h + 4 kq + v][nb * 16 +
+    // (lane & 15)]; the staging memory is reused once every wave has left
+    // the loop
     float* red = reinterpret_cast<float*>(lds);
     __syncthreads();
 #pragma unroll
-    for (int nb = 0; nb < RB; nb++)
+    for (int h = 0; h < HV; h++)
 #pragma unroll
-      for (int v = 0; v < 4; v++) red[(wave * 16 + 4 * kq + v) * R + nb * 16 + row] = acc[nb][v];
+      for (int nb = 0; nb < RB; nb++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) red[((wave * HV + h) * 16 + 4 * kq + v) * R + nb * 16 + row] = acc[h][nb][v];
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 16 * R; idx += NW * 64) {
+    for (int idx = threadIdx.x; idx < 16 * HV * R; idx += NW * 64) {
       const int rr = idx / R, t = idx % R;
       float s = red[rr * R + t];
 #pragma unroll
-      for (int w = 1; w < NW; w++) s += red[(w * 16 + rr) * R + t];
-      const long gr = static_cast<long>(rblk) * 16 + rr;
+      for (int w = 1; w < NW; w++) s += red[(w * 16 * HV + rr) * R + t];
+      const long gr = row0 + rr;
       if (gr < M) {
         if (kparts == 1) Tb[bf16_block_index(gr, t, R)] = static_cast<uint16_t>(f32_to_bf16_bits(s));
         else tpart[(static_cast<long>(part) * M + gr) * R + t] = s;
@@ -429,9 +468,22 @@ static hipError_t launch_act_rb(int rb, const ActArgs& a, hipStream_t st) {
   const long nrb = (a.M + 15) / 16, cus = device_cu_count();
   const bool wide = DOWN && rb > 0 && nrb >= cus && nrb <= 2 * cus && (a.K >> 7) <= 32;
   if (wide) kparts = 1;
-  dim3 grid(static_cast<unsigned>(nrb * kparts)), block(wide ? 512 : 256);
+  // More row blocks than CUs: 32-row workgroups instead (one round; each L1
+  // operand load serves both halves, so the busiest CU moves a third fewer
+  // bytes than with two 16-row blocks).  Without the norm and up to rank
+  // 32: the other forms do not fit the registers twice.
+  constexpr bool PAIR_OK = !NORM;
+  const bool pair = PAIR_OK && wide && nrb > cus && rb <= 2;
+  dim3 grid(static_cast<unsigned>(pair ? (nrb + 1) / 2 : nrb * kparts)), block(wide ? 512 : 256);
 #define SVDQ_ACT_CASE(RBV)                                                                                        \
   case RBV:                                                                                                     \
+    if constexpr (PAIR_OK) {                                                                                    \
+      if (pair) {                                                                                               \
+        hipLaunchKernelGGL((act_kernel<FMT, QUANT, DOWN, (RBV <= 2 ? RBV : 2), NORM, 8, 2>), grid, block, 0, st, \
+                           a.X, a.M, a.K, a.inv_lam, a.rowstat, a.l1t, a.codes, a.scales, a.Tb, kparts, a.tpart); \
+        break;                                                                                                  \
+      }                                                                                                         \
+    }                                                                                                           \
     if (wide)                                                                                                   \
       hipLaunchKernelGGL((act_kernel<FMT, QUANT, DOWN, RBV, NORM, 8>), grid, block, 0, st, a.X, a.M, a.K, a.inv_lam, \
                          a.rowstat, a.l1t, a.codes, a.scales, a.Tb, kparts, a.tpart);                           \

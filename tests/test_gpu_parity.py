@@ -421,18 +421,20 @@ E2M1_MIDPOINTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
 
 
 @pytest.mark.parametrize("fmt", [O.INT4, O.FP4])
-def test_norm_fused_pass(torch_dev, fmt):
+@pytest.mark.parametrize("M,K,N", [(300, 384, 320), (4608, 256, 128)])
+def test_norm_fused_pass(torch_dev, fmt, M, K, N):
     """The LayerNorm-fused activation pass and layer against the oracle's
     norm path.  x_hat comes from fp32 row statistics, so it may differ from
     the oracle's by a few fp32 ulps: scales must be equal except in groups
     whose absmax sits within 1e-5 of a scale rounding boundary, and in every
     other group the codes must be equal except for elements within 1e-4 of a
     rounding tie (where either neighbour is right); T within 2 bf16 ulps; Y to
-    the usual tolerance."""
+    the usual tolerance.  At M = 4608 the pass runs 8-wave workgroups over
+    whole row blocks (FP4: 32-row blocks of two halves)."""
     import w4a4_quantized_gemm_amd as S
     torch, dev = torch_dev
-    _say(f"case: norm-fused pass fmt={fmt}")
-    M, K, N, r, eps = 300, 384, 320, 16, 1e-5
+    _say(f"case: norm-fused pass fmt={fmt} M={M} K={K} N={N}")
+    r, eps = 16, 1e-5
     cfg = WL.C2.with_(name="norm", M=M, K=K, N=N, rank=r, fmt=fmt, w_std=1 / np.sqrt(K),
                       n_outlier_channels=8, bias_std=0.02, seed=91)
     X_bits, W_bits, b_bits = WL.make_layer(cfg)
@@ -485,7 +487,20 @@ def test_norm_fused_pass(torch_dev, fmt):
         Tg = O.bf16_bits_to_f64(untile_bf16(u16_tensor_to_np(T), M, r))
         _, Tref = O.down_proj(qa["xhat"], ref["L1b"])
         ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(Tref), 1e-30))) - 7)
-        assert np.all(np.abs(Tg - Tref) <= 2 * ulp * 1.0001)
+        # T's bound: 2 bf16 ulps (x_hat from fp32 row statistics), plus the
+        # fp32 summation's K 2^-24 sum|products|, plus one bf16 ulp of x_hat
+        # times |L1| for every x_hat within 2^-20 (relative) of a bf16
+        # rounding midpoint, where the kernel's x_hat, a few fp32 ulps away,
+        # may round the other way; the last two terms matter only where T
+        # cancels
+        xh64 = qa["xhat"]
+        xb16 = O.to_bf16(xh64)
+        u16 = np.exp2(np.floor(np.log2(np.maximum(np.abs(xh64), 1e-30))) - 7)
+        near = np.abs(np.abs(xh64 - xb16) - u16 / 2) <= 2.0 ** -20 * np.abs(xh64)
+        L1a = np.abs(ref["L1b"])
+        bound = 2 * ulp + K * 2.0 ** -24 * (np.abs(xb16) @ L1a) + (near * u16) @ L1a
+        excess = np.abs(Tg - Tref) / bound
+        assert np.all(excess <= 1.0001), (float(excess.max()), int((excess > 1.0001).sum()))
         for out in (S.OUT_BF16, S.OUT_F32):
             oname = "bf16" if out == S.OUT_BF16 else "f32"
             Y = layer(X, out_dtype=out, norm=(gamma, beta_t, eps))

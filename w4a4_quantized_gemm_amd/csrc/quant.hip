@@ -470,9 +470,9 @@ static hipError_t launch_act_rb(int rb, const ActArgs& a, hipStream_t st) {
   if (wide) kparts = 1;
   // More row blocks than CUs: 32-row workgroups instead (one round; each L1
   // operand load serves both halves, so the busiest CU moves a third fewer
-  // bytes than with two 16-row blocks).  Without the norm and up to rank
-  // 32: the other forms do not fit the registers twice.
-  constexpr bool PAIR_OK = !NORM;
+  // bytes than with two 16-row blocks).  Up to rank 32, and not for the
+  // INT4 norm-fused form: those do not fit the registers twice.
+  constexpr bool PAIR_OK = !(NORM && FMT == SVDQ_INT4_G64_FP16);
   const bool pair = PAIR_OK && wide && nrb > cus && rb <= 2;
   dim3 grid(static_cast<unsigned>(pair ? (nrb + 1) / 2 : nrb * kparts)), block(wide ? 512 : 256);
 #define SVDQ_ACT_CASE(RBV)                                                                                        \

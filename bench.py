@@ -20,7 +20,8 @@ layer, the unfused layer and the two kernels of the fused layer one after
 the other, each call timed with HIP events on its stream, and the medians,
 10th and 90th percentiles of those per-call times give the kernel times,
 the rooflines and the fused-versus-unfused speedup (interleaving keeps the
-variants on the same clock and cache state).
+variants on the same clock; every call, whatever its variant, takes the next
+buffer set, so none rereads what the call before it left in the cache).
 
 Printed: one JSON line with the effective TOPS of the layer (2 M K N per
 layer time), the kernel roofline of the dominant kernel (the 4-bit GEMM),
@@ -228,7 +229,11 @@ GATE_CYCLES = 200_000     # a short busy kernel ahead of every timed call (see i
 def interleaved(torch, variants, rounds, gate=False):
     """`rounds` rounds, each calling every variant once in order, each call
     bracketed by events on the current stream; returns the per-call times
-    (ms) of every variant.  Where a round's GPU work is long the host runs
+    (ms) of every variant.  Each call gets the running call count as its
+    index, so consecutive calls work on different buffer sets: no variant
+    finds the previous call's inputs in the Infinity Cache (with the round
+    as the index, every variant after a round's first would reread the
+    buffers that the first had just pulled in).  Where a round's GPU work is long the host runs
     ahead and the events time the launches on the GPU.  For calls of a few
     microseconds (gate=True) a fixed-length busy kernel (torch.cuda._sleep)
     runs ahead of each bracket, so the host has enqueued the call's launches
@@ -236,13 +241,14 @@ def interleaved(torch, variants, rounds, gate=False):
     to back, not the host's launch overhead."""
     evs = {name: [] for name, _ in variants}
     sleep = getattr(torch.cuda, "_sleep", None) if gate else None
+    nv = len(variants)
     for k in range(rounds):
-        for name, fn in variants:
+        for v, (name, fn) in enumerate(variants):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             if sleep is not None:
                 sleep(GATE_CYCLES)
             e0.record()
-            fn(k)
+            fn(k * nv + v)
             e1.record()
             evs[name].append((e0, e1))
     torch.cuda.synchronize()
@@ -250,10 +256,10 @@ def interleaved(torch, variants, rounds, gate=False):
 
 
 def layer_fns(S, rig):
-    """The timed calls on a rig (each takes the round index, which picks the
+    """The timed calls on a rig (each takes a call index, which picks the
     buffer set): fused layer, unfused layer, and the fused layer's two
     launches on their own (activation pass, GEMM), which read and write the
-    same buffers as one svdq_linear call."""
+    buffers of one svdq_linear call."""
     d = rig.layer.desc
     n = rig.nsets
     M = rig.cfg.M
@@ -538,6 +544,8 @@ def summarize_trace(trace_dir, name, kind):
                   "GEMM with the slab), unfused calls (quantize-only and down-only activation passes, the",
                   "GEMM without the slab, up_kernel) and split calls (quantize_act + gemm), interleaved, so",
                   "the fused path's kernels appear twice as often.  Durations in microseconds."]
+    lines += ["Every timed call works on the next of several buffer copies (together over twice the",
+              "256 MB Infinity Cache), so no call finds its inputs left in the cache by the call before."]
     lines += ["", f"{'kernel':92s} {'calls':>6} {'avg':>9} {'min':>9} {'max':>9}"]
     for r in rows:
         lines.append(f"{r['Name'][:92]:92s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.1f} "

@@ -421,16 +421,20 @@ E2M1_MIDPOINTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
 
 
 @pytest.mark.parametrize("fmt", [O.INT4, O.FP4])
-@pytest.mark.parametrize("M,K,N", [(300, 384, 320), (4608, 256, 128)])
+@pytest.mark.parametrize("M,K,N", [(300, 384, 320), (4608, 256, 128), (64, 3072, 128), (40, 12288, 64), (32, 16384, 64),
+                                    (24, 20480, 64)])
 def test_norm_fused_pass(torch_dev, fmt, M, K, N):
     """The LayerNorm-fused activation pass and layer against the oracle's
     norm path.  x_hat comes from fp32 row statistics, so it may differ from
     the oracle's by a few fp32 ulps: scales must be equal except in groups
     whose absmax sits within 1e-5 of a scale rounding boundary, and in every
     other group the codes must be equal except for elements within 1e-4 of a
-    rounding tie (where either neighbour is right); T within 2 bf16 ulps; Y to
-    the usual tolerance.  At M = 4608 the pass runs 8-wave workgroups over
-    whole row blocks (FP4: 32-row blocks of two halves)."""
+    rounding tie (where either neighbour is right); T within 2 bf16 ulps plus
+    the fp32 sum's error and the flips of x_hat's bf16 rounding next to a
+    midpoint; Y to the usual tolerance.  At M = 4608 the pass runs 8-wave
+    workgroups over whole row blocks (FP4: 32-row blocks of two halves); the
+    K values take the row statistics' register-held forms (2, 6, 24 and 32
+    vectors per lane) and the streamed one (K = 20480)."""
     import w4a4_quantized_gemm_amd as S
     torch, dev = torch_dev
     _say(f"case: norm-fused pass fmt={fmt} M={M} K={K} N={N}")

@@ -529,10 +529,27 @@ hipError_t launch_act(int fmt, bool quant, bool down, const ActArgs& a, hipStrea
 
 // Row statistics of the norm-fused pass: blocks below ceil(M / 4) give each
 // wave one row: mu = (sum x) / K and rho = 1 / sqrt((sum (x - mu)^2) / K + eps),
-// fp32 sums of 16-byte loads per lane in a fixed order, then a fixed
-// butterfly across the wave; the remaining blocks fold the smoothing into the
-// norm's affine: gamma'[k] = gamma[k] * inv_lambda[k], beta'[k] = beta[k] *
-// inv_lambda[k] (beta = 0 when absent), each rounded once to fp32.
+// fp32 sums over the 16-byte vectors lane, lane + 64, ... of each lane, in
+// that order, then a fixed butterfly across the wave; the remaining blocks
+// fold the smoothing into the norm's affine: gamma'[k] = gamma[k] *
+// inv_lambda[k], beta'[k] = beta[k] * inv_lambda[k] (beta = 0 when absent),
+// each rounded once to fp32.  With NV > 0 (K <= 512 NV) a lane holds its NV
+// vectors of the row in registers: every load of the row is issued at once
+// and X is read from HBM once; NV = 0 streams the row twice (any K).
+__device__ __forceinline__ float vsum8(const u32x4 v) {
+  return bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) + bf16_lo(v.z) + bf16_hi(v.z) + bf16_lo(v.w) +
+         bf16_hi(v.w);
+}
+
+__device__ __forceinline__ float vdev8(const u32x4 v, float mu, float q) {
+  const float d[8] = {bf16_lo(v.x) - mu, bf16_hi(v.x) - mu, bf16_lo(v.y) - mu, bf16_hi(v.y) - mu,
+                      bf16_lo(v.z) - mu, bf16_hi(v.z) - mu, bf16_lo(v.w) - mu, bf16_hi(v.w) - mu};
+#pragma unroll
+  for (int e = 0; e < 8; e++) q = __builtin_fmaf(d[e], d[e], q);
+  return q;
+}
+
+template <int NV>
 __global__ __launch_bounds__(256) void norm_stats_kernel(const uint16_t* __restrict__ X, int M, int K, float eps,
                                                          const uint16_t* __restrict__ gamma,
                                                          const uint16_t* __restrict__ beta,
@@ -553,27 +570,34 @@ __global__ __launch_bounds__(256) void norm_stats_kernel(const uint16_t* __restr
   if (r >= M) return;
   const u32x4* xr = reinterpret_cast<const u32x4*>(X + r * K);
   const int nv = K / 8;                          // 16-byte vectors per row
-  float s = 0.f;
-  for (int i = lane; i < nv; i += 64) {
-    const u32x4 v = xr[i];
-    s += bf16_lo(v.x) + bf16_hi(v.x) + bf16_lo(v.y) + bf16_hi(v.y) + bf16_lo(v.z) + bf16_hi(v.z) + bf16_lo(v.w) +
-         bf16_hi(v.w);
-  }
+  float s = 0.f, q = 0.f;
+  if constexpr (NV > 0) {
+    u32x4 v[NV];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-  const float mu = s / static_cast<float>(K);
-  float q = 0.f;
-  for (int i = lane; i < nv; i += 64) {
-    const u32x4 v = xr[i];
-    const float d[8] = {bf16_lo(v.x) - mu, bf16_hi(v.x) - mu, bf16_lo(v.y) - mu, bf16_hi(v.y) - mu,
-                        bf16_lo(v.z) - mu, bf16_hi(v.z) - mu, bf16_lo(v.w) - mu, bf16_hi(v.w) - mu};
+    for (int j = 0; j < NV; j++) {
+      const int i = lane + 64 * j;
+      v[j] = i < nv ? xr[i] : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-    for (int e = 0; e < 8; e++) q = __builtin_fmaf(d[e], d[e], q);
+    for (int j = 0; j < NV; j++)
+      if (lane + 64 * j < nv) s += vsum8(v[j]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+    const float mu = s / static_cast<float>(K);
+#pragma unroll
+    for (int j = 0; j < NV; j++)
+      if (lane + 64 * j < nv) q = vdev8(v[j], mu, q);
+  } else {
+    for (int i = lane; i < nv; i += 64) s += vsum8(xr[i]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+    const float mu = s / static_cast<float>(K);
+    for (int i = lane; i < nv; i += 64) q = vdev8(xr[i], mu, q);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) q += __shfl_xor(q, o);
   if (lane == 0) {
-    rowstat[2 * r] = mu;
+    rowstat[2 * r] = s / static_cast<float>(K);
     rowstat[2 * r + 1] = 1.0f / __builtin_sqrtf(q / static_cast<float>(K) + eps);
   }
 }
@@ -581,8 +605,19 @@ __global__ __launch_bounds__(256) void norm_stats_kernel(const uint16_t* __restr
 hipError_t launch_norm_stats(const uint16_t* X, int M, int K, float eps, const uint16_t* gamma, const uint16_t* beta,
                              const float* inv_lam, float* rowstat, float* fold, hipStream_t st) {
   const int blocks = (M + 3) / 4 + (K + 255) / 256;
-  hipLaunchKernelGGL(norm_stats_kernel, dim3(blocks), dim3(256), 0, st, X, M, K, eps, gamma, beta, inv_lam, rowstat,
-                     fold);
+  const int per_lane = (K / 8 + 63) / 64;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), 0, st, X, M, K, eps, gamma, beta, inv_lam, rowstat, fold);
+  };
+  if (per_lane <= 2) go(norm_stats_kernel<2>);
+  else if (per_lane <= 4) go(norm_stats_kernel<4>);
+  else if (per_lane <= 6) go(norm_stats_kernel<6>);
+  else if (per_lane <= 8) go(norm_stats_kernel<8>);
+  else if (per_lane <= 12) go(norm_stats_kernel<12>);
+  else if (per_lane <= 16) go(norm_stats_kernel<16>);
+  else if (per_lane <= 24) go(norm_stats_kernel<24>);
+  else if (per_lane <= 32) go(norm_stats_kernel<32>);
+  else go(norm_stats_kernel<0>);
   return hipGetLastError();
 }
 

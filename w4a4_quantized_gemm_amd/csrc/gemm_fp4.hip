@@ -576,16 +576,28 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
       else make_desc(mb0, nb0, seq, S - 1, true, d, o);
       run(oa, sx, sw, G, F_AHEAD - RS, d, o, ~0u, std::false_type{}, HALF);
     } else {
-      // any shape: a descriptor per stage
-#pragma unroll 1
-      for (int st = 0; st < S; st++) {
+      // any shape: a descriptor per stage; the low-rank stages and the FP4
+      // stages in loops of their own, so that each loop body holds one kind
+      // of stage (one body with both kept both sets of operands live and
+      // spilled)
+      auto stage_desc = [&](int st) __attribute__((always_inline)) {
         const int cg = st + F_AHEAD;
         const bool c_next = cg >= S;
         const bool hs = !c_next || has;
         const int cst = !hs ? S - 1 : (c_next ? cg - S : cg);
         make_desc(c_next && hs ? nmb0 : mb0, c_next && hs ? nnb0 : nb0, c_next && hs ? seq + 1 : seq, cst, !hs, d, o);
-        if (SLAB && st < RS) run(oa, sx, sw, G, 1, d, o, st == RS - 1 ? last_mask : ~0u, std::true_type{}, HALF);
-        else run(oa, sx, sw, G, 1, d, o, ~0u, std::false_type{}, HALF);
+      };
+      if constexpr (SLAB) {
+#pragma unroll 1
+        for (int st = 0; st < RS; st++) {
+          stage_desc(st);
+          run(oa, sx, sw, G, 1, d, o, st == RS - 1 ? last_mask : ~0u, std::true_type{}, HALF);
+        }
+      }
+#pragma unroll 1
+      for (int st = SLAB ? RS : 0; st < S; st++) {
+        stage_desc(st);
+        run(oa, sx, sw, G, 1, d, o, ~0u, std::false_type{}, HALF);
       }
     }
     epilogue(mb0, nb0, G - 1, HALF);

@@ -278,7 +278,8 @@ def layer_fns(S, rig):
 
     def gemm(k):
         s = rig.sets[k % n]
-        S.svdq_gemm(d, s["blob"], s["codes"], s["scales"], s["T"] if d.rank else None, M, s["Y"], S.OUT_BF16)
+        S.svdq_gemm(d, s["blob"], s["codes"], s["scales"], s["T"] if d.rank else None, M, s["Y"], S.OUT_BF16,
+                    s["ws"])
 
     return fused, unfused, quant, gemm
 

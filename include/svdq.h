@@ -155,8 +155,12 @@ size_t svdq_prepared_bytes(const svdq_layer_desc* desc);
  * the packed activation codes (ceil(M/32)*32 x K/2 bytes), the scales, the
  * bf16 down-projection (ceil(M/32)*32 x rank) and, for M <= 16384, room for
  * the fp32 partial down-projections of a K-split activation pass
- * (8 x M x rank x 4 bytes); 0 if arguments are invalid.  Every section is
- * written before it is read, so one workspace serves any layer and M. */
+ * (8 x M x rank x 4 bytes); for INT4 layers whose M x N output has at most
+ * 128 tiles of 128 x 128, a last, optional 16 MiB for the fp32 partial
+ * tiles of a K-split GEMM (a workspace that ends before it is accepted and
+ * runs the GEMM unsplit, so a workspace sized for a larger M still serves a
+ * smaller one); 0 if arguments are invalid.  Every section is written
+ * before it is read, so one workspace serves any layer and M. */
 size_t svdq_workspace_bytes(const svdq_layer_desc* desc, int M, int unfused);
 
 /* Byte sizes of svdq_quantize_act's three outputs for M tokens (codes,
@@ -319,10 +323,13 @@ svdq_status svdq_linear_w4a16(const svdq_layer_desc* desc, const void* d_prepare
  * (d_codes, d_scales, d_T in its output layouts; d_T may be NULL when
  * rank == 0).  svdq_linear is svdq_quantize_act followed by this call; the
  * split lets a caller time, overlap or reorder the two stages.
- * Asynchronous. */
+ * d_workspace (optional, NULL allowed): a buffer of ws_bytes >=
+ * svdq_workspace_bytes(desc, M, 0) bytes; only its last section (the
+ * partial tiles of a K-split INT4 GEMM) is used, so without it, or without
+ * that section, the GEMM runs unsplit.  Asynchronous. */
 svdq_status svdq_gemm(const svdq_layer_desc* desc, const void* d_prepared, const void* d_codes,
                       const void* d_scales, const void* d_T, int M, void* d_Y, int out_dtype,
-                      void* stream);
+                      void* d_workspace, size_t ws_bytes, void* stream);
 
 /* The same layer computed the naive way, as separate kernels (walkthrough,
  * Nunchaku section: a separately run low-rank branch re-reads the 16-bit

@@ -146,7 +146,11 @@ def test_runtime_validation_before_device():
     assert w16(ctypes.byref(d), good, good, 4, good, 0, good, ws, None) == 2
     assert w16(ctypes.byref(d0), good, good, 17, good, 0, good, S.svdq_workspace_bytes(d0, 17), None) == 2
     assert w16(ctypes.byref(d0), good, good, 16, None, 0, good, ws0, None) == 1
-    assert w16(ctypes.byref(d0), good, good, 16, good, 0, good, ws0 - 1, None) == 4
+    # (the last 16 MiB, the partial tiles of a K-split GEMM of this INT4 layer
+    # with 72 output tiles at 16 rows, are optional)
+    split = 256 * 128 * 128 * 4
+    assert w16(ctypes.byref(d0), good, good, 16, good, 0, good, ws0 - split - 1, None) == 4
+    assert w16(ctypes.byref(d0), good, good, 16, good, 0, good, ws0 - split, None) != 4
     # the norm-fused calls: gamma required, eps > 0 and finite, workspace required
     ln = lib.svdq_linear_ln
     assert ln(ctypes.byref(d), good, good, None, None, 1e-5, 4608, good, 0, good, ws, None) == 1

@@ -233,6 +233,65 @@ def test_small_shapes(torch_dev, M, K, N, rank, bias, fmt):
     _check_linear(torch_dev, layer, X, X_bits, ref)
 
 
+@pytest.mark.parametrize("M,K,N,rank", [(100, 2048, 384, 32), (300, 1536, 256, 16)])
+def test_int4_gemm_k_split(torch_dev, M, K, N, rank):
+    """INT4 layers with few output tiles split the GEMM's K over workgroups
+    (fp32 partial tiles in the workspace's last section, added in part
+    order with the bias by a second kernel).  With the full workspace the
+    split runs; with a workspace that ends before that optional section the
+    GEMM runs unsplit.  Both match the oracle within the layer's tolerance,
+    in both output types and in the unfused path, and both are
+    deterministic (a repeated call is bit-equal)."""
+    import w4a4_quantized_gemm_amd as S
+    torch, dev = torch_dev
+    _say(f"case: INT4 GEMM K split M={M} K={K} N={N} r={rank}")
+    cfg = WL.C2.with_(name="ksplit", M=M, K=K, N=N, rank=rank, fmt=O.INT4, w_std=1 / np.sqrt(K),
+                      bias_std=0.02, seed=M + K)
+    X_bits, W_bits, b_bits = WL.make_layer(cfg)
+    layer, X, _ = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
+    sec, ref = _check_weights(layer, W_bits, O.INT4, b_bits, X_bits=X_bits, alpha=cfg.alpha)
+    full = S.svdq_workspace_bytes(layer.desc, M)
+    split_bytes = 256 * 128 * 128 * 4
+    ys = {}
+    for ws_bytes in (full, full - split_bytes):
+        ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+        for out in (S.OUT_BF16, S.OUT_F32):
+            oname = "bf16" if out == S.OUT_BF16 else "f32"
+            dt = torch.bfloat16 if out == S.OUT_BF16 else torch.float32
+            for unfused in (False, True):
+                fn = S.svdq_linear_unfused if unfused else S.svdq_linear
+                Y = torch.empty((M, N), dtype=dt, device=dev)
+                fn(layer.desc, layer.blob, X, Y, ws, out)
+                Y2 = torch.full((M, N), float("nan"), dtype=dt, device=dev)
+                fn(layer.desc, layer.blob, X, Y2, ws, out)
+                torch.cuda.synchronize()
+                assert torch.equal(Y, Y2), "repeated call differs"
+                Yn = Y.float().cpu().numpy().astype(np.float64)
+                refY = (O.linear_unfused if unfused else O.linear)(ref, X_bits, oname)["Y"]
+                e = O.rel_fro(Yn, refY)
+                _say(f"  ws={'full' if ws_bytes == full else 'no split section'} {oname} unfused={unfused}: rel err {e:.2e}")
+                assert np.all(np.isfinite(Yn)) and e <= TOL, e
+                ys[(ws_bytes == full, oname, unfused)] = Yn
+    # split and unsplit differ only in the fp32 summation order of the K parts
+    for oname in ("bf16", "f32"):
+        for unfused in (False, True):
+            assert O.rel_fro(ys[(True, oname, unfused)], ys[(False, oname, unfused)]) <= 1e-3
+    # the GEMM stage on its own: with the workspace it splits as svdq_linear
+    # does (bit-equal), without it it runs unsplit (bit-equal to the
+    # truncated-workspace layer)
+    ws = torch.zeros(full, dtype=torch.uint8, device=dev)
+    cb, sb, tb = S.svdq_act_sizes(layer.desc, M)
+    codes = torch.empty(cb, dtype=torch.uint8, device=dev)
+    scales = torch.empty(sb, dtype=torch.uint8, device=dev)
+    T = torch.empty(tb // 2, dtype=torch.bfloat16, device=dev)
+    S.svdq_quantize_act(layer.desc, layer.blob, X, codes, scales, T, ws)
+    for wsarg, key in ((ws, True), (None, False)):
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        S.svdq_gemm(layer.desc, layer.blob, codes, scales, T, M, Y, S.OUT_F32, wsarg)
+        torch.cuda.synchronize()
+        assert np.array_equal(Y.cpu().numpy().astype(np.float64), ys[(key, "f32", False)])
+
+
 @pytest.mark.parametrize("alpha,fmt", [(0.25, O.INT4), (0.75, O.INT4), (0.25, O.FP4), (0.75, O.FP4)])
 def test_smoothing_strengths(torch_dev, alpha, fmt):
     """Smoothing strengths other than 0.5 (the handbook's SmoothQuant

@@ -90,7 +90,7 @@ def _lib() -> ctypes.CDLL:
             "svdq_check_blob": ([D, P, P], S),
             "svdq_quantize_act": ([D, P, P, I, P, P, P, P, Z, P], S),
             "svdq_quantize_act_ln": ([D, P, P, P, P, F, I, P, P, P, P, Z, P], S),
-            "svdq_gemm": ([D, P, P, P, P, I, P, I, P], S),
+            "svdq_gemm": ([D, P, P, P, P, I, P, I, P, Z, P], S),
             "svdq_linear_ln": ([D, P, P, P, P, F, I, P, I, P, Z, P], S),
             "svdq_linear_w4a16": ([D, P, P, I, P, I, P, Z, P], S),
             "svdq_linear": ([D, P, P, I, P, I, P, Z, P], S),
@@ -231,10 +231,12 @@ def svdq_linear_w4a16(desc: LayerDesc, prepared, X, Y, workspace, out_dtype: int
 
 
 def svdq_gemm(desc: LayerDesc, prepared, codes, scales, T, M: int, Y, out_dtype: int = OUT_BF16,
-              stream=None):
-    """The GEMM stage alone, on the outputs of svdq_quantize_act."""
+              workspace=None, stream=None):
+    """The GEMM stage alone, on the outputs of svdq_quantize_act (workspace
+    optional: with it a small INT4 GEMM may split K)."""
     _check(_lib().svdq_gemm(ctypes.byref(desc), _ptr(prepared), _ptr(codes), _ptr(scales), _ptr(T), M,
-                            _ptr(Y), out_dtype, _stream(stream)), "svdq_gemm")
+                            _ptr(Y), out_dtype, _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                            _stream(stream)), "svdq_gemm")
 
 
 def svdq_linear(desc: LayerDesc, prepared, X, Y, workspace, out_dtype: int = OUT_BF16, stream=None):

@@ -116,7 +116,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const int l32 = lane & 31;
   const int lh = lane >> 5;
   const int SW = K / 128;                        // scale words (4 bytes) per row
-  const int stages = K / 128;
+  // K part of this workgroup (grid.y parts; one unless the launch splits K):
+  // stages [s_begin, s_begin + stages) of the K / 128
+  const int part = static_cast<int>(blockIdx.y), kparts = g.kparts;
+  const int s_begin = part * SW / kparts;
+  const int stages = (part + 1) * SW / kparts - s_begin;
   const int wrow0 = wm * (RB * 32), wcol0 = wn * (CB * 32);
 
   f32x16 acc[RB][CB];
@@ -132,7 +136,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   // are computed from real data and never stored, and every load stays
   // unconditional.
   if constexpr (SLAB) {
-    for (int tb = 0; tb < rank / 16; tb++) {
+    // (the first K part only)
+    for (int tb = 0; tb < (part == 0 ? rank / 16 : 0); tb++) {
       bf16x8 b[CB];
 #pragma unroll
       for (int j = 0; j < CB; j++) {
@@ -160,8 +165,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const long KBLK = K / 64;                       // 1 KB blocks per 32-row block
   const int last_ablk = (M + 31) / 32 - 1, last_bblk = N / 32 - 1;
   const int last = stages - 1;
-  const uint8_t* cpa = g.acodes + ((static_cast<long>(min(static_cast<int>(m0 / 32) + wave, last_ablk)) * KBLK) << 10);
-  const uint8_t* cpb = g.wcodes + ((static_cast<long>(min(static_cast<int>(n0 / 32) + wave, last_bblk)) * KBLK) << 10);
+  // (the bases start at the part's first stage: 2 KB of codes per stage)
+  const uint8_t* cpa = g.acodes + ((static_cast<long>(min(static_cast<int>(m0 / 32) + wave, last_ablk)) * KBLK) << 10) +
+                       static_cast<long>(s_begin) * 2048;
+  const uint8_t* cpb = g.wcodes + ((static_cast<long>(min(static_cast<int>(n0 / 32) + wave, last_bblk)) * KBLK) << 10) +
+                       static_cast<long>(s_begin) * 2048;
   const uint8_t* cps;
   uint32_t svoff, sstride;
   if (wave < 2) {
@@ -178,6 +186,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     svoff = static_cast<uint32_t>(c * SW * 4);
     sstride = 4;
   }
+  svoff += static_cast<uint32_t>(s_begin) * sstride;
   const uint32_t lane16 = lane * 16u;
   const uint32_t sdst = wave < 2 ? RING_SA + wave * 256 : RING_SB + (wave - 2) * 256;
   // copy item i (0..4) of stage st into ring slot st % NBUF
@@ -380,6 +389,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   // it, before the epilogue stages its output there
   SVDQ_VM_BARRIER(0);
 
+  // ---- K split: the part's fp32 partial tile (no bias) goes to the
+  // workspace, row-major 128 x 128 per (part, tile); gemm_ysum_kernel adds
+  // the parts
+  if (kparts > 1) {
+    float* yp = g.ypart + (static_cast<long>(part) * tiles_m * tiles_n + static_cast<long>(tm) * tiles_n + tn) *
+                              (BM * BN);
+#pragma unroll
+    for (int rb = 0; rb < RB; rb++)
+#pragma unroll
+      for (int cb = 0; cb < CB; cb++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+          const int row = wrow0 + rb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+          yp[row * BN + wcol0 + cb * 32 + l32] = acc[rb][cb][v];
+        }
+    return;
+  }
+
   // ---- epilogue: bias, rounding, store.  Each wave stages one 32-row
   // slice of its tile at a time in its own LDS region (row-major, output
   // type), then writes whole rows with 16-byte stores.
@@ -422,6 +449,32 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       }
       __builtin_amdgcn_wave_barrier();
     }
+  }
+}
+
+// K-split epilogue: Y = round(sum over the parts, in part order, of the
+// fp32 partial tiles + b); one thread per 4 consecutive columns of a row
+// (N % 32 == 0, so the 4 lie in one tile).
+template <int OUT>
+__global__ __launch_bounds__(256) void gemm_ysum_kernel(const float* __restrict__ ypart, int kparts, int M, int N,
+                                                        const float* __restrict__ bias, void* __restrict__ Y) {
+  const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  const int n4 = N / 4;
+  if (idx >= static_cast<long>(M) * n4) return;
+  const long row = idx / n4;
+  const int col = static_cast<int>(idx - row * n4) * 4;
+  const int tiles_n = (N + BN - 1) / BN;
+  const long tiles = (static_cast<long>(M) + BM - 1) / BM * tiles_n;
+  const long tile = row / BM * tiles_n + col / BN;
+  const float* p = ypart + tile * (BM * BN) + (row % BM) * BN + col % BN;
+  f32x4 s = *reinterpret_cast<const f32x4*>(p);
+  for (int q = 1; q < kparts; q++) s += *reinterpret_cast<const f32x4*>(p + q * tiles * (BM * BN));
+  if (bias) s += *reinterpret_cast<const f32x4*>(bias + col);
+  if constexpr (OUT == SVDQ_OUT_F32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(Y) + row * N + col) = s;
+  } else {
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Y) + row * N + col) =
+        u32x2{f32_to_bf16_bits(s.x) | (f32_to_bf16_bits(s.y) << 16), f32_to_bf16_bits(s.z) | (f32_to_bf16_bits(s.w) << 16)};
   }
 }
 
@@ -523,11 +576,23 @@ hipError_t launch_gemm(int fmt, bool slab, int out_dtype, const GemmArgs& ga, hi
     const int tiles_m = (ga.M + BM - 1) / BM, tiles_n = (ga.N + BN - 1) / BN;
     GemmArgs g = ga;
     g.xcd_map = gemm_xcd_map(g.M, g.N, g.K, tiles_m, tiles_n);
-    dim3 grid(tiles_m * tiles_n), block(256);
+    // K split where the tiles leave at least half of the CUs idle: parts up
+    // to the CU count, at least 4 stages each (the copy ring runs 3 ahead)
+    const int tiles = tiles_m * tiles_n, stages = g.K / 128;
+    g.kparts = 1;
+    if (g.ypart && tiles <= kGemmSplitMaxTiles && 2 * tiles <= device_cu_count())
+      g.kparts = std::max(1, std::min({kGemmMaxParts, device_cu_count() / tiles, kGemmSplitItems / tiles, stages / 4}));
+    dim3 grid(tiles, g.kparts), block(256);
 #define SVDQ_G(S, O) hipLaunchKernelGGL((gemm_kernel<S, O>), grid, block, 0, st, g)
     if (slab) { if (f32) SVDQ_G(true, SVDQ_OUT_F32); else SVDQ_G(true, SVDQ_OUT_BF16); }
     else      { if (f32) SVDQ_G(false, SVDQ_OUT_F32); else SVDQ_G(false, SVDQ_OUT_BF16); }
 #undef SVDQ_G
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || g.kparts == 1) return e;
+    const long n4 = static_cast<long>(g.M) * (g.N / 4);
+    const dim3 rgrid(static_cast<unsigned>((n4 + 255) / 256));
+    if (f32) hipLaunchKernelGGL(gemm_ysum_kernel<SVDQ_OUT_F32>, rgrid, dim3(256), 0, st, g.ypart, g.kparts, g.M, g.N, g.bias, g.Y);
+    else hipLaunchKernelGGL(gemm_ysum_kernel<SVDQ_OUT_BF16>, rgrid, dim3(256), 0, st, g.ypart, g.kparts, g.M, g.N, g.bias, g.Y);
     return hipGetLastError();
   }
   return launch_gemm_fp4(slab, out_dtype, ga, st);

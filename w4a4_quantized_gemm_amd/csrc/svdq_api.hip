@@ -108,7 +108,7 @@ svdq_status run_layer(const svdq_layer_desc* desc, const void* prepared, const v
   if (out_dtype != SVDQ_OUT_BF16 && out_dtype != SVDQ_OUT_F32) return SVDQ_ERR_INVALID_ARGUMENT;
   if (!aligned16(Y) || !aligned16(ws)) return SVDQ_ERR_MISALIGNED;
   const ActLayout A = act_layout(*desc, M);
-  if (ws_bytes < A.total) return SVDQ_ERR_BUFFER_TOO_SMALL;
+  if (ws_bytes < A.required) return SVDQ_ERR_BUFFER_TOO_SMALL;
   if ((st = check_device()) != SVDQ_OK) return st;
 
   const BlobPtrs bp = blob_ptrs(*desc, prepared);
@@ -140,6 +140,8 @@ svdq_status run_layer(const svdq_layer_desc* desc, const void* prepared, const v
   g.K = desc->K;
   g.N = desc->N;
   g.rank = desc->rank;
+  // the split-K GEMM's partial tiles, where the workspace holds them
+  g.ypart = gemm_may_split(*desc, M) && ws_bytes >= A.total ? reinterpret_cast<float*>(w + A.ypart) : nullptr;
 
   if (!unfused) {
     if ((st = from_hip(launch_act(desc->fmt, true, desc->rank > 0, a, s))) != SVDQ_OK) return st;
@@ -281,7 +283,7 @@ svdq_status svdq_quantize_act(const svdq_layer_desc* desc, const void* d_prepare
   if (!d_codes || !d_scales || (desc->rank > 0 && !d_T)) return SVDQ_ERR_INVALID_ARGUMENT;
   if (!aligned16(d_codes) || !aligned16(d_scales) || (d_T && !aligned16(d_T))) return SVDQ_ERR_MISALIGNED;
   if (d_workspace && !aligned16(d_workspace)) return SVDQ_ERR_MISALIGNED;
-  if (d_workspace && ws_bytes < svdq_workspace_bytes(desc, M, 0)) return SVDQ_ERR_BUFFER_TOO_SMALL;
+  if (d_workspace && ws_bytes < act_layout(*desc, M).required) return SVDQ_ERR_BUFFER_TOO_SMALL;
   if ((st = check_device()) != SVDQ_OK) return st;
   const BlobPtrs bp = blob_ptrs(*desc, d_prepared);
   ActArgs a;
@@ -301,12 +303,16 @@ svdq_status svdq_quantize_act(const svdq_layer_desc* desc, const void* d_prepare
 }
 
 svdq_status svdq_gemm(const svdq_layer_desc* desc, const void* d_prepared, const void* d_codes,
-                      const void* d_scales, const void* d_T, int M, void* d_Y, int out_dtype, void* stream) {
+                      const void* d_scales, const void* d_T, int M, void* d_Y, int out_dtype, void* d_workspace,
+                      size_t ws_bytes, void* stream) {
   svdq_status st = validate_runtime(desc, d_prepared, d_codes, M);
   if (st != SVDQ_OK) return st;
   if (!d_scales || !d_Y || (desc->rank > 0 && !d_T)) return SVDQ_ERR_INVALID_ARGUMENT;
   if (out_dtype != SVDQ_OUT_BF16 && out_dtype != SVDQ_OUT_F32) return SVDQ_ERR_INVALID_ARGUMENT;
   if (!aligned16(d_scales) || !aligned16(d_Y) || (d_T && !aligned16(d_T))) return SVDQ_ERR_MISALIGNED;
+  const ActLayout A = act_layout(*desc, M);
+  if (d_workspace && !aligned16(d_workspace)) return SVDQ_ERR_MISALIGNED;
+  if (d_workspace && ws_bytes < A.required) return SVDQ_ERR_BUFFER_TOO_SMALL;
   if ((st = check_device()) != SVDQ_OK) return st;
   const BlobPtrs bp = blob_ptrs(*desc, d_prepared);
   GemmArgs g{};
@@ -322,6 +328,9 @@ svdq_status svdq_gemm(const svdq_layer_desc* desc, const void* d_prepared, const
   g.K = desc->K;
   g.N = desc->N;
   g.rank = desc->rank;
+  g.ypart = d_workspace && gemm_may_split(*desc, M) && ws_bytes >= A.total
+                ? reinterpret_cast<float*>(static_cast<uint8_t*>(d_workspace) + A.ypart)
+                : nullptr;
   return from_hip(launch_gemm(desc->fmt, desc->rank > 0, out_dtype, g, as_stream(stream)));
 }
 
@@ -338,7 +347,7 @@ svdq_status svdq_quantize_act_ln(const svdq_layer_desc* desc, const void* d_prep
   if (!aligned16(d_codes) || !aligned16(d_scales) || !aligned16(d_workspace) || (d_T && !aligned16(d_T)))
     return SVDQ_ERR_MISALIGNED;
   const ActLayout A = act_layout(*desc, M);
-  if (ws_bytes < A.total) return SVDQ_ERR_BUFFER_TOO_SMALL;
+  if (ws_bytes < A.required) return SVDQ_ERR_BUFFER_TOO_SMALL;
   if ((st = check_device()) != SVDQ_OK) return st;
   const BlobPtrs bp = blob_ptrs(*desc, d_prepared);
   uint8_t* w = static_cast<uint8_t*>(d_workspace);
@@ -380,7 +389,7 @@ svdq_status svdq_linear_w4a16(const svdq_layer_desc* desc, const void* d_prepare
   if (out_dtype != SVDQ_OUT_BF16 && out_dtype != SVDQ_OUT_F32) return SVDQ_ERR_INVALID_ARGUMENT;
   if (!aligned16(d_Y) || !aligned16(d_workspace)) return SVDQ_ERR_MISALIGNED;
   const ActLayout A = act_layout(*desc, M);
-  if (ws_bytes < A.total) return SVDQ_ERR_BUFFER_TOO_SMALL;
+  if (ws_bytes < A.required) return SVDQ_ERR_BUFFER_TOO_SMALL;
   if ((st = check_device()) != SVDQ_OK) return st;
   const BlobPtrs bp = blob_ptrs(*desc, d_prepared);
   W4A16Args a;
@@ -412,7 +421,7 @@ svdq_status svdq_linear_noalloc(const svdq_layer_desc* desc, const void* d_prepa
                                 void* d_Y, int out_dtype, void* stream) {
   svdq_status st = validate_runtime(desc, d_prepared, d_X, M);
   if (st != SVDQ_OK) return st;
-  if (act_layout(*desc, M).total > SVDQ_NOALLOC_SCRATCH_BYTES) return SVDQ_ERR_BUFFER_TOO_SMALL;
+  if (act_layout(*desc, M).required > SVDQ_NOALLOC_SCRATCH_BYTES) return SVDQ_ERR_BUFFER_TOO_SMALL;
   if ((st = check_device()) != SVDQ_OK) return st;
   void* ws = scratch_ptr();
   if (!ws) return SVDQ_ERR_HIP;

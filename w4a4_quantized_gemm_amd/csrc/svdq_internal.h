@@ -48,8 +48,24 @@ bool aligned16(const void* p);
 svdq_blob_layout layout_of(const svdq_layer_desc& d);
 
 // Activation-side buffers inside a workspace: packed codes, scales, Tb.
+// The INT4 GEMM splits K over at most kGemmMaxParts parts when its
+// 128 x 128 output tiles number at most kGemmSplitMaxTiles (small M, where
+// the tiles alone leave most CUs idle); the workspace then holds the fp32
+// partial tiles of at most kGemmSplitItems (tile, part) items.
+constexpr int kGemmMaxParts = 8;
+constexpr int kGemmSplitMaxTiles = 128;
+constexpr int kGemmSplitItems = 256;
+constexpr int kGemmTile = 128;
+inline bool gemm_may_split(const svdq_layer_desc& d, int M) {
+  const long tiles = (static_cast<long>(M) + kGemmTile - 1) / kGemmTile * ((d.N + kGemmTile - 1) / kGemmTile);
+  return d.fmt == SVDQ_INT4_G64_FP16 && tiles <= kGemmSplitMaxTiles;
+}
+
 struct ActLayout {
-  uint64_t codes, scales, tb, tpart, rowstat, fold, w4a16, total;
+  // required: the bytes every call needs; total adds the optional last
+  // section (the split-K GEMM's partial tiles: a workspace without it runs
+  // the GEMM unsplit)
+  uint64_t codes, scales, tb, tpart, rowstat, fold, w4a16, ypart, required, total;
   uint64_t codes_bytes, scales_bytes, tb_bytes;
 };
 ActLayout act_layout(const svdq_layer_desc& d, int M);

@@ -44,6 +44,10 @@ struct GemmArgs {
   void* Y;                // M x N, bf16 bits or fp32
   int M, K, N, rank;
   int xcd_map;            // tile -> XCD assignment (tile_of), set by the launch
+  // INT4 GEMM: workspace for the fp32 partial tiles of a K split (at most
+  // kGemmSplitItems 128 x 128 tiles), or null: K is not split
+  float* ypart;
+  int kparts;             // set by the launch (1: no split)
 };
 
 // The tile -> XCD map for a GEMM of tiles_m x tiles_n tiles over M x K

@@ -80,6 +80,10 @@ ActLayout act_layout(const svdq_layer_desc& d, int M) {
   // weight-only layer: the bf16 pieces of x_hat
   A.w4a16 = off;
   if (d.rank == 0 && M <= kW4A16MaxM) off = align256(off + K * 64 * uint64_t(w4a16_planes(M)));
+  // split-K INT4 GEMM (few output tiles): the fp32 partial tiles
+  A.ypart = off;
+  A.required = off;
+  if (gemm_may_split(d, M)) off = align256(off + uint64_t(kGemmSplitItems) * kGemmTile * kGemmTile * 4);
   A.total = off;
   return A;
 }

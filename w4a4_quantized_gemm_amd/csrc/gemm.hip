@@ -73,8 +73,6 @@ __device__ __forceinline__ u32x4 e4m3_hi(const u32x4& c) {
 // fits in 256 without spilling but measured no faster).
 constexpr int RB = 2, CB = 2;                      // 32-row (-column) blocks per wave
 constexpr int BM = 2 * RB * 32, BN = 2 * CB * 32;
-constexpr int NTHREADS = 256;
-constexpr int A_CH = BM * 4 / NTHREADS, B_CH = BN * 4 / NTHREADS;   // 16-byte code pieces per thread and stage
 
 // LDS layout of one K stage (128 K values) of one operand: the codes are
 // widened to E4M3 operand bytes once, as they are stored.  The 2 KB block of

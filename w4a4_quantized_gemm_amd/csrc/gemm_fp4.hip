@@ -478,18 +478,21 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
         d[r] = *reinterpret_cast<const u32x4*>(stg + row * 128 + ((rch ^ (row & 7)) << 4));
       }
     };
+    // the lane's part of every store offset; a store's uniform part adds the
+    // slice's first row and column (rows past the tile's valid rows land at
+    // or past nrec, the resource's end, and are dropped)
+    const uint32_t lane_off = static_cast<uint32_t>(rrow) * rowb + static_cast<uint32_t>(rch) * 16u;
     auto store_slice = [&](int q, const u32x4 (&d)[4]) __attribute__((always_inline)) {
       const int sl = q >> 2, j = q & 3;
       const long c0 = colw + sl * SLW;
-      const bool cols_ok = c0 < N;                          // N % 64 == 0: a whole slice is in or out
       const int trow0 = wm * 128 + j * 32;                  // first slice row in the tile
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        const int row = rrow + 8 * r;
-        const uint32_t off = cols_ok && trow0 + row < valid_rows
-                                 ? static_cast<uint32_t>(trow0 + row) * rowb + static_cast<uint32_t>(c0 * OB) + rch * 16
-                                 : nrec;
-        __builtin_amdgcn_raw_buffer_store_b128(d[r], yr, static_cast<int>(off), 0, 0);
+        // N % 64 == 0: a whole slice is in or out
+        const uint32_t uoff = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+            c0 < N ? static_cast<int>(static_cast<uint32_t>(trow0 + 8 * r) * rowb + static_cast<uint32_t>(c0 * OB))
+                   : static_cast<int>(nrec)));
+        __builtin_amdgcn_raw_buffer_store_b128(d[r], yr, static_cast<int>(lane_off + uoff), 0, 0);
       }
     };
     write_slice(0);

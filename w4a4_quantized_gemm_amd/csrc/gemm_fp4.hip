@@ -85,7 +85,7 @@ __device__ __forceinline__ f32x4 acc_read4(float a, float b, float c, float d) {
 }  // namespace
 
 // GENERAL: any rank and K; otherwise rank/32 <= 3 low-rank stages and at
-// least 3 FP4 stages per tile, where the copy descriptors change only at
+// least 3 FP4 stages per tile (4 without the slab), where the copy descriptors change only at
 // fixed stages of a tile (straight-line runs, no per-stage descriptor work).
 template <bool SLAB, int OUT, bool GENERAL>
 __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
@@ -293,12 +293,18 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
   };
 
   f32x16 acc[4][4];
-  // MFMA t of step kk: weight block i = t / 4, activation block j = t % 4
+  // initial value of the accumulators of weight block i (the tile's bias in
+  // the accumulator layout, the same for every activation block, or zero):
+  // the tile's first MFMA of each accumulator takes it as its source, so no
+  // accumulator is written before the tile's MFMAs
+  f32x16 binit[4];
+  // MFMA t of step kk: weight block i = t / 4, activation block j = t % 4;
+  // FIRST: the tile's first step (accumulators start at binit)
   auto mfma = [&](const Ops& o, const uint32_t (&sx)[4], const uint32_t (&sw)[4], int t, auto KK, auto LR,
-                  uint32_t wmask) __attribute__((always_inline)) {
+                  uint32_t wmask, auto FIRST) __attribute__((always_inline)) {
     constexpr int kk = decltype(KK)::value;
     const int i = t >> 2, j = t & 3;
-    const f32x16 c = acc[i][j];
+    const f32x16 c = decltype(FIRST)::value ? binit[i] : acc[i][j];
     if constexpr (decltype(LR)::value) {
       u32x4 w = o.w[i];
       if constexpr (kk == 1) w &= wmask;
@@ -332,8 +338,8 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
   // HALF (a half item): 8 MFMAs per step on weight blocks 0, 1 (read from
   // blocks 2 h, 2 h + 1), 6 operand pieces, the same copies and waits.
   auto stage = [&](Ops& R0, const uint32_t (&sx)[4], const uint32_t (&sw)[4], uint32_t (&nsx)[4],
-                   uint32_t (&nsw)[4], long G, const CopyDesc& d, CopyOff& o, uint32_t wmask, auto LR, auto HALF)
-      __attribute__((always_inline)) {
+                   uint32_t (&nsw)[4], long G, const CopyDesc& d, CopyOff& o, uint32_t wmask, auto LR, auto HALF,
+                   auto FIRST) __attribute__((always_inline)) {
     constexpr bool H = decltype(HALF)::value;
     constexpr int NT = H ? 8 : 16, NP = H ? 6 : 8;   // MFMAs, operand pieces per step
     const uint32_t hw = H ? half_woff : 0u, hs = H ? half_soff : 0u;
@@ -344,7 +350,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
     Ops R1;
 #pragma unroll
     for (int t = 0; t < NT; t++) {
-      mfma(R0, sx, sw, t, std::integral_constant<int, 0>{}, LR, wmask);
+      mfma(R0, sx, sw, t, std::integral_constant<int, 0>{}, LR, wmask, FIRST);
       __builtin_amdgcn_sched_barrier(0);
       if (t < NP) read_piece(R1, ax, aw, 1, t);
       if (t <= 4) copy_slot(d, o, rc, t);
@@ -356,7 +362,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
     const uint32_t nsxa = rsx + rn * 2048, nswa = rsw + rn * 2048 + hs;
 #pragma unroll
     for (int t = 0; t < NT; t++) {
-      mfma(R1, sx, sw, t, std::integral_constant<int, 1>{}, LR, wmask);
+      mfma(R1, sx, sw, t, std::integral_constant<int, 1>{}, LR, wmask, std::false_type{});
       if (t < NP) read_piece(R0, nx, nw, 0, t);
       if (t < NP) read_scale(nsx, nsw, nsxa, nswa, t);
       if (H ? t >= 3 : t >= 8) copy_slot(d, o, rc, H ? t + 2 : t - 3);
@@ -367,46 +373,43 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
   };
   // n consecutive stages of one kind and descriptor (the next stage's scales
   // are read into (nsx, nsw) and moved into place after each stage)
+  // FIRST: the run starts the tile (n >= 1): its first stage is peeled
   auto run = [&](Ops& R0, uint32_t (&sx)[4], uint32_t (&sw)[4], long& G, int n, const CopyDesc& d, CopyOff& o,
-                 uint32_t wmask_last, auto LR, auto HALF) __attribute__((always_inline)) {
-#pragma unroll 1
-    for (; n > 0; n--, G++) {
+                 uint32_t wmask_last, auto LR, auto HALF, auto FIRST) __attribute__((always_inline)) {
+    auto one = [&](auto F) __attribute__((always_inline)) {
       uint32_t nsx[4], nsw[4];
-      stage(R0, sx, sw, nsx, nsw, G, d, o, n == 1 ? wmask_last : ~0u, LR, HALF);
+      stage(R0, sx, sw, nsx, nsw, G, d, o, n == 1 ? wmask_last : ~0u, LR, HALF, F);
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         sx[q] = nsx[q];
         if (!decltype(HALF)::value || q < 2) sw[q] = nsw[q];
       }
+    };
+    if constexpr (decltype(FIRST)::value) {
+      one(std::true_type{});
+      n--;
+      G++;
     }
+#pragma unroll 1
+    for (; n > 0; n--, G++) one(std::false_type{});
   };
 
   // Accumulators of the tile of turn seq start at its bias (copied into
   // bias buffer seq % 2 with the copies of the tile's stages, the first of
   // which completed at the barrier before the tile's first stage), so the
-  // epilogue only rounds: acc[i][j][v] = b[128 wn + 32 i + 8 (v / 4) + 4 lh + v % 4].
-  auto init_acc = [&](int seq, auto HALF) __attribute__((always_inline)) {
+  // epilogue only rounds: binit[i][v] = b[128 wn + 32 i + 8 (v / 4) + 4 lh + v % 4]
+  // (zero without a bias: the bias buffer then holds unused bytes).
+  auto load_init = [&](int seq, auto HALF) __attribute__((always_inline)) {
     constexpr int NI = decltype(HALF)::value ? 2 : 4;   // weight blocks computed
-    if (has_bias) {
-      const float* bl = reinterpret_cast<const float*>(smem + F_BIAS + (seq & 1) * 1024) + wn * 128 + 4 * (lane >> 5) +
-                        (decltype(HALF)::value ? 64 * hsel : 0);
+    const float* bl = reinterpret_cast<const float*>(smem + F_BIAS + (seq & 1) * 1024) + wn * 128 + 4 * (lane >> 5) +
+                      (decltype(HALF)::value ? 64 * hsel : 0);
 #pragma unroll
-      for (int i = 0; i < NI; i++) {
-        f32x4 b4[4];
+    for (int i = 0; i < NI; i++) {
+      f32x4 b4[4];
 #pragma unroll
-        for (int gq = 0; gq < 4; gq++) b4[gq] = *reinterpret_cast<const f32x4*>(bl + 32 * i + 8 * gq);
+      for (int gq = 0; gq < 4; gq++) b4[gq] = *reinterpret_cast<const f32x4*>(bl + 32 * i + 8 * gq);
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-#pragma unroll
-          for (int v = 0; v < 16; v++) acc[i][j][v] = b4[v >> 2][v & 3];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NI; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-#pragma unroll
-          for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+      for (int v = 0; v < 16; v++) binit[i][v] = has_bias ? b4[v >> 2][v & 3] : 0.f;
     }
   };
 
@@ -553,31 +556,34 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
       read_scale(sx, sw, rsx + rb * 2048, rsw + rb * 2048 + half_soff, 4);
       read_scale(sx, sw, rsx + rb * 2048, rsw + rb * 2048 + half_soff, 5);
     }
-    init_acc(seq, HALF);
+    load_init(seq, HALF);
     const bool has = seq + 1 < my_tiles;         // else the copies repeat the last stage
     if constexpr (!GENERAL) {
       // A, B: stages [0, S - 3), copies of this tile's FP4 stages from stage 3
       make_desc(mb0, nb0, seq, F_AHEAD, false, d, o);
-      if constexpr (SLAB) run(oa, sx, sw, G, RS, d, o, last_mask, std::true_type{}, HALF);
-      run(oa, sx, sw, G, S - F_AHEAD - RS, d, o, ~0u, std::false_type{}, HALF);
+      // (the tile's first stage: the first low-rank stage, or without the
+      // slab the first FP4 stage: the launch gives this schedule at least 4
+      // FP4 stages then)
+      if constexpr (SLAB) run(oa, sx, sw, G, RS, d, o, last_mask, std::true_type{}, HALF, std::true_type{});
+      run(oa, sx, sw, G, S - F_AHEAD - RS, d, o, ~0u, std::false_type{}, HALF, std::bool_constant<!SLAB>{});
       // C: copies of the next tile's low-rank stages (the odd tail stage,
       // with its own second-step bases, separately)
       if constexpr (SLAB) {
         if (RS > 1) {
           if (has) make_desc(nmb0, nnb0, seq + 1, 0, false, d, o);
           else make_desc(mb0, nb0, seq, S - 1, true, d, o);
-          run(oa, sx, sw, G, RS - 1, d, o, ~0u, std::false_type{}, HALF);
+          run(oa, sx, sw, G, RS - 1, d, o, ~0u, std::false_type{}, HALF, std::false_type{});
         }
         if (RS > 0) {
           if (has) make_desc(nmb0, nnb0, seq + 1, RS - 1, false, d, o);
           else make_desc(mb0, nb0, seq, S - 1, true, d, o);
-          run(oa, sx, sw, G, 1, d, o, ~0u, std::false_type{}, HALF);
+          run(oa, sx, sw, G, 1, d, o, ~0u, std::false_type{}, HALF, std::false_type{});
         }
       }
       // D: copies of the next tile's FP4 stages
       if (has) make_desc(nmb0, nnb0, seq + 1, RS, false, d, o);
       else make_desc(mb0, nb0, seq, S - 1, true, d, o);
-      run(oa, sx, sw, G, F_AHEAD - RS, d, o, ~0u, std::false_type{}, HALF);
+      run(oa, sx, sw, G, F_AHEAD - RS, d, o, ~0u, std::false_type{}, HALF, std::false_type{});
     } else {
       // any shape: a descriptor per stage; the low-rank stages and the FP4
       // stages in loops of their own, so that each loop body holds one kind
@@ -590,17 +596,22 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
         const int cst = !hs ? S - 1 : (c_next ? cg - S : cg);
         make_desc(c_next && hs ? nmb0 : mb0, c_next && hs ? nnb0 : nb0, c_next && hs ? seq + 1 : seq, cst, !hs, d, o);
       };
+      // (the tile's first stage peeled: its MFMAs start the accumulators)
+      stage_desc(0);
       if constexpr (SLAB) {
+        run(oa, sx, sw, G, 1, d, o, RS == 1 ? last_mask : ~0u, std::true_type{}, HALF, std::true_type{});
 #pragma unroll 1
-        for (int st = 0; st < RS; st++) {
+        for (int st = 1; st < RS; st++) {
           stage_desc(st);
-          run(oa, sx, sw, G, 1, d, o, st == RS - 1 ? last_mask : ~0u, std::true_type{}, HALF);
+          run(oa, sx, sw, G, 1, d, o, st == RS - 1 ? last_mask : ~0u, std::true_type{}, HALF, std::false_type{});
         }
+      } else {
+        run(oa, sx, sw, G, 1, d, o, ~0u, std::false_type{}, HALF, std::true_type{});
       }
 #pragma unroll 1
-      for (int st = SLAB ? RS : 0; st < S; st++) {
+      for (int st = SLAB ? RS : 1; st < S; st++) {
         stage_desc(st);
-        run(oa, sx, sw, G, 1, d, o, ~0u, std::false_type{}, HALF);
+        run(oa, sx, sw, G, 1, d, o, ~0u, std::false_type{}, HALF, std::false_type{});
       }
     }
     epilogue(mb0, nb0, G - 1, HALF);
@@ -639,7 +650,7 @@ hipError_t launch_gemm_fp4(bool slab, int out_dtype, const GemmArgs& ga, hipStre
   dim3 grid(stages >= 3 ? std::min(tiles, device_cu_count()) : tiles), block(256);
   const bool f32 = out_dtype == SVDQ_OUT_F32;
   const int rs = slab ? (g.rank / 16 + 1) / 2 : 0;
-  const bool general = rs > 3 || stages < rs + 3;
+  const bool general = rs > 3 || stages < rs + 3 || (!slab && stages < 4);
 #define SVDQ_F(S, O, GEN) hipLaunchKernelGGL((gemm_fp4_kernel<S, O, GEN>), grid, block, 0, st, g)
 #define SVDQ_F2(S, O) do { if (general) SVDQ_F(S, O, true); else SVDQ_F(S, O, false); } while (0)
   if (slab) { if (f32) SVDQ_F2(true, SVDQ_OUT_F32); else SVDQ_F2(true, SVDQ_OUT_BF16); }

@@ -155,9 +155,9 @@ size_t svdq_prepared_bytes(const svdq_layer_desc* desc);
  * the packed activation codes (ceil(M/32)*32 x K/2 bytes), the scales, the
  * bf16 down-projection (ceil(M/32)*32 x rank) and, for M <= 16384, room for
  * the fp32 partial down-projections of a K-split activation pass
- * (8 x M x rank x 4 bytes); for INT4 layers whose M x N output has at most
- * 128 tiles of 128 x 128, a last, optional 16 MiB for the fp32 partial
- * tiles of a K-split GEMM (a workspace that ends before it is accepted and
+ * (8 x M x rank x 4 bytes); for layers whose M x N output has few tiles
+ * (INT4: at most 128 of 128 x 128; FP4: at most 32 of 256 x 256), a last,
+ * optional 16 MiB for the fp32 partial tiles of a K-split GEMM (a workspace that ends before it is accepted and
  * runs the GEMM unsplit, so a workspace sized for a larger M still serves a
  * smaller one); 0 if arguments are invalid.  Every section is written
  * before it is read, so one workspace serves any layer and M. */

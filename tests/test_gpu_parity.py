@@ -233,23 +233,25 @@ def test_small_shapes(torch_dev, M, K, N, rank, bias, fmt):
     _check_linear(torch_dev, layer, X, X_bits, ref)
 
 
+@pytest.mark.parametrize("fmt", [O.INT4, O.FP4])
 @pytest.mark.parametrize("M,K,N,rank", [(100, 2048, 384, 32), (300, 1536, 256, 16)])
-def test_int4_gemm_k_split(torch_dev, M, K, N, rank):
-    """INT4 layers with few output tiles split the GEMM's K over workgroups
-    (fp32 partial tiles in the workspace's last section, added in part
-    order with the bias by a second kernel).  With the full workspace the
+def test_gemm_k_split(torch_dev, M, K, N, rank, fmt):
+    """Layers with few output tiles split the GEMM's K over workgroups
+    (fp32 partial results in the workspace's last section, added in part
+    order with the bias by a second kernel; FP4 parts other than the first
+    zero their low-rank operand).  With the full workspace the
     split runs; with a workspace that ends before that optional section the
     GEMM runs unsplit.  Both match the oracle within the layer's tolerance,
     in both output types and in the unfused path, and both are
     deterministic (a repeated call is bit-equal)."""
     import w4a4_quantized_gemm_amd as S
     torch, dev = torch_dev
-    _say(f"case: INT4 GEMM K split M={M} K={K} N={N} r={rank}")
-    cfg = WL.C2.with_(name="ksplit", M=M, K=K, N=N, rank=rank, fmt=O.INT4, w_std=1 / np.sqrt(K),
+    _say(f"case: GEMM K split fmt={fmt} M={M} K={K} N={N} r={rank}")
+    cfg = WL.C2.with_(name="ksplit", M=M, K=K, N=N, rank=rank, fmt=fmt, w_std=1 / np.sqrt(K),
                       bias_std=0.02, seed=M + K)
     X_bits, W_bits, b_bits = WL.make_layer(cfg)
     layer, X, _ = _prepare(torch_dev, cfg, X_bits, W_bits, b_bits)
-    sec, ref = _check_weights(layer, W_bits, O.INT4, b_bits, X_bits=X_bits, alpha=cfg.alpha)
+    sec, ref = _check_weights(layer, W_bits, fmt, b_bits, X_bits=X_bits, alpha=cfg.alpha)
     full = S.svdq_workspace_bytes(layer.desc, M)
     split_bytes = 256 * 128 * 128 * 4
     ys = {}

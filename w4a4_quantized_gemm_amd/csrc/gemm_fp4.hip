@@ -96,8 +96,14 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
   const int M = g.M, K = g.K, N = g.N;
   const int RK = SLAB ? g.rank / 16 : 0;          // 16-rank blocks of Tb / L2b
   const int RS = (RK + 1) >> 1;                   // low-rank stages, 32 ranks each
-  const int KS = K >> 7;                          // FP4 stages, 128 K each
-  const int S = RS + KS;                          // stages per tile (>= 1)
+  // K split (few tiles, small M): an item is a (tile, K part) pair, part p
+  // taking FP4 stages p KS .. p KS + KS - 1 and writing its fp32 partial
+  // tile (no bias) to plane p of Y; every part keeps the low-rank stages,
+  // whose weight operand parts p > 0 zero, so all items have S stages
+  const int KP = g.kparts;                        // K parts (1: no split)
+  const int KSF = K >> 7;                         // FP4 stages of the whole K, 128 K each
+  const int KS = KSF / KP;                        // FP4 stages per item
+  const int S = RS + KS;                          // stages per item (>= 1)
   const long KB64 = K >> 6;                       // 1 KB code blocks per 32-row block
   const uint8_t* __restrict__ acodes = g.acodes;
   const uint8_t* __restrict__ wcodes = g.wcodes;
@@ -112,6 +118,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
 
   const int tiles_m = (M + F_TILE - 1) / F_TILE, tiles_n = (N + F_TILE - 1) / F_TILE;
   const int ntiles = tiles_m * tiles_n;
+  const int nitems = ntiles * KP;
   const int xmap = g.xcd_map;
   const int grid = static_cast<int>(gridDim.x), wg = static_cast<int>(blockIdx.x);
   // Tail split: when the last round of tiles (ntiles mod grid of them) fills
@@ -123,12 +130,12 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
   // then possibly one half item, whose waves compute weight blocks 2 h and
   // 2 h + 1 of their four (columns 64 h .. 64 h + 63 of each 128-column
   // half); its copies are the whole tile's, as for any tile.
-  const int rounds = ntiles / grid, rtail = ntiles - rounds * grid;
+  const int rounds = nitems / grid, rtail = nitems - rounds * grid;
   const bool split = (grid & 7) == 0 && rtail > 0 && 2 * rtail <= grid && S >= F_AHEAD;
   const int xcd = wg & 7, kx = wg >> 3;
   const int tails_x = xcd < rtail ? (rtail - 1 - xcd) / 8 + 1 : 0;   // tail tiles on this XCD
   const bool half_item = split && kx < 2 * tails_x;
-  const int nfull = split ? rounds : (ntiles - wg + grid - 1) / grid;  // >= 1: the grid never exceeds the tile count
+  const int nfull = split ? rounds : (nitems - wg + grid - 1) / grid;  // >= 1: the grid never exceeds the item count
   const int my_tiles = nfull + (half_item ? 1 : 0);                      // items
   const int hsel = kx & 1;                                               // the half item's column half
   const uint32_t half_woff = static_cast<uint32_t>(hsel) * 4096u;       // its weight blocks in the stage
@@ -140,9 +147,15 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
   const int wm = wave >> 1, wn = wave & 1;        // 128-row half, 128-column half of the tile
   const uint32_t lane16 = lane * 16;
 
-  auto tile_blocks = [&](int seq, int& mb0, int& nb0) __attribute__((always_inline)) {
+  // item of this workgroup's turn seq; its tile is item % ntiles, its K part item / ntiles
+  auto item_of = [&](int seq) __attribute__((always_inline)) {
+    return seq < nfull ? wg + seq * grid : rounds * grid + xcd + 8 * (kx >> 1);
+  };
+  auto tile_blocks = [&](int seq, int& mb0, int& nb0, int& part) __attribute__((always_inline)) {
     int tm, tn;
-    tile_of(seq < nfull ? wg + seq * grid : rounds * grid + xcd + 8 * (kx >> 1), tiles_m, tiles_n, xmap, tm, tn);
+    const int it = item_of(seq);
+    part = KP > 1 ? wave_uniform(it / ntiles) : 0;
+    tile_of(it - part * ntiles, tiles_m, tiles_n, xmap, tm, tn);
     // uniform by construction; made scalar so that addresses and buffer
     // resources built from them stay in SGPRs
     mb0 = wave_uniform(tm * (F_TILE / 32));
@@ -183,9 +196,9 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
   struct CopyOff {
     uint32_t v, ve;                     // per-lane offsets: blocks, the ninth copy
   };
-  // descriptor of a run starting at stage cst of the tile (mb0, nb0) of turn
-  // `turn`; rep: the run repeats that stage
-  auto make_desc = [&](int mb0, int nb0, int turn, int cst, bool rep, CopyDesc& d, CopyOff& o)
+  // descriptor of a run starting at stage cst of the item (tile (mb0, nb0),
+  // K part `part`) of turn `turn`; rep: the run repeats that stage
+  auto make_desc = [&](int mb0, int nb0, int part, int turn, int cst, bool rep, CopyDesc& d, CopyOff& o)
       __attribute__((always_inline)) {
     const bool lr = SLAB && cst < RS;
     const int xa = min(mb0 + 2 * wave, last_ablk), xb = min(mb0 + 2 * wave + 1, last_ablk);
@@ -207,7 +220,8 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
     d.w[1] = wa0 + dk - 1024;
     d.w[2] = wb0 - 2048;
     d.w[3] = wb0 + dk - 3072;
-    const int ks = lr ? 0 : cst - RS;             // FP4 stage (low-rank stages copy unused scales of stage 0)
+    // FP4 stage within the whole K (low-rank stages copy unused scales of stage 0)
+    const int ks = lr ? 0 : cst - RS + part * KS;
     d.inc = rep ? 0u : 2048u;
     o.v = lane16 + static_cast<uint32_t>(lr ? cst : ks) * 2048u;
     if (wave < 2) {
@@ -215,10 +229,10 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
       // tile, relative to the tile's first (clamped) row block
       const int first = wave == 0 ? min(mb0, last_ablk) : min(nb0, last_bblk);
       const int blk = wave == 0 ? min(mb0 + (lane >> 3), last_ablk) : min(nb0 + (lane >> 3), last_bblk);
-      d.e = (wave == 0 ? ascales : wscales) + static_cast<long>(first) * KS * 128;
+      d.e = (wave == 0 ? ascales : wscales) + static_cast<long>(first) * KSF * 128;
       d.e_lds = 0u;
       d.einc = (rep || lr) ? 0u : 128u;
-      o.ve = static_cast<uint32_t>((blk - first) * KS * 128 + ks * 128 + (lane & 7) * 16);
+      o.ve = static_cast<uint32_t>((blk - first) * KSF * 128 + ks * 128 + (lane & 7) * 16);
     } else {
       // bias: lane l takes columns 4 l .. 4 l + 3 of the tile (clamped to the
       // matrix); without a bias 1 KB of the activation codes (never used)
@@ -298,6 +312,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
   // the tile's first MFMA of each accumulator takes it as its source, so no
   // accumulator is written before the tile's MFMAs
   f32x16 binit[4];
+  uint32_t lrm = ~0u;                             // the item's low-rank mask: ~0 for K part 0, else 0
   // MFMA t of step kk: weight block i = t / 4, activation block j = t % 4;
   // FIRST: the tile's first step (accumulators start at binit)
   auto mfma = [&](const Ops& o, const uint32_t (&sx)[4], const uint32_t (&sw)[4], int t, auto KK, auto LR,
@@ -306,8 +321,9 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
     const int i = t >> 2, j = t & 3;
     const f32x16 c = decltype(FIRST)::value ? binit[i] : acc[i][j];
     if constexpr (decltype(LR)::value) {
-      u32x4 w = o.w[i];
-      if constexpr (kk == 1) w &= wmask;
+      // wmask: step 0 the item's low-rank mask (zero for K parts > 0), step 1
+      // that and the odd-tail mask
+      const u32x4 w = o.w[i] & wmask;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w),
                                                          __builtin_bit_cast(bf16x8, o.x[j]), c, 0, 0, 0);
     } else {
@@ -350,7 +366,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
     Ops R1;
 #pragma unroll
     for (int t = 0; t < NT; t++) {
-      mfma(R0, sx, sw, t, std::integral_constant<int, 0>{}, LR, wmask, FIRST);
+      mfma(R0, sx, sw, t, std::integral_constant<int, 0>{}, LR, lrm, FIRST);
       __builtin_amdgcn_sched_barrier(0);
       if (t < NP) read_piece(R1, ax, aw, 1, t);
       if (t <= 4) copy_slot(d, o, rc, t);
@@ -362,7 +378,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
     const uint32_t nsxa = rsx + rn * 2048, nswa = rsw + rn * 2048 + hs;
 #pragma unroll
     for (int t = 0; t < NT; t++) {
-      mfma(R1, sx, sw, t, std::integral_constant<int, 1>{}, LR, wmask, std::false_type{});
+      mfma(R1, sx, sw, t, std::integral_constant<int, 1>{}, LR, wmask & lrm, std::false_type{});
       if (t < NP) read_piece(R0, nx, nw, 0, t);
       if (t < NP) read_scale(nsx, nsw, nsxa, nswa, t);
       if (H ? t >= 3 : t >= 8) copy_slot(d, o, rc, H ? t + 2 : t - 3);
@@ -424,7 +440,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
   // every wave's read-back ahead of those copies).  Rows past M and columns
   // past N get an offset past the buffer resource and are dropped, so every
   // store instruction issues (the waits count them).
-  auto epilogue = [&](int mb0, int nb0, long G, auto HALF) __attribute__((always_inline)) {
+  auto epilogue = [&](int mb0, int nb0, int part, long G, auto HALF) __attribute__((always_inline)) {
     // lane indices recomputed through an opaque move, so that the compiler
     // does not hoist the epilogue's per-lane addresses out of the tile loop
     int lane_e;
@@ -440,7 +456,8 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
     const int valid_rows = static_cast<int>(min(static_cast<long>(M) - m0, static_cast<long>(F_TILE)));
     const uint32_t nrec = static_cast<uint32_t>(valid_rows) * rowb;
     const __amdgpu_buffer_rsrc_t yr =
-        __builtin_amdgcn_make_buffer_rsrc(static_cast<uint8_t*>(Yout) + m0 * rowb, 0, static_cast<int>(nrec), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(static_cast<uint8_t*>(Yout) + (static_cast<long>(part) * M + m0) * rowb, 0,
+                                          static_cast<int>(nrec), 0x00020000);
     // read-back: lane reads chunk (lane % 8) of slice rows lane / 8 + 8 r
     const int rrow = lane_e >> 3, rch = lane_e & 7;
     constexpr int NSL = OUT == SVDQ_OUT_F32 ? 4 : 2;        // column slices of the wave's 128 columns
@@ -517,15 +534,15 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
 
   // ---- prologue: the copies of stages 0 .. 2 of the first tile, stage 0
   // published and read
-  int mb0, nb0, nmb0, nnb0;
-  tile_blocks(0, mb0, nb0);
-  tile_blocks(min(1, my_tiles - 1), nmb0, nnb0);
+  int mb0, nb0, kp0, nmb0, nnb0, nkp0;            // tile blocks and K part of the current and next items
+  tile_blocks(0, mb0, nb0, kp0);
+  tile_blocks(min(1, my_tiles - 1), nmb0, nnb0, nkp0);
   CopyDesc d;
   CopyOff o;
 #pragma unroll 1
   for (int p = 0; p < F_AHEAD; p++) {
     // (first tile: S >= 3 whenever it has a successor; otherwise repeat its last stage)
-    make_desc(mb0, nb0, 0, min(p, S - 1), p >= S, d, o);
+    make_desc(mb0, nb0, kp0, 0, min(p, S - 1), p >= S, d, o);
     copy_all(d, o, p);
   }
   // stage 0 complete: the copies of stages 1 and 2 may stay in flight
@@ -544,7 +561,8 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
     if (seq > 0) {
       mb0 = nmb0;
       nb0 = nnb0;
-      tile_blocks(min(seq + 1, my_tiles - 1), nmb0, nnb0);
+      kp0 = nkp0;
+      tile_blocks(min(seq + 1, my_tiles - 1), nmb0, nnb0, nkp0);
     }
     if constexpr (decltype(HALF)::value) {
       // the previous stage read this stage's weight operands and scales of
@@ -557,10 +575,11 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
       read_scale(sx, sw, rsx + rb * 2048, rsw + rb * 2048 + half_soff, 5);
     }
     load_init(seq, HALF);
+    lrm = kp0 == 0 ? ~0u : 0u;
     const bool has = seq + 1 < my_tiles;         // else the copies repeat the last stage
     if constexpr (!GENERAL) {
       // A, B: stages [0, S - 3), copies of this tile's FP4 stages from stage 3
-      make_desc(mb0, nb0, seq, F_AHEAD, false, d, o);
+      make_desc(mb0, nb0, kp0, seq, F_AHEAD, false, d, o);
       // (the tile's first stage: the first low-rank stage, or without the
       // slab the first FP4 stage: the launch gives this schedule at least 4
       // FP4 stages then)
@@ -570,19 +589,19 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
       // with its own second-step bases, separately)
       if constexpr (SLAB) {
         if (RS > 1) {
-          if (has) make_desc(nmb0, nnb0, seq + 1, 0, false, d, o);
-          else make_desc(mb0, nb0, seq, S - 1, true, d, o);
+          if (has) make_desc(nmb0, nnb0, nkp0, seq + 1, 0, false, d, o);
+          else make_desc(mb0, nb0, kp0, seq, S - 1, true, d, o);
           run(oa, sx, sw, G, RS - 1, d, o, ~0u, std::false_type{}, HALF, std::false_type{});
         }
         if (RS > 0) {
-          if (has) make_desc(nmb0, nnb0, seq + 1, RS - 1, false, d, o);
-          else make_desc(mb0, nb0, seq, S - 1, true, d, o);
+          if (has) make_desc(nmb0, nnb0, nkp0, seq + 1, RS - 1, false, d, o);
+          else make_desc(mb0, nb0, kp0, seq, S - 1, true, d, o);
           run(oa, sx, sw, G, 1, d, o, ~0u, std::false_type{}, HALF, std::false_type{});
         }
       }
       // D: copies of the next tile's FP4 stages
-      if (has) make_desc(nmb0, nnb0, seq + 1, RS, false, d, o);
-      else make_desc(mb0, nb0, seq, S - 1, true, d, o);
+      if (has) make_desc(nmb0, nnb0, nkp0, seq + 1, RS, false, d, o);
+      else make_desc(mb0, nb0, kp0, seq, S - 1, true, d, o);
       run(oa, sx, sw, G, F_AHEAD - RS, d, o, ~0u, std::false_type{}, HALF, std::false_type{});
     } else {
       // any shape: a descriptor per stage; the low-rank stages and the FP4
@@ -594,7 +613,8 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
         const bool c_next = cg >= S;
         const bool hs = !c_next || has;
         const int cst = !hs ? S - 1 : (c_next ? cg - S : cg);
-        make_desc(c_next && hs ? nmb0 : mb0, c_next && hs ? nnb0 : nb0, c_next && hs ? seq + 1 : seq, cst, !hs, d, o);
+        make_desc(c_next && hs ? nmb0 : mb0, c_next && hs ? nnb0 : nb0, c_next && hs ? nkp0 : kp0,
+                  c_next && hs ? seq + 1 : seq, cst, !hs, d, o);
       };
       // (the tile's first stage peeled: its MFMAs start the accumulators)
       stage_desc(0);
@@ -614,7 +634,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs g) {
         run(oa, sx, sw, G, 1, d, o, ~0u, std::false_type{}, HALF, std::false_type{});
       }
     }
-    epilogue(mb0, nb0, G - 1, HALF);
+    epilogue(mb0, nb0, kp0, G - 1, HALF);
   };
 #pragma unroll 1
   for (int seq = 0; seq < nfull; seq++) item(seq, std::false_type{});
@@ -637,6 +657,31 @@ int device_cu_count() {
   return n;
 }
 
+// K-split epilogue: Y = round(sum over the K parts, in part order, of the
+// fp32 partial planes (M x N each) + b); one thread per 4 consecutive
+// columns of a row.
+template <int OUT>
+__global__ __launch_bounds__(256) void gemm_fp4_ysum_kernel(const float* __restrict__ ypart, int kparts, int M, int N,
+                                                            const float* __restrict__ bias, void* __restrict__ Y) {
+  const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  const int n4 = N / 4;
+  const long plane = static_cast<long>(M) * N;
+  if (idx >= static_cast<long>(M) * n4) return;
+  const long row = idx / n4;
+  const int col = static_cast<int>(idx - row * n4) * 4;
+  const float* p = ypart + row * N + col;
+  f32x4 s = *reinterpret_cast<const f32x4*>(p);
+  for (int q = 1; q < kparts; q++) s += *reinterpret_cast<const f32x4*>(p + q * plane);
+  if (bias) s += *reinterpret_cast<const f32x4*>(bias + col);
+  if constexpr (OUT == SVDQ_OUT_F32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(Y) + row * N + col) = s;
+  } else {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Y) + row * N + col) =
+        u32x2{f32_to_bf16_bits(s.x) | (f32_to_bf16_bits(s.y) << 16), f32_to_bf16_bits(s.z) | (f32_to_bf16_bits(s.w) << 16)};
+  }
+}
+
 hipError_t launch_gemm_fp4(bool slab, int out_dtype, const GemmArgs& ga, hipStream_t st) {
   const int tiles_m = (ga.M + F_TILE - 1) / F_TILE, tiles_n = (ga.N + F_TILE - 1) / F_TILE;
   const int tiles = tiles_m * tiles_n;
@@ -644,12 +689,31 @@ hipError_t launch_gemm_fp4(bool slab, int out_dtype, const GemmArgs& ga, hipStre
   // the strip maps need the grid's workgroups spread evenly over the XCDs
   // (a grid that is a multiple of 8 walking all tiles)
   g.xcd_map = gemm_xcd_map(g.M, g.N, g.K, tiles_m, tiles_n);
-  // a workgroup walks several tiles only when a tile has at least 3 stages,
-  // so that the copies (3 stages ahead) never run more than one tile ahead
-  const int stages = (slab ? (g.rank / 16 + 1) / 2 : 0) + g.K / 128;
-  dim3 grid(stages >= 3 ? std::min(tiles, device_cu_count()) : tiles), block(256);
-  const bool f32 = out_dtype == SVDQ_OUT_F32;
+  // K split where the tiles leave at least half of the CUs idle: parts
+  // dividing the FP4 stages, at least 4 stages each, up to the CU count over
+  // the tiles and kFp4SplitItems items (the partial planes then fit the
+  // workspace's split section)
+  const int cus = device_cu_count(), ks_all = g.K / 128;
+  g.kparts = 1;
+  if (g.ypart && tiles <= kFp4SplitMaxTiles && 2 * tiles <= cus) {
+    int kp = std::min({kGemmMaxParts, cus / tiles, kFp4SplitItems / tiles, ks_all / 4});
+    while (kp > 1 && ks_all % kp) kp--;
+    g.kparts = std::max(1, kp);
+  }
+  const bool split = g.kparts > 1;
+  const int items = tiles * g.kparts;
+  // a workgroup walks several items only when an item has at least 3
+  // stages, so that the copies (3 stages ahead) never run more than one item
+  // ahead
   const int rs = slab ? (g.rank / 16 + 1) / 2 : 0;
+  const int stages = rs + ks_all / g.kparts;
+  dim3 grid(stages >= 3 ? std::min(items, cus) : items), block(256);
+  // the split's parts write fp32 partial planes without the bias
+  if (split) {
+    g.Y = g.ypart;
+    g.bias = nullptr;
+  }
+  const bool f32 = split || out_dtype == SVDQ_OUT_F32;
   const bool general = rs > 3 || stages < rs + 3 || (!slab && stages < 4);
 #define SVDQ_F(S, O, GEN) hipLaunchKernelGGL((gemm_fp4_kernel<S, O, GEN>), grid, block, 0, st, g)
 #define SVDQ_F2(S, O) do { if (general) SVDQ_F(S, O, true); else SVDQ_F(S, O, false); } while (0)
@@ -657,6 +721,14 @@ hipError_t launch_gemm_fp4(bool slab, int out_dtype, const GemmArgs& ga, hipStre
   else      { if (f32) SVDQ_F2(false, SVDQ_OUT_F32); else SVDQ_F2(false, SVDQ_OUT_BF16); }
 #undef SVDQ_F2
 #undef SVDQ_F
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !split) return e;
+  const long n4 = static_cast<long>(ga.M) * (ga.N / 4);
+  const dim3 rgrid(static_cast<unsigned>((n4 + 255) / 256));
+  if (out_dtype == SVDQ_OUT_F32)
+    hipLaunchKernelGGL(gemm_fp4_ysum_kernel<SVDQ_OUT_F32>, rgrid, dim3(256), 0, st, ga.ypart, g.kparts, ga.M, ga.N, ga.bias, ga.Y);
+  else
+    hipLaunchKernelGGL(gemm_fp4_ysum_kernel<SVDQ_OUT_BF16>, rgrid, dim3(256), 0, st, ga.ypart, g.kparts, ga.M, ga.N, ga.bias, ga.Y);
   return hipGetLastError();
 }
 

@@ -52,13 +52,24 @@ svdq_blob_layout layout_of(const svdq_layer_desc& d);
 // 128 x 128 output tiles number at most kGemmSplitMaxTiles (small M, where
 // the tiles alone leave most CUs idle); the workspace then holds the fp32
 // partial tiles of at most kGemmSplitItems (tile, part) items.
+// The FP4 GEMM likewise with at most kFp4SplitMaxTiles tiles of 256 x 256
+// and kFp4SplitItems items (fp32 partial M x N planes, one per part).  Both
+// fit the same 16 MiB section.
 constexpr int kGemmMaxParts = 8;
 constexpr int kGemmSplitMaxTiles = 128;
 constexpr int kGemmSplitItems = 256;
 constexpr int kGemmTile = 128;
+constexpr int kFp4SplitMaxTiles = 32;
+constexpr int kFp4SplitItems = 64;
+constexpr int kFp4Tile = 256;
+constexpr uint64_t kGemmSplitBytes = uint64_t(16) << 20;
 inline bool gemm_may_split(const svdq_layer_desc& d, int M) {
-  const long tiles = (static_cast<long>(M) + kGemmTile - 1) / kGemmTile * ((d.N + kGemmTile - 1) / kGemmTile);
-  return d.fmt == SVDQ_INT4_G64_FP16 && tiles <= kGemmSplitMaxTiles;
+  if (d.fmt == SVDQ_INT4_G64_FP16) {
+    const long tiles = (static_cast<long>(M) + kGemmTile - 1) / kGemmTile * ((d.N + kGemmTile - 1) / kGemmTile);
+    return tiles <= kGemmSplitMaxTiles;
+  }
+  const long tiles = (static_cast<long>(M) + kFp4Tile - 1) / kFp4Tile * ((d.N + kFp4Tile - 1) / kFp4Tile);
+  return tiles <= kFp4SplitMaxTiles;
 }
 
 struct ActLayout {

@@ -83,7 +83,7 @@ ActLayout act_layout(const svdq_layer_desc& d, int M) {
   // split-K INT4 GEMM (few output tiles): the fp32 partial tiles
   A.ypart = off;
   A.required = off;
-  if (gemm_may_split(d, M)) off = align256(off + uint64_t(kGemmSplitItems) * kGemmTile * kGemmTile * 4);
+  if (gemm_may_split(d, M)) off = align256(off + kGemmSplitBytes);
   A.total = off;
   return A;
 }
